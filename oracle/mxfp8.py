@@ -1,0 +1,143 @@
+"""fp8-aware oracle for the MXFP8 forward variant.
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check, benchmark CPU baseline).
+
+[P2] (ai.warp-studio.com, section on the TE mechanisms) names a group-aware
+MXFP8 grouped GEMM for the expert matmuls; [P3 §13.6] asks for per-tile
+rather than per-tensor scales and fp32 accumulation. The pages give no
+bit-level rule, so this follows the public OCP Microscaling (MX) v1.0 format:
+
+  * blocks of 32 consecutive elements along each GEMM's contraction
+    dimension share one E8M0 scale 2^X;
+  * X = floor(log2(amax)) - 8, where 8 is the largest exponent of E4M3,
+    clamped to [-127, 127]; the stored scale code is X + 127;
+  * each element is v / 2^X rounded to the nearest E4M3 value (ties to an
+    even mantissa) and saturated to +-448; an all-zero block gets code 0.
+
+Both operands of all three expert GEMMs are quantised: x and W1/W3 along
+d_model, h and W2 along d_ff. Products are then taken in fp64 on the
+dequantised values.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import torch
+
+from .moe_oracle import _f64, _token_subset, swiglu
+
+F64 = torch.float64
+E4M3_MAX = 448.0
+E4M3_EMAX = 8
+BLOCK = 32
+
+
+def e4m3_values() -> torch.Tensor:
+    """Value of each of the 256 E4M3 (e4m3fn) codes from the format's
+    definition: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits;
+    exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; there
+    is no infinity."""
+    vals = []
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            vals.append(float("nan"))
+        elif e == 0:
+            vals.append(s * (m / 8.0) * 2.0 ** -6)
+        else:
+            vals.append(s * (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return torch.tensor(vals, dtype=F64)
+
+
+def e4m3_round(v: torch.Tensor) -> torch.Tensor:
+    """Nearest E4M3 value to each element (fp64 in, fp64 out), ties to an
+    even mantissa, saturating to +-448. In the binade [2^e, 2^(e+1)) the
+    E4M3 spacing is 2^(e-3); below 2^-6 it is the subnormal step 2^-9."""
+    v = _f64(v)
+    a = v.abs()
+    _, ex = torch.frexp(a)               # a = m * 2^ex, m in [0.5, 1)
+    e = torch.clamp(ex.to(F64) - 1.0, min=-6.0)
+    q = torch.pow(2.0, e - 3.0)
+    r = torch.round(a / q) * q           # torch.round: half to even
+    r = torch.clamp(r, max=E4M3_MAX)
+    r = torch.where(a == 0, torch.zeros_like(r), r)
+    return torch.copysign(r, v)
+
+
+def _block_view(v: torch.Tensor, block: int):
+    if v.shape[-1] % block:
+        raise ValueError("last dimension must be a multiple of the block")
+    return v.reshape(*v.shape[:-1], v.shape[-1] // block, block)
+
+
+def mx_quantize(v: torch.Tensor, block: int = BLOCK):
+    """Quantise along the last dimension. Returns (q, codes): q are the
+    E4M3 element values (fp64, on the E4M3 grid) with the same shape as v;
+    codes are the uint8 E8M0 scale codes, one per block."""
+    vb = _block_view(_f64(v), block)
+    amax = vb.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)
+    X = torch.where(amax > 0, ex.to(F64) - 1.0 - E4M3_EMAX,
+                    torch.full_like(amax, -127.0))
+    X = torch.clamp(X, -127.0, 127.0)
+    q = e4m3_round(vb / torch.pow(2.0, X).unsqueeze(-1))
+    codes = (X + 127.0).to(torch.uint8)
+    return q.reshape(v.shape), codes
+
+
+def mx_dequantize(q: torch.Tensor, codes: torch.Tensor,
+                  block: int = BLOCK) -> torch.Tensor:
+    """q * 2^(code - 127) per block, fp64."""
+    qb = _block_view(_f64(q), block)
+    scale = torch.pow(2.0, codes.to(F64) - 127.0)
+    return (qb * scale.unsqueeze(-1)).reshape(q.shape)
+
+
+def mx_roundtrip(v: torch.Tensor, block: int = BLOCK) -> torch.Tensor:
+    """Quantise then dequantise along the last dimension."""
+    q, c = mx_quantize(v, block)
+    return mx_dequantize(q, c, block)
+
+
+def forward_mxfp8(x, w1, w3, w2, idx, w, ws1=None, ws3=None, ws2=None,
+                  tokens: Optional[Sequence[int]] = None,
+                  weight_cache: Optional[dict] = None) -> torch.Tensor:
+    """The [P3 §9] per-expert layer with every expert GEMM operand MX
+    quantised: x and W1/W3 along d_model, h and W2 along d_ff. h is
+    quantised from its fp64 value. Gate weights and the combine stay in
+    fp64. ``weight_cache`` (a dict) keeps dequantised weights between
+    calls."""
+    cache = {} if weight_cache is None else weight_cache
+
+    def wq(name, e, t):
+        key = (name, e)
+        if key not in cache:
+            cache[key] = mx_roundtrip(t)
+        return cache[key]
+
+    def ffn(X, W1, W3, W2):
+        a = X @ W1.T
+        b = X @ W3.T
+        h = mx_roundtrip(swiglu(a, b))
+        return h @ W2.T
+
+    sel = _token_subset(x.shape[0], tokens)
+    xq = mx_roundtrip(_f64(x[sel]))
+    idx_s = idx[sel]
+    w_s = _f64(w[sel])
+    out = torch.zeros(xq.shape, dtype=F64)
+    for e in range(w1.shape[0]):
+        mask = idx_s == e
+        if not bool(mask.any()):
+            continue
+        rows, ks = mask.nonzero(as_tuple=True)
+        Y = ffn(xq[rows], wq("w1", e, w1[e]), wq("w3", e, w3[e]),
+                wq("w2", e, w2[e]))
+        out.index_add_(0, rows, Y * w_s[rows, ks].unsqueeze(-1))
+    if ws1 is not None:
+        out += ffn(xq, wq("ws1", -1, ws1), wq("ws3", -1, ws3),
+                   wq("ws2", -1, ws2))
+    return out

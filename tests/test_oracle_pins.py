@@ -1,0 +1,410 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix:
+brute force on tiny inputs, closed forms, special cases that reduce to
+library routines, invariants, and hand-worked examples. CPU only."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import moe_inputs as mi
+
+F64 = torch.float64
+
+
+def _rand_layer(T, d, f, E, K, seed=0, shared=0, gate="softmax", bias=False):
+    cfg = mi.MoEConfig("t", T, d, f, E, K, f_shared=shared, gate=gate,
+                       dtype="f32", bias=bias)
+    inp = mi.make_inputs(cfg, seed)
+    logits = inp["x"].float() @ inp["wr"].float().T
+    idx, w = oracle.route(logits, K, gate, inp["bias"])
+    return cfg, inp, logits, idx, w
+
+
+# --------------------------------------------------------------- selection
+def _subset_definition(keys_row, K):
+    """The unique K-subset S such that every member beats every non-member
+    under (key desc, id asc); found by trying every subset."""
+    E = len(keys_row)
+    wins = []
+    for S in itertools.combinations(range(E), K):
+        rest = [u for u in range(E) if u not in S]
+        ok = all(keys_row[s] > keys_row[u] or
+                 (keys_row[s] == keys_row[u] and s < u)
+                 for s in S for u in rest)
+        if ok:
+            wins.append(S)
+    assert len(wins) == 1
+    return set(wins[0])
+
+
+@pytest.mark.parametrize("E,K", [(1, 1), (3, 1), (5, 2), (6, 3), (7, 7), (7, 4)])
+def test_topk_matches_subset_bruteforce(E, K):
+    logits = torch.cat([mi.tie_logits(20, E),
+                        torch.randn(20, E, generator=torch.Generator().manual_seed(E))])
+    keys = oracle.selection_keys(logits)
+    idx = oracle.topk_select(keys, K)
+    for t in range(logits.shape[0]):
+        row = keys[t].tolist()
+        assert set(idx[t].tolist()) == _subset_definition(row, K)
+        sel = idx[t].tolist()
+        for a, b in zip(sel, sel[1:]):          # rank order of the K outputs
+            assert row[a] > row[b] or (row[a] == row[b] and a < b)
+
+
+def test_topk_with_bias_matches_bruteforce():
+    g = torch.Generator().manual_seed(3)
+    logits = torch.randn(30, 6, generator=g)
+    bias = (torch.rand(6, generator=g) - 0.5) * 0.4
+    keys = oracle.selection_keys(logits, bias)
+    idx = oracle.topk_select(keys, 2)
+    ref = (logits + bias).tolist()               # fp32 sums, as on the device
+    for t in range(30):
+        assert set(idx[t].tolist()) == _subset_definition(ref[t], 2)
+
+
+@pytest.mark.parametrize("gate", ["softmax", "sigmoid"])
+def test_all_equal_logits(gate):
+    logits = torch.full((4, 8), 0.3)
+    idx, w = oracle.route(logits, 3, gate)
+    assert idx.tolist() == [[0, 1, 2]] * 4
+    assert torch.allclose(w, torch.full((4, 3), 1 / 3, dtype=F64), rtol=0, atol=1e-15)
+
+
+def test_k_equals_e_and_single_expert():
+    logits = torch.tensor([[0.5, -1.0, 2.0, 0.5]])
+    idx, w = oracle.route(logits, 4, "softmax")
+    assert idx.tolist() == [[2, 0, 3, 1]]
+    ref = torch.softmax(logits.double(), dim=1)[0, [2, 0, 3, 1]]
+    assert torch.allclose(w[0], ref, rtol=1e-15, atol=0)
+    idx, w = oracle.route(torch.tensor([[1.7], [-3.0]]), 1, "sigmoid")
+    assert idx.tolist() == [[0], [0]] and w.tolist() == [[1.0], [1.0]]
+
+
+def test_bias_flips_selection_but_not_weights():
+    # selection on logits + bias, weights from raw sigmoid (P3 §6.3)
+    logits = torch.tensor([[0.0, 0.05]])
+    bias = torch.tensor([0.1, -0.1])
+    idx, w = oracle.route(logits, 1, "sigmoid", bias)
+    assert idx.tolist() == [[0]] and w.tolist() == [[1.0]]
+    idx, w = oracle.route(logits, 2, "sigmoid", bias)
+    assert idx.tolist() == [[0, 1]]
+    s0, s1 = 1 / (1 + math.exp(-0.0)), 1 / (1 + math.exp(-float(np.float32(0.05))))
+    assert abs(float(w[0, 0]) - s0 / (s0 + s1)) < 1e-15
+
+
+def test_signed_zero_tie_and_nan():
+    idx, _ = oracle.route(torch.tensor([[-0.0, 0.0], [0.0, -0.0]]), 1, "softmax")
+    assert idx.tolist() == [[0], [0]]
+    idx, _ = oracle.route(torch.tensor([[float("nan"), 1.0, -5.0]]), 2, "softmax")
+    assert idx.tolist() == [[1, 2]]
+
+
+def test_hand_worked_example():
+    # logits [1, 2, 0], top-2: experts 2nd then 1st; softmax weights
+    # e^2/(e^2+e) = e/(e+1) and 1/(e+1); sigmoid weights s(2)/(s(2)+s(1)).
+    logits = torch.tensor([[1.0, 2.0, 0.0]])
+    idx, w = oracle.route(logits, 2, "softmax")
+    assert idx.tolist() == [[1, 0]]
+    e = math.e
+    assert abs(float(w[0, 0]) - e / (e + 1)) < 1e-15
+    assert abs(float(w[0, 1]) - 1 / (e + 1)) < 1e-15
+    idx, w = oracle.route(logits, 2, "sigmoid")
+    s2, s1 = 1 / (1 + math.exp(-2)), 1 / (1 + math.exp(-1))
+    assert abs(float(w[0, 0]) - s2 / (s1 + s2)) < 1e-15
+
+
+@pytest.mark.parametrize("gate", ["softmax", "sigmoid"])
+def test_weights_closed_forms(gate):
+    g = torch.Generator().manual_seed(7)
+    logits = torch.randn(64, 16, generator=g) * 3
+    idx, w = oracle.route(logits, 4, gate)
+    assert torch.allclose(w.sum(1), torch.ones(64, dtype=F64), rtol=0, atol=1e-12)
+    L = logits.double()
+    full = torch.softmax(L, 1) if gate == "softmax" else torch.sigmoid(L)
+    sel = torch.gather(full, 1, idx)
+    assert torch.allclose(w, sel / sel.sum(1, keepdim=True), rtol=1e-14, atol=0)
+
+
+# ------------------------------------------------------------- permutation
+def test_permutation_invariants_and_library_sort():
+    cfg, inp, logits, idx, w = _rand_layer(97, 16, 8, 11, 3, seed=1)
+    E, TK = 11, 97 * 3
+    counts, offsets, src, dest = oracle.permute(idx, E)
+    flat = idx.reshape(-1)
+    assert counts.tolist() == torch.bincount(flat, minlength=E).tolist()
+    assert int(counts.sum()) == TK and int(offsets[-1]) == TK
+    assert sorted(src.tolist()) == list(range(TK))
+    assert (dest[src] == torch.arange(TK)).all()
+    assert (src == torch.sort(flat, stable=True).indices).all()
+    for e in range(E):
+        grp = src[offsets[e]:offsets[e + 1]]
+        assert (flat[grp] == e).all()
+        assert (grp[1:] > grp[:-1]).all()
+
+
+def test_zipf_synthesis_realises_designed_loads():
+    T, E, K = 2048, 128, 8
+    logits, loads = mi.synth_logits(T, E, K, 10, 1.2, 0)
+    idx, w = oracle.route(logits, K, "softmax")
+    counts, offsets, _, _ = oracle.permute(idx, E)
+    assert counts.tolist() == loads.tolist()
+    assert int((counts == 0).sum()) == 10 and int(counts.max()) <= T
+    # at the full skewed shape the two largest experts hit the cap T
+    full = mi.zipf_loads(16384, 128, 8, 10, 1.2, 0)
+    assert sorted(full.tolist())[-2:] == [16384, 16384] and full.sum() == 131072
+
+
+# ------------------------------------------------------------------ experts
+def test_single_expert_is_textbook_swiglu():
+    cfg, inp, logits, idx, w = _rand_layer(33, 24, 40, 1, 1, seed=2)
+    out = oracle.forward(inp["x"], inp["w1"], inp["w3"], inp["w2"], idx, w)
+    x = inp["x"].double()
+    ref = (F.silu(x @ inp["w1"][0].double().T) * (x @ inp["w3"][0].double().T)) \
+        @ inp["w2"][0].double().T
+    assert torch.allclose(out, ref, rtol=0, atol=1e-12 * ref.abs().max())
+
+
+@pytest.mark.parametrize("shape", [(13, 8, 16, 5, 2, 0, "softmax"),
+                                   (9, 16, 8, 6, 3, 12, "sigmoid"),
+                                   (20, 8, 8, 7, 7, 0, "softmax")])
+def test_three_formulations_agree(shape):
+    T, d, f, E, K, fs, gate = shape
+    cfg, inp, logits, idx, w = _rand_layer(T, d, f, E, K, seed=4, shared=fs, gate=gate)
+    args = (inp["x"], inp["w1"], inp["w3"], inp["w2"], idx, w,
+            inp["ws1"], inp["ws3"], inp["ws2"])
+    a = oracle.forward(*args)
+    b = oracle.forward_gather(*args)
+    c = oracle.dense_masked_forward(*args)
+    scale = a.abs().max()
+    assert (a - b).abs().max() <= 1e-12 * scale
+    assert (a - c).abs().max() <= 1e-12 * scale
+    # token subsets give the same rows
+    sub = [0, T // 2, T - 1]
+    assert torch.equal(oracle.forward(*args, tokens=sub), a[sub]) or \
+        (oracle.forward(*args, tokens=sub) - a[sub]).abs().max() <= 1e-13 * scale
+
+
+def test_empty_expert_and_stage_composition():
+    T, d, f, E, K = 16, 8, 12, 6, 2
+    cfg, inp, logits, idx, w = _rand_layer(T, d, f, E, K, seed=5)
+    idx = torch.where(idx == 3, torch.full_like(idx, 4), idx)  # expert 3 empty
+    idx[:, 1] = torch.where(idx[:, 1] == idx[:, 0], (idx[:, 0] + 1) % E, idx[:, 1])
+    idx = torch.where(idx == 3, torch.full_like(idx, 5), idx)
+    assert (idx[:, 0] != idx[:, 1]).all() and not (idx == 3).any()
+    counts, offsets, src, dest = oracle.permute(idx, E)
+    assert counts[3] == 0
+    x_perm = inp["x"][src // K]
+    _, _, h = oracle.stage_gemm1(x_perm, offsets, inp["w1"], inp["w3"])
+    y = oracle.stage_gemm2(h, offsets, inp["w2"])
+    out = oracle.stage_combine(y, dest, w)
+    ref = oracle.forward(inp["x"], inp["w1"], inp["w3"], inp["w2"], idx, w)
+    assert (out - ref).abs().max() <= 1e-12 * ref.abs().max()
+
+
+def test_combine_k1_w1_is_inverse_permutation():
+    T, d = 10, 4
+    y = torch.randn(T, d).to(torch.bfloat16)
+    dest = torch.randperm(T, generator=torch.Generator().manual_seed(0))
+    out = oracle.stage_combine(y, dest, torch.ones(T, 1))
+    assert torch.equal(out, y[dest].double())
+
+
+# ----------------------------------------------------------------- backward
+def _loss(inp, idx, w, dy, **over):
+    args = dict(x=inp["x"], w1=inp["w1"], w3=inp["w3"], w2=inp["w2"])
+    args.update(over)
+    out = oracle.forward(args["x"], args["w1"], args["w3"], args["w2"], idx, w,
+                         inp["ws1"], inp["ws3"], inp["ws2"])
+    return float((out * dy.double()).sum())
+
+
+@pytest.mark.parametrize("shared", [0, 6])
+def test_backward_matches_finite_differences(shared):
+    T, d, f, E, K = 7, 5, 6, 4, 2
+    cfg, inp, logits, idx, w = _rand_layer(T, d, f, E, K, seed=6, shared=shared)
+    for k in ("x", "w1", "w3", "w2", "ws1", "ws3", "ws2"):
+        if inp[k] is not None:
+            inp[k] = inp[k].double()
+    dy = torch.randn(T, d, generator=torch.Generator().manual_seed(9), dtype=F64)
+    g = oracle.backward(inp["x"], inp["w1"], inp["w3"], inp["w2"], idx, w, dy,
+                        inp["ws1"], inp["ws3"], inp["ws2"])
+    eps = 1e-6
+    rng = np.random.default_rng(0)
+    for name, key in [("x", "dx"), ("w1", "dw1"), ("w3", "dw3"), ("w2", "dw2")]:
+        base = inp[name]
+        for _ in range(6):
+            pos = tuple(int(rng.integers(0, s)) for s in base.shape)
+            p, m = base.clone(), base.clone()
+            p[pos] += eps
+            m[pos] -= eps
+            fd = (_loss(inp, idx, w, dy, **{name: p}) -
+                  _loss(inp, idx, w, dy, **{name: m})) / (2 * eps)
+            assert abs(fd - float(g[key][pos])) <= 1e-6 * (1 + abs(fd)), (name, pos)
+    for _ in range(4):
+        t, k = int(rng.integers(0, T)), int(rng.integers(0, K))
+        p, m = w.clone(), w.clone()
+        p[t, k] += eps
+        m[t, k] -= eps
+        fd = (_loss(inp, idx, p, dy) - _loss(inp, idx, m, dy)) / (2 * eps)
+        assert abs(fd - float(g["d_w"][t, k])) <= 1e-6 * (1 + abs(fd))
+    if shared:
+        for name, key in [("ws1", "dws1"), ("ws3", "dws3"), ("ws2", "dws2")]:
+            base = inp[name]
+            pos = tuple(int(rng.integers(0, s)) for s in base.shape)
+            p, m = base.clone(), base.clone()
+            p[pos] += eps
+            m[pos] -= eps
+            i2 = dict(inp)
+            i2[name] = p
+            lp = _loss(i2, idx, w, dy)
+            i2[name] = m
+            lm = _loss(i2, idx, w, dy)
+            assert abs((lp - lm) / (2 * eps) - float(g[key][pos])) <= 1e-6
+
+
+def test_backward_matches_autograd_dense():
+    """Autograd through a dense masked layer built from library ops."""
+    T, d, f, E, K = 9, 6, 10, 5, 2
+    cfg, inp, logits, idx, w = _rand_layer(T, d, f, E, K, seed=8)
+    x = inp["x"].double().requires_grad_()
+    W1 = inp["w1"].double().requires_grad_()
+    W3 = inp["w3"].double().requires_grad_()
+    W2 = inp["w2"].double().requires_grad_()
+    wl = w.clone().requires_grad_()
+    G = torch.zeros(T, E, dtype=F64).scatter(1, idx, wl)
+    h = F.silu(torch.einsum("td,efd->tef", x, W1)) * torch.einsum("td,efd->tef", x, W3)
+    out = torch.einsum("tef,edf,te->td", h, W2, G)
+    dy = torch.randn(T, d, generator=torch.Generator().manual_seed(1), dtype=F64)
+    out.backward(dy)
+    g = oracle.backward(inp["x"], inp["w1"], inp["w3"], inp["w2"], idx, w, dy)
+    for a, b in [(x.grad, g["dx"]), (W1.grad, g["dw1"]), (W3.grad, g["dw3"]),
+                 (W2.grad, g["dw2"]), (wl.grad, g["d_w"])]:
+        assert (a - b).abs().max() <= 1e-12 * (1 + b.abs().max())
+
+
+def test_backward_sampled_equals_full():
+    T, d, f, E, K = 24, 8, 16, 6, 2
+    cfg, inp, logits, idx, w = _rand_layer(T, d, f, E, K, seed=10, shared=8)
+    dy = torch.randn(T, d, generator=torch.Generator().manual_seed(2))
+    args = (inp["x"], inp["w1"], inp["w3"], inp["w2"], idx, w, dy)
+    sh = (inp["ws1"], inp["ws3"], inp["ws2"])
+    full = oracle.backward(*args, *sh)
+    toks = [0, 5, 23]
+    cols = [(0, 0), (2, 7), (5, 15)]
+    s = oracle.backward_sampled(*args, toks, cols, *sh)
+    assert (s["dx"] - full["dx"][toks]).abs().max() <= 1e-12
+    assert (s["d_w"] - full["d_w"][toks]).abs().max() <= 1e-12
+    for i, (e, j) in enumerate(cols):
+        assert (s["dw1_rows"][i] - full["dw1"][e, j]).abs().max() <= 1e-12
+        assert (s["dw3_rows"][i] - full["dw3"][e, j]).abs().max() <= 1e-12
+        assert (s["dw2_cols"][i] - full["dw2"][e, :, j]).abs().max() <= 1e-12
+
+
+# -------------------------------------------------------------------- mxfp8
+def test_e4m3_code_table():
+    v = oracle.e4m3_values()
+    fin = v[~torch.isnan(v)]
+    assert fin.numel() == 254 and float(fin.max()) == 448.0
+    assert float(fin[fin > 0].min()) == 2.0 ** -9
+    assert torch.unique(fin).numel() == 253      # +0 and -0 coincide
+    # the format's own table agrees with torch's e4m3fn decoding
+    codes = torch.arange(256, dtype=torch.uint8)
+    tv = codes.view(torch.float8_e4m3fn).to(F64)
+    both_nan = torch.isnan(tv) & torch.isnan(v)
+    assert (both_nan | (tv == v)).all()
+
+
+def test_e4m3_round_identity_ties_and_library_cast():
+    v = oracle.e4m3_values()
+    fin = v[~torch.isnan(v)]
+    assert torch.equal(oracle.e4m3_round(fin), fin)
+    # midpoints between neighbours go to the even mantissa
+    assert float(oracle.e4m3_round(torch.tensor([1.0625]))) == 1.0
+    assert float(oracle.e4m3_round(torch.tensor([1.1875]))) == 1.25
+    assert float(oracle.e4m3_round(torch.tensor([500.0]))) == 448.0
+    assert float(oracle.e4m3_round(torch.tensor([-464.0]))) == -448.0
+    # against the library cast (RNE, non-saturating) after clamping to 448
+    g = torch.Generator().manual_seed(0)
+    r = torch.cat([torch.randn(20000, generator=g, dtype=F64) * s
+                   for s in (1e-3, 0.1, 1, 30, 300)])
+    mids = ((torch.sort(torch.unique(fin)).values[1:] +
+             torch.sort(torch.unique(fin)).values[:-1]) / 2)
+    r = torch.cat([r, mids, -mids])
+    lib = r.clamp(-448, 448).to(torch.float8_e4m3fn).to(F64)
+    assert torch.equal(oracle.e4m3_round(r).abs(), lib.abs())
+
+
+def test_mx_block_rule():
+    # amax 3 -> X = floor(log2 3) - 8 = -7, 3 * 2^7 = 384 is exact in E4M3
+    v = torch.full((1, 32), 3.0, dtype=F64)
+    q, c = oracle.mx_quantize(v)
+    assert int(c[0, 0]) == 127 - 7 and torch.equal(q, torch.full_like(v, 384.0))
+    assert torch.equal(oracle.mx_dequantize(q, c), v)
+    # an all-zero block gets scale code 0 and zero elements
+    q, c = oracle.mx_quantize(torch.zeros(2, 64, dtype=F64))
+    assert c.tolist() == [[0, 0], [0, 0]] and (q == 0).all()
+    # blocks made of E4M3 values times a power of two quantise exactly
+    vals = oracle.e4m3_values()
+    fin = vals[~torch.isnan(vals)]
+    g = torch.Generator().manual_seed(1)
+    for X in (-20, -3, 0, 5):
+        blk = fin[torch.randint(0, fin.numel(), (4, 32), generator=g)]
+        blk[:, 0] = 448.0                        # amax in [256, 512)
+        v = blk * 2.0 ** X
+        q, c = oracle.mx_quantize(v)
+        assert (c == 127 + X).all()
+        assert torch.equal(oracle.mx_dequantize(q, c), v)
+    # error bound of one quantisation: with X = floor(log2 amax) - 8 the
+    # scaled block max lies in [256, 512); elements whose scaled value is at
+    # most 448 round with error <= |v| 2^-4 (normal) or 2^(X-10)
+    # (subnormal); larger ones saturate to 448 * 2^X, an error below amax/8
+    v = torch.randn(64, 256, generator=g, dtype=F64)
+    rt = oracle.mx_roundtrip(v).reshape(64, 8, 32)
+    blocks = v.reshape(64, 8, 32)
+    amax = blocks.abs().amax(-1, keepdim=True)
+    _, ex = torch.frexp(amax)
+    scale = torch.pow(2.0, ex.double() - 1 - 8)
+    err = (rt - blocks).abs()
+    inrange = blocks.abs() <= 448 * scale
+    assert (err[inrange] <= (blocks.abs() * 2.0 ** -4 + scale * 2.0 ** -10)[inrange]).all()
+    assert (err[~inrange] == (blocks.abs() - 448 * scale)[~inrange]).all()
+    assert (err <= amax / 8).all() and (~inrange).any()
+
+
+def test_mxfp8_forward_close_to_exact():
+    cfg, inp, logits, idx, w = _rand_layer(40, 64, 96, 4, 2, seed=11)
+    exact = oracle.forward(inp["x"], inp["w1"], inp["w3"], inp["w2"], idx, w)
+    q = oracle.forward_mxfp8(inp["x"], inp["w1"], inp["w3"], inp["w2"], idx, w)
+    rel = (q - exact).abs().max() / exact.abs().max()
+    assert 1e-4 < float(rel) < 0.2
+
+
+# --------------------------------------------------------------- accounting
+def test_accounting_against_page_figures():
+    import json
+    import os
+    from ragged_grouped_gemm_router_amd import accounting as acc
+    p = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
+    g = json.load(open(p))
+    c = g["comm_bytes_per_token_layer"]
+    b = acc.comm_bytes_per_token(c["K"], c["D"], c["bytes_per_elem"])
+    assert round(b / 1000) == c["printed_kB"]
+    v = g["v3_training_flops"]
+    fl = acc.training_flops_6nt(v["N_act"], v["T"])
+    assert abs(fl / v["printed"] - 1) < 0.01
+    h = g["v3_gpu_hours"]
+    hours = h["flops"] / (h["effective_tflops"] * 1e12 * 3600)
+    assert abs(hours / h["printed_hours"] - 1) < 0.01
+    a = g["v3_active_fraction"]
+    assert round(100 * a["active"] / a["total"], 1) == a["printed_pct"]
+    cb = g["fine_grained_combinations"]
+    assert math.comb(8, 2) == cb["n8_k2_printed"]
+    # the printed ~4e11 for C(256, 8) is wrong by 10^3 (it is ~4.1e14): not a pin
+    assert 4.0e14 < math.comb(256, 8) < 4.2e14
+    # a SwiGLU expert is three d x f matrices, so 6 d f flops per copy
+    assert acc.routed_fwd_flops(4096, 14336, 16384) == 5_772_436_045_824
+    assert acc.train_flops(acc.routed_fwd_flops(1, 1, 1)) == 18
