@@ -1,0 +1,214 @@
+"""Benchmark of the dropless MoE layer forward on one MI355X.
+
+A step is one whole forward of the layer (router GEMM, top-K gate,
+histogram/scan/permute, grouped SwiGLU GEMM 1, grouped GEMM 2, combine) on
+one batch of seeded synthetic input already resident in HBM. Three input
+batches rotate so no step reuses the previous step's activations from the
+last-level cache. The default workload is the Mixtral-8x7B-shaped layer
+(T=8192, d_model=4096, d_ff=14336, E=8, top-2 softmax, bf16).
+
+Prints ONE JSON line. Per-stage times come from HIP events the library
+records on the launch stream between its kernels; the roofline object
+reports the dominant kernel (grouped GEMM 1 + SwiGLU) against the bf16
+MFMA peak; the CPU baseline times the fp64 oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MoE layer fwd TFLOP/s (routed FLOPs) + % bf16 MFMA peak; "
+          "permute GB/s")
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (recorded by the library on its stream)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")  # the copy torch already loaded
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [
+            ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e.value)
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        st = self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a],
+                                          self.ev[b])
+        assert st == 0, st
+        return out.value
+
+
+def workload(name):
+    import moe_inputs as mi
+    table = {"mixtral": mi.MIXTRAL, "deepseek": mi.DEEPSEEK_V3,
+             "skewed": mi.SKEWED, "tiny": mi.TINY_FP32}
+    return table[name]
+
+
+def cpu_baseline(cfg, ginp, logits_gpu, n_tokens):
+    """Time the fp64 oracle forward (weight upcast included) on the first
+    n_tokens tokens, on the host cores. D2H copies happen before timing."""
+    import torch
+    import oracle
+    threads = min(len(os.sched_getaffinity(0)),
+                  int(os.environ.get("OMP_NUM_THREADS", "16")))
+    torch.set_num_threads(threads)
+    toks = list(range(n_tokens))
+    c = {k: (v.cpu() if isinstance(v, torch.Tensor) else v)
+         for k, v in ginp.items() if k in ("x", "w1", "w3", "w2", "bias",
+                                           "ws1", "ws3", "ws2")}
+    logits = (ginp["logits_in"] if ginp.get("logits_in") is not None
+              else logits_gpu)[:n_tokens].cpu()
+    t0 = time.perf_counter()
+    idx, w = oracle.route(logits, cfg.K, cfg.gate, c.get("bias"))
+    oracle.forward(c["x"][:n_tokens], c["w1"], c["w3"], c["w2"], idx, w,
+                   c.get("ws1"), c.get("ws3"), c.get("ws2"), tokens=toks)
+    dt = time.perf_counter() - t0
+    from ragged_grouped_gemm_router_amd import accounting as acc
+    flops = acc.routed_fwd_flops(cfg.d, cfg.f, n_tokens * cfg.K)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"first {n_tokens} tokens ({n_tokens * cfg.K} routed "
+                       f"copies) of {cfg.name}; fp64 torch CPU per-expert "
+                       f"loop incl. weight upcast; {dt:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral",
+                    choices=["mixtral", "deepseek", "skewed", "tiny"])
+    ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} "
+              "is not supported (the layer does not shard across GPUs here)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_inputs as mi
+    from ragged_grouped_gemm_router_amd import accounting as acc
+    from ragged_grouped_gemm_router_amd import binding as B
+    from ragged_grouped_gemm_router_amd import layer as L
+
+    cfg = workload(args.workload)
+    dev = "cuda"
+    log(f"bench: workload {cfg.name}")
+    base = mi.make_inputs(cfg, 0, device=dev)
+    batches = [base]
+    for s in (1, 2):
+        b = dict(base)
+        b["x"] = mi.randn((cfg.T, cfg.d), 1.0, s, "x", cfg.torch_dtype, dev)
+        if cfg.synth_logits:
+            lg, _ = mi.synth_logits(cfg.T, cfg.E, cfg.K, cfg.n_zero,
+                                    cfg.zipf_s, s)
+            b["logits_in"] = lg.to(dev)
+        batches.append(b)
+    desc = B.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.K, cfg.f_shared,
+                       cfg.gate, cfg.dtype)
+    bufs = [L.alloc_forward(desc, dev) for _ in batches]
+    n_steps = args.warmup + args.steps
+    ev = HipEvents(B.MOE_FWD_NEVENTS * max(args.steps, 1))
+    stream = torch.cuda.current_stream()
+
+    log("bench: warmup")
+    for i in range(args.warmup):
+        L.forward(desc, batches[i % 3], bufs[i % 3])
+    torch.cuda.synchronize()
+    log("bench: timed steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev.ev[i * B.MOE_FWD_NEVENTS:(i + 1) * B.MOE_FWD_NEVENTS]
+        L.forward(desc, batches[i % 3], bufs[i % 3], events=e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / max(args.steps, 1) * 1e3
+    log(f"bench: {ms_step:.3f} ms/step")
+
+    n = B.MOE_FWD_NEVENTS
+    stage = {"route": 0.0, "permute": 0.0, "gemm1_swiglu": 0.0,
+             "gemm2_shared": 0.0, "combine": 0.0}
+    for i in range(args.steps):
+        o = i * n
+        stage["route"] += ev.ms(o + 0, o + 1)
+        stage["permute"] += ev.ms(o + 1, o + 2)
+        stage["gemm1_swiglu"] += ev.ms(o + 2, o + 3)
+        stage["gemm2_shared"] += ev.ms(o + 3, o + 4)
+        stage["combine"] += ev.ms(o + 4, o + 5)
+    stage = {k: v / args.steps for k, v in stage.items()}
+
+    TK = cfg.TK
+    b = 4 if cfg.dtype == "f32" else 2
+    routed = acc.routed_fwd_flops(cfg.d, cfg.f, TK)
+    g1 = acc.gemm1_flops(cfg.d, cfg.f, TK)
+    value = routed / (ms_step * 1e-3) / 1e12
+    gemm_s = (stage["gemm1_swiglu"] + stage["gemm2_shared"]) * 1e-3
+    perm_bytes = acc.permute_bytes(cfg.T, cfg.K, cfg.d, b)
+    comb_bytes = acc.combine_bytes(cfg.T, cfg.K, cfg.d, b, cfg.f_shared > 0)
+    k5_tflops = g1 / (stage["gemm1_swiglu"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
+        "data": "synthetic: seeded N(0,1) tokens, N(0,1/fan_in) random-init "
+                "weights" + (", Zipf-synthesised router logits"
+                             if cfg.synth_logits else ""),
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d,
+                   "d_ff": cfg.f, "E": cfg.E, "K": cfg.K,
+                   "d_ff_shared": cfg.f_shared, "gate": cfg.gate,
+                   "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "grouped_gemm_tflops": round(routed / gemm_s / 1e12, 2),
+        "permute_GBps": round(perm_bytes / (stage["permute"] * 1e-3) / 1e9, 1),
+        "combine_GBps": round(comb_bytes / (stage["combine"] * 1e-3) / 1e9, 1),
+        "stages_ms": {k: round(v, 4) for k, v in stage.items()},
+        "roofline": {
+            "kernel": "grouped GEMM 1 + SwiGLU (mfma_gemm, dual B)",
+            "bound": "mfma",
+            "achieved": round(k5_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(k5_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(cfg, base, bufs[0]["logits"],
+                                            args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,256 @@
+/*
+ * moe.h - C ABI of a dropless Mixture-of-Experts expert layer for one AMD
+ * Instinct MI355X (gfx950): router, top-K gating, expert histogram and
+ * stable permutation, ragged grouped SwiGLU GEMMs on MFMA, gate-weighted
+ * combine, optional shared expert, backward pass, and an MXFP8 forward.
+ *
+ * Pages cited:
+ *   [P1] kongchang.com, "JAX中加速Dropless MoE训练：NVIDIA Transformer
+ *        Engine解析", section "Dropless MoE：解决 token 丢弃问题" (every token
+ *        copy reaches its experts; no capacity, no drops) and section
+ *        "高效的分组矩阵运算" (grouped GEMM over ragged groups, no padding).
+ *   [P2] ai.warp-studio.com, "JAXにおけるDropless MoE訓練をNVIDIA Transformer
+ *        Engineで劇的に加速する技術分析", section on the TE mechanisms
+ *        (grouped GEMM in one call over ragged experts; group-aware MXFP8;
+ *        shapes that stay on the device so graphs need no host shapes).
+ *   [P3] quant67.com, "【大模型基础设施工程】08：MoE 训练工程": §4.1 softmax
+ *        top-K gate with renormalisation, §4.3 sigmoid gate, §5 shared
+ *        expert, §6.3 route bias for selection only, §9 the single-GPU
+ *        MoE layer (SwiGLU experts, per-expert gather, index_add combine,
+ *        load counts), §11.3 sparse backward, §12.5 sort-based permutation
+ *        and its inverse, §12.7 gate math in fp32, §13.6 fp8 with per-tile
+ *        scales and fp32 accumulation.
+ *
+ * Conventions (all entry points):
+ *   - Every tensor pointer is a DEVICE pointer, row-major, 16-byte aligned,
+ *     owned by the caller. The library allocates nothing, frees nothing,
+ *     never synchronises, and keeps no state between calls (reentrant).
+ *   - Weights use the linear-layer [out, in] layout: W1, W3 are
+ *     [E, d_ff, d_model], W2 is [E, d_model, d_ff], the router is
+ *     [E, d_model]; shared-expert weights are [d_ff_shared, d_model] and
+ *     [d_model, d_ff_shared].
+ *   - "act" dtype (desc->act_dtype) is the element type of x, weights,
+ *     x_perm, h, y_perm, y_shared, out and gradients: fp32 or bf16.
+ *     Logits, gate weights and all accumulation are fp32.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is
+ *     enqueued asynchronously; nothing depends on host-visible shapes, so
+ *     every call can be captured in a HIP graph and replayed with new
+ *     routing.
+ *   - Errors: only host-checkable arguments are validated. On any error
+ *     no work is enqueued and a status != MOE_OK is returned. MOE_EHIP
+ *     reports a launch error from the HIP runtime. Device-side data (e.g.
+ *     an expert id outside [0, E) in topk_idx) is not validated.
+ *   - T == 0 is valid: the descriptor is checked, then MOE_OK is returned
+ *     with nothing enqueued and no pointer read (pointers may be NULL).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK            0
+#define MOE_EINVAL        1  /* NULL pointer, negative or inconsistent size */
+#define MOE_EUNSUPPORTED  2  /* valid but outside this build's limits     */
+#define MOE_EWORKSPACE    3  /* workspace smaller than moe_workspace_size */
+#define MOE_EHIP          4  /* HIP runtime reported an error             */
+
+/* element types */
+#define MOE_F32    0
+#define MOE_BF16   1
+#define MOE_MXFP8  2  /* gemm_dtype only: E4M3 elements, E8M0 scale per 32 */
+
+/* gating */
+#define MOE_GATE_SOFTMAX 0  /* [P3 §4.1] */
+#define MOE_GATE_SIGMOID 1  /* [P3 §4.3] */
+
+/* flags */
+#define MOE_FLAG_SAVE_ACTS 1  /* forward stores the pre-activations a, b */
+
+/* limits of this build */
+#define MOE_K_MAX 16
+#define MOE_E_MAX 1024
+
+/* Number of stage-boundary events moe_forward / moe_backward can record. */
+#define MOE_FWD_NEVENTS 6
+#define MOE_BWD_NEVENTS 8
+
+typedef struct moe_desc {
+  int32_t T;            /* tokens (batch x sequence flattened), >= 0       */
+  int32_t d_model;      /* multiple of 8 (bf16/fp32), of 32 (MXFP8)        */
+  int32_t d_ff;         /* routed expert hidden size, same rule            */
+  int32_t E;            /* routed experts, 1..MOE_E_MAX                    */
+  int32_t K;            /* experts per token, 1..min(E, MOE_K_MAX)         */
+  int32_t d_ff_shared;  /* shared expert hidden size, 0 = none [P3 §5]     */
+  int32_t gate;         /* MOE_GATE_SOFTMAX | MOE_GATE_SIGMOID             */
+  int32_t act_dtype;    /* MOE_F32 | MOE_BF16                              */
+  int32_t gemm_dtype;   /* = act_dtype, or MOE_MXFP8 (forward, bf16 act)   */
+  int32_t flags;        /* MOE_FLAG_*                                      */
+} moe_desc;
+
+/* One set of SwiGLU expert weights [P3 §9]: y = W2 (silu(W1 x) * (W3 x)).
+ * For the routed experts the leading dimension is E; for the shared
+ * expert it is absent. With gemm_dtype == MOE_MXFP8 the w* pointers hold
+ * E4M3 bytes (quantised by moe_quantize_mxfp8) and *_scales hold the
+ * E8M0 codes, one per 32 elements along the row: w1/w3 scales are
+ * [E, d_ff, d_model/32], w2 scales [E, d_model, d_ff/32]. */
+typedef struct moe_expert_weights {
+  const void* w1;
+  const void* w3;
+  const void* w2;
+  const uint8_t* w1_scales;
+  const uint8_t* w3_scales;
+  const uint8_t* w2_scales;
+} moe_expert_weights;
+
+/* Forward arguments. Required unless marked optional. */
+typedef struct moe_fwd_args {
+  const void* x;              /* [T, d_model] act                            */
+  const void* w_router;       /* [E, d_model] act; unused if logits_in       */
+  const float* route_bias;    /* optional [E]: selection only [P3 §6.3]      */
+  const float* logits_in;     /* optional [T, E]: bypasses the router GEMM   */
+  moe_expert_weights routed;  /* [E, ...]                                    */
+  moe_expert_weights shared;  /* used iff d_ff_shared > 0                    */
+  void* out;                  /* [T, d_model] act                            */
+  /* routing state, kept for backward */
+  float* logits;              /* [T, E] fp32; required iff logits_in == NULL */
+  int32_t* topk_idx;          /* [T, K] expert ids, rank order               */
+  float* topk_w;              /* [T, K] renormalised gate weights            */
+  int32_t* counts;            /* [E] copies per expert                       */
+  int32_t* offsets;           /* [E+1] exclusive prefix of counts            */
+  int32_t* sorted_src;        /* [T*K] copy j = t*K+k at each sorted slot    */
+  int32_t* dest;              /* [T*K] sorted slot of each copy j            */
+  /* activations */
+  void* x_perm;               /* [T*K, d_model] act (MXFP8: E4M3 bytes)      */
+  uint8_t* x_perm_scales;     /* MXFP8 only: [T*K, d_model/32] E8M0          */
+  void* h;                    /* [T*K, d_ff] act (MXFP8: optional, unused)   */
+  void* y_perm;               /* [T*K, d_model] act, unweighted expert out   */
+  void* y_shared;             /* [T, d_model] act; required iff shared       */
+  void* act_a;                /* [T*K, d_ff] act; required iff SAVE_ACTS     */
+  void* act_b;                /* [T*K, d_ff] act; required iff SAVE_ACTS     */
+  void* events[MOE_FWD_NEVENTS]; /* optional hipEvent_t, recorded at: start,
+                                    after routing, after permute, after GEMM1,
+                                    after GEMM2 (+shared), after combine      */
+} moe_fwd_args;
+
+/* Backward arguments: gradients of sum(dy * out) with the routing fixed
+ * and the gate weights as leaves [P3 §11.3]. Experts that received no
+ * token get dW = 0. */
+typedef struct moe_bwd_args {
+  const void* dy;             /* [T, d_model] act                            */
+  const void* x;              /* [T, d_model] act                            */
+  moe_expert_weights routed;  /* act dtype (MXFP8 backward unsupported)      */
+  moe_expert_weights shared;
+  /* saved forward state (as written by moe_forward) */
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const int32_t* offsets;
+  const int32_t* sorted_src;
+  const int32_t* dest;
+  const void* x_perm;
+  const void* h;
+  const void* y_perm;
+  const void* act_a;          /* optional: NULL = recompute a, b             */
+  const void* act_b;
+  /* outputs */
+  void* dx;                   /* [T, d_model] act                            */
+  void* dw1;                  /* [E, d_ff, d_model] act                      */
+  void* dw3;                  /* [E, d_ff, d_model] act                      */
+  void* dw2;                  /* [E, d_model, d_ff] act                      */
+  float* d_topk_w;            /* [T, K] fp32                                 */
+  void* events[MOE_BWD_NEVENTS]; /* optional hipEvent_t stage boundaries     */
+} moe_bwd_args;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_str(moe_status s);
+
+/* Bytes of scratch workspace moe_permute / moe_grouped_gemm_swiglu /
+ * moe_forward (for_backward == 0) or moe_backward (for_backward != 0)
+ * need for this descriptor. Written to *bytes. */
+moe_status moe_workspace_size(const moe_desc* desc, int for_backward,
+                              size_t* bytes);
+
+/* Router and gate [P3 §4.1, §4.3, §6.3, §12.7].
+ * logits = x W_router^T (fp32 accumulate) unless logits_in is given.
+ * Selection key: logit (+ route_bias[e] if given, added in fp32); -0.0
+ * equals +0.0 and NaN counts as -inf. The K experts with the largest
+ * keys are chosen, ties to the lowest expert id, and written to
+ * topk_idx[t, 0..K-1] in (key descending, id ascending) order.
+ * Weights use the raw logits: softmax over the K selected logits, or
+ * sigmoid(logit) / sum of the K sigmoids; they sum to 1 (1/K each if
+ * the sum is 0). logits_out receives the logits when computed (may be
+ * NULL if logits_in is given). */
+moe_status moe_route(const moe_desc* desc, const void* x,
+                     const void* w_router, const float* route_bias,
+                     const float* logits_in, float* logits_out,
+                     int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Histogram, prefix scan and stable permutation [P3 §9, §12.5].
+ * counts[e] = #{(t,k): topk_idx[t,k] == e}; offsets = exclusive prefix
+ * (offsets[E] = T*K: nothing dropped, nothing padded [P1]). Copies are
+ * ordered by (expert, j = t*K+k): sorted_src[p] = j, dest[j] = p, and
+ * x_perm[p] = x[j / K] (bit copy; with gemm_dtype MXFP8, E4M3 codes plus
+ * E8M0 scales in x_perm_scales). Integer work, bit-exact, atomic-free on
+ * global memory. */
+moe_status moe_permute(const moe_desc* desc, const void* x,
+                       const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_src, int32_t* dest,
+                       void* x_perm, uint8_t* x_perm_scales, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Ragged grouped SwiGLU GEMMs [P1 grouped GEMM; P2; P3 §9 Expert]. For
+ * each expert e and sorted rows p in [offsets[e], offsets[e+1]):
+ *   a = x_perm[p] W1_e^T, b = x_perm[p] W3_e^T   (fp32 accumulate)
+ *   h[p] = silu(a) * b                           (stored in act dtype)
+ *   y_perm[p] = h[p] W2_e^T                      (stored in act dtype)
+ * The tile list over (expert, row tile) is built on the device from
+ * offsets; no host synchronisation. act_a/act_b (optional) receive a, b.
+ * If x_shared is non-NULL and d_ff_shared > 0, the shared expert runs on
+ * every token: y_shared = SwiGLU_shared(x_shared). MXFP8: x_perm and
+ * x_perm_scales are E4M3/E8M0, weights must be quantised; h may be NULL. */
+moe_status moe_grouped_gemm_swiglu(const moe_desc* desc, const void* x_perm,
+                                   const uint8_t* x_perm_scales,
+                                   const int32_t* offsets,
+                                   const moe_expert_weights* routed,
+                                   const void* x_shared,
+                                   const moe_expert_weights* shared,
+                                   void* h, void* y_perm, void* y_shared,
+                                   void* act_a, void* act_b, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/* Gate-weighted unpermute and combine [P3 §9, §12.5 step 6, §5]:
+ * out[t] = sum_{k<K} topk_w[t,k] * y_perm[dest[t*K+k]] (+ y_shared[t]),
+ * accumulated in fp32 in k order and rounded once. Deterministic: each
+ * output row is owned by one workgroup; no atomics. y_shared may be NULL. */
+moe_status moe_unpermute_combine(const moe_desc* desc, const void* y_perm,
+                                 const int32_t* dest, const float* topk_w,
+                                 const void* y_shared, void* out,
+                                 void* stream);
+
+/* Whole forward: route, permute, grouped GEMMs (+ shared), combine. */
+moe_status moe_forward(const moe_desc* desc, const moe_fwd_args* args,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Whole backward (see moe_bwd_args). Deterministic: weight gradients are
+ * owned tile by tile (no split-K atomics). */
+moe_status moe_backward(const moe_desc* desc, const moe_bwd_args* args,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* MX quantisation of a bf16 [rows, cols] matrix along its rows (cols a
+ * multiple of 32), per the OCP MX v1.0 rule: X = floor(log2(amax)) - 8
+ * per 32-element block (clamped to [-127, 127]); scale code X + 127;
+ * element = E4M3 round-to-nearest-even of v / 2^X, saturated to +-448.
+ * Writes q [rows, cols] E4M3 bytes and scales [rows, cols/32]. */
+moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows,
+                              int64_t cols, uint8_t* q, uint8_t* scales,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,444 @@
+// C ABI of the MoE layer: argument validation, workspace carving and the
+// launch sequence of each entry point. No allocation, no synchronisation,
+// no state kept between calls.
+#include <climits>
+#include <cstdlib>
+#include <cstring>
+
+#include "gemm.h"
+#include "launch.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr long kMaxCopies = 1L << 30;  // int32 slots with headroom
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+moe_status check_desc(const moe_desc* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->T < 0 || d->d_model <= 0 || d->d_ff <= 0 || d->E <= 0 || d->K <= 0 ||
+      d->d_ff_shared < 0)
+    return MOE_EINVAL;
+  if (d->K > d->E) return MOE_EINVAL;
+  if (d->gate != MOE_GATE_SOFTMAX && d->gate != MOE_GATE_SIGMOID) return MOE_EINVAL;
+  if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_EINVAL;
+  if (d->flags & ~MOE_FLAG_SAVE_ACTS) return MOE_EINVAL;
+  if (d->K > MOE_K_MAX || d->E > MOE_E_MAX) return MOE_EUNSUPPORTED;
+  if (d->gemm_dtype != d->act_dtype) {
+    if (d->gemm_dtype == MOE_MXFP8 && d->act_dtype == MOE_BF16) return MOE_EUNSUPPORTED;
+    return MOE_EINVAL;
+  }
+  if (d->d_model % 8 || d->d_ff % 8 || d->d_ff_shared % 8) return MOE_EUNSUPPORTED;
+  if ((long)d->T * d->K > kMaxCopies) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+// Forward scratch: permute histogram, tile prefixes, shared-expert hidden.
+struct FwdWs {
+  int32_t* block_hist;
+  int32_t* tile_off[kNumTileBM];
+  void* h_shared;
+};
+struct BwdWs {
+  int32_t* tile_off[kNumTileBM];
+  void* dy_perm;
+  void* da;
+  void* db;
+  void* dx_perm;
+};
+
+size_t fwd_ws_layout(const moe_desc* d, char* base, FwdWs* w) {
+  const long TK = (long)d->T * d->K;
+  const long nblk = cdiv(TK, kPermChunk);
+  size_t o = 0;
+  if (w) w->block_hist = (int32_t*)(base + o);
+  o = align_up(o + sizeof(int32_t) * (size_t)(d->E * (nblk > 0 ? nblk : 1)));
+  for (int i = 0; i < kNumTileBM; ++i) {
+    if (w) w->tile_off[i] = (int32_t*)(base + o);
+    o = align_up(o + sizeof(int32_t) * (size_t)(d->E + 1));
+  }
+  if (w) w->h_shared = base + o;
+  o = align_up(o + act_bytes(d->act_dtype) * (size_t)d->T * d->d_ff_shared);
+  return o;
+}
+
+size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
+  const size_t TK = (size_t)d->T * d->K, b = act_bytes(d->act_dtype);
+  size_t o = 0;
+  for (int i = 0; i < kNumTileBM; ++i) {
+    if (w) w->tile_off[i] = (int32_t*)(base + o);
+    o = align_up(o + sizeof(int32_t) * (size_t)(d->E + 1));
+  }
+  if (w) w->dy_perm = base + o;
+  o = align_up(o + b * TK * d->d_model);
+  if (w) w->da = base + o;
+  o = align_up(o + b * TK * d->d_ff);
+  if (w) w->db = base + o;
+  o = align_up(o + b * TK * d->d_ff);
+  if (w) w->dx_perm = base + o;
+  o = align_up(o + b * TK * d->d_model);
+  return o;
+}
+
+bool force_simt() {
+  static const int v = [] {
+    const char* s = getenv("MOE_GEMM_BACKEND");
+    return (s && strcmp(s, "simt") == 0) ? 1 : 0;
+  }();
+  return v != 0;
+}
+
+GemmParams gp() {
+  GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.K1 = INT_MAX;
+  p.G = 1;
+  return p;
+}
+
+hipError_t run_gemm(GemmOp op, int dtype, GemmParams p,
+                    int32_t* const* tile_off, hipStream_t s) {
+  if (dtype == MOE_BF16 && !force_simt() && mfma_supported(op, p))
+    return gemm_mfma(op, p, tile_off, s);
+  if (op != kOpWgrad) {
+    if (p.off) {
+      p.tile_off = tile_off[tile_bm_slot(kSimtBM)];
+      p.tiles_m_max = (int)(cdiv(p.M, kSimtBM) + (p.G < p.M ? p.G : p.M));
+    } else {
+      p.tiles_m_max = (int)cdiv(p.M, kSimtBM);
+    }
+  }
+  return gemm_simt(op, dtype, p, s);
+}
+
+void record(void* ev, hipStream_t s) {
+  if (ev) (void)hipEventRecord((hipEvent_t)ev, s);
+}
+
+// --- building blocks shared by the entry points --------------------------
+hipError_t do_route(const moe_desc* d, const void* x, const void* wr,
+                    const float* bias, const float* logits_in,
+                    float* logits_out, int32_t* idx, float* w, hipStream_t s) {
+  const float* L = logits_in;
+  if (!L) {
+    GemmParams p = gp();
+    p.M = d->T; p.N = d->E; p.K = d->d_model;
+    p.A = x; p.lda = d->d_model;
+    p.B = wr; p.ldb = d->d_model;
+    p.C = logits_out; p.ldc = d->E;
+    hipError_t e = run_gemm(kOpRouter, d->act_dtype, p, nullptr, s);
+    if (e != hipSuccess) return e;
+    L = logits_out;
+  }
+  return launch_topk(L, bias, d->T, d->E, d->K, d->gate, idx, w, s);
+}
+
+hipError_t do_permute(const moe_desc* d, const void* x, const int32_t* idx,
+                      int32_t* counts, int32_t* offsets, int32_t* src,
+                      int32_t* dest, void* x_perm, const FwdWs& ws,
+                      hipStream_t s) {
+  const int TK = d->T * d->K;
+  hipError_t e = launch_histogram_scan(idx, TK, d->E, ws.block_hist, counts,
+                                       offsets, ws.tile_off, s);
+  if (e != hipSuccess) return e;
+  e = launch_rank(idx, TK, d->E, ws.block_hist, src, dest, s);
+  if (e != hipSuccess) return e;
+  return launch_scatter_rows(x, d->T, d->K,
+                             (long)d->d_model * act_bytes(d->act_dtype), dest,
+                             x_perm, s);
+}
+
+hipError_t do_gemm1(const moe_desc* d, const void* A, const int32_t* off,
+                    int rows, int G, const void* w1, const void* w3, int f,
+                    void* h, void* a_out, void* b_out, int32_t* const* toff,
+                    hipStream_t s) {
+  GemmParams p = gp();
+  p.M = rows; p.N = f; p.K = d->d_model; p.G = G; p.off = off;
+  p.A = A; p.lda = d->d_model;
+  p.B = w1; p.B2 = w3; p.ldb = d->d_model; p.sB = (long)f * d->d_model;
+  p.C = h; p.C2 = a_out; p.C3 = b_out; p.ldc = f;
+  return run_gemm(kOpGemm1, d->act_dtype, p, toff, s);
+}
+
+hipError_t do_gemm2(const moe_desc* d, const void* h, const int32_t* off,
+                    int rows, int G, const void* w2, int f, void* y,
+                    int32_t* const* toff, hipStream_t s) {
+  GemmParams p = gp();
+  p.M = rows; p.N = d->d_model; p.K = f; p.G = G; p.off = off;
+  p.A = h; p.lda = f;
+  p.B = w2; p.ldb = f; p.sB = (long)d->d_model * f;
+  p.C = y; p.ldc = d->d_model;
+  return run_gemm(kOpGemm2, d->act_dtype, p, toff, s);
+}
+
+hipError_t do_experts(const moe_desc* d, const void* x_perm,
+                      const int32_t* offsets, const moe_expert_weights* rw,
+                      const void* x_shared, const moe_expert_weights* sw,
+                      void* h, void* y_perm, void* y_shared, void* act_a,
+                      void* act_b, const FwdWs& ws, hipStream_t s,
+                      void* ev_mid) {
+  const int TK = d->T * d->K;
+  hipError_t e = do_gemm1(d, x_perm, offsets, TK, d->E, rw->w1, rw->w3,
+                          d->d_ff, h, act_a, act_b, ws.tile_off, s);
+  if (e != hipSuccess) return e;
+  record(ev_mid, s);
+  e = do_gemm2(d, h, offsets, TK, d->E, rw->w2, d->d_ff, y_perm, ws.tile_off, s);
+  if (e != hipSuccess) return e;
+  if (x_shared && d->d_ff_shared > 0) {
+    e = do_gemm1(d, x_shared, nullptr, d->T, 1, sw->w1, sw->w3,
+                 d->d_ff_shared, ws.h_shared, nullptr, nullptr, ws.tile_off, s);
+    if (e != hipSuccess) return e;
+    e = do_gemm2(d, ws.h_shared, nullptr, d->T, 1, sw->w2, d->d_ff_shared,
+                 y_shared, ws.tile_off, s);
+  }
+  return e;
+}
+
+bool weights_ok(const moe_expert_weights* w) {
+  return w && w->w1 && w->w3 && w->w2;
+}
+
+}  // namespace
+
+// ===========================================================================
+extern "C" {
+
+const char* moe_status_str(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: outside this build's limits";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
+  }
+  return "unknown moe_status";
+}
+
+moe_status moe_workspace_size(const moe_desc* desc, int for_backward,
+                              size_t* bytes) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_EINVAL;
+  *bytes = for_backward ? bwd_ws_layout(desc, nullptr, nullptr)
+                        : fwd_ws_layout(desc, nullptr, nullptr);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_desc* d, const void* x, const void* w_router,
+                     const float* route_bias, const float* logits_in,
+                     float* logits_out, int32_t* topk_idx, float* topk_w,
+                     void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;  // nothing is accessed
+  if (!topk_idx || !topk_w) return MOE_EINVAL;
+  if (!logits_in && (!x || !w_router || !logits_out)) return MOE_EINVAL;
+  return hip_status(do_route(d, x, w_router, route_bias, logits_in,
+                             logits_out, topk_idx, topk_w,
+                             (hipStream_t)stream));
+}
+
+moe_status moe_permute(const moe_desc* d, const void* x,
+                       const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_src, int32_t* dest,
+                       void* x_perm, uint8_t* x_perm_scales, void* ws,
+                       size_t ws_bytes, void* stream) {
+  (void)x_perm_scales;
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;  // nothing is accessed
+  if (!x || !topk_idx || !counts || !offsets || !sorted_src || !dest ||
+      !x_perm || !ws)
+    return MOE_EINVAL;
+  if (ws_bytes < fwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
+  FwdWs w;
+  fwd_ws_layout(d, (char*)ws, &w);
+  return hip_status(do_permute(d, x, topk_idx, counts, offsets, sorted_src,
+                               dest, x_perm, w, (hipStream_t)stream));
+}
+
+moe_status moe_grouped_gemm_swiglu(const moe_desc* d, const void* x_perm,
+                                   const uint8_t* x_perm_scales,
+                                   const int32_t* offsets,
+                                   const moe_expert_weights* routed,
+                                   const void* x_shared,
+                                   const moe_expert_weights* shared, void* h,
+                                   void* y_perm, void* y_shared, void* act_a,
+                                   void* act_b, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  (void)x_perm_scales;
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;  // nothing is accessed
+  if (!x_perm || !offsets || !weights_ok(routed) || !h || !y_perm || !ws)
+    return MOE_EINVAL;
+  const bool use_shared = x_shared && d->d_ff_shared > 0;
+  if (use_shared && (!weights_ok(shared) || !y_shared)) return MOE_EINVAL;
+  if ((d->flags & MOE_FLAG_SAVE_ACTS) && (!act_a || !act_b)) return MOE_EINVAL;
+  if (ws_bytes < fwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
+  FwdWs w;
+  fwd_ws_layout(d, (char*)ws, &w);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_tile_prefix(offsets, d->E, w.tile_off, s);
+  if (e != hipSuccess) return MOE_EHIP;
+  const bool save = d->flags & MOE_FLAG_SAVE_ACTS;
+  return hip_status(do_experts(d, x_perm, offsets, routed,
+                               use_shared ? x_shared : nullptr, shared, h,
+                               y_perm, y_shared, save ? act_a : nullptr,
+                               save ? act_b : nullptr, w, s, nullptr));
+}
+
+moe_status moe_unpermute_combine(const moe_desc* d, const void* y_perm,
+                                 const int32_t* dest, const float* topk_w,
+                                 const void* y_shared, void* out,
+                                 void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;  // nothing is accessed
+  if (!y_perm || !dest || !topk_w || !out) return MOE_EINVAL;
+  return hip_status(launch_combine(d->act_dtype, y_perm, dest, topk_w,
+                                   y_shared, out, d->T, d->K, d->d_model,
+                                   (hipStream_t)stream));
+}
+
+moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
+                       size_t ws_bytes, void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;  // nothing is accessed
+  if (!a || !ws || !a->x || !a->out || !weights_ok(&a->routed)) return MOE_EINVAL;
+  if (!a->logits_in && (!a->w_router || !a->logits)) return MOE_EINVAL;
+  if (!a->topk_idx || !a->topk_w || !a->counts || !a->offsets ||
+      !a->sorted_src || !a->dest || !a->x_perm || !a->h || !a->y_perm)
+    return MOE_EINVAL;
+  const bool shared = d->d_ff_shared > 0;
+  if (shared && (!weights_ok(&a->shared) || !a->y_shared)) return MOE_EINVAL;
+  const bool save = d->flags & MOE_FLAG_SAVE_ACTS;
+  if (save && (!a->act_a || !a->act_b)) return MOE_EINVAL;
+  if (ws_bytes < fwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
+  FwdWs w;
+  fwd_ws_layout(d, (char*)ws, &w);
+  hipStream_t s = (hipStream_t)stream;
+  record(a->events[0], s);
+  hipError_t e = do_route(d, a->x, a->w_router, a->route_bias, a->logits_in,
+                          a->logits, a->topk_idx, a->topk_w, s);
+  if (e != hipSuccess) return MOE_EHIP;
+  record(a->events[1], s);
+  e = do_permute(d, a->x, a->topk_idx, a->counts, a->offsets, a->sorted_src,
+                 a->dest, a->x_perm, w, s);
+  if (e != hipSuccess) return MOE_EHIP;
+  record(a->events[2], s);
+  e = do_experts(d, a->x_perm, a->offsets, &a->routed,
+                 shared ? a->x : nullptr, &a->shared, a->h, a->y_perm,
+                 a->y_shared, save ? a->act_a : nullptr,
+                 save ? a->act_b : nullptr, w, s, a->events[3]);
+  if (e != hipSuccess) return MOE_EHIP;
+  record(a->events[4], s);
+  e = launch_combine(d->act_dtype, a->y_perm, a->dest, a->topk_w,
+                     shared ? a->y_shared : nullptr, a->out, d->T, d->K,
+                     d->d_model, s);
+  if (e != hipSuccess) return MOE_EHIP;
+  record(a->events[5], s);
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
+                        size_t ws_bytes, void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;  // nothing is accessed
+  if (!a || !ws || !a->dy || !weights_ok(&a->routed) || !a->topk_w ||
+      !a->offsets || !a->dest || !a->x_perm || !a->h || !a->y_perm ||
+      !a->dx || !a->dw1 || !a->dw3 || !a->dw2 || !a->d_topk_w)
+    return MOE_EINVAL;
+  if ((a->act_a == nullptr) != (a->act_b == nullptr)) return MOE_EINVAL;
+  if (d->d_ff_shared > 0) return MOE_EUNSUPPORTED;
+  if (ws_bytes < bwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
+  BwdWs w;
+  bwd_ws_layout(d, (char*)ws, &w);
+  hipStream_t s = (hipStream_t)stream;
+  const int TK = d->T * d->K, dm = d->d_model, f = d->d_ff, E = d->E;
+  const int dt = d->act_dtype;
+  hipError_t e;
+#define MOE_TRY(x)                         \
+  do {                                     \
+    e = (x);                               \
+    if (e != hipSuccess) return MOE_EHIP;  \
+  } while (0)
+  record(a->events[0], s);
+  MOE_TRY(launch_tile_prefix(a->offsets, E, w.tile_off, s));
+  // combine^T: dy_perm = w * dy, d_topk_w = <dy, y_perm>
+  MOE_TRY(launch_combine_bwd(dt, a->dy, a->y_perm, a->dest, a->topk_w,
+                             w.dy_perm, a->d_topk_w, d->T, d->K, dm, s));
+  record(a->events[1], s);
+  // pre-activations: saved, or recomputed into the da/db buffers
+  const void* sa = a->act_a;
+  const void* sb = a->act_b;
+  if (!sa) {
+    MOE_TRY(do_gemm1(d, a->x_perm, a->offsets, TK, E, a->routed.w1,
+                     a->routed.w3, f, nullptr, w.da, w.db, w.tile_off, s));
+    sa = w.da;
+    sb = w.db;
+  }
+  record(a->events[2], s);
+  {  // dh = dy_perm W2_e, then (da, db) from the SwiGLU derivative
+    GemmParams p = gp();
+    p.M = TK; p.N = f; p.K = dm; p.G = E; p.off = a->offsets;
+    p.A = w.dy_perm; p.lda = dm;
+    p.B = a->routed.w2; p.ldb = f; p.sB = (long)dm * f;
+    p.C = w.da; p.C2 = w.db; p.ldc = f;
+    p.aux_a = sa; p.aux_b = sb;
+    MOE_TRY(run_gemm(kOpDgrad2, dt, p, w.tile_off, s));
+  }
+  record(a->events[3], s);
+  {  // dx_perm = da W1_e + db W3_e
+    GemmParams p = gp();
+    p.M = TK; p.N = dm; p.K = 2 * f; p.K1 = f; p.G = E; p.off = a->offsets;
+    p.A = w.da; p.A2 = w.db; p.lda = f;
+    p.B = a->routed.w1; p.B2 = a->routed.w3; p.ldb = dm; p.sB = (long)f * dm;
+    p.C = w.dx_perm; p.ldc = dm;
+    MOE_TRY(run_gemm(kOpDgrad1, dt, p, w.tile_off, s));
+  }
+  record(a->events[4], s);
+  MOE_TRY(launch_combine(dt, w.dx_perm, a->dest, nullptr, nullptr, a->dx,
+                         d->T, d->K, dm, s));
+  record(a->events[5], s);
+  {  // dW2_e = dy_perm_e^T h_e
+    GemmParams p = gp();
+    p.M = dm; p.N = f; p.G = E; p.off = a->offsets;
+    p.A = w.dy_perm; p.lda = dm;
+    p.B = a->h; p.ldb = f;
+    p.C = a->dw2; p.ldc = f; p.sC = (long)dm * f;
+    MOE_TRY(run_gemm(kOpWgrad, dt, p, w.tile_off, s));
+  }
+  record(a->events[6], s);
+  for (int which = 0; which < 2; ++which) {  // dW1_e = da^T x_perm, dW3_e
+    GemmParams p = gp();
+    p.M = f; p.N = dm; p.G = E; p.off = a->offsets;
+    p.A = which ? w.db : w.da; p.lda = f;
+    p.B = a->x_perm; p.ldb = dm;
+    p.C = which ? a->dw3 : a->dw1; p.ldc = dm; p.sC = (long)f * dm;
+    MOE_TRY(run_gemm(kOpWgrad, dt, p, w.tile_off, s));
+  }
+  record(a->events[7], s);
+#undef MOE_TRY
+  return MOE_OK;
+}
+
+moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows,
+                              int64_t cols, uint8_t* q, uint8_t* scales,
+                              void* stream) {
+  if (!src_bf16 || !q || !scales || rows < 0 || cols <= 0) return MOE_EINVAL;
+  if (cols % 32) return MOE_EUNSUPPORTED;
+  (void)stream;
+  return MOE_EUNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal launchers of the layer's non-GEMM kernels.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// Copies handled by one histogram / ranking workgroup.
+constexpr int kPermChunk = 1024;
+
+hipError_t launch_topk(const float* logits, const float* bias, int T, int E,
+                       int K, int gate, int32_t* idx, float* w,
+                       hipStream_t s);
+
+// block_hist: [E, nblk] int32 scratch; tile_off: kNumTileBM arrays of E+1.
+hipError_t launch_histogram_scan(const int32_t* idx, int TK, int E,
+                                 int32_t* block_hist, int32_t* counts,
+                                 int32_t* offsets, int32_t* const* tile_off,
+                                 hipStream_t s);
+// tile_off[i][e] = sum_{e' < e} ceil(count_e' / kTileBM[i]) from offsets.
+hipError_t launch_tile_prefix(const int32_t* offsets, int E,
+                              int32_t* const* tile_off, hipStream_t s);
+hipError_t launch_rank(const int32_t* idx, int TK, int E,
+                       const int32_t* block_hist, int32_t* sorted_src,
+                       int32_t* dest, hipStream_t s);
+// x_perm[dest[t*K+k]] = x[t] for all t, k (row bytes % 16 == 0).
+hipError_t launch_scatter_rows(const void* x, int T, int K, long row_bytes,
+                               const int32_t* dest, void* x_perm,
+                               hipStream_t s);
+// out[t] = sum_k w[t,k] * y[dest[t*K+k]] (+ add[t]); w == NULL means 1.
+hipError_t launch_combine(int dtype, const void* y, const int32_t* dest,
+                          const float* w, const void* add, void* out, int T,
+                          int K, int d, hipStream_t s);
+// dy_perm[dest[t*K+k]] = w[t,k] * dy[t]; d_w[t,k] = <dy[t], y[dest[t*K+k]]>
+hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y,
+                              const int32_t* dest, const float* w,
+                              void* dy_perm, float* d_w, int T, int K, int d,
+                              hipStream_t s);
+
+// MXFP8 (E4M3 elements, E8M0 scale per 32 along rows).
+hipError_t launch_quantize_mxfp8(const void* src, long rows, long cols,
+                                 uint8_t* q, uint8_t* scales, hipStream_t s);
+hipError_t launch_scatter_rows_mxfp8(const void* x, int T, int K, int d,
+                                     const int32_t* dest, uint8_t* xq,
+                                     uint8_t* xs, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,135 @@
+"""The C-ABI library loads, exports every function include/moe.h declares,
+and rejects bad arguments on the host before touching the GPU. CPU only:
+every call here fails validation, so no HIP work is ever enqueued."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from ragged_grouped_gemm_router_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_named_calls():
+    fns = declared_functions()
+    for name in ("moe_route", "moe_permute", "moe_grouped_gemm_swiglu",
+                 "moe_unpermute_combine", "moe_forward", "moe_backward"):
+        assert name in fns
+    assert set(fns) == set(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_struct_layouts_match_header():
+    # int32 x 10; six pointers; pointer-only argument blocks
+    assert ctypes.sizeof(B.MoeDesc) == 40
+    assert ctypes.sizeof(B.MoeExpertWeights) == 48
+    n_ptr_fwd = 4 + 1 + 14 + B.MOE_FWD_NEVENTS
+    assert ctypes.sizeof(B.MoeFwdArgs) == 8 * n_ptr_fwd + 2 * 48
+    n_ptr_bwd = 2 + 15 + B.MOE_BWD_NEVENTS
+    assert ctypes.sizeof(B.MoeBwdArgs) == 8 * n_ptr_bwd + 2 * 48
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.moe_status_str(s).startswith(b"MOE_")
+    assert b"unknown" in lib.moe_status_str(99)
+
+
+def _ws(desc, bwd=False):
+    return B.moe_workspace_size(desc, bwd)
+
+
+def test_workspace_size_host_only():
+    d = B.make_desc(4096, 7168, 2048, 256, 8, 2048, "sigmoid")
+    n = _ws(d)
+    assert n >= 4 * 256 * 32 + 2 * 4096 * 2048  # histogram + shared hidden
+    nb = _ws(d.__class__(4096, 7168, 2048, 256, 8, 0, 1, 1, 1, 0), True)
+    assert nb >= 2 * 32768 * (2 * 7168 + 2 * 2048)
+
+
+@pytest.mark.parametrize("fields,code", [
+    (dict(K=3, E=2), B.MOE_EINVAL),              # K > E
+    (dict(K=0), B.MOE_EINVAL),
+    (dict(T=-1), B.MOE_EINVAL),
+    (dict(E=2000, K=2), B.MOE_EUNSUPPORTED),     # E > E_MAX
+    (dict(K=17, E=64), B.MOE_EUNSUPPORTED),      # K > K_MAX
+    (dict(d_model=100), B.MOE_EUNSUPPORTED),     # not a multiple of 8
+    (dict(gate=7), B.MOE_EINVAL),
+    (dict(act_dtype=5), B.MOE_EINVAL),
+    (dict(flags=8), B.MOE_EINVAL),
+])
+def test_bad_descriptor(fields, code):
+    d = B.make_desc(64, 128, 256, 8, 2)
+    for k, v in fields.items():
+        setattr(d, k, v)
+    n = ctypes.c_size_t(0)
+    assert B.load().moe_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == code
+    fake = 0x1000
+    assert B.load().moe_route(ctypes.byref(d), fake, fake, None, None, fake,
+                              fake, fake, None) == code
+
+
+def test_null_pointers_rejected():
+    lib = B.load()
+    d = B.make_desc(64, 128, 256, 8, 2)
+    fake = 0x1000
+    # missing topk outputs
+    assert lib.moe_route(ctypes.byref(d), fake, fake, None, None, fake, None,
+                         fake, None) == B.MOE_EINVAL
+    # router needed but no logits_out
+    assert lib.moe_route(ctypes.byref(d), fake, fake, None, None, None, fake,
+                         fake, None) == B.MOE_EINVAL
+    assert lib.moe_unpermute_combine(ctypes.byref(d), None, fake, fake, None,
+                                     fake, None) == B.MOE_EINVAL
+    assert lib.moe_route(None, fake, fake, None, None, fake, fake, fake,
+                         None) == B.MOE_EINVAL
+
+
+def test_workspace_too_small_rejected():
+    lib = B.load()
+    d = B.make_desc(64, 128, 256, 8, 2)
+    fake = 0x1000
+    st = lib.moe_permute(ctypes.byref(d), fake, fake, fake, fake, fake, fake,
+                         fake, None, fake, 16, None)
+    assert st == B.MOE_EWORKSPACE
+    a = B.MoeFwdArgs()
+    for name in ("x", "w_router", "out", "logits", "topk_idx", "topk_w",
+                 "counts", "offsets", "sorted_src", "dest", "x_perm", "h",
+                 "y_perm"):
+        setattr(a, name, fake)
+    a.routed = B.MoeExpertWeights(fake, fake, fake, None, None, None)
+    assert lib.moe_forward(ctypes.byref(d), ctypes.byref(a), fake, 16,
+                           None) == B.MOE_EWORKSPACE
+    a.h = None
+    assert lib.moe_forward(ctypes.byref(d), ctypes.byref(a), fake, 1 << 30,
+                           None) == B.MOE_EINVAL
+
+
+def test_save_acts_requires_buffers():
+    lib = B.load()
+    d = B.make_desc(64, 128, 256, 8, 2, save_acts=True)
+    fake = 0x1000
+    w = B.MoeExpertWeights(fake, fake, fake, None, None, None)
+    st = lib.moe_grouped_gemm_swiglu(ctypes.byref(d), fake, None, fake,
+                                     ctypes.byref(w), None, ctypes.byref(w),
+                                     fake, fake, None, None, None, fake,
+                                     1 << 30, None)
+    assert st == B.MOE_EINVAL
