@@ -1,0 +1,89 @@
+"""Backward parity: dX, dW1, dW3, dW2 and the gate-weight gradients from
+the HIP path against the oracle's closed-form backward (routing fixed,
+gate weights as leaves). Small shapes in full; the Mixtral-shaped
+training step on sampled tokens and hidden columns."""
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from moe_testlib import (DEV, check_routing_exact, desc_of, inputs, rel_err,
+                         tol)
+from ragged_grouped_gemm_router_amd import layer as L
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    mi.TINY_FP32,
+    mi.MoEConfig("mixtral_like_T1024_d256_f512_E8_K2", 1024, 256, 512, 8, 2),
+    mi.MoEConfig("mixtral_like_f32_T256_d128_f96_E4_K2", 256, 128, 96, 4, 2,
+                 dtype="f32"),
+    mi.MoEConfig("skewed_like_T1024_d128_f192_E16_K4", 1024, 128, 192, 16, 4,
+                 synth_logits=True, n_zero=3, zipf_s=1.2),
+    mi.MoEConfig("many_experts_T256_d256_f128_E64_K8_sigmoid", 256, 256, 128,
+                 64, 8, gate="sigmoid", bias=True),
+]
+
+
+def _run(cfg, cinp, ginp, save_acts):
+    desc = desc_of(cfg, save_acts=save_acts)
+    fb = L.alloc_forward(desc, DEV)
+    L.forward(desc, ginp, fb)
+    gb = L.alloc_backward(desc, DEV)
+    L.backward(desc, ginp, fb, ginp["dy"], gb)
+    torch.cuda.synchronize()
+    return fb, gb
+
+
+@pytest.mark.parametrize("save_acts", [True, False], ids=["saved", "recompute"])
+@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
+def test_backward_parity(cfg, save_acts):
+    cinp, ginp = inputs(cfg, seed=2, with_dy=True)
+    fb, gb = _run(cfg, cinp, ginp, save_acts)
+    idx, w, counts, *_ = check_routing_exact(cfg, cinp, fb)
+    ref = oracle.backward(cinp["x"], cinp["w1"], cinp["w3"], cinp["w2"], idx,
+                          w, cinp["dy"])
+    for k, rk in (("dx", "dx"), ("dw1", "dw1"), ("dw3", "dw3"),
+                  ("dw2", "dw2"), ("d_topk_w", "d_w")):
+        err = rel_err(gb[k], ref[rk])
+        assert err <= tol(cfg), (k, err)
+    # experts that received no token get exactly zero gradient
+    for e in (counts == 0).nonzero().flatten().tolist():
+        assert (gb["dw1"][e] == 0).all() and (gb["dw2"][e] == 0).all()
+
+
+def test_backward_deterministic():
+    cfg = CASES[3]
+    cinp, ginp = inputs(cfg, seed=4, with_dy=True)
+    _, g1 = _run(cfg, cinp, ginp, True)
+    _, g2 = _run(cfg, cinp, ginp, True)
+    for k in ("dx", "dw1", "dw3", "dw2", "d_topk_w"):
+        assert torch.equal(g1[k], g2[k]), k
+
+
+def test_training_step_full_size_sampled():
+    """Mixtral-shaped forward + backward at full size; dX and d_topk_w on
+    sampled tokens, dW1/dW3 rows and dW2 columns on sampled hidden units."""
+    cfg = mi.MIXTRAL_TRAIN
+    ginp = mi.make_inputs(cfg, 0, device=DEV, with_dy=True)
+    desc = desc_of(cfg, save_acts=True)
+    fb = L.alloc_forward(desc, DEV)
+    L.forward(desc, ginp, fb)
+    gb = L.alloc_backward(desc, DEV)
+    L.backward(desc, ginp, fb, ginp["dy"], gb)
+    torch.cuda.synchronize()
+    idx, w, counts, *_ = check_routing_exact(cfg, {"logits_in": None,
+                                                   "bias": None}, fb)
+    g = torch.Generator().manual_seed(0)
+    toks = sorted(set(torch.randint(0, cfg.T, (6,), generator=g).tolist()))
+    cols = [(int(torch.randint(0, cfg.E, (1,), generator=g)),
+             int(torch.randint(0, cfg.f, (1,), generator=g))) for _ in range(3)]
+    ref = oracle.backward_sampled(ginp["x"], ginp["w1"], ginp["w3"],
+                                  ginp["w2"], idx, w, ginp["dy"], toks, cols)
+    t = torch.tensor(toks, device=DEV)
+    assert rel_err(gb["dx"][t], ref["dx"]) <= 1e-2
+    assert rel_err(gb["d_topk_w"][t], ref["d_w"]) <= 1e-2
+    for i, (e, j) in enumerate(cols):
+        assert rel_err(gb["dw1"][e, j], ref["dw1_rows"][i]) <= 1e-2, (e, j)
+        assert rel_err(gb["dw3"][e, j], ref["dw3_rows"][i]) <= 1e-2, (e, j)
+        assert rel_err(gb["dw2"][e, :, j], ref["dw2_cols"][i]) <= 1e-2, (e, j)
