@@ -101,6 +101,9 @@ def main():
                     choices=["mixtral", "deepseek", "skewed", "tiny"])
     ap.add_argument("--cpu-tokens", type=int, default=640)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first "
+                         "(a known-size kernel to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} "
@@ -133,6 +136,16 @@ def main():
     n_steps = args.warmup + args.steps
     ev = HipEvents(B.MOE_FWD_NEVENTS * max(args.steps, 1))
     stream = torch.cuda.current_stream()
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: calibration copy of {args.copy_calibration_mib} MiB done")
+        del src, dst
 
     log("bench: warmup")
     for i in range(args.warmup):

@@ -14,8 +14,10 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                        "libmoe_mi355x.so")
+# MOE_LIB_PATH selects another build of the same library (kernel variants
+# built with different compile-time switches, for A/B measurements).
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2

@@ -18,10 +18,34 @@
 // logical tiles, and logical tiles are ordered n-group-major, then row
 // tile, then n within the group, so the ~32 tiles an XCD runs together
 // share B panels and A rows in that XCD's L2.
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
+
 #include "gemm.h"
 
 namespace moe {
 namespace {
+
+// LDS position of 16-byte chunk c in a tile row of CPR chunks. The LDS of
+// gfx950 has 64 banks of 4 bytes, so a 128-bit read serves 16 lanes per
+// pass; those lanes read the same logical chunk of 16 consecutive rows,
+// which lie two (CPR = 8) or four (CPR = 4) to a 256-byte bank line. The
+// XOR with the row's line index gives each of them its own 16-byte bank
+// group. (MOE_LDS_SWZ=0 selects the 32-bank form, kept for comparison.)
+#ifndef MOE_LDS_SWZ
+#define MOE_LDS_SWZ 1
+#endif
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int c) {
+#if MOE_LDS_SWZ == 1
+  if constexpr (CPR == 8) return c ^ ((row >> 1) & 7);
+  else return c ^ ((row >> 2) & 3);
+#else
+  if constexpr (CPR == 8) return c ^ (row & 7);
+  else return c ^ ((row >> 1) & 3);
+#endif
+}
 
 template <int ROWS, int BK, int NT, bool KC>
 struct TileLoader {
@@ -79,7 +103,7 @@ struct TileLoader {
   }
 
   __device__ __forceinline__ static int slot(int row, int c) {
-    return row * CPR + (c ^ (row & (CPR - 1)));
+    return row * CPR + swz<CPR>(row, c);
   }
 
   __device__ __forceinline__ void store(u32x4* lds, int tid) const {
@@ -106,6 +130,94 @@ __device__ __forceinline__ float fast_sigmoid(float a) {
   return 1.0f / (1.0f + __expf(-a));
 }
 
+struct Tile {
+  int g, m0, m_end, n0, k_beg, k_end;
+};
+
+// Decode this workgroup's output tile. Returns false for surplus
+// workgroups (beyond the device-side tile count).
+template <int BM, int BN, int SCHED>
+__device__ __forceinline__ bool lookup_tile(const GemmParams& p, Tile& t) {
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  t.g = 0;
+  t.k_beg = 0;
+  t.k_end = p.K;
+  if (SCHED == kSchedM) {
+    constexpr int GN = 4;
+    const int MT = p.tiles_m_max;
+    const int ng = L / (MT * GN);
+    const int within = L % (MT * GN);
+    const int gsz = min(GN, tiles_n - ng * GN);
+    if (gsz <= 0 || within >= MT * gsz) return false;
+    const int mt = within / gsz;
+    t.n0 = (ng * GN + within % gsz) * BN;
+    if (p.off == nullptr) {
+      t.m0 = mt * BM;
+      t.m_end = p.M;
+      return t.m0 < t.m_end;
+    }
+    if (mt >= p.tile_off[p.G]) return false;
+    t.g = upper_group(p.tile_off, p.G, mt);
+    t.m0 = p.off[t.g] + (mt - p.tile_off[t.g]) * BM;
+    t.m_end = p.off[t.g + 1];
+    return true;
+  }
+  const int tiles_m = (p.M + BM - 1) / BM;
+  if (L >= p.G * tiles_m * tiles_n) return false;
+  t.g = L / (tiles_m * tiles_n);
+  const int rem = L % (tiles_m * tiles_n);
+  t.m0 = (rem / tiles_n) * BM;
+  t.n0 = (rem % tiles_n) * BN;
+  t.m_end = p.M;
+  t.k_beg = p.off[t.g];
+  t.k_end = p.off[t.g + 1];
+  return true;
+}
+
+// 32x32 accumulator layout: element r of lane l is row
+// 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block.
+template <int WM, int WN, int MB, int NB, int NB_OPS, int EPI, int SCHED,
+          typename TO>
+__device__ __forceinline__ void epilogue(const GemmParams& p, const Tile& t,
+                                         f32x16 (&acc)[NB_OPS][MB][NB],
+                                         int wm, int wn, int lane) {
+  TO* C = (TO*)p.C + (SCHED == kSchedK ? (long)t.g * p.sC : 0);
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int col = t.n0 + wn * WN + j * 32 + lane % 32;
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = t.m0 + wm * WM + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+        if (row >= t.m_end) continue;
+        const long o = (long)row * p.ldc + col;
+        const float v = acc[0][i][j][r];
+        if (EPI == kEpiStore) {
+          C[o] = from_f32<TO>(v);
+        } else if (EPI == kEpiSwiglu) {
+          const float b = acc[NB_OPS - 1][i][j][r];
+          if (C) C[o] = from_f32<TO>(v * fast_sigmoid(v) * b);
+          if (p.C2) ((TO*)p.C2)[o] = from_f32<TO>(v);
+          if (p.C3) ((TO*)p.C3)[o] = from_f32<TO>(b);
+        } else {
+          const float a = to_f32(((const bf16*)p.aux_a)[o]);
+          const float b = to_f32(((const bf16*)p.aux_b)[o]);
+          const float s = fast_sigmoid(a);
+          C[o] = from_f32<TO>(v * b * s * (1.0f + a * (1.0f - s)));
+          ((TO*)p.C2)[o] = from_f32<TO>(v * a * s);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged kernel: any operand layout (used where an operand is
+// stored with its row index contiguous, i.e. the backward products).
+// ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WGM, int WGN, bool A_KC, bool B_KC,
           bool DUAL, int EPI, int SCHED, typename TO>
 __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm(GemmParams p) {
@@ -121,43 +233,10 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm(GemmParams p) {
   __shared__ u32x4 lds[2 * STAGE];
 
   const int tid = threadIdx.x;
-  const int tiles_n = (p.N + BN - 1) / BN;
-
-  // ---------------------------------------------------------- tile lookup
-  int g = 0, m0, m_end, n0, k_beg = 0, k_end = p.K;
-  {
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    if (SCHED == kSchedM) {
-      constexpr int GN = 4;
-      const int MT = p.tiles_m_max;
-      const int ng = L / (MT * GN);
-      const int within = L % (MT * GN);
-      const int gsz = min(GN, tiles_n - ng * GN);
-      if (gsz <= 0 || within >= MT * gsz) return;
-      const int mt = within / gsz;
-      n0 = (ng * GN + within % gsz) * BN;
-      if (p.off == nullptr) {
-        m0 = mt * BM;
-        m_end = p.M;
-        if (m0 >= m_end) return;
-      } else {
-        if (mt >= p.tile_off[p.G]) return;
-        g = upper_group(p.tile_off, p.G, mt);
-        m0 = p.off[g] + (mt - p.tile_off[g]) * BM;
-        m_end = p.off[g + 1];
-      }
-    } else {
-      const int tiles_m = (p.M + BM - 1) / BM;
-      if (L >= p.G * tiles_m * tiles_n) return;
-      g = L / (tiles_m * tiles_n);
-      const int rem = L % (tiles_m * tiles_n);
-      m0 = (rem / tiles_n) * BM;
-      n0 = (rem % tiles_n) * BN;
-      m_end = p.M;
-      k_beg = p.off[g];
-      k_end = p.off[g + 1];
-    }
-  }
+  Tile t;
+  if (!lookup_tile<BM, BN, SCHED>(p, t)) return;
+  const int m0 = t.m0, m_end = t.m_end, n0 = t.n0, k_beg = t.k_beg,
+            k_end = t.k_end;
 
   const int wave = tid / kWave, lane = tid % kWave;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -173,7 +252,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm(GemmParams p) {
   TileLoader<BM, BK, NT, A_KC> la;
   TileLoader<BN, BK, NT, B_KC> lb[NB_OPS];
 
-  const long b_goff = SCHED == kSchedM ? (long)g * p.sB : 0;
+  const long b_goff = SCHED == kSchedM ? (long)t.g * p.sB : 0;
   auto issue_loads = [&](int k0) {
     const bf16* A = (const bf16*)p.A;
     const bf16* B0 = (const bf16*)p.B;
@@ -215,7 +294,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int row = wm * WM + i * 32 + lane % 32;
-        af[i] = __builtin_bit_cast(bf16x8, sA[row * CPR + (c ^ (row & (CPR - 1)))]);
+        af[i] = __builtin_bit_cast(bf16x8, sA[row * CPR + swz<CPR>(row, c)]);
       }
 #pragma unroll
       for (int o = 0; o < NB_OPS; ++o)
@@ -223,7 +302,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm(GemmParams p) {
         for (int j = 0; j < NB; ++j) {
           const int row = wn * WN + j * 32 + lane % 32;
           bfr[o][j] = __builtin_bit_cast(
-              bf16x8, sA[A_CH + o * B_CH + row * CPR + (c ^ (row & (CPR - 1)))]);
+              bf16x8, sA[A_CH + o * B_CH + row * CPR + swz<CPR>(row, c)]);
         }
 #pragma unroll
       for (int o = 0; o < NB_OPS; ++o)
@@ -237,40 +316,215 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm(GemmParams p) {
     if (kt + 1 < nk) commit(cur ^ 1);
     __syncthreads();
   }
+  epilogue<WM, WN, MB, NB, NB_OPS, EPI, SCHED, TO>(p, t, acc, wm, wn, lane);
+}
 
-  // -------------------------------------------------------------- epilogue
-  // 32x32 accumulator layout: element r of lane l is row
-  // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block.
-  TO* C = (TO*)p.C + (SCHED == kSchedK ? (long)g * p.sC : 0);
+// ---------------------------------------------------------------------------
+// Direct-to-LDS kernel for k-contiguous operands (the forward products).
+//
+// global_load_lds_dwordx4 moves 16 bytes per lane from HBM straight into
+// LDS: lane l of a wave writes LDS bytes [base + 16 l, base + 16 l + 16),
+// so one instruction fills 1 KB = RPI rows of the tile. Each lane fetches
+// the global chunk that belongs at its LDS position under the XOR
+// swizzle, so the operands need no registers on their way in and there is
+// no LDS-write phase. S stages form a ring: the loads for k-tile kt+S-1 are
+// issued right after the barrier that ends the use of its stage, S-1
+// tiles ahead of the MFMAs that consume them. Rows past the group's end
+// (and columns past N) are fetched from the last valid row: their
+// products land only in outputs the epilogue discards. K must be a
+// multiple of BK.
+// ---------------------------------------------------------------------------
+
+template <int BM, int BN, int BK, int S, int WGM, int WGN, bool DUAL, int EPI,
+          typename TO>
+__global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) {
+  constexpr int NW = WGM * WGN;
+  constexpr int NB_OPS = DUAL ? 2 : 1;
+  constexpr int CPR = BK / 8;
+  constexpr int RPI = 64 / CPR;  // rows per 1 KB wave instruction
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  constexpr int STAGE = A_BYTES + NB_OPS * B_BYTES;
+  constexpr int A_INS = BM / RPI / NW, B_INS = BN / RPI / NW;
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile shape");
+  static_assert(MB >= 1 && NB >= 1 && BK % 16 == 0, "tile shape");
+
+  __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
+
+  Tile t;
+  if (!lookup_tile<BM, BN, kSchedM>(p, t)) return;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  // per-lane source offsets (elements) of each load instruction
+  const int r_in = lane / CPR, phys = lane % CPR;
+  const bf16* A = (const bf16*)p.A;
+  long a_off[A_INS];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
+  for (int j = 0; j < A_INS; ++j) {
+    const int row = (j * NW + wave) * RPI + r_in;
+    const int grow = min(t.m0 + row, t.m_end - 1);
+    a_off[j] = (long)grow * p.lda + swz<CPR>(row, phys) * 8;
+  }
+  const bf16* Bop[NB_OPS];
+  Bop[0] = (const bf16*)p.B + (long)t.g * p.sB;
+  if (DUAL) Bop[NB_OPS - 1] = (const bf16*)p.B2 + (long)t.g * p.sB;
+  long b_off[B_INS];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int col = n0 + wn * WN + j * 32 + lane % 32;
-      if (col >= p.N) continue;
+  for (int j = 0; j < B_INS; ++j) {
+    const int row = (j * NW + wave) * RPI + r_in;
+    const int grow = min(t.n0 + row, p.N - 1);
+    b_off[j] = (long)grow * p.ldb + swz<CPR>(row, phys) * 8;
+  }
+
+  // DMA instruction d of a k-tile (d < A_INS: operand A, then each B)
+  auto issue_one = [&](int kt, int stage, int d) {
+    char* base = lds + stage * STAGE;
+    const long k0 = (long)kt * BK;
+    if (d < A_INS) {
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(A + a_off[d] + k0),
+          (__attribute__((address_space(3))) void*)(base + (d * NW + wave) * 1024),
+          16, 0, 0);
+    } else {
+      const int o = (d - A_INS) / B_INS, j = (d - A_INS) % B_INS;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(Bop[o] + b_off[j] + k0),
+          (__attribute__((address_space(3))) void*)(base + A_BYTES + o * B_BYTES +
+                                                    (j * NW + wave) * 1024),
+          16, 0, 0);
+    }
+  };
+  auto issue = [&](int kt, int stage) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WM + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-        if (row >= m_end) continue;
-        const long o = (long)row * p.ldc + col;
-        const float v = acc[0][i][j][r];
-        if (EPI == kEpiStore) {
-          C[o] = from_f32<TO>(v);
-        } else if (EPI == kEpiSwiglu) {
-          const float b = acc[NB_OPS - 1][i][j][r];
-          if (C) C[o] = from_f32<TO>(v * fast_sigmoid(v) * b);
-          if (p.C2) ((TO*)p.C2)[o] = from_f32<TO>(v);
-          if (p.C3) ((TO*)p.C3)[o] = from_f32<TO>(b);
-        } else {
-          const float a = to_f32(((const bf16*)p.aux_a)[o]);
-          const float b = to_f32(((const bf16*)p.aux_b)[o]);
-          const float s = fast_sigmoid(a);
-          C[o] = from_f32<TO>(v * b * s * (1.0f + a * (1.0f - s)));
-          ((TO*)p.C2)[o] = from_f32<TO>(v * a * s);
+    for (int d = 0; d < A_INS + NB_OPS * B_INS; ++d) issue_one(kt, stage, d);
+  };
+
+  f32x16 acc[NB_OPS][MB][NB];
+#pragma unroll
+  for (int o = 0; o < NB_OPS; ++o)
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[o][i][j] = f32x16{};
+
+  const int nk = p.K / BK;
+  constexpr int KS = BK / 16;  // 16-wide k-substeps per k-tile
+  static_assert(S == 2 && KS % 2 == 0, "two stages, even substep count");
+
+  // fragments of one 16-wide k-substep
+  struct Frags {
+    bf16x8 a[MB], b[NB_OPS][NB];
+  };
+  constexpr int N_READ = MB + NB_OPS * NB;        // fragment reads per substep
+  constexpr int N_MFMA = NB_OPS * MB * NB;        // MFMAs per substep
+  constexpr int N_LOAD = A_INS + NB_OPS * B_INS;  // DMA instructions per k-tile
+  // fragment r of substep ks (r < MB: A block r, else B block)
+  auto read_one = [&](const char* sb, int ks, Frags& f, int r) {
+    const int c = ks * 2 + lane / 32;
+    if (r < MB) {
+      const int row = wm * WM + r * 32 + lane % 32;
+      f.a[r] = *(const bf16x8*)(sb + row * (BK * 2) + swz<CPR>(row, c) * 16);
+    } else {
+      const int o = (r - MB) / NB, j = (r - MB) % NB;
+      const int row = wn * WN + j * 32 + lane % 32;
+      f.b[o][j] = *(const bf16x8*)(sb + A_BYTES + o * B_BYTES + row * (BK * 2) +
+                                   swz<CPR>(row, c) * 16);
+    }
+  };
+  // MFMA q of a substep, q = (o * MB + i) * NB + j
+  auto mfma_one = [&](const Frags& f, int q) {
+    const int o = q / (MB * NB), i = (q / NB) % MB, j = q % NB;
+    acc[o][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        f.a[i], f.b[o][j], acc[o][i][j], 0, 0, 0);
+  };
+
+  // Tile barrier: this wave's LDS reads and DMA writes are complete (vmcnt
+  // and lgkmcnt at the given counts), then all waves meet. The fences order
+  // LDS accesses around the barrier without waiting for other memory.
+  auto barrier_after = [&](auto vm_left) {
+    constexpr int n = decltype(vm_left)::value;
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
+  // Prologue: k-tiles 0 and 1 in flight; wait for tile 0 only.
+  issue(0, 0);
+  if (nk > 1) {
+    issue(1, 1);
+    barrier_after(std::integral_constant<int, N_LOAD>{});
+  } else {
+    barrier_after(std::integral_constant<int, 0>{});
+  }
+  Frags fa, fb;
+#pragma unroll
+  for (int r = 0; r < N_READ; ++r) read_one(lds, 0, fa, r);
+
+  // One region per 16-wide substep. The MFMAs run on fragments read a
+  // region earlier; the memory instructions of the region (the next
+  // substep's fragment reads and, at the last substep of a k-tile, the DMA
+  // of k-tile kt+2 into the stage tile kt used) sit between them, at most a
+  // few per MFMA, so the in-order issue of a long memory burst never leaves
+  // the matrix pipe idle. The first H MFMAs precede every new read: their
+  // wait for the current fragments then covers no read issued here. Every
+  // step is fenced with sched_barrier to keep this order.
+  constexpr int H = N_MFMA >= 8 ? 2 : 1;
+#define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* sb = lds + (kt & 1) * STAGE;
+    const char* sb_next = lds + ((kt + 1) & 1) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      Frags& cur = (ks & 1) ? fb : fa;
+      Frags& nxt = (ks & 1) ? fa : fb;
+      const bool last = ks + 1 == KS;
+      // memory ops of this region: N_READ reads (+ N_LOAD DMAs if last)
+      constexpr int NM_MAX = N_READ + N_LOAD;
+      const int nm = last ? NM_MAX : N_READ;
+      MOE_FENCE();
+#pragma unroll
+      for (int q = 0; q < H; ++q) mfma_one(cur, q);
+      MOE_FENCE();
+      if (last) {
+        // Branch-free so the wait counters stay exact: past the last tile
+        // the reads return unused data and the DMA fetches the last k-tile
+        // again into a stage that is no longer read.
+        barrier_after(std::integral_constant<int, 0>{});
+        MOE_FENCE();
+      }
+      int m = 0;  // next memory op
+#pragma unroll
+      for (int q = H; q < N_MFMA; ++q) {
+        // memory ops assigned to the slot before MFMA q
+        const int m_end = (q - H + 1) * nm / (N_MFMA - H);
+#pragma unroll
+        for (int mm = 0; mm < NM_MAX; ++mm) {
+          if (mm < m || mm >= m_end) continue;
+          if (!last) {
+            read_one(sb, ks + 1, nxt, mm);
+          } else {
+            // reads spread evenly among the DMAs: op mm is a read iff the
+            // running read quota floor(x * N_READ / NM_MAX) steps at it
+            const int rb = mm * N_READ / NM_MAX;
+            if ((mm + 1) * N_READ / NM_MAX != rb)
+              read_one(sb_next, 0, nxt, rb);
+            else
+              issue_one(min(kt + 2, nk - 1), kt & 1, mm - rb);
+          }
+          MOE_FENCE();
         }
+        m = m_end;
+        mfma_one(cur, q);
+        MOE_FENCE();
       }
     }
   }
+#undef MOE_FENCE
+  __builtin_amdgcn_s_waitcnt(0);  // no load may still target LDS at exit
+  epilogue<WM, WN, MB, NB, NB_OPS, EPI, kSchedM, TO>(p, t, acc, wm, wn, lane);
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, bool A_KC, bool B_KC,
@@ -293,6 +547,28 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int BK, int S, int WGM, int WGN, bool DUAL, int EPI,
+          typename TO>
+hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
+  const long tiles_n = (p.N + BN - 1) / BN;
+  long tiles = (tiles_n + 3) / 4 * p.tiles_m_max * 4;
+  if (tiles <= 0) return hipSuccess;
+  tiles = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
+  if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, BK, S, WGM, WGN, DUAL, EPI, TO>),
+                     dim3((unsigned)tiles), dim3(WGM * WGN * kWave), 0, s, p);
+  return hipGetLastError();
+}
+
+template <bool DUAL, int EPI, typename TO>
+hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
+  // big: 256 x 256 outputs (256 x 128 x 2 dual) over 8 waves, two per
+  // SIMD, each holding 128 x 64 (128 x 32 x 2) in accumulators.
+  if (big)
+    return launch_dl<256, DUAL ? 128 : 256, 64, 2, 2, 4, DUAL, EPI, TO>(p, s);
+  return launch_dl<128, DUAL ? 64 : 128, 64, 2, 2, 2, DUAL, EPI, TO>(p, s);
+}
+
 // Large tiles: 256 x 256 outputs (256 x 128 per B in the dual form),
 // 4 waves of 128 x 128 (128 x 64 x 2). Small tiles: 128 x 128 (128 x 64).
 template <bool A_KC, bool B_KC, bool DUAL, int EPI, int SCHED, typename TO>
@@ -305,6 +581,16 @@ hipError_t launch_sized(bool big, const GemmParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+// MOE_GEMM_BACKEND=staged keeps the register-staged kernel for every
+// product (a testing aid: both kernels must agree with the oracle).
+bool force_staged() {
+  static const bool v = [] {
+    const char* e = getenv("MOE_GEMM_BACKEND");
+    return e && strcmp(e, "staged") == 0;
+  }();
+  return v;
+}
 
 bool mfma_supported(GemmOp op, const GemmParams& p) {
   // 16-byte chunk loads need K (and K1) in multiples of 8; the k-tile of
@@ -334,6 +620,19 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
       p.tiles_m_max = (p.M + bm - 1) / bm + (p.G < p.M ? p.G : p.M);
     } else {
       p.tiles_m_max = (p.M + bm - 1) / bm;
+    }
+  }
+  // k-contiguous operands with whole k-tiles go straight to LDS
+  if (p.K % 64 == 0 && !force_staged()) {
+    switch (op) {
+      case kOpRouter:
+        return launch_dl_sized<false, kEpiStore, float>(big, p, s);
+      case kOpGemm1:
+        return launch_dl_sized<true, kEpiSwiglu, bf16>(big, p, s);
+      case kOpGemm2:
+        return launch_dl_sized<false, kEpiStore, bf16>(big, p, s);
+      default:
+        break;
     }
   }
   switch (op) {
