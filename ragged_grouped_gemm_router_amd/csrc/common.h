@@ -79,6 +79,7 @@ struct GemmParams {
   void* C; void* C2; void* C3; long ldc; long sC;
   const void* aux_a; const void* aux_b;  // kEpiSwigluBwd: saved a, b (ld = ldc)
   int tiles_m_max;                      // upper bound of row tiles (kSchedM)
+  int group_n;                          // n-tiles per rasterization group
 };
 
 }  // namespace moe

@@ -144,7 +144,7 @@ __device__ __forceinline__ bool lookup_tile(const GemmParams& p, Tile& t) {
   t.k_beg = 0;
   t.k_end = p.K;
   if (SCHED == kSchedM) {
-    constexpr int GN = 4;
+    const int GN = p.group_n;
     const int MT = p.tiles_m_max;
     const int ng = L / (MT * GN);
     const int within = L % (MT * GN);
@@ -533,8 +533,8 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
   const long tiles_n = (p.N + BN - 1) / BN;
   long tiles;
   if (SCHED == kSchedM) {
-    const long ngroups = (tiles_n + 3) / 4;
-    tiles = ngroups * p.tiles_m_max * 4;
+    const long ngroups = (tiles_n + p.group_n - 1) / p.group_n;
+    tiles = ngroups * p.tiles_m_max * p.group_n;
   } else {
     tiles = (long)p.G * ((p.M + BM - 1) / BM) * tiles_n;
   }
@@ -551,7 +551,7 @@ template <int BM, int BN, int BK, int S, int WGM, int WGN, bool DUAL, int EPI,
           typename TO>
 hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
   const long tiles_n = (p.N + BN - 1) / BN;
-  long tiles = (tiles_n + 3) / 4 * p.tiles_m_max * 4;
+  long tiles = (tiles_n + p.group_n - 1) / p.group_n * p.tiles_m_max * p.group_n;
   if (tiles <= 0) return hipSuccess;
   tiles = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
@@ -592,6 +592,16 @@ bool force_staged() {
   return v;
 }
 
+// n-tiles per rasterization group (MOE_TILE_GROUP_N overrides, for tuning)
+int tile_group_n() {
+  static const int v = [] {
+    const char* e = getenv("MOE_TILE_GROUP_N");
+    const int n = e ? atoi(e) : 0;
+    return n > 0 ? n : 4;
+  }();
+  return v;
+}
+
 bool mfma_supported(GemmOp op, const GemmParams& p) {
   // 16-byte chunk loads need K (and K1) in multiples of 8; the k-tile of
   // a K-concatenation must not straddle the seam; transposed (row
@@ -606,6 +616,7 @@ bool mfma_supported(GemmOp op, const GemmParams& p) {
 hipError_t gemm_mfma(GemmOp op, GemmParams p,
                      const int32_t* const* tile_off_by_bm, hipStream_t s) {
   if (!mfma_supported(op, p)) return hipErrorNotSupported;
+  p.group_n = tile_group_n();
   // Big tiles when the average group has enough rows to fill them.
   bool big;
   if (op == kOpWgrad) {
