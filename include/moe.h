@@ -89,7 +89,9 @@ typedef struct moe_desc {
   int32_t d_ff_shared;  /* shared expert hidden size, 0 = none [P3 §5]     */
   int32_t gate;         /* MOE_GATE_SOFTMAX | MOE_GATE_SIGMOID             */
   int32_t act_dtype;    /* MOE_F32 | MOE_BF16                              */
-  int32_t gemm_dtype;   /* = act_dtype, or MOE_MXFP8 (forward, bf16 act)   */
+  int32_t gemm_dtype;   /* = act_dtype, or MOE_MXFP8 (forward only, bf16
+                           act, d_model and d_ff multiples of 128, no
+                           shared expert, no MOE_FLAG_SAVE_ACTS)           */
   int32_t flags;        /* MOE_FLAG_*                                      */
 } moe_desc;
 
@@ -128,7 +130,9 @@ typedef struct moe_fwd_args {
   /* activations */
   void* x_perm;               /* [T*K, d_model] act (MXFP8: E4M3 bytes)      */
   uint8_t* x_perm_scales;     /* MXFP8 only: [T*K, d_model/32] E8M0          */
-  void* h;                    /* [T*K, d_ff] act (MXFP8: optional, unused)   */
+  void* h;                    /* [T*K, d_ff] act. MXFP8: E4M3 codes [T*K,
+                                 d_ff] then E8M0 scales [T*K, d_ff/32]
+                                 (fits in a bf16-sized buffer)              */
   void* y_perm;               /* [T*K, d_model] act, unweighted expert out   */
   void* y_shared;             /* [T, d_model] act; required iff shared       */
   void* act_a;                /* [T*K, d_ff] act; required iff SAVE_ACTS     */
@@ -210,6 +214,12 @@ moe_status moe_permute(const moe_desc* desc, const void* x,
  *   y_perm[p] = h[p] W2_e^T                      (stored in act dtype)
  * The tile list over (expert, row tile) is built on the device from
  * offsets; no host synchronisation. act_a/act_b (optional) receive a, b.
+ * MXFP8 (gemm_dtype): both operands of both GEMMs are E4M3 with one E8M0
+ * scale per 32 elements along the contraction dimension (x_perm and W1/W3
+ * along d_model, h and W2 along d_ff), accumulated in fp32 [P2 MXFP8
+ * grouped GEMM; P3 §13.6 per-tile scales]; h is quantised from the fp32
+ * SwiGLU value in the GEMM 1 epilogue and stored in the h buffer as codes
+ * then scales; y_perm is bf16.
  * If x_shared is non-NULL and d_ff_shared > 0, the shared expert runs on
  * every token: y_shared = SwiGLU_shared(x_shared). MXFP8: x_perm and
  * x_perm_scales are E4M3/E8M0, weights must be quantised; h may be NULL. */
@@ -237,7 +247,8 @@ moe_status moe_forward(const moe_desc* desc, const moe_fwd_args* args,
                        void* ws, size_t ws_bytes, void* stream);
 
 /* Whole backward (see moe_bwd_args). Deterministic: weight gradients are
- * owned tile by tile (no split-K atomics). */
+ * owned tile by tile (no split-K atomics). MOE_EUNSUPPORTED for MXFP8
+ * descriptors and for a shared expert. */
 moe_status moe_backward(const moe_desc* desc, const moe_bwd_args* args,
                         void* ws, size_t ws_bytes, void* stream);
 

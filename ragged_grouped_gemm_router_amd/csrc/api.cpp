@@ -31,11 +31,16 @@ moe_status check_desc(const moe_desc* d) {
   if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_EINVAL;
   if (d->flags & ~MOE_FLAG_SAVE_ACTS) return MOE_EINVAL;
   if (d->K > MOE_K_MAX || d->E > MOE_E_MAX) return MOE_EUNSUPPORTED;
-  if (d->gemm_dtype != d->act_dtype) {
-    if (d->gemm_dtype == MOE_MXFP8 && d->act_dtype == MOE_BF16) return MOE_EUNSUPPORTED;
+  if (d->gemm_dtype != d->act_dtype &&
+      !(d->gemm_dtype == MOE_MXFP8 && d->act_dtype == MOE_BF16))
     return MOE_EINVAL;
-  }
   if (d->d_model % 8 || d->d_ff % 8 || d->d_ff_shared % 8) return MOE_EUNSUPPORTED;
+  if (d->gemm_dtype == MOE_MXFP8) {
+    // whole 128-element k-tiles for both GEMMs; no shared expert and no
+    // saved pre-activations on this path
+    if (d->d_model % 128 || d->d_ff % 128) return MOE_EUNSUPPORTED;
+    if (d->d_ff_shared > 0 || (d->flags & MOE_FLAG_SAVE_ACTS)) return MOE_EUNSUPPORTED;
+  }
   if ((long)d->T * d->K > kMaxCopies) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
@@ -142,14 +147,17 @@ hipError_t do_route(const moe_desc* d, const void* x, const void* wr,
 
 hipError_t do_permute(const moe_desc* d, const void* x, const int32_t* idx,
                       int32_t* counts, int32_t* offsets, int32_t* src,
-                      int32_t* dest, void* x_perm, const FwdWs& ws,
-                      hipStream_t s) {
+                      int32_t* dest, void* x_perm, uint8_t* x_perm_scales,
+                      const FwdWs& ws, hipStream_t s) {
   const int TK = d->T * d->K;
   hipError_t e = launch_histogram_scan(idx, TK, d->E, ws.block_hist, counts,
                                        offsets, ws.tile_off, s);
   if (e != hipSuccess) return e;
   e = launch_rank(idx, TK, d->E, ws.block_hist, src, dest, s);
   if (e != hipSuccess) return e;
+  if (d->gemm_dtype == MOE_MXFP8)
+    return launch_scatter_rows_mxfp8(x, d->T, d->K, d->d_model, dest,
+                                     (uint8_t*)x_perm, x_perm_scales, s);
   return launch_scatter_rows(x, d->T, d->K,
                              (long)d->d_model * act_bytes(d->act_dtype), dest,
                              x_perm, s);
@@ -176,6 +184,39 @@ hipError_t do_gemm2(const moe_desc* d, const void* h, const int32_t* off,
   p.B = w2; p.ldb = f; p.sB = (long)d->d_model * f;
   p.C = y; p.ldc = d->d_model;
   return run_gemm(kOpGemm2, d->act_dtype, p, toff, s);
+}
+
+// MXFP8 expert GEMMs. h lives in the caller's h buffer as E4M3 codes
+// [T*K, d_ff] followed by E8M0 scales [T*K, d_ff/32].
+hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
+                         const uint8_t* x_perm_scales, const int32_t* offsets,
+                         const moe_expert_weights* rw, void* h, void* y_perm,
+                         const FwdWs& ws, hipStream_t s, void* ev_mid) {
+  const int TK = d->T * d->K, dm = d->d_model, f = d->d_ff;
+  uint8_t* hq = (uint8_t*)h;
+  uint8_t* hs = hq + (size_t)TK * f;
+  GemmParams p = gp();
+  p.M = TK; p.N = f; p.K = dm; p.G = d->E; p.off = offsets;
+  p.A = x_perm; p.lda = dm; p.As = x_perm_scales;
+  p.B = rw->w1; p.B2 = rw->w3; p.ldb = dm; p.sB = (long)f * dm;
+  p.Bs = rw->w1_scales; p.B2s = rw->w3_scales;
+  p.ld_s = dm / 32; p.sBs = (long)f * (dm / 32);
+  p.C = hq; p.C2 = hs; p.ldc = f;
+  hipError_t e = gemm_mfma(kOpGemm1Mx, p, ws.tile_off, s);
+  if (e != hipSuccess) return e;
+  record(ev_mid, s);
+  p = gp();
+  p.M = TK; p.N = dm; p.K = f; p.G = d->E; p.off = offsets;
+  p.A = hq; p.lda = f; p.As = hs;
+  p.B = rw->w2; p.ldb = f; p.sB = (long)dm * f;
+  p.Bs = rw->w2_scales; p.ld_s = f / 32; p.sBs = (long)dm * (f / 32);
+  p.C = y_perm; p.ldc = dm;
+  return gemm_mfma(kOpGemm2Mx, p, ws.tile_off, s);
+}
+
+bool mx_weights_ok(const moe_expert_weights* w) {
+  return w && w->w1 && w->w3 && w->w2 && w->w1_scales && w->w3_scales &&
+         w->w2_scales;
 }
 
 hipError_t do_experts(const moe_desc* d, const void* x_perm,
@@ -250,18 +291,19 @@ moe_status moe_permute(const moe_desc* d, const void* x,
                        int32_t* offsets, int32_t* sorted_src, int32_t* dest,
                        void* x_perm, uint8_t* x_perm_scales, void* ws,
                        size_t ws_bytes, void* stream) {
-  (void)x_perm_scales;
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
   if (d->T == 0) return MOE_OK;  // nothing is accessed
   if (!x || !topk_idx || !counts || !offsets || !sorted_src || !dest ||
       !x_perm || !ws)
     return MOE_EINVAL;
+  if (d->gemm_dtype == MOE_MXFP8 && !x_perm_scales) return MOE_EINVAL;
   if (ws_bytes < fwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
   FwdWs w;
   fwd_ws_layout(d, (char*)ws, &w);
   return hip_status(do_permute(d, x, topk_idx, counts, offsets, sorted_src,
-                               dest, x_perm, w, (hipStream_t)stream));
+                               dest, x_perm, x_perm_scales, w,
+                               (hipStream_t)stream));
 }
 
 moe_status moe_grouped_gemm_swiglu(const moe_desc* d, const void* x_perm,
@@ -273,12 +315,13 @@ moe_status moe_grouped_gemm_swiglu(const moe_desc* d, const void* x_perm,
                                    void* y_perm, void* y_shared, void* act_a,
                                    void* act_b, void* ws, size_t ws_bytes,
                                    void* stream) {
-  (void)x_perm_scales;
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
   if (d->T == 0) return MOE_OK;  // nothing is accessed
   if (!x_perm || !offsets || !weights_ok(routed) || !h || !y_perm || !ws)
     return MOE_EINVAL;
+  const bool mx = d->gemm_dtype == MOE_MXFP8;
+  if (mx && (!x_perm_scales || !mx_weights_ok(routed))) return MOE_EINVAL;
   const bool use_shared = x_shared && d->d_ff_shared > 0;
   if (use_shared && (!weights_ok(shared) || !y_shared)) return MOE_EINVAL;
   if ((d->flags & MOE_FLAG_SAVE_ACTS) && (!act_a || !act_b)) return MOE_EINVAL;
@@ -288,6 +331,9 @@ moe_status moe_grouped_gemm_swiglu(const moe_desc* d, const void* x_perm,
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_tile_prefix(offsets, d->E, w.tile_off, s);
   if (e != hipSuccess) return MOE_EHIP;
+  if (mx)
+    return hip_status(do_experts_mx(d, x_perm, x_perm_scales, offsets, routed,
+                                    h, y_perm, w, s, nullptr));
   const bool save = d->flags & MOE_FLAG_SAVE_ACTS;
   return hip_status(do_experts(d, x_perm, offsets, routed,
                                use_shared ? x_shared : nullptr, shared, h,
@@ -322,6 +368,8 @@ moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
   if (shared && (!weights_ok(&a->shared) || !a->y_shared)) return MOE_EINVAL;
   const bool save = d->flags & MOE_FLAG_SAVE_ACTS;
   if (save && (!a->act_a || !a->act_b)) return MOE_EINVAL;
+  const bool mx = d->gemm_dtype == MOE_MXFP8;
+  if (mx && (!a->x_perm_scales || !mx_weights_ok(&a->routed))) return MOE_EINVAL;
   if (ws_bytes < fwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
   FwdWs w;
   fwd_ws_layout(d, (char*)ws, &w);
@@ -332,13 +380,17 @@ moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
   if (e != hipSuccess) return MOE_EHIP;
   record(a->events[1], s);
   e = do_permute(d, a->x, a->topk_idx, a->counts, a->offsets, a->sorted_src,
-                 a->dest, a->x_perm, w, s);
+                 a->dest, a->x_perm, a->x_perm_scales, w, s);
   if (e != hipSuccess) return MOE_EHIP;
   record(a->events[2], s);
-  e = do_experts(d, a->x_perm, a->offsets, &a->routed,
-                 shared ? a->x : nullptr, &a->shared, a->h, a->y_perm,
-                 a->y_shared, save ? a->act_a : nullptr,
-                 save ? a->act_b : nullptr, w, s, a->events[3]);
+  if (mx)
+    e = do_experts_mx(d, a->x_perm, a->x_perm_scales, a->offsets, &a->routed,
+                      a->h, a->y_perm, w, s, a->events[3]);
+  else
+    e = do_experts(d, a->x_perm, a->offsets, &a->routed,
+                   shared ? a->x : nullptr, &a->shared, a->h, a->y_perm,
+                   a->y_shared, save ? a->act_a : nullptr,
+                   save ? a->act_b : nullptr, w, s, a->events[3]);
   if (e != hipSuccess) return MOE_EHIP;
   record(a->events[4], s);
   e = launch_combine(d->act_dtype, a->y_perm, a->dest, a->topk_w,
@@ -359,7 +411,7 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
       !a->dx || !a->dw1 || !a->dw3 || !a->dw2 || !a->d_topk_w)
     return MOE_EINVAL;
   if ((a->act_a == nullptr) != (a->act_b == nullptr)) return MOE_EINVAL;
-  if (d->d_ff_shared > 0) return MOE_EUNSUPPORTED;
+  if (d->d_ff_shared > 0 || d->gemm_dtype == MOE_MXFP8) return MOE_EUNSUPPORTED;
   if (ws_bytes < bwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
   BwdWs w;
   bwd_ws_layout(d, (char*)ws, &w);
@@ -437,8 +489,9 @@ moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows,
                               void* stream) {
   if (!src_bf16 || !q || !scales || rows < 0 || cols <= 0) return MOE_EINVAL;
   if (cols % 32) return MOE_EUNSUPPORTED;
-  (void)stream;
-  return MOE_EUNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  return hip_status(launch_quantize_mxfp8(src_bf16, rows, cols, q, scales,
+                                          (hipStream_t)stream));
 }
 
 }  // extern "C"

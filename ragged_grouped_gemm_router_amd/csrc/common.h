@@ -68,6 +68,8 @@ enum : int {
   kEpiStore = 0,      // C = acc
   kEpiSwiglu = 1,     // C = silu(acc) * acc2; C2 = acc, C3 = acc2 if set
   kEpiSwigluBwd = 2,  // dh = acc; C = dh * b * silu'(a), C2 = dh * silu(a)
+  kEpiSwigluMx = 3,   // h = silu(acc) * acc2 as MXFP8: C = E4M3 codes [M, N],
+                      // C2 = E8M0 scales [M, N/32] (blocks along N)
 };
 
 struct GemmParams {
@@ -80,6 +82,10 @@ struct GemmParams {
   const void* aux_a; const void* aux_b;  // kEpiSwigluBwd: saved a, b (ld = ldc)
   int tiles_m_max;                      // upper bound of row tiles (kSchedM)
   int group_n;                          // n-tiles per rasterization group
+  // MXFP8 operands: E8M0 scales per 32 elements along k, row stride ld_s
+  // bytes (= K/32); B scales have group stride sBs bytes.
+  const uint8_t* As; const uint8_t* Bs; const uint8_t* B2s;
+  long ld_s; long sBs;
 };
 
 }  // namespace moe

@@ -13,6 +13,8 @@ enum GemmOp : int {
   kOpDgrad2 = 3,  // dh = dy_perm W2_e -> (da, db) via the SwiGLU derivative
   kOpDgrad1 = 4,  // dx_perm = da W1_e + db W3_e          (K-concatenation)
   kOpWgrad = 5,   // dW_e = L_e^T R_e over the expert's rows (ragged K)
+  kOpGemm1Mx = 6, // GEMM 1 on MXFP8 operands; h written as MXFP8
+  kOpGemm2Mx = 7, // GEMM 2 on MXFP8 operands; y_perm in bf16
 };
 
 // Row-tile heights for which the permute step publishes tile prefixes.

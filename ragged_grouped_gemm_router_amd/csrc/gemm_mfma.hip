@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "gemm.h"
+#include "mx.h"
 
 namespace moe {
 namespace {
@@ -335,20 +336,76 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm(GemmParams p) {
 // multiple of BK.
 // ---------------------------------------------------------------------------
 
-template <int BM, int BN, int BK, int S, int WGM, int WGN, bool DUAL, int EPI,
-          typename TO>
+// MXFP8 epilogue of the up-projection: h = silu(a) * b quantised along N in
+// blocks of 32. In the 32x32 accumulator layout the 32 columns of one block
+// row sit in the 32 lanes of a half-wave (same register), so the block's
+// amax is a 5-step butterfly within the half.
+template <int WM, int WN, int MB, int NB>
+__device__ __forceinline__ void epilogue_swiglu_mx(const GemmParams& p,
+                                                   const Tile& t,
+                                                   f32x16 (&acc)[2][MB][NB],
+                                                   int wm, int wn, int lane) {
+  uint8_t* hq = (uint8_t*)p.C;
+  uint8_t* hs = (uint8_t*)p.C2;
+  const int ldq = p.ldc, lds_h = p.ldc / 32;
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int col = t.n0 + wn * WN + j * 32 + lane % 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = t.m0 + wm * WM + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+        const float a = acc[0][i][j][r], b = acc[1][i][j][r];
+        const float h = a * fast_sigmoid(a) * b;
+        float m = fabsf(h);
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+        const int X = mx_block_exponent(m);
+        if (row < t.m_end && col < p.N) {
+          hq[(long)row * ldq + col] = (uint8_t)e4m3_encode(h * mx_inv_scale(X));
+          if (lane % 32 == 0) hs[(long)row * lds_h + col / 32] = (uint8_t)(X + 127);
+        }
+      }
+    }
+  }
+}
+
+// Operand formats of the direct-to-LDS kernel.
+//   bf16 : v_mfma_f32_32x32x16_bf16, 8 bf16 per lane per fragment
+//   MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3, 32 bytes per lane per
+//          fragment = one 32-element MX block of the lane's row, with that
+//          block's E8M0 scale passed per lane
+template <bool MX> struct Fmt;
+template <> struct Fmt<false> {
+  static constexpr int ES = 2, KSTEP = 16, FC = 1;
+  typedef bf16x8 Frag;
+};
+template <> struct Fmt<true> {
+  static constexpr int ES = 1, KSTEP = 64, FC = 2;
+  typedef int32_t Frag __attribute__((ext_vector_type(8)));
+};
+
+template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
+          typename TO, bool MX>
 __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) {
+  using F = Fmt<MX>;
+  typedef typename F::Frag Frag;
   constexpr int NW = WGM * WGN;
   constexpr int NB_OPS = DUAL ? 2 : 1;
-  constexpr int CPR = BK / 8;
-  constexpr int RPI = 64 / CPR;  // rows per 1 KB wave instruction
+  constexpr int RB = 128;            // bytes of one tile row per k-tile
+  constexpr int BK = RB / F::ES;     // k-tile in elements
+  constexpr int KS = BK / F::KSTEP;  // MFMA k-substeps per k-tile
+  constexpr int CPR = RB / 16;       // 16-byte chunks per tile row
+  constexpr int RPI = 64 / CPR;      // rows per 1 KB wave instruction
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MB = WM / 32, NB = WN / 32;
-  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
   constexpr int STAGE = A_BYTES + NB_OPS * B_BYTES;
   constexpr int A_INS = BM / RPI / NW, B_INS = BN / RPI / NW;
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile shape");
-  static_assert(MB >= 1 && NB >= 1 && BK % 16 == 0, "tile shape");
+  static_assert(MB >= 1 && NB >= 1, "tile shape");
+  static_assert(S == 2 && KS % 2 == 0, "two stages, even substep count");
 
   __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
 
@@ -357,31 +414,31 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int wm = wave / WGN, wn = wave % WGN;
 
-  // per-lane source offsets (elements) of each load instruction
+  // per-lane byte offsets of each DMA instruction's source
   const int r_in = lane / CPR, phys = lane % CPR;
-  const bf16* A = (const bf16*)p.A;
+  const char* A = (const char*)p.A;
   long a_off[A_INS];
 #pragma unroll
   for (int j = 0; j < A_INS; ++j) {
     const int row = (j * NW + wave) * RPI + r_in;
     const int grow = min(t.m0 + row, t.m_end - 1);
-    a_off[j] = (long)grow * p.lda + swz<CPR>(row, phys) * 8;
+    a_off[j] = (long)grow * p.lda * F::ES + swz<CPR>(row, phys) * 16;
   }
-  const bf16* Bop[NB_OPS];
-  Bop[0] = (const bf16*)p.B + (long)t.g * p.sB;
-  if (DUAL) Bop[NB_OPS - 1] = (const bf16*)p.B2 + (long)t.g * p.sB;
+  const char* Bop[NB_OPS];
+  Bop[0] = (const char*)p.B + (long)t.g * p.sB * F::ES;
+  if (DUAL) Bop[NB_OPS - 1] = (const char*)p.B2 + (long)t.g * p.sB * F::ES;
   long b_off[B_INS];
 #pragma unroll
   for (int j = 0; j < B_INS; ++j) {
     const int row = (j * NW + wave) * RPI + r_in;
     const int grow = min(t.n0 + row, p.N - 1);
-    b_off[j] = (long)grow * p.ldb + swz<CPR>(row, phys) * 8;
+    b_off[j] = (long)grow * p.ldb * F::ES + swz<CPR>(row, phys) * 16;
   }
 
   // DMA instruction d of a k-tile (d < A_INS: operand A, then each B)
   auto issue_one = [&](int kt, int stage, int d) {
     char* base = lds + stage * STAGE;
-    const long k0 = (long)kt * BK;
+    const long k0 = (long)kt * RB;
     if (d < A_INS) {
       __builtin_amdgcn_global_load_lds(
           (const void*)(A + a_off[d] + k0),
@@ -401,6 +458,33 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     for (int d = 0; d < A_INS + NB_OPS * B_INS; ++d) issue_one(kt, stage, d);
   };
 
+  // MXFP8: the 4 E8M0 codes of a row for one k-tile are one aligned dword;
+  // they are loaded a tile ahead (s_nxt) and swapped in at the tile barrier
+  constexpr int NSC = MX ? MB + NB_OPS * NB : 1;
+  const uint8_t* sc_row[NSC];
+  uint32_t s_cur[NSC], s_nxt[NSC];
+  if constexpr (MX) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int row = min(t.m0 + wm * WM + i * 32 + lane % 32, t.m_end - 1);
+      sc_row[i] = p.As + (long)row * p.ld_s;
+    }
+#pragma unroll
+    for (int o = 0; o < NB_OPS; ++o)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int row = min(t.n0 + wn * WN + j * 32 + lane % 32, p.N - 1);
+        sc_row[MB + o * NB + j] =
+            (o ? p.B2s : p.Bs) + (long)t.g * p.sBs + (long)row * p.ld_s;
+      }
+  }
+  auto load_scales = [&](int kt) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int q = 0; q < NSC; ++q) s_nxt[q] = *(const uint32_t*)(sc_row[q] + kt * 4);
+    }
+  };
+
   f32x16 acc[NB_OPS][MB][NB];
 #pragma unroll
   for (int o = 0; o < NB_OPS; ++o)
@@ -410,34 +494,61 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
       for (int j = 0; j < NB; ++j) acc[o][i][j] = f32x16{};
 
   const int nk = p.K / BK;
-  constexpr int KS = BK / 16;  // 16-wide k-substeps per k-tile
-  static_assert(S == 2 && KS % 2 == 0, "two stages, even substep count");
 
-  // fragments of one 16-wide k-substep
+  // fragments of one k-substep
   struct Frags {
-    bf16x8 a[MB], b[NB_OPS][NB];
+    Frag a[MB], b[NB_OPS][NB];
   };
   constexpr int N_READ = MB + NB_OPS * NB;        // fragment reads per substep
   constexpr int N_MFMA = NB_OPS * MB * NB;        // MFMAs per substep
   constexpr int N_LOAD = A_INS + NB_OPS * B_INS;  // DMA instructions per k-tile
+  auto read_frag = [&](const char* sb, int row, int ks) {
+    if constexpr (MX) {
+      // The scaled MFMA takes bytes 0-15 of a lane from the substep's first
+      // 32-element block and bytes 16-31 from its second; half-wave h holds
+      // the h-th 16 elements of each block (chunks 4 ks + h and 4 ks + 2 + h
+      // of the 128-byte row), matching the per-lane scales of block
+      // 2 ks + h of lanes h*32 + row.
+      const int c_lo = ks * 4 + lane / 32, c_hi = c_lo + 2;
+      const u32x4 lo = *(const u32x4*)(sb + row * RB + swz<CPR>(row, c_lo) * 16);
+      const u32x4 hi = *(const u32x4*)(sb + row * RB + swz<CPR>(row, c_hi) * 16);
+      return Frag{(int32_t)lo[0], (int32_t)lo[1], (int32_t)lo[2], (int32_t)lo[3],
+                  (int32_t)hi[0], (int32_t)hi[1], (int32_t)hi[2], (int32_t)hi[3]};
+    } else {
+      const int c = ks * 2 + lane / 32;
+      return *(const Frag*)(sb + row * RB + swz<CPR>(row, c) * 16);
+    }
+  };
   // fragment r of substep ks (r < MB: A block r, else B block)
   auto read_one = [&](const char* sb, int ks, Frags& f, int r) {
-    const int c = ks * 2 + lane / 32;
     if (r < MB) {
-      const int row = wm * WM + r * 32 + lane % 32;
-      f.a[r] = *(const bf16x8*)(sb + row * (BK * 2) + swz<CPR>(row, c) * 16);
+      f.a[r] = read_frag(sb, wm * WM + r * 32 + lane % 32, ks);
     } else {
       const int o = (r - MB) / NB, j = (r - MB) % NB;
-      const int row = wn * WN + j * 32 + lane % 32;
-      f.b[o][j] = *(const bf16x8*)(sb + A_BYTES + o * B_BYTES + row * (BK * 2) +
-                                   swz<CPR>(row, c) * 16);
+      f.b[o][j] = read_frag(sb + A_BYTES + o * B_BYTES,
+                            wn * WN + j * 32 + lane % 32, ks);
+    }
+  };
+  // per-lane E8M0 scale operands of one substep: block ks*2 + lane/32
+  uint32_t sc[NSC];
+  auto substep_scales = [&](int ks) {
+    if constexpr (MX) {
+      const int sh = 8 * (ks * 2 + lane / 32);
+#pragma unroll
+      for (int q = 0; q < NSC; ++q) sc[q] = (s_cur[q] >> sh) & 0xffu;
     }
   };
   // MFMA q of a substep, q = (o * MB + i) * NB + j
   auto mfma_one = [&](const Frags& f, int q) {
     const int o = q / (MB * NB), i = (q / NB) % MB, j = q % NB;
-    acc[o][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        f.a[i], f.b[o][j], acc[o][i][j], 0, 0, 0);
+    if constexpr (MX) {
+      acc[o][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          f.a[i], f.b[o][j], acc[o][i][j], 0, 0, 0, (int)sc[i], 0,
+          (int)sc[MB + o * NB + j]);
+    } else {
+      acc[o][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          f.a[i], f.b[o][j], acc[o][i][j], 0, 0, 0);
+    }
   };
 
   // Tile barrier: this wave's LDS reads and DMA writes are complete (vmcnt
@@ -451,7 +562,9 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
-  // Prologue: k-tiles 0 and 1 in flight; wait for tile 0 only.
+  // Prologue: (scales of k-tile 0,) k-tiles 0 and 1 in flight; wait for
+  // everything but tile 1.
+  load_scales(0);
   issue(0, 0);
   if (nk > 1) {
     issue(1, 1);
@@ -459,18 +572,24 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   } else {
     barrier_after(std::integral_constant<int, 0>{});
   }
+  if constexpr (MX) {
+#pragma unroll
+    for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
+  }
   Frags fa, fb;
 #pragma unroll
   for (int r = 0; r < N_READ; ++r) read_one(lds, 0, fa, r);
 
-  // One region per 16-wide substep. The MFMAs run on fragments read a
-  // region earlier; the memory instructions of the region (the next
-  // substep's fragment reads and, at the last substep of a k-tile, the DMA
-  // of k-tile kt+2 into the stage tile kt used) sit between them, at most a
-  // few per MFMA, so the in-order issue of a long memory burst never leaves
-  // the matrix pipe idle. The first H MFMAs precede every new read: their
-  // wait for the current fragments then covers no read issued here. Every
-  // step is fenced with sched_barrier to keep this order.
+  // One region per k-substep. The MFMAs run on fragments read a region
+  // earlier; the memory instructions of the region (the next substep's
+  // fragment reads and, at the last substep of a k-tile, the DMA of k-tile
+  // kt+2 into the stage tile kt used) sit between them, at most a few per
+  // MFMA, so the in-order issue of a long memory burst never leaves the
+  // matrix pipe idle. The first H MFMAs precede every new read: their wait
+  // for the current fragments then covers no read issued here. Every step
+  // is fenced with sched_barrier to keep this order. (MXFP8: the next
+  // tile's scales are fetched in the first region and swapped in after the
+  // tile barrier, once their wait is free.)
   constexpr int H = N_MFMA >= 8 ? 2 : 1;
 #define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
   for (int kt = 0; kt < nk; ++kt) {
@@ -484,15 +603,24 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
       // memory ops of this region: N_READ reads (+ N_LOAD DMAs if last)
       constexpr int NM_MAX = N_READ + N_LOAD;
       const int nm = last ? NM_MAX : N_READ;
+      substep_scales(ks);
       MOE_FENCE();
 #pragma unroll
       for (int q = 0; q < H; ++q) mfma_one(cur, q);
       MOE_FENCE();
+      if (ks == 0) {
+        load_scales(min(kt + 1, nk - 1));
+        MOE_FENCE();
+      }
       if (last) {
         // Branch-free so the wait counters stay exact: past the last tile
         // the reads return unused data and the DMA fetches the last k-tile
         // again into a stage that is no longer read.
         barrier_after(std::integral_constant<int, 0>{});
+        if constexpr (MX) {
+#pragma unroll
+          for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
+        }
         MOE_FENCE();
       }
       int m = 0;  // next memory op
@@ -524,7 +652,10 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   }
 #undef MOE_FENCE
   __builtin_amdgcn_s_waitcnt(0);  // no load may still target LDS at exit
-  epilogue<WM, WN, MB, NB, NB_OPS, EPI, kSchedM, TO>(p, t, acc, wm, wn, lane);
+  if constexpr (EPI == kEpiSwigluMx)
+    epilogue_swiglu_mx<WM, WN, MB, NB>(p, t, acc, wm, wn, lane);
+  else
+    epilogue<WM, WN, MB, NB, NB_OPS, EPI, kSchedM, TO>(p, t, acc, wm, wn, lane);
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, bool A_KC, bool B_KC,
@@ -547,26 +678,26 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int S, int WGM, int WGN, bool DUAL, int EPI,
-          typename TO>
+template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
+          typename TO, bool MX>
 hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
   const long tiles_n = (p.N + BN - 1) / BN;
   long tiles = (tiles_n + p.group_n - 1) / p.group_n * p.tiles_m_max * p.group_n;
   if (tiles <= 0) return hipSuccess;
   tiles = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, BK, S, WGM, WGN, DUAL, EPI, TO>),
+  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, S, WGM, WGN, DUAL, EPI, TO, MX>),
                      dim3((unsigned)tiles), dim3(WGM * WGN * kWave), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool DUAL, int EPI, typename TO>
+template <bool DUAL, int EPI, typename TO, bool MX = false>
 hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
   // big: 256 x 256 outputs (256 x 128 x 2 dual) over 8 waves, two per
   // SIMD, each holding 128 x 64 (128 x 32 x 2) in accumulators.
   if (big)
-    return launch_dl<256, DUAL ? 128 : 256, 64, 2, 2, 4, DUAL, EPI, TO>(p, s);
-  return launch_dl<128, DUAL ? 64 : 128, 64, 2, 2, 2, DUAL, EPI, TO>(p, s);
+    return launch_dl<256, DUAL ? 128 : 256, 2, 2, 4, DUAL, EPI, TO, MX>(p, s);
+  return launch_dl<128, DUAL ? 64 : 128, 2, 2, 2, DUAL, EPI, TO, MX>(p, s);
 }
 
 // Large tiles: 256 x 256 outputs (256 x 128 per B in the dual form),
@@ -607,6 +738,10 @@ bool mfma_supported(GemmOp op, const GemmParams& p) {
   // a K-concatenation must not straddle the seam; transposed (row
   // contiguous) operands are loaded 8 rows at a time.
   if (p.K % 8) return false;
+  // MXFP8 products run only on the direct-to-LDS kernel: whole 128-byte
+  // k-tiles (K % 128) and 32-column scale blocks in the output (N % 32)
+  if ((op == kOpGemm1Mx || op == kOpGemm2Mx) && (p.K % 128 || p.N % 32))
+    return false;
   if (op == kOpDgrad1 && p.K1 % 64) return false;
   if ((op == kOpDgrad2 || op == kOpDgrad1) && p.N % 8) return false;
   if (op == kOpWgrad && (p.M % 8 || p.N % 8)) return false;
@@ -646,6 +781,10 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
         break;
     }
   }
+  if (op == kOpGemm1Mx)
+    return launch_dl_sized<true, kEpiSwigluMx, bf16, true>(big, p, s);
+  if (op == kOpGemm2Mx)
+    return launch_dl_sized<false, kEpiStore, bf16, true>(big, p, s);
   switch (op) {
     case kOpRouter:
       return launch_sized<true, true, false, kEpiStore, kSchedM, float>(big, p, s);
@@ -659,6 +798,8 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
       return launch_sized<true, false, false, kEpiStore, kSchedM, bf16>(big, p, s);
     case kOpWgrad:
       return launch_sized<false, false, false, kEpiStore, kSchedK, bf16>(big, p, s);
+    default:
+      break;
   }
   return hipErrorInvalidValue;
 }

@@ -16,8 +16,35 @@ def act_torch_dtype(desc: B.MoeDesc) -> torch.dtype:
     return torch.float32 if desc.act_dtype == B.MOE_F32 else torch.bfloat16
 
 
+def is_mx(desc: B.MoeDesc) -> bool:
+    return desc.gemm_dtype == B.MOE_MXFP8
+
+
+def quantize_mxfp8(t: torch.Tensor):
+    """MX-quantise a bf16 tensor along its last dimension on the device:
+    (E4M3 codes as uint8 with t's shape, E8M0 scales [..., cols/32])."""
+    cols = t.shape[-1]
+    rows = t.numel() // cols
+    q = torch.empty(t.shape, dtype=torch.uint8, device=t.device)
+    sc = torch.empty(*t.shape[:-1], cols // 32, dtype=torch.uint8,
+                     device=t.device)
+    B.moe_quantize_mxfp8(t.contiguous(), rows, cols, q, sc)
+    return q, sc
+
+
+def quantize_expert_weights(inp: dict) -> dict:
+    """MXFP8 copies of the routed expert weights (quantised once, along
+    each matrix's rows = the contraction dimension of its GEMM)."""
+    out = {}
+    for k in ("w1", "w3", "w2"):
+        out[k], out[k + "_s"] = quantize_mxfp8(inp[k])
+    return out
+
+
 def alloc_forward(desc: B.MoeDesc, device="cuda") -> dict:
-    """Every caller-owned forward buffer for ``desc`` plus the workspace."""
+    """Every caller-owned forward buffer for ``desc`` plus the workspace.
+    MXFP8: x_perm holds E4M3 codes with scales in x_perm_scales, and h
+    holds E4M3 codes [T*K, d_ff] followed by E8M0 scales."""
     T, d, f, E, K = desc.T, desc.d_model, desc.d_ff, desc.E, desc.K
     TK = T * K
     dt = act_torch_dtype(desc)
@@ -36,8 +63,13 @@ def alloc_forward(desc: B.MoeDesc, device="cuda") -> dict:
         "y_perm": torch.empty(TK, d, dtype=dt, device=device),
         "y_shared": (torch.empty(T, d, dtype=dt, device=device)
                      if desc.d_ff_shared else None),
-        "act_a": None, "act_b": None,
+        "act_a": None, "act_b": None, "x_perm_scales": None,
     }
+    if is_mx(desc):
+        u8 = torch.uint8
+        bufs["x_perm"] = torch.empty(TK, d, dtype=u8, device=device)
+        bufs["x_perm_scales"] = torch.empty(TK, d // 32, dtype=u8, device=device)
+        bufs["h"] = torch.empty(TK * f + TK * (f // 32), dtype=u8, device=device)
     if desc.flags & B.MOE_FLAG_SAVE_ACTS:
         bufs["act_a"] = torch.empty(TK, f, dtype=dt, device=device)
         bufs["act_b"] = torch.empty(TK, f, dtype=dt, device=device)
@@ -54,11 +86,16 @@ def fwd_args(inp: dict, bufs: dict,
     a.w_router = p(inp.get("wr"))
     a.route_bias = p(inp.get("bias"))
     a.logits_in = p(inp.get("logits_in"))
-    a.routed = B.expert_weights(inp["w1"], inp["w3"], inp["w2"])
+    if inp.get("mx") is not None:
+        m = inp["mx"]
+        a.routed = B.expert_weights(m["w1"], m["w3"], m["w2"], m["w1_s"],
+                                    m["w3_s"], m["w2_s"])
+    else:
+        a.routed = B.expert_weights(inp["w1"], inp["w3"], inp["w2"])
     a.shared = B.expert_weights(inp.get("ws1"), inp.get("ws3"), inp.get("ws2"))
     for k in ("out", "logits", "topk_idx", "topk_w", "counts", "offsets",
-              "sorted_src", "dest", "x_perm", "h", "y_perm", "y_shared",
-              "act_a", "act_b"):
+              "sorted_src", "dest", "x_perm", "x_perm_scales", "h", "y_perm",
+              "y_shared", "act_a", "act_b"):
         setattr(a, k, p(bufs.get(k)))
     if inp.get("logits_in") is not None:
         a.logits = None

@@ -75,6 +75,11 @@ def test_workspace_size_host_only():
     (dict(gate=7), B.MOE_EINVAL),
     (dict(act_dtype=5), B.MOE_EINVAL),
     (dict(flags=8), B.MOE_EINVAL),
+    (dict(gemm_dtype=B.MOE_F32), B.MOE_EINVAL),             # bf16 act, f32 gemm
+    (dict(gemm_dtype=B.MOE_MXFP8, d_model=160), B.MOE_EUNSUPPORTED),
+    (dict(gemm_dtype=B.MOE_MXFP8, d_ff_shared=128), B.MOE_EUNSUPPORTED),
+    (dict(gemm_dtype=B.MOE_MXFP8, flags=B.MOE_FLAG_SAVE_ACTS),
+     B.MOE_EUNSUPPORTED),
 ])
 def test_bad_descriptor(fields, code):
     d = B.make_desc(64, 128, 256, 8, 2)
