@@ -102,6 +102,9 @@ def main():
                     choices=["mixtral", "deepseek", "skewed", "tiny"])
     ap.add_argument("--cpu-tokens", type=int, default=640)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step: forward (activations saved) "
+                         "plus backward; FLOPs counted as 3x the forward")
     ap.add_argument("--mxfp8", action="store_true",
                     help="expert GEMMs on MXFP8 operands (weights quantised "
                          "once, before timing)")
@@ -135,7 +138,15 @@ def main():
             b["logits_in"] = lg.to(dev)
         batches.append(b)
     desc = B.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.K, cfg.f_shared,
-                       cfg.gate, cfg.dtype, mxfp8=args.mxfp8)
+                       cfg.gate, cfg.dtype, mxfp8=args.mxfp8,
+                       save_acts=args.backward)
+    gbufs = None
+    if args.backward:
+        for s, b in enumerate(batches):
+            b["dy"] = mi.randn((cfg.T, cfg.d), 1.0, s, "dy", cfg.torch_dtype,
+                               dev)
+        gbufs = [L.alloc_backward(desc, dev) for _ in batches]
+        bev = HipEvents(B.MOE_BWD_NEVENTS * max(args.steps, 1))
     if args.mxfp8:
         mx = L.quantize_expert_weights(base)
         for b in batches:
@@ -156,15 +167,25 @@ def main():
         log(f"bench: calibration copy of {args.copy_calibration_mib} MiB done")
         del src, dst
 
+    def step(i, timed):
+        j = i % 3
+        e = (ev.ev[i * B.MOE_FWD_NEVENTS:(i + 1) * B.MOE_FWD_NEVENTS]
+             if timed else None)
+        L.forward(desc, batches[j], bufs[j], events=e)
+        if args.backward:
+            be = (bev.ev[i * B.MOE_BWD_NEVENTS:(i + 1) * B.MOE_BWD_NEVENTS]
+                  if timed else None)
+            L.backward(desc, batches[j], bufs[j], batches[j]["dy"], gbufs[j],
+                       events=be)
+
     log("bench: warmup")
     for i in range(args.warmup):
-        L.forward(desc, batches[i % 3], bufs[i % 3])
+        step(i, False)
     torch.cuda.synchronize()
     log("bench: timed steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
-        e = ev.ev[i * B.MOE_FWD_NEVENTS:(i + 1) * B.MOE_FWD_NEVENTS]
-        L.forward(desc, batches[i % 3], bufs[i % 3], events=e)
+        step(i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / max(args.steps, 1) * 1e3
@@ -181,19 +202,33 @@ def main():
         stage["gemm2_shared"] += ev.ms(o + 3, o + 4)
         stage["combine"] += ev.ms(o + 4, o + 5)
     stage = {k: v / args.steps for k, v in stage.items()}
+    bstage = None
+    if args.backward:
+        names = ["combine_bwd", "recompute", "dgrad2_swiglu_bwd", "dgrad1",
+                 "gather_sum_dx", "wgrad_w2", "wgrad_w1_w3"]
+        bstage = dict.fromkeys(names, 0.0)
+        for i in range(args.steps):
+            o = i * B.MOE_BWD_NEVENTS
+            for q, nm in enumerate(names):
+                bstage[nm] += bev.ms(o + q, o + q + 1) / args.steps
 
     TK = cfg.TK
     b = 4 if cfg.dtype == "f32" else 2
     routed = acc.routed_fwd_flops(cfg.d, cfg.f, TK)
     g1 = acc.gemm1_flops(cfg.d, cfg.f, TK)
-    value = routed / (ms_step * 1e-3) / 1e12
+    step_flops = acc.train_flops(routed) if args.backward else routed
+    value = step_flops / (ms_step * 1e-3) / 1e12
     gemm_s = (stage["gemm1_swiglu"] + stage["gemm2_shared"]) * 1e-3
     perm_bytes = acc.permute_bytes(cfg.T, cfg.K, cfg.d, b)
     comb_bytes = acc.combine_bytes(cfg.T, cfg.K, cfg.d, b, cfg.f_shared > 0)
     k5_tflops = g1 / (stage["gemm1_swiglu"] * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if args.mxfp8 else PEAK_BF16_TFLOPS
+    metric = METRIC
+    if args.backward:
+        metric = ("MoE layer training step (fwd+bwd) TFLOP/s, FLOPs = 3x "
+                  "routed forward")
     line = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -217,6 +252,8 @@ def main():
         "permute_GBps": round(perm_bytes / (stage["permute"] * 1e-3) / 1e9, 1),
         "combine_GBps": round(comb_bytes / (stage["combine"] * 1e-3) / 1e9, 1),
         "stages_ms": {k: round(v, 4) for k, v in stage.items()},
+        "stages_ms_backward": ({k: round(v, 4) for k, v in bstage.items()}
+                               if bstage else None),
         "roofline": {
             "kernel": "grouped GEMM 1 + SwiGLU (mfma_gemm_dl, dual B)",
             "bound": "mfma",
