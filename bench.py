@@ -29,6 +29,38 @@ METRIC = ("MoE layer fwd TFLOP/s (routed FLOPs) + % bf16 MFMA peak; "
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (the fp32 path runs on VALU)
+
+# Bytes per launch of grouped GEMM 1 + SwiGLU on the Mixtral-shaped layer,
+# from rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled by what the same
+# counters read for a 1 GiB device copy (FETCH x2, WRITE x1). They describe
+# the kernel built from sources with this digest and nothing else.
+GEMM1_TRAFFIC = {
+    "workload": "mixtral8x7b_T8192_d4096_f14336_E8_K2",
+    "src_digest": "4c510ec927c1e9af",
+    "fetch_bytes": 9_232_604_160,
+    "write_bytes": 469_762_560,
+}
+GEMM_SOURCES = ("gemm_mfma.hip", "common.h", "gemm.h")
+
+
+def gemm_src_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "ragged_grouped_gemm_router_amd", "csrc",
+                               f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def gemm1_traffic(cfg, mxfp8):
+    """Counter-derived bytes per launch, or None when they do not describe
+    the kernel this run timed (another workload, MXFP8, changed sources)."""
+    t = GEMM1_TRAFFIC
+    if mxfp8 or cfg.name != t["workload"] or gemm_src_digest() != t["src_digest"]:
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
 
 
 def log(*a):
@@ -221,8 +253,23 @@ def main():
     gemm_s = (stage["gemm1_swiglu"] + stage["gemm2_shared"]) * 1e-3
     perm_bytes = acc.permute_bytes(cfg.T, cfg.K, cfg.d, b)
     comb_bytes = acc.combine_bytes(cfg.T, cfg.K, cfg.d, b, cfg.f_shared > 0)
-    k5_tflops = g1 / (stage["gemm1_swiglu"] * 1e-3) / 1e12
-    peak = PEAK_FP8_TFLOPS if args.mxfp8 else PEAK_BF16_TFLOPS
+    k5_s = stage["gemm1_swiglu"] * 1e-3
+    k5_tflops = g1 / k5_s / 1e12
+    peak = (PEAK_FP8_TFLOPS if args.mxfp8 else
+            PEAK_FP32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS)
+    g1_bytes = acc.gemm1_bytes(cfg.E, cfg.d, cfg.f, TK,
+                               1 + 1 / 32 if args.mxfp8 else b)
+    # GEMM 1's own arithmetic intensity decides its bound: the weight
+    # stream dominates when few rows share each expert (DeepSeek-V3 shape).
+    if g1 / g1_bytes < peak * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        k5_roof = {"bound": "hbm",
+                   "achieved": round(g1_bytes / k5_s / 1e9, 1),
+                   "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                   "frac": round(g1_bytes / k5_s / 1e9 / PEAK_HBM_GBPS, 4)}
+    else:
+        k5_roof = {"bound": "mfma", "achieved": round(k5_tflops, 2),
+                   "peak": peak, "unit": "TFLOP/s",
+                   "frac": round(k5_tflops / peak, 4)}
     metric = METRIC
     if args.backward:
         metric = ("MoE layer training step (fwd+bwd) TFLOP/s, FLOPs = 3x "
@@ -255,13 +302,11 @@ def main():
         "stages_ms_backward": ({k: round(v, 4) for k, v in bstage.items()}
                                if bstage else None),
         "roofline": {
-            "kernel": "grouped GEMM 1 + SwiGLU (mfma_gemm_dl, dual B)",
-            "bound": "mfma",
-            "achieved": round(k5_tflops, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(k5_tflops / peak, 4),
-            "traffic": None,
+            "kernel": "grouped GEMM 1 + SwiGLU (dual B: W1 and W3)",
+            **k5_roof,
+            "algorithmic_bytes": int(g1_bytes),
+            "algorithmic_flops": g1,
+            "traffic": gemm1_traffic(cfg, args.mxfp8),
         },
     }
     if not args.no_cpu_baseline:

@@ -63,3 +63,9 @@ def combine_bytes(T: int, K: int, d: int, b: int, shared: bool) -> int:
 
 def expert_weight_bytes(E: int, d: int, f: int, b: int) -> int:
     return 3 * E * d * f * b
+
+
+def gemm1_bytes(E: int, d: int, f: int, copies: int, b: float) -> float:
+    """Grouped GEMM 1 + SwiGLU: read x_perm and W1, W3 once, write h.
+    For MXFP8 pass b = 1 + 1/32 (one E8M0 scale per 32 elements)."""
+    return copies * d * b + 2 * E * f * d * b + copies * f * b
