@@ -48,6 +48,23 @@ __device__ __forceinline__ int swz(int row, int c) {
 #endif
 }
 
+// Raw (untyped, unswizzled) buffer resource starting at `base`, with the
+// range check at its 4 GiB maximum: the DMA loads below address it with a
+// per-lane offset plus a scalar k offset, both far smaller than that.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kBufWord3 = 0x00020000;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1,
+                                           kBufWord3);
+}
+// 16 bytes per lane from r + voff + soff into LDS at dst + 16 * lane. (A
+// plain function: called straight from a kernel template, the builtin
+// keeps clang's host pass from emitting that kernel's launch stub.)
+__device__ __forceinline__ void dma16(Rsrc r, char* dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
+
 template <int ROWS, int BK, int NT, bool KC>
 struct TileLoader {
   static constexpr int CPR = BK / 8;  // 16-byte chunks per LDS row
@@ -411,46 +428,49 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 
   Tile t;
   if (!lookup_tile<BM, BN, kSchedM>(p, t)) return;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  // wave-uniform, so every LDS destination below is a scalar (M0) value
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WGN, wn = wave % WGN;
+  static_assert(CPR == 8, "128-byte tile rows");
 
-  // per-lane byte offsets of each DMA instruction's source
+  // DMA sources: buffer resources based at the tile's first row, so the
+  // per-lane offsets stay small at any problem size and the k-tile offset
+  // rides in the scalar offset; each lane fetches the 16-byte chunk that
+  // belongs at its (swizzled) LDS position.
   const int r_in = lane / CPR, phys = lane % CPR;
-  const char* A = (const char*)p.A;
-  long a_off[A_INS];
+  const Rsrc ra = make_rsrc((const char*)p.A + (long)t.m0 * p.lda * F::ES);
+  int a_off[A_INS];
 #pragma unroll
   for (int j = 0; j < A_INS; ++j) {
     const int row = (j * NW + wave) * RPI + r_in;
     const int grow = min(t.m0 + row, t.m_end - 1);
-    a_off[j] = (long)grow * p.lda * F::ES + swz<CPR>(row, phys) * 16;
+    a_off[j] = (grow - t.m0) * p.lda * F::ES + swz<CPR>(row, phys) * 16;
   }
-  const char* Bop[NB_OPS];
-  Bop[0] = (const char*)p.B + (long)t.g * p.sB * F::ES;
-  if (DUAL) Bop[NB_OPS - 1] = (const char*)p.B2 + (long)t.g * p.sB * F::ES;
-  long b_off[B_INS];
+  Rsrc rb[NB_OPS];
+  rb[0] = make_rsrc((const char*)p.B +
+                    ((long)t.g * p.sB + (long)t.n0 * p.ldb) * F::ES);
+  if (DUAL)
+    rb[NB_OPS - 1] = make_rsrc((const char*)p.B2 +
+                               ((long)t.g * p.sB + (long)t.n0 * p.ldb) * F::ES);
+  int b_off[B_INS];
 #pragma unroll
   for (int j = 0; j < B_INS; ++j) {
     const int row = (j * NW + wave) * RPI + r_in;
     const int grow = min(t.n0 + row, p.N - 1);
-    b_off[j] = (long)grow * p.ldb * F::ES + swz<CPR>(row, phys) * 16;
+    b_off[j] = (grow - t.n0) * p.ldb * F::ES + swz<CPR>(row, phys) * 16;
   }
 
   // DMA instruction d of a k-tile (d < A_INS: operand A, then each B)
   auto issue_one = [&](int kt, int stage, int d) {
     char* base = lds + stage * STAGE;
-    const long k0 = (long)kt * RB;
+    const int k0 = kt * RB;
     if (d < A_INS) {
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(A + a_off[d] + k0),
-          (__attribute__((address_space(3))) void*)(base + (d * NW + wave) * 1024),
-          16, 0, 0);
+      dma16(ra, base + (d * NW + wave) * 1024, a_off[d], k0);
     } else {
       const int o = (d - A_INS) / B_INS, j = (d - A_INS) % B_INS;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(Bop[o] + b_off[j] + k0),
-          (__attribute__((address_space(3))) void*)(base + A_BYTES + o * B_BYTES +
-                                                    (j * NW + wave) * 1024),
-          16, 0, 0);
+      dma16(rb[o], base + A_BYTES + o * B_BYTES + (j * NW + wave) * 1024,
+            b_off[j], k0);
     }
   };
   auto issue = [&](int kt, int stage) {
@@ -502,31 +522,35 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   constexpr int N_READ = MB + NB_OPS * NB;        // fragment reads per substep
   constexpr int N_MFMA = NB_OPS * MB * NB;        // MFMAs per substep
   constexpr int N_LOAD = A_INS + NB_OPS * B_INS;  // DMA instructions per k-tile
-  auto read_frag = [&](const char* sb, int row, int ks) {
+  // Fragment rows differ from the lane's first row by multiples of 32, so
+  // they share its swizzle: the chunk position depends on the lane and the
+  // substep only, and the block offset is an immediate of the LDS read.
+  const int lrow = lane % 32, half = lane / 32, sw = (lrow >> 1) & 7;
+  const int a_row0 = (wm * WM + lrow) * RB;
+  const int b_row0 = A_BYTES + (wn * WN + lrow) * RB;
+  auto read_frag = [&](const char* rowp, int ks) {
     if constexpr (MX) {
       // The scaled MFMA takes bytes 0-15 of a lane from the substep's first
       // 32-element block and bytes 16-31 from its second; half-wave h holds
       // the h-th 16 elements of each block (chunks 4 ks + h and 4 ks + 2 + h
       // of the 128-byte row), matching the per-lane scales of block
       // 2 ks + h of lanes h*32 + row.
-      const int c_lo = ks * 4 + lane / 32, c_hi = c_lo + 2;
-      const u32x4 lo = *(const u32x4*)(sb + row * RB + swz<CPR>(row, c_lo) * 16);
-      const u32x4 hi = *(const u32x4*)(sb + row * RB + swz<CPR>(row, c_hi) * 16);
+      const int c_lo = ks * 4 + half, c_hi = c_lo + 2;
+      const u32x4 lo = *(const u32x4*)(rowp + (c_lo ^ sw) * 16);
+      const u32x4 hi = *(const u32x4*)(rowp + (c_hi ^ sw) * 16);
       return Frag{(int32_t)lo[0], (int32_t)lo[1], (int32_t)lo[2], (int32_t)lo[3],
                   (int32_t)hi[0], (int32_t)hi[1], (int32_t)hi[2], (int32_t)hi[3]};
     } else {
-      const int c = ks * 2 + lane / 32;
-      return *(const Frag*)(sb + row * RB + swz<CPR>(row, c) * 16);
+      return *(const Frag*)(rowp + ((ks * 2 + half) ^ sw) * 16);
     }
   };
   // fragment r of substep ks (r < MB: A block r, else B block)
   auto read_one = [&](const char* sb, int ks, Frags& f, int r) {
     if (r < MB) {
-      f.a[r] = read_frag(sb, wm * WM + r * 32 + lane % 32, ks);
+      f.a[r] = read_frag(sb + a_row0 + r * 32 * RB, ks);
     } else {
       const int o = (r - MB) / NB, j = (r - MB) % NB;
-      f.b[o][j] = read_frag(sb + A_BYTES + o * B_BYTES,
-                            wn * WN + j * 32 + lane % 32, ks);
+      f.b[o][j] = read_frag(sb + b_row0 + o * B_BYTES + j * 32 * RB, ks);
     }
   };
   // per-lane E8M0 scale operands of one substep: block ks*2 + lane/32
@@ -691,12 +715,32 @@ hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// waves of a big direct-to-LDS tile: 4 or 8 (MOE_BIG_TILE_WAVES, for tuning)
+// waves of a big direct-to-LDS tile forced by MOE_BIG_TILE_WAVES (4 or 8,
+// for tuning), else 0
+int big_tile_waves() {
+  static const int v = [] {
+    const char* e = getenv("MOE_BIG_TILE_WAVES");
+    const int n = e ? atoi(e) : 0;
+    return n == 4 || n == 8 ? n : 0;
+  }();
+  return v;
+}
+
+
 template <bool DUAL, int EPI, typename TO, bool MX = false>
 hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
-  // big: 256 x 256 outputs (256 x 128 x 2 dual) over 8 waves, two per
-  // SIMD, each holding 128 x 64 (128 x 32 x 2) in accumulators.
-  if (big)
+  // big: 256 x 256 outputs (256 x 128 x 2 dual), either over 8 waves, two
+  // per SIMD, each holding 128 x 64 (128 x 32 x 2) in accumulators, or over
+  // 4 waves, one per SIMD, each holding 128 x 128 (128 x 64 x 2). Eight
+  // waves hide latency better and win for bf16; the single-B MXFP8 product
+  // takes four (its 8-wave form runs out of registers and spills).
+  if (big) {
+    const int forced = big_tile_waves();
+    if (forced == 4 || (forced == 0 && MX && !DUAL))
+      return launch_dl<256, DUAL ? 128 : 256, 2, 2, 2, DUAL, EPI, TO, MX>(p, s);
     return launch_dl<256, DUAL ? 128 : 256, 2, 2, 4, DUAL, EPI, TO, MX>(p, s);
+  }
   return launch_dl<128, DUAL ? 64 : 128, 2, 2, 2, DUAL, EPI, TO, MX>(p, s);
 }
 
