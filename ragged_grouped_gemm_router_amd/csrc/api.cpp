@@ -48,6 +48,7 @@ moe_status check_desc(const moe_desc* d) {
 // Forward scratch: permute histogram, tile prefixes, shared-expert hidden.
 struct FwdWs {
   int32_t* block_hist;
+  int32_t* rank;
   int32_t* tile_off[kNumTileBM];
   void* h_shared;
 };
@@ -65,6 +66,8 @@ size_t fwd_ws_layout(const moe_desc* d, char* base, FwdWs* w) {
   size_t o = 0;
   if (w) w->block_hist = (int32_t*)(base + o);
   o = align_up(o + sizeof(int32_t) * (size_t)(d->E * (nblk > 0 ? nblk : 1)));
+  if (w) w->rank = (int32_t*)(base + o);
+  o = align_up(o + sizeof(int32_t) * (size_t)(TK > 0 ? TK : 1));
   for (int i = 0; i < kNumTileBM; ++i) {
     if (w) w->tile_off[i] = (int32_t*)(base + o);
     o = align_up(o + sizeof(int32_t) * (size_t)(d->E + 1));
@@ -150,17 +153,18 @@ hipError_t do_permute(const moe_desc* d, const void* x, const int32_t* idx,
                       int32_t* dest, void* x_perm, uint8_t* x_perm_scales,
                       const FwdWs& ws, hipStream_t s) {
   const int TK = d->T * d->K;
-  hipError_t e = launch_histogram_scan(idx, TK, d->E, ws.block_hist, counts,
-                                       offsets, ws.tile_off, s);
+  hipError_t e = launch_hist_rank_scan(idx, TK, d->E, ws.block_hist, ws.rank,
+                                       counts, offsets, ws.tile_off, s);
   if (e != hipSuccess) return e;
-  e = launch_rank(idx, TK, d->E, ws.block_hist, src, dest, s);
-  if (e != hipSuccess) return e;
-  if (d->gemm_dtype == MOE_MXFP8)
+  if (d->gemm_dtype == MOE_MXFP8) {
+    e = launch_slots(idx, ws.block_hist, ws.rank, TK, d->E, dest, src, s);
+    if (e != hipSuccess) return e;
     return launch_scatter_rows_mxfp8(x, d->T, d->K, d->d_model, dest,
                                      (uint8_t*)x_perm, x_perm_scales, s);
-  return launch_scatter_rows(x, d->T, d->K,
-                             (long)d->d_model * act_bytes(d->act_dtype), dest,
-                             x_perm, s);
+  }
+  return launch_scatter(x, idx, ws.block_hist, ws.rank, d->T, d->E, d->K,
+                        (long)d->d_model * act_bytes(d->act_dtype), dest, src,
+                        x_perm, s);
 }
 
 hipError_t do_gemm1(const moe_desc* d, const void* A, const int32_t* off,

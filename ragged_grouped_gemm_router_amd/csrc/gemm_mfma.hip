@@ -422,7 +422,9 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   constexpr int A_INS = BM / RPI / NW, B_INS = BN / RPI / NW;
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile shape");
   static_assert(MB >= 1 && NB >= 1, "tile shape");
-  static_assert(S == 2 && KS % 2 == 0, "two stages, even substep count");
+  static_assert(S >= 2 && (S & (S - 1)) == 0 && KS % 2 == 0,
+                "power-of-two stage count, even substep count");
+  static_assert((S - 1) * (A_INS + (DUAL ? 2 : 1) * B_INS) <= 63, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
 
@@ -586,16 +588,13 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
-  // Prologue: (scales of k-tile 0,) k-tiles 0 and 1 in flight; wait for
-  // everything but tile 1.
+  // Prologue: (scales of k-tile 0,) k-tiles 0 .. S-1 in flight (past the
+  // last tile, the last one again, into stages nobody reads); wait for
+  // tile 0.
   load_scales(0);
-  issue(0, 0);
-  if (nk > 1) {
-    issue(1, 1);
-    barrier_after(std::integral_constant<int, N_LOAD>{});
-  } else {
-    barrier_after(std::integral_constant<int, 0>{});
-  }
+#pragma unroll
+  for (int i = 0; i < S; ++i) issue(min(i, nk - 1), i);
+  barrier_after(std::integral_constant<int, (S - 1) * N_LOAD>{});
   if constexpr (MX) {
 #pragma unroll
     for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
@@ -607,18 +606,20 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // One region per k-substep. The MFMAs run on fragments read a region
   // earlier; the memory instructions of the region (the next substep's
   // fragment reads and, at the last substep of a k-tile, the DMA of k-tile
-  // kt+2 into the stage tile kt used) sit between them, at most a few per
+  // kt+S into the stage tile kt used) sit between them, at most a few per
   // MFMA, so the in-order issue of a long memory burst never leaves the
-  // matrix pipe idle. The first H MFMAs precede every new read: their wait
-  // for the current fragments then covers no read issued here. Every step
-  // is fenced with sched_barrier to keep this order. (MXFP8: the next
-  // tile's scales are fetched in the first region and swapped in after the
-  // tile barrier, once their wait is free.)
-  constexpr int H = N_MFMA >= 8 ? 2 : 1;
+  // matrix pipe idle. The tile barrier waits until only the S-2 newest
+  // tiles' DMA is outstanding, i.e. for tile kt+1. The first H MFMAs
+  // precede every new read: their wait for the current fragments then
+  // covers no read issued here. Every step is fenced with sched_barrier to
+  // keep this order. (MXFP8: the next tile's scales are fetched in the
+  // first region and swapped in after the tile barrier, once their wait is
+  // free.)
+  constexpr int H = N_MFMA >= 8 ? 2 : N_MFMA >= 2 ? 1 : 0;
 #define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
   for (int kt = 0; kt < nk; ++kt) {
-    const char* sb = lds + (kt & 1) * STAGE;
-    const char* sb_next = lds + ((kt + 1) & 1) * STAGE;
+    const char* sb = lds + (kt & (S - 1)) * STAGE;
+    const char* sb_next = lds + ((kt + 1) & (S - 1)) * STAGE;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       Frags& cur = (ks & 1) ? fb : fa;
@@ -640,7 +641,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
         // Branch-free so the wait counters stay exact: past the last tile
         // the reads return unused data and the DMA fetches the last k-tile
         // again into a stage that is no longer read.
-        barrier_after(std::integral_constant<int, 0>{});
+        barrier_after(std::integral_constant<int, (S - 2) * N_LOAD>{});
         if constexpr (MX) {
 #pragma unroll
           for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
@@ -664,7 +665,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
             if ((mm + 1) * N_READ / NM_MAX != rb)
               read_one(sb_next, 0, nxt, rb);
             else
-              issue_one(min(kt + 2, nk - 1), kt & 1, mm - rb);
+              issue_one(min(kt + S, nk - 1), kt & (S - 1), mm - rb);
           }
           MOE_FENCE();
         }
@@ -804,7 +805,7 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
     const long rows_per_group = p.off ? (long)p.M / (p.G > 0 ? p.G : 1) : p.M;
     big = rows_per_group >= 192 && p.N >= 256;
     if (op == kOpRouter) big = false;
-    const int bm = big ? 256 : 128;
+    const int bm = op == kOpRouter && p.N <= 32 ? 32 : big ? 256 : 128;
     if (p.off) {
       p.tile_off = tile_off_by_bm[tile_bm_slot(bm)];
       p.tiles_m_max = (p.M + bm - 1) / bm + (p.G < p.M ? p.G : p.M);
@@ -816,6 +817,10 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   if (p.K % 64 == 0 && !force_staged()) {
     switch (op) {
       case kOpRouter:
+        // few experts: one wave per 32 x 32 tile, eight k-tiles in flight,
+        // so the skinny product spreads over every CU and hides latency
+        if (p.N <= 32)
+          return launch_dl<32, 32, 8, 1, 1, false, kEpiStore, float, false>(p, s);
         return launch_dl_sized<false, kEpiStore, float>(big, p, s);
       case kOpGemm1:
         return launch_dl_sized<true, kEpiSwiglu, bf16>(big, p, s);

@@ -12,21 +12,28 @@ hipError_t launch_topk(const float* logits, const float* bias, int T, int E,
                        int K, int gate, int32_t* idx, float* w,
                        hipStream_t s);
 
-// block_hist: [E, nblk] int32 scratch; tile_off: kNumTileBM arrays of E+1.
-hipError_t launch_histogram_scan(const int32_t* idx, int TK, int E,
-                                 int32_t* block_hist, int32_t* counts,
-                                 int32_t* offsets, int32_t* const* tile_off,
-                                 hipStream_t s);
+// Counting sort of the T*K copies by expert (stable in the copy index).
+// block_hist: [nblk, E] int32 scratch, nblk = ceil(TK / kPermChunk), left
+// holding the first slot of every (chunk, expert); rank: [TK] int32, each
+// copy's rank among its chunk's copies of the same expert; tile_off:
+// kNumTileBM arrays of E+1 (row-tile prefix per tile height).
+hipError_t launch_hist_rank_scan(const int32_t* idx, int TK, int E,
+                                 int32_t* block_hist, int32_t* rank,
+                                 int32_t* counts, int32_t* offsets,
+                                 int32_t* const* tile_off, hipStream_t s);
 // tile_off[i][e] = sum_{e' < e} ceil(count_e' / kTileBM[i]) from offsets.
 hipError_t launch_tile_prefix(const int32_t* offsets, int E,
                               int32_t* const* tile_off, hipStream_t s);
-hipError_t launch_rank(const int32_t* idx, int TK, int E,
-                       const int32_t* block_hist, int32_t* sorted_src,
-                       int32_t* dest, hipStream_t s);
-// x_perm[dest[t*K+k]] = x[t] for all t, k (row bytes % 16 == 0).
-hipError_t launch_scatter_rows(const void* x, int T, int K, long row_bytes,
-                               const int32_t* dest, void* x_perm,
-                               hipStream_t s);
+// dest / sorted_src of every copy from the sort above, and x_perm[dest[j]]
+// = x[j / K] (row_bytes % 16 == 0).
+hipError_t launch_scatter(const void* x, const int32_t* idx,
+                          const int32_t* first, const int32_t* rank, int T,
+                          int E, int K, long row_bytes, int32_t* dest,
+                          int32_t* sorted_src, void* x_perm, hipStream_t s);
+// dest / sorted_src only.
+hipError_t launch_slots(const int32_t* idx, const int32_t* first,
+                        const int32_t* rank, int TK, int E, int32_t* dest,
+                        int32_t* sorted_src, hipStream_t s);
 // out[t] = sum_k w[t,k] * y[dest[t*K+k]] (+ add[t]); w == NULL means 1.
 hipError_t launch_combine(int dtype, const void* y, const int32_t* dest,
                           const float* w, const void* add, void* out, int T,

@@ -1,123 +1,49 @@
 // Expert histogram, prefix scan, stable permutation, row scatter, and the
 // gate-weighted combine (forward and backward).
 //
-// Counting sort in three passes, no atomics on global memory:
-//   1. each workgroup counts its chunk of kPermChunk copies into an LDS
-//      histogram and writes it as column b of block_hist[E, nblk];
-//   2. one workgroup turns block_hist into per-(expert, chunk) starting
-//      slots: an exclusive scan over chunks per expert, plus the expert's
-//      offset from an exclusive scan over experts; it also publishes the
-//      expert offsets and the row-tile prefix for each GEMM tile height;
-//   3. one wavefront per chunk walks its copies in order, 64 at a time;
-//      lanes with the same expert find each other with log2(E) ballots,
-//      rank among themselves by popcount, and the last of them advances
-//      the expert's running slot in LDS. Order within an expert therefore
-//      follows the copy index j = t*K + k, which makes the sort stable.
+// Counting sort in three kernels, no atomics on global memory:
+//   1. hist_rank: each workgroup takes a chunk of kPermChunk copies (copy
+//      j = t*K + k); each of its four waves walks its quarter in order, 64
+//      copies at a time, finds the lanes holding the same expert with
+//      log2(E) ballots and ranks them by popcount against a per-wave LDS
+//      count. A prefix over the four waves then gives every copy its rank
+//      among the chunk's copies of its expert, in copy order, and the
+//      chunk's histogram is written as row b of block_hist[nblk, E];
+//   2. scan: one workgroup; a few threads per expert each sum a range of
+//      chunks, and one exclusive scan over all (expert, range) pairs gives
+//      each range its first slot. block_hist becomes, in place, the first
+//      slot of every (chunk, expert); counts, offsets and the row-tile
+//      prefix of every GEMM tile height are written too;
+//   3. scatter: slot of copy j = block_hist[j / kPermChunk, e] + its rank.
+//      Each workgroup writes dest and sorted_src for its tokens' copies,
+//      then copies their rows, reading each row of x once.
+// The order within an expert follows the copy index, so the sort is stable.
 #include "gemm.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ idx,
-                                                   int TK, int E,
-                                                   int32_t* __restrict__ block_hist,
-                                                   int nblk) {
-  __shared__ int32_t h[MOE_E_MAX];
-  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
-  __syncthreads();
-  const int b = blockIdx.x;
-  const int j_end = min(TK, (b + 1) * kPermChunk);
-  for (int j = b * kPermChunk + threadIdx.x; j < j_end; j += 256)
-    atomicAdd(&h[idx[j]], 1);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) block_hist[(long)e * nblk + b] = h[e];
-}
+constexpr int kRankWaves = 4;
+constexpr int kRankPerWave = kPermChunk / kRankWaves;
+static_assert(kRankPerWave % kWave == 0, "chunk split");
 
-// Exclusive scan of one value per thread over a 1024-thread block.
-__device__ int block_exclusive_scan(int v, int32_t (*buf)[1024]) {
-  const int tid = threadIdx.x;
-  int pin = 0;
-  buf[0][tid] = v;
+__global__ __launch_bounds__(kRankWaves * kWave) void hist_rank_kernel(
+    const int32_t* __restrict__ idx, int TK, int E, int nbits,
+    int32_t* __restrict__ block_hist, int32_t* __restrict__ rank) {
+  __shared__ int32_t cnt[kRankWaves][MOE_E_MAX];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int w = tid / kWave, lane = tid % kWave;
+  for (int i = tid; i < kRankWaves * E; i += kRankWaves * kWave)
+    cnt[i / E][i % E] = 0;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int x = buf[pin][tid];
-    if (tid >= off) x += buf[pin][tid - off];
-    buf[pin ^ 1][tid] = x;
-    pin ^= 1;
-    __syncthreads();
-  }
-  const int incl = buf[pin][tid];
-  __syncthreads();
-  return incl - v;
-}
-
-struct TileOffPtrs { int32_t* p[kNumTileBM]; };
-
-__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ block_hist,
-                                                    int nblk, int E,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    TileOffPtrs toff) {
-  __shared__ int32_t buf[2][1024];
-  const int e = threadIdx.x;
-  int total = 0;
-  if (e < E) {
-    int32_t* row = block_hist + (long)e * nblk;
-    for (int b = 0; b < nblk; ++b) {
-      const int v = row[b];
-      row[b] = total;
-      total += v;
-    }
-  }
-  const int excl = block_exclusive_scan(total, buf);
-  if (e < E) {
-    counts[e] = total;
-    offsets[e] = excl;
-    int32_t* row = block_hist + (long)e * nblk;
-    for (int b = 0; b < nblk; ++b) row[b] += excl;
-  }
-  if (e == E - 1) offsets[E] = excl + total;
+  constexpr int R = kRankPerWave / kWave;
+  int ex[R], rk[R];
+  const int j0 = b * kPermChunk + w * kRankPerWave;
 #pragma unroll
-  for (int s = 0; s < kNumTileBM; ++s) {
-    const int bm = kTileBM[s];
-    const int tiles = e < E ? (total + bm - 1) / bm : 0;
-    const int tx = block_exclusive_scan(tiles, buf);
-    if (e < E) toff.p[s][e] = tx;
-    if (e == E - 1) toff.p[s][E] = tx + tiles;
-  }
-}
-
-// Row-tile prefix for every tile height from the expert offsets alone.
-__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ offsets,
-                                                           int E, TileOffPtrs toff) {
-  __shared__ int32_t buf[2][1024];
-  const int e = threadIdx.x;
-  const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
-#pragma unroll
-  for (int s = 0; s < kNumTileBM; ++s) {
-    const int bm = kTileBM[s];
-    const int tiles = (cnt + bm - 1) / bm;
-    const int tx = block_exclusive_scan(tiles, buf);
-    if (e < E) toff.p[s][e] = tx;
-    if (e == E - 1) toff.p[s][E] = tx + tiles;
-  }
-}
-
-__global__ __launch_bounds__(kWave) void rank_kernel(const int32_t* __restrict__ idx,
-                                                     int TK, int E, int nbits,
-                                                     const int32_t* __restrict__ block_hist,
-                                                     int nblk,
-                                                     int32_t* __restrict__ sorted_src,
-                                                     int32_t* __restrict__ dest) {
-  __shared__ int32_t run[MOE_E_MAX];
-  const int b = blockIdx.x, lane = threadIdx.x;
-  for (int e = lane; e < E; e += kWave) run[e] = block_hist[(long)e * nblk + b];
-  __syncthreads();
-  const int j_end = min(TK, (b + 1) * kPermChunk);
-  for (int j0 = b * kPermChunk; j0 < j_end; j0 += kWave) {
-    const int j = j0 + lane;
-    const bool valid = j < j_end;
+  for (int r = 0; r < R; ++r) {
+    const int j = j0 + r * kWave + lane;
+    const bool valid = j < TK;
     const int e = valid ? idx[j] : 0;
     uint64_t m = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
@@ -125,27 +51,226 @@ __global__ __launch_bounds__(kWave) void rank_kernel(const int32_t* __restrict__
       const uint64_t bal = __ballot(valid && on);
       m &= on ? bal : ~bal;
     }
+    ex[r] = e;
+    rk[r] = 0;
     if (valid) {
-      const int base = run[e];
-      const int p = base + __popcll(m & ((1ull << lane) - 1ull));
-      dest[j] = p;
-      sorted_src[p] = j;
-      if ((m >> lane) == 1ull) run[e] = base + __popcll(m);
+      const int base = cnt[w][e];  // every lane of the group reads first
+      rk[r] = base + __popcll(m & ((1ull << lane) - 1ull));
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (m >> lane) == 1ull) cnt[w][e] += __popcll(m);
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // per expert: chunk count, and each wave's first rank (in place)
+  for (int e = tid; e < E; e += kRankWaves * kWave) {
+    int run = 0;
+#pragma unroll
+    for (int q = 0; q < kRankWaves; ++q) {
+      const int c = cnt[q][e];
+      cnt[q][e] = run;
+      run += c;
+    }
+    block_hist[(long)b * E + e] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int j = j0 + r * kWave + lane;
+    if (j < TK) rank[j] = cnt[w][ex[r]] + rk[r];
   }
 }
 
-__global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4* __restrict__ x,
-                                                           long n, int K, int cpr,
-                                                           const int32_t* __restrict__ dest,
-                                                           u32x4* __restrict__ xp) {
-  const long i = blockIdx.x * 256L + threadIdx.x;
-  if (i >= n) return;
-  const long t = i / cpr;
-  const int c = (int)(i % cpr);
-  const u32x4 v = x[i];
-  for (int k = 0; k < K; ++k) xp[(long)dest[t * K + k] * cpr + c] = v;
+// Exclusive scan over a 1024-thread block of N values per thread at once
+// (v[i] of thread t scanned across threads): an inclusive scan inside each
+// wave by shuffles, then one pass over the 16 wave totals. wsum holds
+// 16 * N ints of LDS.
+template <int N>
+__device__ void block_exclusive_scan(int (&v)[N], int32_t* wsum) {
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  int x[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = v[i];
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int y = __shfl_up(x[i], off);
+      if (lane >= off) x[i] += y;
+    }
+  }
+  if (lane == kWave - 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i) wsum[i * 16 + wv] = x[i];
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int s = lane < 16 ? wsum[i * 16 + lane] : 0;
+      const int own = s;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const int y = __shfl_up(s, off);
+        if (lane >= off) s += y;
+      }
+      if (lane < 16) wsum[i * 16 + lane] = s - own;  // exclusive wave base
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = x[i] - v[i] + wsum[i * 16 + wv];
+  __syncthreads();
+}
+
+struct TileOffPtrs { int32_t* p[kNumTileBM]; };
+
+// Row-tile prefix of every tile height, from expert counts (thread e).
+__device__ void write_tile_prefix(int cnt, int E, const TileOffPtrs& toff,
+                                  int32_t* wsum) {
+  const int e = threadIdx.x;
+  int tiles[kNumTileBM], tx[kNumTileBM];
+#pragma unroll
+  for (int s = 0; s < kNumTileBM; ++s) {
+    tiles[s] = e < E ? (cnt + kTileBM[s] - 1) / kTileBM[s] : 0;
+    tx[s] = tiles[s];
+  }
+  block_exclusive_scan(tx, wsum);
+#pragma unroll
+  for (int s = 0; s < kNumTileBM; ++s) {
+    if (e < E) toff.p[s][e] = tx[s];
+    if (e == E - 1) toff.p[s][E] = tx[s] + tiles[s];
+  }
+}
+
+// block_hist[nblk, E] of counts -> first slot of each (chunk, expert).
+// Thread tid = e * tpe + sub sums chunks [sub * cps, ...) of expert e; the
+// block scan in that (expert-major) order yields the range's first slot.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ block_hist,
+                                                    int nblk, int E, int tpe,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    TileOffPtrs toff) {
+  __shared__ int32_t wsum[16 * kNumTileBM];
+  __shared__ int32_t first[MOE_E_MAX], cnt_s[MOE_E_MAX];
+  const int tid = threadIdx.x;
+  const int e = tid / tpe, sub = tid % tpe;
+  const int cps = (nblk + tpe - 1) / tpe;
+  const int b0 = min(nblk, sub * cps), b1 = min(nblk, b0 + cps);
+  // 8 chunks per step, loads first, so their latencies overlap
+  constexpr int U = 8;
+  int sum = 0;
+  if (e < E)
+    for (int b = b0; b < b1; b += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = b + u < b1 ? block_hist[(long)(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) sum += v[u];
+    }
+  int ex[1] = {sum};
+  block_exclusive_scan(ex, wsum);
+  const int excl = ex[0];
+  if (e < E) {
+    int run = excl;
+    for (int b = b0; b < b1; b += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = b + u < b1 ? block_hist[(long)(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b + u < b1) block_hist[(long)(b + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    if (sub == 0) {
+      first[e] = excl;
+      offsets[e] = excl;
+    }
+  }
+  if (tid == 1023) offsets[E] = excl + sum;  // total copies
+  __syncthreads();
+  if (e < E && sub == tpe - 1) cnt_s[e] = excl + sum - first[e];
+  __syncthreads();
+  const int cnt = tid < E ? cnt_s[tid] : 0;
+  if (tid < E) counts[tid] = cnt;
+  write_tile_prefix(cnt, E, toff, wsum);
+}
+
+// Row-tile prefix for every tile height from the expert offsets alone.
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ offsets,
+                                                           int E, TileOffPtrs toff) {
+  __shared__ int32_t wsum[16 * kNumTileBM];
+  const int e = threadIdx.x;
+  const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+  write_tile_prefix(cnt, E, toff, wsum);
+}
+
+// Slots of this workgroup's copies (tokens [t0, t0 + tpb)) into LDS, and
+// dest / sorted_src for them. Returns the number of copies.
+__device__ __forceinline__ int block_slots(const int32_t* __restrict__ idx,
+                                           const int32_t* __restrict__ first,
+                                           const int32_t* __restrict__ rank,
+                                           int E, int K, long t0, int tpb, int T,
+                                           int32_t* __restrict__ dest,
+                                           int32_t* __restrict__ sorted_src,
+                                           int32_t* slot) {
+  const int ntok = (int)min((long)tpb, T - t0);
+  const int n = ntok * K;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const long j = t0 * K + i;
+    const int p = first[(j / kPermChunk) * E + idx[j]] + rank[j];
+    slot[i] = p;
+    dest[j] = p;
+    sorted_src[p] = (int)j;
+  }
+  __syncthreads();
+  return ntok;
+}
+
+constexpr int kScatterThreads = 256;
+
+__global__ __launch_bounds__(256) void slots_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ first,
+    const int32_t* __restrict__ rank, long TK, int E,
+    int32_t* __restrict__ dest, int32_t* __restrict__ sorted_src) {
+  const long j = blockIdx.x * 256L + threadIdx.x;
+  if (j >= TK) return;
+  const int p = first[(j / kPermChunk) * E + idx[j]] + rank[j];
+  dest[j] = p;
+  sorted_src[p] = (int)j;
+}
+
+// x_perm[slot(t, k)] = x[t] for the workgroup's tpb tokens; cpr 16-byte
+// chunks per row.
+__global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ first, const int32_t* __restrict__ rank,
+    int T, int E, int K, int cpr, int tpb, int32_t* __restrict__ dest,
+    int32_t* __restrict__ sorted_src, u32x4* __restrict__ xp) {
+  __shared__ int32_t slot[kScatterThreads];
+  const long t0 = (long)blockIdx.x * tpb;
+  const int ntok = block_slots(idx, first, rank, E, K, t0, tpb, T, dest,
+                               sorted_src, slot);
+  const int n = ntok * cpr;
+  constexpr int U = 4;  // chunks in flight per thread
+  for (int i0 = threadIdx.x; i0 < n; i0 += U * kScatterThreads) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kScatterThreads;
+      if (i < n) v[u] = x[(t0 + i / cpr) * cpr + i % cpr];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kScatterThreads;
+      if (i < n) {
+        const int tl = i / cpr, c = i % cpr;
+        for (int k = 0; k < K; ++k) xp[(long)slot[tl * K + k] * cpr + c] = v[u];
+      }
+    }
+  }
 }
 
 // 8 consecutive elements <-> fp32
@@ -170,34 +295,56 @@ __device__ __forceinline__ void store8(bf16* p, const float* v) {
   *(bf16x8*)p = a;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
-                                                      const int32_t* __restrict__ dest,
-                                                      const float* __restrict__ w,
-                                                      const T* __restrict__ add,
-                                                      T* __restrict__ out, long n,
-                                                      int K, int d) {
-  const long i = blockIdx.x * 256L + threadIdx.x;
-  if (i >= n) return;
-  const int cpr = d / 8;
-  const long t = i / cpr;
-  const int c = (int)(i % cpr) * 8;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int k = 0; k < K; ++k) {
-    const long p = dest[t * K + k];
-    const float wk = w ? w[t * K + k] : 1.0f;
-    float v[8];
-    load8(y + p * d + c, v);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = fmaf(wk, v[q], acc[q]);
+// out[t] = sum_k w[t,k] * y[dest[t*K+k]] (+ add[t]) for the workgroup's
+// tpb tokens, 8 columns per item, fp32 accumulation in k order and one
+// rounding; U items per thread keep U*K row loads in flight.
+template <typename T, int U>
+__global__ __launch_bounds__(kScatterThreads) void combine_kernel(
+    const T* __restrict__ y, const int32_t* __restrict__ dest,
+    const float* __restrict__ w, const T* __restrict__ add, T* __restrict__ out,
+    int Ttok, int K, int d, int tpb) {
+  __shared__ int32_t sd[kScatterThreads];
+  __shared__ float sw[kScatterThreads];
+  const long t0 = (long)blockIdx.x * tpb;
+  const int ntok = (int)min((long)tpb, Ttok - t0);
+  for (int i = threadIdx.x; i < ntok * K; i += kScatterThreads) {
+    sd[i] = dest[t0 * K + i];
+    sw[i] = w ? w[t0 * K + i] : 1.0f;
   }
-  if (add) {
-    float v[8];
-    load8(add + t * d + c, v);
+  __syncthreads();
+  const int cpr = d / 8, n = ntok * cpr;
+  for (int i0 = threadIdx.x; i0 < n; i0 += U * kScatterThreads) {
+    float acc[U][8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += v[q];
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kScatterThreads;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[u][q] = 0.0f;
+      if (i >= n) continue;
+      const int tl = i / cpr, c = (i % cpr) * 8;
+      for (int k = 0; k < K; ++k) {
+        float v[8];
+        load8(y + (long)sd[tl * K + k] * d + c, v);
+        const float wk = sw[tl * K + k];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[u][q] = fmaf(wk, v[q], acc[u][q]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kScatterThreads;
+      if (i >= n) continue;
+      const int tl = i / cpr, c = (i % cpr) * 8;
+      const long o = (t0 + tl) * d + c;
+      if (add) {
+        float v[8];
+        load8(add + o, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[u][q] += v[q];
+      }
+      store8(out + o, acc[u]);
+    }
   }
-  store8(out + t * d + c, acc);
 }
 
 template <typename T>
@@ -251,19 +398,45 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
   }
 }
 
+int perm_nbits(int E) {
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  return nbits;
+}
+
 }  // namespace
 
-hipError_t launch_histogram_scan(const int32_t* idx, int TK, int E,
-                                 int32_t* block_hist, int32_t* counts,
-                                 int32_t* offsets, int32_t* const* tile_off,
-                                 hipStream_t s) {
+// tokens per scatter workgroup: ~64 KB of rows, at most kScatterThreads
+// copies
+int scatter_tokens_per_block(int K, long row_bytes) {
+  long tpb = 65536 / (row_bytes > 0 ? row_bytes : 1);
+  if (tpb < 1) tpb = 1;
+  if (tpb > kScatterThreads / K) tpb = kScatterThreads / K;
+  return (int)tpb;
+}
+
+hipError_t launch_hist_rank_scan(const int32_t* idx, int TK, int E,
+                                 int32_t* block_hist, int32_t* rank,
+                                 int32_t* counts, int32_t* offsets,
+                                 int32_t* const* tile_off, hipStream_t s) {
   const int nblk = (TK + kPermChunk - 1) / kPermChunk;
-  hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(256), 0, s, idx, TK, E,
-                     block_hist, nblk);
+  hipLaunchKernelGGL(hist_rank_kernel, dim3(nblk), dim3(kRankWaves * kWave), 0,
+                     s, idx, TK, E, perm_nbits(E), block_hist, rank);
   TileOffPtrs tp;
   for (int i = 0; i < kNumTileBM; ++i) tp.p[i] = tile_off[i];
+  int ep = 1;
+  while (ep < E) ep <<= 1;
+  const int tpe = 1024 / ep;  // threads per expert (E <= 1024)
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, block_hist, nblk,
-                     E, counts, offsets, tp);
+                     E, tpe, counts, offsets, tp);
+  return hipGetLastError();
+}
+
+hipError_t launch_slots(const int32_t* idx, const int32_t* first,
+                        const int32_t* rank, int TK, int E, int32_t* dest,
+                        int32_t* sorted_src, hipStream_t s) {
+  hipLaunchKernelGGL(slots_kernel, dim3((unsigned)((TK + 255) / 256)), dim3(256),
+                     0, s, idx, first, rank, (long)TK, E, dest, sorted_src);
   return hipGetLastError();
 }
 
@@ -275,40 +448,45 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int E,
   return hipGetLastError();
 }
 
-hipError_t launch_rank(const int32_t* idx, int TK, int E,
-                       const int32_t* block_hist, int32_t* sorted_src,
-                       int32_t* dest, hipStream_t s) {
-  const int nblk = (TK + kPermChunk - 1) / kPermChunk;
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
-  hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(kWave), 0, s, idx, TK, E,
-                     nbits, block_hist, nblk, sorted_src, dest);
+hipError_t launch_scatter(const void* x, const int32_t* idx,
+                          const int32_t* first, const int32_t* rank, int T,
+                          int E, int K, long row_bytes, int32_t* dest,
+                          int32_t* sorted_src, void* x_perm, hipStream_t s) {
+  const int tpb = scatter_tokens_per_block(K, row_bytes);
+  const long blocks = (T + tpb - 1) / tpb;
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)blocks), dim3(kScatterThreads),
+                     0, s, (const u32x4*)x, idx, first, rank, T, E, K,
+                     (int)(row_bytes / 16), tpb, dest, sorted_src,
+                     (u32x4*)x_perm);
   return hipGetLastError();
 }
 
-hipError_t launch_scatter_rows(const void* x, int T, int K, long row_bytes,
-                               const int32_t* dest, void* x_perm,
-                               hipStream_t s) {
-  const int cpr = (int)(row_bytes / 16);
-  const long n = (long)T * cpr;
-  hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)((n + 255) / 256)),
-                     dim3(256), 0, s, (const u32x4*)x, n, K, cpr, dest,
-                     (u32x4*)x_perm);
+template <typename T>
+hipError_t launch_combine_t(const T* y, const int32_t* dest, const float* w,
+                            const T* add, T* out, int Ttok, int K, int d,
+                            hipStream_t s) {
+  const int tpb = scatter_tokens_per_block(K, (long)d * sizeof(T));
+  const dim3 grid((unsigned)((Ttok + tpb - 1) / tpb)), block(kScatterThreads);
+  if (K >= 8)
+    hipLaunchKernelGGL((combine_kernel<T, 1>), grid, block, 0, s, y, dest, w, add,
+                       out, Ttok, K, d, tpb);
+  else if (K >= 4)
+    hipLaunchKernelGGL((combine_kernel<T, 2>), grid, block, 0, s, y, dest, w, add,
+                       out, Ttok, K, d, tpb);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, 4>), grid, block, 0, s, y, dest, w, add,
+                       out, Ttok, K, d, tpb);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(int dtype, const void* y, const int32_t* dest,
                           const float* w, const void* add, void* out, int T,
                           int K, int d, hipStream_t s) {
-  const long n = (long)T * (d / 8);
-  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
   if (dtype == MOE_F32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s, (const float*)y,
-                       dest, w, (const float*)add, (float*)out, n, K, d);
-  else
-    hipLaunchKernelGGL(combine_kernel<bf16>, grid, block, 0, s, (const bf16*)y,
-                       dest, w, (const bf16*)add, (bf16*)out, n, K, d);
-  return hipGetLastError();
+    return launch_combine_t((const float*)y, dest, w, (const float*)add,
+                            (float*)out, T, K, d, s);
+  return launch_combine_t((const bf16*)y, dest, w, (const bf16*)add, (bf16*)out,
+                          T, K, d, s);
 }
 
 hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y,
