@@ -57,6 +57,18 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1,
                                            kBufWord3);
 }
+// Resource over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ Rsrc make_rsrc_n(const void* base, long bytes) {
+  const long n = bytes < 0 ? 0 : (bytes > 0x7fffffffL ? 0x7fffffffL : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n,
+                                           kBufWord3);
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16 (see the backward kernel for the lane layout).
+__device__ __forceinline__ s16x4 lds_read_tr16(const char* a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)a);
+}
 // 16 bytes per lane from r + voff + soff into LDS at dst + 16 * lane. (A
 // plain function: called straight from a kernel template, the builtin
 // keeps clang's host pass from emitting that kernel's launch stub.)
@@ -191,6 +203,65 @@ __device__ __forceinline__ bool lookup_tile(const GemmParams& p, Tile& t) {
   t.k_beg = p.off[t.g];
   t.k_end = p.off[t.g + 1];
   return true;
+}
+
+// Tile output through LDS: the fp32 values of the wave's 32x32 blocks
+// (value(i, j, r) for accumulator element r of block (i, j)) go to LDS as
+// rows of the tile, ROWS at a time, and every thread then hands
+// store(row, col, v[8]) eight consecutive columns of one row, so global
+// traffic moves in 16-byte row-contiguous pieces instead of 2-byte
+// scattered ones. The row pitch is padded by 8 floats so that the two
+// half-waves' stores (rows 4 apart) use disjoint banks. The caller has
+// finished reading LDS for operands; the LDS is free on return.
+template <int BM, int BN, int WM, int WN, int MB, int NB, int NT, int ROWS>
+struct StageOut {
+  static constexpr int PITCH = BN + 8;
+  static constexpr int BYTES = ROWS * PITCH * 4;
+  static_assert(BM % ROWS == 0, "pass rows");
+
+  template <typename V, typename St>
+  __device__ __forceinline__ static void run(char* lds, int wm, int wn,
+                                             int lane, V value, St store) {
+    float* st = (float*)lds;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int pass = 0; pass < BM / ROWS; ++pass) {
+      const int r0 = pass * ROWS;
+      __syncthreads();  // LDS free (operands read, or previous pass out)
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int rb = wm * WM + i * 32;  // block's first tile row
+        if (rb + 32 <= r0 || rb >= r0 + ROWS) continue;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int col = wn * WN + j * 32 + lane % 32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rb + 8 * (r / 4) + 4 * (lane / 32) + r % 4 - r0;
+            st[row * PITCH + col] = value(i, j, r);
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int CH = ROWS * (BN / 8);
+#pragma unroll 2
+      for (int c = tid; c < CH; c += NT) {
+        const int row = c / (BN / 8), col = (c % (BN / 8)) * 8;
+        const f32x4 lo = *(const f32x4*)(st + row * PITCH + col);
+        const f32x4 hi = *(const f32x4*)(st + row * PITCH + col + 4);
+        float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        store(r0 + row, col, v);
+      }
+    }
+    __syncthreads();
+  }
+};
+
+__device__ __forceinline__ bf16x8 pack8(const float* v) {
+  bf16x8 o;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) o[q] = (bf16)v[q];
+  return o;
 }
 
 // 32x32 accumulator layout: element r of lane l is row
@@ -683,6 +754,253 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     epilogue<WM, WN, MB, NB, NB_OPS, EPI, kSchedM, TO>(p, t, acc, wm, wn, lane);
 }
 
+// Direct-to-LDS form for the backward products (bf16), where operands may
+// be stored k-major: element (row r, contraction index k) at base[k*ld + r]
+// (the row-major form, base[r*ld + k], is loaded as in the forward). A
+// k-major k-tile is DMA'd as it lies: 64 rows of the contraction index,
+// each R = BM or BN elements long, its 16-byte chunk c at position
+// c ^ (4 * (k & 3)). The MFMA fragment (32 operand rows x 16 k) is read
+// with two ds_read_b64_tr_b16: within each 16-lane group, lane j points at
+// k-row kb + j/4, elements r0 + 4*(j%4) .. +3, and the transposing read
+// hands lane i the four k values kb..kb+3 of element r0 + i. Rows kb..kb+3
+// sit in distinct quarters of the 64 banks, so the reads are conflict-free.
+//
+// SCHED = kSchedK contracts over each group's ragged row range (weight
+// gradients: C_g = A_g^T B_g); k-tiles past the range read zeros, since
+// every k-tile's buffer resource ends at the range end. KCAT contracts over
+// the concatenation [A | A2] . [B ; B2] with K1 rows in the first part.
+template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, bool KCAT,
+          int EPI, int SCHED>
+__global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
+  typedef bf16x8 Frag;
+  constexpr int NW = WGM * WGN, S = 2;
+  constexpr int RB = 128, BK = 64, KS = BK / 16;  // bytes / elements / substeps
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  // DMA instructions per wave and k-tile (1 KB each)
+  constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;
+  constexpr int N_LOAD = A_INS + B_INS;
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile shape");
+  static_assert(BM >= 128 && BN >= 128 && MB >= 1 && NB >= 1, "tile shape");
+
+  constexpr int kEpiRows = BM > 128 ? 128 : BM;
+  constexpr int EPI_BYTES = StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>::BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[S * STAGE > EPI_BYTES ? S * STAGE : EPI_BYTES];
+
+  Tile t;
+  if (!lookup_tile<BM, BN, SCHED>(p, t)) return;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  // k-tiles: rows [k_beg, k_end) of the contraction (SCHED K), else
+  // [0, K) or its two halves (KCAT)
+  const int kspan = SCHED == kSchedK ? t.k_end - t.k_beg : (KCAT ? p.K1 : p.K);
+  const int nk1 = (kspan + BK - 1) / BK;
+  const int nk = KCAT ? 2 * nk1 : nk1;
+
+  // Source of DMA instruction d of operand X (rows [r0, r0 + R) of the
+  // tile) for k-tile kt. Row-major: 8 rows of 128 bytes, as the forward.
+  // k-major: 1024 / (2R) k-rows of 2R bytes; the resource starts at the
+  // k-tile's first row and ends with the valid rows (zeros past them).
+  auto dma = [&](const void* X, int ld, int r0, int r_end, int R, bool km,
+                 int kt, char* dst, int d) {
+    const int kt_part = KCAT && kt >= nk1 ? kt - nk1 : kt;
+    const int kbase = (SCHED == kSchedK ? t.k_beg : 0) + kt_part * BK;
+    if (!km) {
+      const int row = (d * NW + wave) * 8 + lane / 8, phys = lane % 8;
+      const int grow = min(r0 + row, r_end - 1);
+      const Rsrc rs = make_rsrc((const char*)X + (long)r0 * ld * 2);
+      dma16(rs, dst, (grow - r0) * ld * 2 + swz<8>(row, phys) * 16, kbase * 2);
+    } else {
+      const int cpk = R / 8;  // chunks per k-row
+      const int kr = (d * NW + wave) * (64 / cpk) + lane / cpk;
+      const int c = (lane % cpk) ^ (4 * (kr & 3));
+      const int rows_left =
+          SCHED == kSchedK ? t.k_end - kbase : kspan - kt_part * BK;
+      const char* base = (const char*)X + ((long)kbase * ld + r0) * 2;
+      dma16(make_rsrc_n(base, ((long)rows_left * ld - r0) * 2), dst,
+            kr * ld * 2 + c * 16, 0);
+    }
+  };
+  const void* Aop[2] = {p.A, KCAT ? p.A2 : p.A};
+  const void* Bop[2] = {(const char*)p.B + (SCHED == kSchedM ? (long)t.g * p.sB * 2 : 0),
+                        (const char*)(KCAT ? p.B2 : p.B) +
+                            (SCHED == kSchedM ? (long)t.g * p.sB * 2 : 0)};
+  auto issue_one = [&](int kt, int stage, int d) {
+    char* base = lds + stage * STAGE;
+    const int part = KCAT && kt >= nk1 ? 1 : 0;
+    if (d < A_INS) {
+      dma(Aop[part], p.lda, t.m0, t.m_end, BM, A_KM, kt, base + (d * NW + wave) * 1024, d);
+    } else {
+      const int j = d - A_INS;
+      dma(Bop[part], p.ldb, t.n0, p.N, BN, B_KM, kt,
+          base + A_BYTES + (j * NW + wave) * 1024, j);
+    }
+  };
+  auto issue = [&](int kt, int stage) {
+#pragma unroll
+    for (int d = 0; d < N_LOAD; ++d) issue_one(kt, stage, d);
+  };
+
+  // fragment reads: row-major as in the forward; k-major by two transposing
+  // reads of 4 k each
+  const int lrow = lane % 32, half = lane / 32, sw = (lrow >> 1) & 7;
+  const int grp = lane / 16, gj = lane % 16;
+  auto read_rm = [&](const char* op, int row0, int ks) {
+    return *(const Frag*)(op + (row0 + lrow) * RB + (((ks * 2 + half) ^ sw) * 16));
+  };
+  auto read_km = [&](const char* op, int R, int row0, int ks) {
+    const int r = row0 + 16 * (grp & 1) + 4 * (gj & 3);
+    s16x4 v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = ks * 16 + 8 * (grp >> 1) + 4 * h + (gj >> 2);
+      const int c = (r >> 3) ^ (4 * (k & 3));
+      v[h] = lds_read_tr16(op + k * (R * 2) + c * 16 + (r & 7) * 2);
+    }
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 w = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(Frag, w);
+  };
+  struct Frags {
+    Frag a[MB], b[NB];
+  };
+  constexpr int N_READ = MB + NB;
+  constexpr int N_MFMA = MB * NB;
+  auto read_one = [&](const char* sb, int ks, Frags& f, int r) {
+    if (r < MB) {
+      const int row0 = wm * WM + r * 32;
+      f.a[r] = A_KM ? read_km(sb, BM, row0, ks) : read_rm(sb, row0, ks);
+    } else {
+      const int j = r - MB, row0 = wn * WN + j * 32;
+      f.b[j] = B_KM ? read_km(sb + A_BYTES, BN, row0, ks)
+                    : read_rm(sb + A_BYTES, row0, ks);
+    }
+  };
+
+  f32x16 acc[1][MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[0][i][j] = f32x16{};
+  auto mfma_one = [&](const Frags& f, int q) {
+    const int i = q / NB, j = q % NB;
+    acc[0][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j],
+                                                           acc[0][i][j], 0, 0, 0);
+  };
+  auto barrier_after = [&](auto vm_left) {
+    constexpr int n = decltype(vm_left)::value;
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
+  if (nk > 0) {
+    issue(0, 0);
+    issue(min(1, nk - 1), 1);
+    barrier_after(std::integral_constant<int, N_LOAD>{});
+    Frags fa, fb;
+#pragma unroll
+    for (int r = 0; r < N_READ; ++r) read_one(lds, 0, fa, r);
+    // the forward kernel's fenced schedule: each substep's MFMAs with the
+    // next substep's reads (and, at the last, the DMA of tile kt+2) spread
+    // among them; branch-free at the end so the wait counts stay exact
+    constexpr int H = N_MFMA >= 8 ? 2 : 1;
+#define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* sb = lds + (kt & 1) * STAGE;
+      const char* sb_next = lds + ((kt + 1) & 1) * STAGE;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        Frags& cur = (ks & 1) ? fb : fa;
+        Frags& nxt = (ks & 1) ? fa : fb;
+        const bool last = ks + 1 == KS;
+        constexpr int NM_MAX = N_READ + N_LOAD;
+        const int nm = last ? NM_MAX : N_READ;
+        MOE_FENCE();
+#pragma unroll
+        for (int q = 0; q < H; ++q) mfma_one(cur, q);
+        MOE_FENCE();
+        if (last) {
+          barrier_after(std::integral_constant<int, 0>{});
+          MOE_FENCE();
+        }
+        int m = 0;
+#pragma unroll
+        for (int q = H; q < N_MFMA; ++q) {
+          const int m_end = (q - H + 1) * nm / (N_MFMA - H);
+#pragma unroll
+          for (int mm = 0; mm < NM_MAX; ++mm) {
+            if (mm < m || mm >= m_end) continue;
+            if (!last) {
+              read_one(sb, ks + 1, nxt, mm);
+            } else {
+              const int rb = mm * N_READ / NM_MAX;
+              if ((mm + 1) * N_READ / NM_MAX != rb)
+                read_one(sb_next, 0, nxt, rb);
+              else
+                issue_one(min(kt + 2, nk - 1), kt & 1, mm - rb);
+            }
+            MOE_FENCE();
+          }
+          m = m_end;
+          mfma_one(cur, q);
+          MOE_FENCE();
+        }
+      }
+    }
+#undef MOE_FENCE
+    __builtin_amdgcn_s_waitcnt(0);  // no load may still target LDS at exit
+  }
+  // through LDS: ROWS rows per pass (the stages are free now)
+  bf16* C = (bf16*)p.C + (SCHED == kSchedK ? (long)t.g * p.sC : 0);
+  auto value = [&](int i, int j, int r) { return acc[0][i][j][r]; };
+  auto store = [&](int row, int col, const float* v) {
+    const int grow = t.m0 + row, gcol = t.n0 + col;
+    if (grow >= t.m_end || gcol >= p.N) return;
+    const long o = (long)grow * p.ldc + gcol;
+    if constexpr (EPI == kEpiStore) {
+      *(bf16x8*)(C + o) = pack8(v);
+    } else {  // SwiGLU backward from dh = v and the saved a, b
+      const bf16x8 a8 = *(const bf16x8*)((const bf16*)p.aux_a + o);
+      const bf16x8 b8 = *(const bf16x8*)((const bf16*)p.aux_b + o);
+      float da[8], db[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float a = (float)a8[q], b = (float)b8[q];
+        const float sg = fast_sigmoid(a);
+        da[q] = v[q] * b * sg * (1.0f + a * (1.0f - sg));
+        db[q] = v[q] * a * sg;
+      }
+      *(bf16x8*)(C + o) = pack8(da);
+      *(bf16x8*)((bf16*)p.C2 + o) = pack8(db);
+    }
+  };
+  StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>::run(lds, wm, wn, lane,
+                                                              value, store);
+}
+
+template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, bool KCAT,
+          int EPI, int SCHED>
+hipError_t launch_t(const GemmParams& p, hipStream_t s) {
+  const long tiles_n = (p.N + BN - 1) / BN;
+  long tiles;
+  if (SCHED == kSchedM)
+    tiles = (tiles_n + p.group_n - 1) / p.group_n * p.tiles_m_max * p.group_n;
+  else
+    tiles = (long)p.G * ((p.M + BM - 1) / BM) * tiles_n;
+  if (tiles <= 0) return hipSuccess;
+  tiles = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
+  if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((mfma_gemm_t<BM, BN, WGM, WGN, A_KM, B_KM, KCAT, EPI, SCHED>),
+                     dim3((unsigned)tiles), dim3(WGM * WGN * kWave), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int BK, int WGM, int WGN, bool A_KC, bool B_KC,
           bool DUAL, int EPI, int SCHED, typename TO>
 hipError_t launch(const GemmParams& p, hipStream_t s) {
@@ -829,6 +1147,22 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
       default:
         break;
     }
+  }
+  // backward products on the direct-to-LDS kernel with k-major operands
+  if (!force_staged()) {
+    const bool w4 = big_tile_waves() == 4;
+    if (op == kOpDgrad2 && p.K % 64 == 0)
+      return !big ? launch_t<128, 128, 2, 2, false, true, false, kEpiSwigluBwd, kSchedM>(p, s)
+             : w4 ? launch_t<256, 256, 2, 2, false, true, false, kEpiSwigluBwd, kSchedM>(p, s)
+                  : launch_t<256, 256, 2, 4, false, true, false, kEpiSwigluBwd, kSchedM>(p, s);
+    if (op == kOpDgrad1 && p.K1 % 64 == 0 && p.K == 2 * p.K1)
+      return !big ? launch_t<128, 128, 2, 2, false, true, true, kEpiStore, kSchedM>(p, s)
+             : w4 ? launch_t<256, 256, 2, 2, false, true, true, kEpiStore, kSchedM>(p, s)
+                  : launch_t<256, 256, 2, 4, false, true, true, kEpiStore, kSchedM>(p, s);
+    if (op == kOpWgrad)
+      return !big ? launch_t<128, 128, 2, 2, true, true, false, kEpiStore, kSchedK>(p, s)
+             : w4 ? launch_t<256, 256, 2, 2, true, true, false, kEpiStore, kSchedK>(p, s)
+                  : launch_t<256, 256, 2, 4, true, true, false, kEpiStore, kSchedK>(p, s);
   }
   if (op == kOpGemm1Mx)
     return launch_dl_sized<true, kEpiSwigluMx, bf16, true>(big, p, s);
