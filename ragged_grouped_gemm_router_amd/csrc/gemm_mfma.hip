@@ -497,7 +497,13 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
                 "power-of-two stage count, even substep count");
   static_assert((S - 1) * (A_INS + (DUAL ? 2 : 1) * B_INS) <= 63, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
+  // the epilogue stages 128 rows at a time (all but the quantising one)
+  constexpr int kEpiRows = BM > 128 ? 128 : BM;
+  constexpr int EPI_BYTES =
+      EPI == kEpiSwigluMx
+          ? 0
+          : StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>::BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[S * STAGE > EPI_BYTES ? S * STAGE : EPI_BYTES];
 
   Tile t;
   if (!lookup_tile<BM, BN, kSchedM>(p, t)) return;
@@ -748,10 +754,47 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   }
 #undef MOE_FENCE
   __builtin_amdgcn_s_waitcnt(0);  // no load may still target LDS at exit
-  if constexpr (EPI == kEpiSwigluMx)
+  if constexpr (EPI == kEpiSwigluMx) {
     epilogue_swiglu_mx<WM, WN, MB, NB>(p, t, acc, wm, wn, lane);
-  else
-    epilogue<WM, WN, MB, NB, NB_OPS, EPI, kSchedM, TO>(p, t, acc, wm, wn, lane);
+  } else {
+    // through LDS in 16-byte row pieces: the output (SwiGLU of the two
+    // accumulators, or the plain product), then any saved pre-activations
+    using SO = StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>;
+    auto put = [&](TO* dst) {
+      return [=](int row, int col, const float* v) {
+        const int grow = t.m0 + row, gcol = t.n0 + col;
+        if (grow >= t.m_end || gcol >= p.N) return;
+        TO* o = dst + (long)grow * p.ldc + gcol;
+        if constexpr (sizeof(TO) == 2) {
+          *(bf16x8*)o = pack8(v);
+        } else {
+          *(f32x4*)o = f32x4{v[0], v[1], v[2], v[3]};
+          *(f32x4*)(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        }
+      };
+    };
+    if constexpr (EPI == kEpiSwiglu) {
+      if (p.C)
+        SO::run(lds, wm, wn, lane,
+                [&](int i, int j, int r) {
+                  const float a = acc[0][i][j][r], b = acc[NB_OPS - 1][i][j][r];
+                  return a * fast_sigmoid(a) * b;
+                },
+                put((TO*)p.C));
+      if (p.C2)
+        SO::run(lds, wm, wn, lane,
+                [&](int i, int j, int r) { return acc[0][i][j][r]; },
+                put((TO*)p.C2));
+      if (p.C3)
+        SO::run(lds, wm, wn, lane,
+                [&](int i, int j, int r) { return acc[NB_OPS - 1][i][j][r]; },
+                put((TO*)p.C3));
+    } else {
+      SO::run(lds, wm, wn, lane,
+              [&](int i, int j, int r) { return acc[0][i][j][r]; },
+              put((TO*)p.C));
+    }
+  }
 }
 
 // Direct-to-LDS form for the backward products (bf16), where operands may
