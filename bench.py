@@ -37,9 +37,9 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (the fp32 path runs on VALU)
 # the kernel built from sources with this digest and nothing else.
 GEMM1_TRAFFIC = {
     "workload": "mixtral8x7b_T8192_d4096_f14336_E8_K2",
-    "src_digest": "4c510ec927c1e9af",
-    "fetch_bytes": 9_232_604_160,
-    "write_bytes": 469_762_560,
+    "src_digest": "97c82171b33693d7",
+    "fetch_bytes": 10_838_082_986,
+    "write_bytes": 469_762_048,
 }
 GEMM_SOURCES = ("gemm_mfma.hip", "common.h", "gemm.h")
 
@@ -132,7 +132,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral",
                     choices=["mixtral", "deepseek", "skewed", "tiny"])
-    ap.add_argument("--cpu-tokens", type=int, default=640)
+    ap.add_argument("--cpu-tokens", type=int, default=6144,
+                    help="tokens of the workload the fp64 oracle runs for the "
+                         "CPU baseline (about 10 s on 16 host cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step: forward (activations saved) "
