@@ -392,3 +392,46 @@ def backward_sampled(x, w1, w3, w2, idx, w, dy, tokens, cols,
         dw2_cols.append(g.T @ h)
     return {"dx": dx, "d_w": d_w, "dw1_rows": dw1_rows,
             "dw3_rows": dw3_rows, "dw2_cols": dw2_cols}
+
+
+# --------------------------------------------------------------------------
+# Router backward: the gate-weight gradient through the gate to the logits,
+# the router weights and the tokens. The selection is piecewise constant,
+# so only the K selected logits of a token receive gradient.
+# --------------------------------------------------------------------------
+
+def gate_logit_grad(logits: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
+                    d_w: torch.Tensor, gate: str) -> torch.Tensor:
+    """d loss / d logits [T, E] (fp64) from d loss / d topk_w [T, K].
+
+    softmax [P3 §4.1]: w = softmax over the selected logits, so
+    dL_k = w_k (d_w_k - sum_j w_j d_w_j) on the selected experts.
+    sigmoid [P3 §4.3]: w_k = s_k / S with s = sigmoid(L), S = sum of the
+    selected s, so dL_m = s_m (1 - s_m) / S * (d_w_m - sum_k w_k d_w_k).
+    A token whose weights fell back to 1/K (all selected sigmoids zero) has
+    a constant gate and gets zero gradient."""
+    L = _f64(logits)
+    idx = idx.to(torch.int64)
+    w = _f64(w)
+    d_w = _f64(d_w)
+    Ls = torch.gather(L, 1, idx)
+    inner = (w * d_w).sum(dim=1, keepdim=True)
+    if gate == "softmax":
+        g = w * (d_w - inner)
+    elif gate == "sigmoid":
+        s = _sigmoid(Ls)
+        S = s.sum(dim=1, keepdim=True)
+        g = torch.where(S > 0, s * (1.0 - s) / torch.where(S > 0, S, 1.0)
+                        * (d_w - inner), torch.zeros_like(s))
+    else:
+        raise ValueError(gate)
+    out = torch.zeros_like(L)
+    out.scatter_(1, idx, g)
+    return out
+
+
+def router_backward(x, wr, logits, idx, w, d_w, gate: str):
+    """Gradients of the router: d_logits [T, E], d_wr = d_logits^T x
+    [E, d] and the router's share of dx, d_logits wr [T, d] (fp64)."""
+    dl = gate_logit_grad(logits, idx, w, d_w, gate)
+    return {"d_logits": dl, "d_wr": dl.T @ _f64(x), "dx": dl @ _f64(wr)}

@@ -408,3 +408,50 @@ def test_accounting_against_page_figures():
     # a SwiGLU expert is three d x f matrices, so 6 d f flops per copy
     assert acc.routed_fwd_flops(4096, 14336, 16384) == 5_772_436_045_824
     assert acc.train_flops(acc.routed_fwd_flops(1, 1, 1)) == 18
+
+
+@pytest.mark.parametrize("gate", ["softmax", "sigmoid"])
+def test_router_backward_matches_autograd(gate):
+    """The closed-form gate Jacobian equals autograd through
+    logits = x Wr^T, a fixed selection and the renormalised weights."""
+    g = torch.Generator().manual_seed(11)
+    T, d, E, K = 12, 10, 6, 3
+    x = torch.randn(T, d, generator=g, dtype=torch.float64)
+    wr = torch.randn(E, d, generator=g, dtype=torch.float64)
+    d_w = torch.randn(T, K, generator=g, dtype=torch.float64)
+    idx = oracle.topk_select(oracle.selection_keys(x @ wr.T), K)
+    xa, wra = x.clone().requires_grad_(), wr.clone().requires_grad_()
+    L = xa @ wra.T
+    Ls = torch.gather(L, 1, idx)
+    z = torch.softmax(Ls, dim=1) if gate == "softmax" else torch.sigmoid(Ls)
+    wt = z / z.sum(dim=1, keepdim=True)
+    (wt * d_w).sum().backward()
+    L0 = (x @ wr.T).detach()
+    w = oracle.gate_weights(L0, idx, gate)
+    r = oracle.router_backward(x, wr, L0, idx, w, d_w, gate)
+    assert torch.allclose(r["d_wr"], wra.grad, rtol=0, atol=1e-12)
+    assert torch.allclose(r["dx"], xa.grad, rtol=0, atol=1e-12)
+    # unselected logits get exactly zero
+    mask = torch.zeros(T, E, dtype=torch.bool)
+    mask.scatter_(1, idx, True)
+    assert torch.all(r["d_logits"][~mask] == 0)
+
+
+def test_router_backward_invariants():
+    """softmax: the logit gradient of a token sums to zero (shifting all
+    logits leaves the weights unchanged); uniform d_w gives zero gradient
+    in both modes (the weights always sum to one)."""
+    g = torch.Generator().manual_seed(12)
+    T, E, K = 9, 8, 4
+    L = torch.randn(T, E, generator=g, dtype=torch.float64)
+    idx = oracle.topk_select(oracle.selection_keys(L), K)
+    d_w = torch.randn(T, K, generator=g, dtype=torch.float64)
+    w = oracle.gate_weights(L, idx, "softmax")
+    dl = oracle.gate_logit_grad(L, idx, w, d_w, "softmax")
+    assert torch.allclose(dl.sum(dim=1), torch.zeros(T, dtype=torch.float64),
+                          atol=1e-14)
+    for gate in ("softmax", "sigmoid"):
+        w = oracle.gate_weights(L, idx, gate)
+        dl = oracle.gate_logit_grad(L, idx, w, torch.full((T, K), 0.7,
+                                    dtype=torch.float64), gate)
+        assert torch.allclose(dl, torch.zeros_like(dl), atol=1e-14)
