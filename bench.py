@@ -82,6 +82,10 @@ class HipEvents:
             assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
             self.ev.append(e.value)
 
+    def record(self, i, stream):
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        assert self.hip.hipEventRecord(self.ev[i], stream.cuda_stream) == 0
+
     def ms(self, a, b):
         out = ctypes.c_float()
         st = self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a],
@@ -180,7 +184,9 @@ def main():
             b["dy"] = mi.randn((cfg.T, cfg.d), 1.0, s, "dy", cfg.torch_dtype,
                                dev)
         gbufs = [L.alloc_backward(desc, dev) for _ in batches]
+        rbufs = [L.alloc_router_backward(desc, dev) for _ in batches]
         bev = HipEvents(B.MOE_BWD_NEVENTS * max(args.steps, 1))
+        rev = HipEvents(2 * max(args.steps, 1))
     if args.mxfp8:
         mx = L.quantize_expert_weights(base)
         for b in batches:
@@ -211,6 +217,13 @@ def main():
                   if timed else None)
             L.backward(desc, batches[j], bufs[j], batches[j]["dy"], gbufs[j],
                        events=be)
+            if not cfg.synth_logits:  # router backward: the gate to Wr and dx
+                if timed:
+                    rev.record(2 * i, stream)
+                L.router_backward(desc, batches[j], bufs[j], gbufs[j],
+                                  rbufs[j])
+                if timed:
+                    rev.record(2 * i + 1, stream)
 
     log("bench: warmup")
     for i in range(args.warmup):
@@ -245,6 +258,9 @@ def main():
             o = i * B.MOE_BWD_NEVENTS
             for q, nm in enumerate(names):
                 bstage[nm] += bev.ms(o + q, o + q + 1) / args.steps
+        if not cfg.synth_logits:
+            bstage["router_backward"] = sum(
+                rev.ms(2 * i, 2 * i + 1) for i in range(args.steps)) / args.steps
 
     TK = cfg.TK
     b = 4 if cfg.dtype == "f32" else 2

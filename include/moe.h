@@ -252,6 +252,33 @@ moe_status moe_forward(const moe_desc* desc, const moe_fwd_args* args,
 moe_status moe_backward(const moe_desc* desc, const moe_bwd_args* args,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes of moe_router_backward (independent of its pointers). */
+moe_status moe_router_workspace_size(const moe_desc* desc, size_t* bytes);
+
+/* Router backward: the gate-weight gradient d_topk_w [T, K] (from
+ * moe_backward) carried through the renormalised gate [P3 §4.1, §4.3] to
+ * the logits, the router weights and the tokens. The selection is held
+ * fixed (it is piecewise constant in the logits), so only the K selected
+ * logits of a token get gradient:
+ *   softmax: d_logits[t, e_k] = w_k (d_w_k - sum_j w_j d_w_j);
+ *   sigmoid: d_logits[t, e_k] = s_k (1 - s_k) / S (d_w_k - sum_j w_j d_w_j),
+ *            s = sigmoid(logit), S = sum of the selected s (0 if S == 0);
+ * with w = topk_w and logits the forward's fp32 logits [T, E] (the raw
+ * logits: a route bias only moves the selection). Writes d_logits [T, E]
+ * fp32 (zero off the selection) and d_w_router [E, d_model] = d_logits^T x
+ * in the activation dtype, and ADDS d_logits * w_router [T, d_model] into
+ * dx (in/out, activation dtype: e.g. moe_backward's dx, so that dx becomes
+ * the whole layer's input gradient). x and w_router are as in the forward.
+ * d_w_router is the sum of fixed token-range partial sums taken in a fixed
+ * order: deterministic. MOE_EINVAL on a NULL pointer, MOE_EWORKSPACE if
+ * ws_bytes < moe_router_workspace_size. */
+moe_status moe_router_backward(const moe_desc* desc, const void* x,
+                               const void* w_router, const float* logits,
+                               const int32_t* topk_idx, const float* topk_w,
+                               const float* d_topk_w, float* d_logits,
+                               void* d_w_router, void* dx, void* ws,
+                               size_t ws_bytes, void* stream);
+
 /* MX quantisation of a bf16 [rows, cols] matrix along its rows (cols a
  * multiple of 32), per the OCP MX v1.0 rule: X = floor(log2(amax)) - 8
  * per 32-element block (clamped to [-127, 127]); scale code X + 127;

@@ -28,7 +28,8 @@ MOE_FWD_NEVENTS, MOE_BWD_NEVENTS = 6, 8
 
 EXPORTED = ["moe_status_str", "moe_workspace_size", "moe_route",
             "moe_permute", "moe_grouped_gemm_swiglu", "moe_unpermute_combine",
-            "moe_forward", "moe_backward", "moe_quantize_mxfp8"]
+            "moe_forward", "moe_backward", "moe_router_workspace_size",
+            "moe_router_backward", "moe_quantize_mxfp8"]
 
 
 class MoeError(RuntimeError):
@@ -101,6 +102,9 @@ def load() -> ctypes.CDLL:
                                    c_size_t, c_void_p]),
         "moe_quantize_mxfp8": (c_int32, [c_void_p, c_int64, c_int64,
                                          c_void_p, c_void_p, c_void_p]),
+        "moe_router_workspace_size": (c_int32, [D, POINTER(c_size_t)]),
+        "moe_router_backward": (c_int32, [D] + [c_void_p] * 10 +
+                                [c_size_t, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -209,6 +213,23 @@ def moe_backward(desc, args: MoeBwdArgs, ws, stream=None):
                               ws.numel() * ws.element_size(),
                               stream if stream is not None else current_stream()),
           "moe_backward")
+
+
+def moe_router_workspace_size(desc: MoeDesc) -> int:
+    n = c_size_t(0)
+    check(load().moe_router_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+          "moe_router_workspace_size")
+    return n.value
+
+
+def moe_router_backward(desc, x, w_router, logits, topk_idx, topk_w,
+                        d_topk_w, d_logits, d_w_router, dx, ws, stream=None):
+    check(load().moe_router_backward(
+        ctypes.byref(desc), ptr(x), ptr(w_router), ptr(logits), ptr(topk_idx),
+        ptr(topk_w), ptr(d_topk_w), ptr(d_logits), ptr(d_w_router), ptr(dx),
+        ptr(ws), ws.numel() * ws.element_size(),
+        stream if stream is not None else current_stream()),
+        "moe_router_backward")
 
 
 def moe_quantize_mxfp8(src, rows, cols, q, scales, stream=None):

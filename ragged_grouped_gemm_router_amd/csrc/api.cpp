@@ -113,9 +113,11 @@ GemmParams gp() {
 
 hipError_t run_gemm(GemmOp op, int dtype, GemmParams p,
                     int32_t* const* tile_off, hipStream_t s) {
-  if (dtype == MOE_BF16 && !force_simt() && mfma_supported(op, p))
+  // the router's backward products are small and always run on SIMT
+  const bool router_bwd = op == kOpRouterDx || op == kOpRouterDw;
+  if (dtype == MOE_BF16 && !force_simt() && !router_bwd && mfma_supported(op, p))
     return gemm_mfma(op, p, tile_off, s);
-  if (op != kOpWgrad) {
+  if (op != kOpWgrad && op != kOpRouterDw) {
     if (p.off) {
       p.tile_off = tile_off[tile_bm_slot(kSimtBM)];
       p.tiles_m_max = (int)(cdiv(p.M, kSimtBM) + (p.G < p.M ? p.G : p.M));
@@ -253,6 +255,38 @@ bool weights_ok(const moe_expert_weights* w) {
 }  // namespace
 
 // ===========================================================================
+// Router backward workspace: d_logits in the activation dtype [T, E], the
+// token-range partial sums of the router-weight gradient [G, E, d] fp32,
+// the G + 1 range bounds, and the router's share of dx [T, d].
+struct RouterWs {
+  void* dl_a;
+  float* part;
+  int32_t* split;
+  void* dx_router;
+  int G;
+};
+
+int router_splits(int T) {
+  const int G = T / 256;
+  return G < 1 ? 1 : (G > 64 ? 64 : G);
+}
+
+size_t router_ws_layout(const moe_desc* d, char* base, RouterWs* w) {
+  const size_t b = act_bytes(d->act_dtype), T = d->T, E = d->E,
+               dm = d->d_model;
+  const int G = router_splits(d->T);
+  size_t o = 0;
+  if (w) { w->dl_a = base + o; w->G = G; }
+  o = align_up(o + b * T * E);
+  if (w) w->part = (float*)(base + o);
+  o = align_up(o + sizeof(float) * (size_t)G * E * dm);
+  if (w) w->split = (int32_t*)(base + o);
+  o = align_up(o + sizeof(int32_t) * (size_t)(G + 1));
+  if (w) w->dx_router = base + o;
+  o = align_up(o + b * T * dm);
+  return o;
+}
+
 extern "C" {
 
 const char* moe_status_str(moe_status st) {
@@ -273,6 +307,61 @@ moe_status moe_workspace_size(const moe_desc* desc, int for_backward,
   if (!bytes) return MOE_EINVAL;
   *bytes = for_backward ? bwd_ws_layout(desc, nullptr, nullptr)
                         : fwd_ws_layout(desc, nullptr, nullptr);
+  return MOE_OK;
+}
+
+moe_status moe_router_workspace_size(const moe_desc* desc, size_t* bytes) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_EINVAL;
+  *bytes = router_ws_layout(desc, nullptr, nullptr);
+  return MOE_OK;
+}
+
+moe_status moe_router_backward(const moe_desc* d, const void* x,
+                               const void* w_router, const float* logits,
+                               const int32_t* topk_idx, const float* topk_w,
+                               const float* d_topk_w, float* d_logits,
+                               void* d_w_router, void* dx, void* ws,
+                               size_t ws_bytes, void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;  // nothing is accessed
+  if (!x || !w_router || !logits || !topk_idx || !topk_w || !d_topk_w ||
+      !d_logits || !d_w_router || !dx || !ws)
+    return MOE_EINVAL;
+  if (ws_bytes < router_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
+  RouterWs w;
+  router_ws_layout(d, (char*)ws, &w);
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = d->act_dtype, T = d->T, E = d->E, dm = d->d_model;
+  hipError_t e;
+#define MOE_TRY(x)                         \
+  do {                                     \
+    e = (x);                               \
+    if (e != hipSuccess) return MOE_EHIP;  \
+  } while (0)
+  MOE_TRY(launch_router_grad(dt, logits, topk_idx, topk_w, d_topk_w, T, E,
+                             d->K, d->gate, d_logits, w.dl_a, w.G, w.split, s));
+  {  // the router's share of dx: d_logits Wr, added to dx
+    GemmParams p = gp();
+    p.M = T; p.N = dm; p.K = E;
+    p.A = w.dl_a; p.lda = E;
+    p.B = w_router; p.ldb = dm;
+    p.C = w.dx_router; p.ldc = dm;
+    MOE_TRY(run_gemm(kOpRouterDx, dt, p, nullptr, s));
+    MOE_TRY(launch_add_inplace(dt, dx, w.dx_router, (long)T * dm, s));
+  }
+  {  // d Wr = d_logits^T x: partial sums over G token ranges, then their sum
+    GemmParams p = gp();
+    p.M = E; p.N = dm; p.G = w.G; p.off = w.split;
+    p.A = w.dl_a; p.lda = E;
+    p.B = x; p.ldb = dm;
+    p.C = w.part; p.ldc = dm; p.sC = (long)E * dm;
+    MOE_TRY(run_gemm(kOpRouterDw, dt, p, nullptr, s));
+    MOE_TRY(launch_reduce_parts(dt, w.part, (long)E * dm, w.G, d_w_router, s));
+  }
+#undef MOE_TRY
   return MOE_OK;
 }
 

@@ -15,6 +15,8 @@ enum GemmOp : int {
   kOpWgrad = 5,   // dW_e = L_e^T R_e over the expert's rows (ragged K)
   kOpGemm1Mx = 6, // GEMM 1 on MXFP8 operands; h written as MXFP8
   kOpGemm2Mx = 7, // GEMM 2 on MXFP8 operands; y_perm in bf16
+  kOpRouterDx = 8,  // dx_router[T,d] = d_logits[T,E] Wr[E,d]   (1 group)
+  kOpRouterDw = 9,  // part_g[E,d] = d_logits_g^T x_g over token range g (fp32)
 };
 
 // Row-tile heights for which the permute step publishes tile prefixes.

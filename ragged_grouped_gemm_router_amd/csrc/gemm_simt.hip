@@ -168,6 +168,12 @@ hipError_t dispatch(GemmOp op, const GemmParams& p, hipStream_t s) {
       return launch<T, T, true, false, false, kEpiStore, kSchedM>(p, s);
     case kOpWgrad:
       return launch<T, T, false, false, false, kEpiStore, kSchedK>(p, s);
+    case kOpRouterDx:
+      return launch<T, T, true, false, false, kEpiStore, kSchedM>(p, s);
+    case kOpRouterDw:
+      return launch<T, float, false, false, false, kEpiStore, kSchedK>(p, s);
+    default:
+      break;
   }
   return hipErrorInvalidValue;
 }

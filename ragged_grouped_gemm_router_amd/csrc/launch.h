@@ -44,6 +44,20 @@ hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y,
                               void* dy_perm, float* d_w, int T, int K, int d,
                               hipStream_t s);
 
+// Router backward. d_logits [T,E] fp32 and the same in the activation
+// dtype (d_logits_a); split [G+1] token ranges for the partial sums.
+hipError_t launch_router_grad(int dtype, const float* logits,
+                              const int32_t* idx, const float* w,
+                              const float* d_w, int T, int E, int K, int gate,
+                              float* d_logits, void* d_logits_a, int G,
+                              int32_t* split, hipStream_t s);
+// out[i] = sum_{g < G} part[g * n + i] (fixed order), in dtype.
+hipError_t launch_reduce_parts(int dtype, const float* part, long n, int G,
+                               void* out, hipStream_t s);
+// y += x elementwise (n % 8 == 0).
+hipError_t launch_add_inplace(int dtype, void* y, const void* x, long n,
+                              hipStream_t s);
+
 // MXFP8 (E4M3 elements, E8M0 scale per 32 along rows).
 hipError_t launch_quantize_mxfp8(const void* src, long rows, long cols,
                                  uint8_t* q, uint8_t* scales, hipStream_t s);

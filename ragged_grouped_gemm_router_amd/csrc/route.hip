@@ -119,3 +119,119 @@ hipError_t launch_topk(const float* logits, const float* bias, int T, int E,
 }
 
 }  // namespace moe
+
+namespace moe {
+namespace {
+
+// Gate backward, one wavefront per token: d loss / d logits from
+// d loss / d topk_w. Lane e writes logit e (and e + 64, ...) once: the
+// selected ones get w_k (d_w_k - <w, d_w>) (softmax) or
+// s_k (1 - s_k) / S (d_w_k - <w, d_w>) with s = sigmoid(logit), S the sum
+// of the selected s (sigmoid; zero if S == 0, where the weights were 1/K);
+// the rest get zero. Also the same values in the activation dtype.
+template <typename TA>
+__global__ __launch_bounds__(256) void router_grad_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ idx,
+    const float* __restrict__ w, const float* __restrict__ d_w, int T, int E,
+    int K, int gate, float* __restrict__ d_logits, TA* __restrict__ d_logits_a) {
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;
+  const long r = (long)t * K;
+  float inner = 0.0f, S = 0.0f;
+  for (int k = 0; k < K; ++k) {
+    inner = fmaf(w[r + k], d_w[r + k], inner);
+    if (gate == MOE_GATE_SIGMOID) {
+      const float l = logits[(long)t * E + idx[r + k]];
+      S += 1.0f / (1.0f + expf(-l));
+    }
+  }
+  for (int e = lane; e < E; e += kWave) {
+    float g = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      if (idx[r + k] != e) continue;
+      const float dd = d_w[r + k] - inner;
+      if (gate == MOE_GATE_SOFTMAX) {
+        g = w[r + k] * dd;
+      } else if (S > 0.0f) {
+        const float s = 1.0f / (1.0f + expf(-logits[(long)t * E + e]));
+        g = s * (1.0f - s) / S * dd;
+      }
+    }
+    d_logits[(long)t * E + e] = g;
+    d_logits_a[(long)t * E + e] = (TA)g;
+  }
+}
+
+// out[i] = sum_g part[g * n + i] in g order (fixed, so deterministic)
+template <typename TO>
+__global__ __launch_bounds__(256) void reduce_parts_kernel(
+    const float* __restrict__ part, long n, int G, TO* __restrict__ out) {
+  const long i = blockIdx.x * 256L + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int g = 0; g < G; ++g) s += part[g * n + i];
+  out[i] = (TO)s;
+}
+
+// y[i] += x[i], 8 elements per thread (n % 8 == 0)
+template <typename T>
+__global__ __launch_bounds__(256) void add_inplace_kernel(
+    T* __restrict__ y, const T* __restrict__ x, long n8) {
+  const long i = blockIdx.x * 256L + threadIdx.x;
+  if (i >= n8) return;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    y[i * 8 + q] = (T)((float)y[i * 8 + q] + (float)x[i * 8 + q]);
+}
+
+// split[g] = g * T / G: token ranges of the router-weight partial sums
+__global__ void split_kernel(int T, int G, int32_t* __restrict__ split) {
+  const int g = threadIdx.x;
+  if (g <= G) split[g] = (int)((long)g * T / G);
+}
+
+}  // namespace
+
+hipError_t launch_router_grad(int dtype, const float* logits,
+                              const int32_t* idx, const float* w,
+                              const float* d_w, int T, int E, int K, int gate,
+                              float* d_logits, void* d_logits_a, int G,
+                              int32_t* split, hipStream_t s) {
+  const dim3 grid((T + 3) / 4), block(256);
+  if (dtype == MOE_F32)
+    hipLaunchKernelGGL(router_grad_kernel<float>, grid, block, 0, s, logits,
+                       idx, w, d_w, T, E, K, gate, d_logits, (float*)d_logits_a);
+  else
+    hipLaunchKernelGGL(router_grad_kernel<bf16>, grid, block, 0, s, logits, idx,
+                       w, d_w, T, E, K, gate, d_logits, (bf16*)d_logits_a);
+  hipLaunchKernelGGL(split_kernel, dim3(1), dim3(1024), 0, s, T, G, split);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_parts(int dtype, const float* part, long n, int G,
+                               void* out, hipStream_t s) {
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (dtype == MOE_F32)
+    hipLaunchKernelGGL(reduce_parts_kernel<float>, grid, block, 0, s, part, n, G,
+                       (float*)out);
+  else
+    hipLaunchKernelGGL(reduce_parts_kernel<bf16>, grid, block, 0, s, part, n, G,
+                       (bf16*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_inplace(int dtype, void* y, const void* x, long n,
+                              hipStream_t s) {
+  const long n8 = n / 8;
+  const dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
+  if (dtype == MOE_F32)
+    hipLaunchKernelGGL(add_inplace_kernel<float>, grid, block, 0, s, (float*)y,
+                       (const float*)x, n8);
+  else
+    hipLaunchKernelGGL(add_inplace_kernel<bf16>, grid, block, 0, s, (bf16*)y,
+                       (const bf16*)x, n8);
+  return hipGetLastError();
+}
+
+}  // namespace moe

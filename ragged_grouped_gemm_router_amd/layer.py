@@ -149,3 +149,27 @@ def backward(desc: B.MoeDesc, inp: dict, fbufs: dict, dy: torch.Tensor,
     B.moe_backward(desc, bwd_args(inp, fbufs, dy, gbufs, events), gbufs["ws"],
                    stream)
     return gbufs
+
+
+def alloc_router_backward(desc: B.MoeDesc, device="cuda") -> dict:
+    T, d, E = desc.T, desc.d_model, desc.E
+    dt = act_torch_dtype(desc)
+    return {
+        "d_logits": torch.empty(T, E, dtype=torch.float32, device=device),
+        "d_w_router": torch.empty(E, d, dtype=dt, device=device),
+        "ws": torch.empty(max(B.moe_router_workspace_size(desc), 1),
+                          dtype=torch.uint8, device=device),
+    }
+
+
+def router_backward(desc: B.MoeDesc, inp: dict, fbufs: dict, gbufs: dict,
+                    rbufs: dict, stream=None) -> dict:
+    """After backward(): carries gbufs["d_topk_w"] through the gate into
+    rbufs["d_logits"] and rbufs["d_w_router"], and adds the router's share
+    of the input gradient into gbufs["dx"]."""
+    B.moe_router_backward(desc, inp["x"], inp["wr"], fbufs["logits"],
+                          fbufs["topk_idx"], fbufs["topk_w"],
+                          gbufs["d_topk_w"], rbufs["d_logits"],
+                          rbufs["d_w_router"], gbufs["dx"], rbufs["ws"],
+                          stream)
+    return rbufs

@@ -138,3 +138,23 @@ def test_save_acts_requires_buffers():
                                      fake, fake, None, None, None, fake,
                                      1 << 30, None)
     assert st == B.MOE_EINVAL
+
+
+def test_router_backward_validation():
+    lib = B.load()
+    d = B.make_desc(64, 128, 256, 8, 2)
+    fake = 0x1000
+    n = ctypes.c_size_t(0)
+    assert lib.moe_router_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_OK
+    assert n.value >= 64 * 128 * 2  # the router's share of dx
+    args = [fake] * 9
+    # a missing d_topk_w
+    bad = list(args)
+    bad[5] = None
+    assert lib.moe_router_backward(ctypes.byref(d), *bad, fake, n.value,
+                                   None) == B.MOE_EINVAL
+    assert lib.moe_router_backward(ctypes.byref(d), *args, fake, 16,
+                                   None) == B.MOE_EWORKSPACE
+    z = B.make_desc(0, 128, 256, 8, 2)
+    assert lib.moe_router_backward(ctypes.byref(z), *([None] * 9), None, 0,
+                                   None) == B.MOE_OK
