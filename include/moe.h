@@ -167,6 +167,9 @@ typedef struct moe_bwd_args {
   void* dw3;                  /* [E, d_ff, d_model] act                      */
   void* dw2;                  /* [E, d_model, d_ff] act                      */
   float* d_topk_w;            /* [T, K] fp32                                 */
+  void* dws1;                 /* [d_ff_shared, d_model] act; iff shared      */
+  void* dws3;                 /* [d_ff_shared, d_model] act; iff shared      */
+  void* dws2;                 /* [d_model, d_ff_shared] act; iff shared      */
   void* events[MOE_BWD_NEVENTS]; /* optional hipEvent_t stage boundaries     */
 } moe_bwd_args;
 
@@ -247,8 +250,10 @@ moe_status moe_forward(const moe_desc* desc, const moe_fwd_args* args,
                        void* ws, size_t ws_bytes, void* stream);
 
 /* Whole backward (see moe_bwd_args). Deterministic: weight gradients are
- * owned tile by tile (no split-K atomics). MOE_EUNSUPPORTED for MXFP8
- * descriptors and for a shared expert. */
+ * owned tile by tile (no split-K atomics). The shared expert [P3 §5] is an
+ * ungated SwiGLU FFN over every token: its pre-activations are recomputed,
+ * its gradients written to dws1/dws3/dws2 and its share of dx added into
+ * dx. MOE_EUNSUPPORTED for MXFP8 descriptors. */
 moe_status moe_backward(const moe_desc* desc, const moe_bwd_args* args,
                         void* ws, size_t ws_bytes, void* stream);
 

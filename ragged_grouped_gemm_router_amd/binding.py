@@ -70,6 +70,7 @@ class MoeBwdArgs(ctypes.Structure):
         ("y_perm", c_void_p), ("act_a", c_void_p), ("act_b", c_void_p),
         ("dx", c_void_p), ("dw1", c_void_p), ("dw3", c_void_p),
         ("dw2", c_void_p), ("d_topk_w", c_void_p),
+        ("dws1", c_void_p), ("dws3", c_void_p), ("dws2", c_void_p),
         ("events", c_void_p * MOE_BWD_NEVENTS)]
 
 

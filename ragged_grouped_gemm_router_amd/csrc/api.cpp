@@ -58,6 +58,13 @@ struct BwdWs {
   void* da;
   void* db;
   void* dx_perm;
+  // shared expert: recomputed a, b (then da, db in place), h, its share of
+  // dx, and the one-group row range [0, T)
+  void* sa;
+  void* sb;
+  void* sh;
+  void* sdx;
+  int32_t* srange;
 };
 
 size_t fwd_ws_layout(const moe_desc* d, char* base, FwdWs* w) {
@@ -92,6 +99,19 @@ size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
   o = align_up(o + b * TK * d->d_ff);
   if (w) w->dx_perm = base + o;
   o = align_up(o + b * TK * d->d_model);
+  if (d->d_ff_shared > 0) {
+    const size_t T = d->T, fs = d->d_ff_shared;
+    void** bufs[3] = {w ? &w->sa : nullptr, w ? &w->sb : nullptr,
+                      w ? &w->sh : nullptr};
+    for (void** q : bufs) {
+      if (q) *q = base + o;
+      o = align_up(o + b * T * fs);
+    }
+    if (w) w->sdx = base + o;
+    o = align_up(o + b * T * d->d_model);
+    if (w) w->srange = (int32_t*)(base + o);
+    o = align_up(o + 2 * sizeof(int32_t));
+  }
   return o;
 }
 
@@ -504,7 +524,10 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
       !a->dx || !a->dw1 || !a->dw3 || !a->dw2 || !a->d_topk_w)
     return MOE_EINVAL;
   if ((a->act_a == nullptr) != (a->act_b == nullptr)) return MOE_EINVAL;
-  if (d->d_ff_shared > 0 || d->gemm_dtype == MOE_MXFP8) return MOE_EUNSUPPORTED;
+  if (d->gemm_dtype == MOE_MXFP8) return MOE_EUNSUPPORTED;
+  const bool shared = d->d_ff_shared > 0;
+  if (shared && (!weights_ok(&a->shared) || !a->dws1 || !a->dws3 || !a->dws2))
+    return MOE_EINVAL;
   if (ws_bytes < bwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
   BwdWs w;
   bwd_ws_layout(d, (char*)ws, &w);
@@ -532,6 +555,12 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     sa = w.da;
     sb = w.db;
   }
+  const int fs = d->d_ff_shared;
+  if (shared) {  // shared expert over every token: h, a, b
+    MOE_TRY(launch_split(d->T, 1, w.srange, s));
+    MOE_TRY(do_gemm1(d, a->x, nullptr, d->T, 1, a->shared.w1, a->shared.w3,
+                     fs, w.sh, w.sa, w.sb, w.tile_off, s));
+  }
   record(a->events[2], s);
   {  // dh = dy_perm W2_e, then (da, db) from the SwiGLU derivative
     GemmParams p = gp();
@@ -540,6 +569,15 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.B = a->routed.w2; p.ldb = f; p.sB = (long)dm * f;
     p.C = w.da; p.C2 = w.db; p.ldc = f;
     p.aux_a = sa; p.aux_b = sb;
+    MOE_TRY(run_gemm(kOpDgrad2, dt, p, w.tile_off, s));
+  }
+  if (shared) {  // ungated: dh_s = dy Ws2, (da_s, db_s) in place of (a_s, b_s)
+    GemmParams p = gp();
+    p.M = d->T; p.N = fs; p.K = dm;
+    p.A = a->dy; p.lda = dm;
+    p.B = a->shared.w2; p.ldb = fs;
+    p.C = w.sa; p.C2 = w.sb; p.ldc = fs;
+    p.aux_a = w.sa; p.aux_b = w.sb;
     MOE_TRY(run_gemm(kOpDgrad2, dt, p, w.tile_off, s));
   }
   record(a->events[3], s);
@@ -551,9 +589,17 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.C = w.dx_perm; p.ldc = dm;
     MOE_TRY(run_gemm(kOpDgrad1, dt, p, w.tile_off, s));
   }
+  if (shared) {  // dx_s = da_s Ws1 + db_s Ws3
+    GemmParams p = gp();
+    p.M = d->T; p.N = dm; p.K = 2 * fs; p.K1 = fs;
+    p.A = w.sa; p.A2 = w.sb; p.lda = fs;
+    p.B = a->shared.w1; p.B2 = a->shared.w3; p.ldb = dm;
+    p.C = w.sdx; p.ldc = dm;
+    MOE_TRY(run_gemm(kOpDgrad1, dt, p, w.tile_off, s));
+  }
   record(a->events[4], s);
-  MOE_TRY(launch_combine(dt, w.dx_perm, a->dest, nullptr, nullptr, a->dx,
-                         d->T, d->K, dm, s));
+  MOE_TRY(launch_combine(dt, w.dx_perm, a->dest, nullptr,
+                         shared ? w.sdx : nullptr, a->dx, d->T, d->K, dm, s));
   record(a->events[5], s);
   {  // dW2_e = dy_perm_e^T h_e
     GemmParams p = gp();
@@ -561,6 +607,14 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.A = w.dy_perm; p.lda = dm;
     p.B = a->h; p.ldb = f;
     p.C = a->dw2; p.ldc = f; p.sC = (long)dm * f;
+    MOE_TRY(run_gemm(kOpWgrad, dt, p, w.tile_off, s));
+  }
+  if (shared) {  // dWs2 = dy^T h_s
+    GemmParams p = gp();
+    p.M = dm; p.N = fs; p.G = 1; p.off = w.srange;
+    p.A = a->dy; p.lda = dm;
+    p.B = w.sh; p.ldb = fs;
+    p.C = a->dws2; p.ldc = fs;
     MOE_TRY(run_gemm(kOpWgrad, dt, p, w.tile_off, s));
   }
   record(a->events[6], s);
@@ -571,6 +625,14 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.B = a->x_perm; p.ldb = dm;
     p.C = which ? a->dw3 : a->dw1; p.ldc = dm; p.sC = (long)f * dm;
     MOE_TRY(run_gemm(kOpWgrad, dt, p, w.tile_off, s));
+    if (shared) {  // dWs1 = da_s^T x, dWs3 = db_s^T x
+      GemmParams q = gp();
+      q.M = fs; q.N = dm; q.G = 1; q.off = w.srange;
+      q.A = which ? w.sb : w.sa; q.lda = fs;
+      q.B = a->x; q.ldb = dm;
+      q.C = which ? a->dws3 : a->dws1; q.ldc = dm;
+      MOE_TRY(run_gemm(kOpWgrad, dt, q, w.tile_off, s));
+    }
   }
   record(a->events[7], s);
 #undef MOE_TRY

@@ -51,6 +51,8 @@ hipError_t launch_router_grad(int dtype, const float* logits,
                               const float* d_w, int T, int E, int K, int gate,
                               float* d_logits, void* d_logits_a, int G,
                               int32_t* split, hipStream_t s);
+// split[g] = g * T / G for g = 0..G (G <= 1023).
+hipError_t launch_split(int T, int G, int32_t* split, hipStream_t s);
 // out[i] = sum_{g < G} part[g * n + i] (fixed order), in dtype.
 hipError_t launch_reduce_parts(int dtype, const float* part, long n, int G,
                                void* out, hipStream_t s);

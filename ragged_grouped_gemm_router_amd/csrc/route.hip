@@ -209,6 +209,11 @@ hipError_t launch_router_grad(int dtype, const float* logits,
   return hipGetLastError();
 }
 
+hipError_t launch_split(int T, int G, int32_t* split, hipStream_t s) {
+  hipLaunchKernelGGL(split_kernel, dim3(1), dim3(1024), 0, s, T, G, split);
+  return hipGetLastError();
+}
+
 hipError_t launch_reduce_parts(int dtype, const float* part, long n, int G,
                                void* out, hipStream_t s) {
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);

@@ -113,6 +113,7 @@ def forward(desc: B.MoeDesc, inp: dict, bufs: dict, events=None,
 
 def alloc_backward(desc: B.MoeDesc, device="cuda") -> dict:
     T, d, f, E, K = desc.T, desc.d_model, desc.d_ff, desc.E, desc.K
+    fs = desc.d_ff_shared
     dt = act_torch_dtype(desc)
     return {
         "dx": torch.empty(T, d, dtype=dt, device=device),
@@ -122,6 +123,10 @@ def alloc_backward(desc: B.MoeDesc, device="cuda") -> dict:
         "d_topk_w": torch.empty(T, K, dtype=torch.float32, device=device),
         "ws": torch.empty(max(B.moe_workspace_size(desc, True), 1),
                           dtype=torch.uint8, device=device),
+        **({"dws1": torch.empty(fs, d, dtype=dt, device=device),
+            "dws3": torch.empty(fs, d, dtype=dt, device=device),
+            "dws2": torch.empty(d, fs, dtype=dt, device=device)}
+           if fs > 0 else {}),
     }
 
 
@@ -136,8 +141,8 @@ def bwd_args(inp: dict, fbufs: dict, dy: torch.Tensor, gbufs: dict,
     for k in ("topk_idx", "topk_w", "offsets", "sorted_src", "dest", "x_perm",
               "h", "y_perm", "act_a", "act_b"):
         setattr(a, k, p(fbufs.get(k)))
-    for k in ("dx", "dw1", "dw3", "dw2", "d_topk_w"):
-        setattr(a, k, p(gbufs[k]))
+    for k in ("dx", "dw1", "dw3", "dw2", "d_topk_w", "dws1", "dws3", "dws2"):
+        setattr(a, k, p(gbufs.get(k)))
     if events:
         for i, ev in enumerate(events[:B.MOE_BWD_NEVENTS]):
             a.events[i] = ev

@@ -43,7 +43,7 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.MoeExpertWeights) == 48
     n_ptr_fwd = 4 + 1 + 14 + B.MOE_FWD_NEVENTS
     assert ctypes.sizeof(B.MoeFwdArgs) == 8 * n_ptr_fwd + 2 * 48
-    n_ptr_bwd = 2 + 15 + B.MOE_BWD_NEVENTS
+    n_ptr_bwd = 2 + 18 + B.MOE_BWD_NEVENTS
     assert ctypes.sizeof(B.MoeBwdArgs) == 8 * n_ptr_bwd + 2 * 48
 
 

@@ -52,6 +52,31 @@ def test_backward_parity(cfg, save_acts):
         assert (gb["dw1"][e] == 0).all() and (gb["dw2"][e] == 0).all()
 
 
+SHARED = [
+    mi.MoEConfig("shared_deepseek_like_T512_d256_f128_E16_K4_fs256", 512, 256,
+                 128, 16, 4, f_shared=256, gate="sigmoid", bias=True),
+    mi.MoEConfig("shared_f32_T128_d64_f64_E4_K2_fs96", 128, 64, 64, 4, 2,
+                 f_shared=96, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("save_acts", [True, False], ids=["saved", "recompute"])
+@pytest.mark.parametrize("cfg", SHARED, ids=[c.name for c in SHARED])
+def test_backward_shared_expert(cfg, save_acts):
+    """With an ungated shared expert: its weight gradients, and dx holding
+    both the routed and the shared share."""
+    cinp, ginp = inputs(cfg, seed=3, with_dy=True)
+    fb, gb = _run(cfg, cinp, ginp, save_acts)
+    idx, w, *_ = check_routing_exact(cfg, cinp, fb)
+    ref = oracle.backward(cinp["x"], cinp["w1"], cinp["w3"], cinp["w2"], idx,
+                          w, cinp["dy"], cinp["ws1"], cinp["ws3"], cinp["ws2"])
+    for k, rk in (("dx", "dx"), ("dw1", "dw1"), ("dw3", "dw3"), ("dw2", "dw2"),
+                  ("d_topk_w", "d_w"), ("dws1", "dws1"), ("dws3", "dws3"),
+                  ("dws2", "dws2")):
+        err = rel_err(gb[k], ref[rk])
+        assert err <= tol(cfg), (k, err)
+
+
 def test_backward_deterministic():
     cfg = CASES[3]
     cinp, ginp = inputs(cfg, seed=4, with_dy=True)
