@@ -82,7 +82,7 @@ typedef int32_t moe_status;
 
 typedef struct moe_desc {
   int32_t T;            /* tokens (batch x sequence flattened), >= 0       */
-  int32_t d_model;      /* multiple of 8 (bf16/fp32), of 32 (MXFP8)        */
+  int32_t d_model;      /* multiple of 8 (bf16/fp32), of 128 (MXFP8)       */
   int32_t d_ff;         /* routed expert hidden size, same rule            */
   int32_t E;            /* routed experts, 1..MOE_E_MAX                    */
   int32_t K;            /* experts per token, 1..min(E, MOE_K_MAX)         */
@@ -90,8 +90,8 @@ typedef struct moe_desc {
   int32_t gate;         /* MOE_GATE_SOFTMAX | MOE_GATE_SIGMOID             */
   int32_t act_dtype;    /* MOE_F32 | MOE_BF16                              */
   int32_t gemm_dtype;   /* = act_dtype, or MOE_MXFP8 (forward only, bf16
-                           act, d_model and d_ff multiples of 128, no
-                           shared expert, no MOE_FLAG_SAVE_ACTS)           */
+                           act, d_model, d_ff and d_ff_shared multiples of
+                           128, no MOE_FLAG_SAVE_ACTS)                     */
   int32_t flags;        /* MOE_FLAG_*                                      */
 } moe_desc;
 
@@ -225,7 +225,8 @@ moe_status moe_permute(const moe_desc* desc, const void* x,
  * then scales; y_perm is bf16.
  * If x_shared is non-NULL and d_ff_shared > 0, the shared expert runs on
  * every token: y_shared = SwiGLU_shared(x_shared). MXFP8: x_perm and
- * x_perm_scales are E4M3/E8M0, weights must be quantised; h may be NULL. */
+ * x_perm_scales are E4M3/E8M0 and all weights (routed and shared) must be
+ * quantised; x_shared stays bf16 and is quantised into the workspace. */
 moe_status moe_grouped_gemm_swiglu(const moe_desc* desc, const void* x_perm,
                                    const uint8_t* x_perm_scales,
                                    const int32_t* offsets,

@@ -36,10 +36,11 @@ moe_status check_desc(const moe_desc* d) {
     return MOE_EINVAL;
   if (d->d_model % 8 || d->d_ff % 8 || d->d_ff_shared % 8) return MOE_EUNSUPPORTED;
   if (d->gemm_dtype == MOE_MXFP8) {
-    // whole 128-element k-tiles for both GEMMs; no shared expert and no
-    // saved pre-activations on this path
-    if (d->d_model % 128 || d->d_ff % 128) return MOE_EUNSUPPORTED;
-    if (d->d_ff_shared > 0 || (d->flags & MOE_FLAG_SAVE_ACTS)) return MOE_EUNSUPPORTED;
+    // whole 128-element k-tiles for every GEMM; no saved pre-activations
+    // on this path
+    if (d->d_model % 128 || d->d_ff % 128 || d->d_ff_shared % 128)
+      return MOE_EUNSUPPORTED;
+    if (d->flags & MOE_FLAG_SAVE_ACTS) return MOE_EUNSUPPORTED;
   }
   if ((long)d->T * d->K > kMaxCopies) return MOE_EUNSUPPORTED;
   return MOE_OK;
@@ -49,6 +50,8 @@ moe_status check_desc(const moe_desc* d) {
 struct FwdWs {
   int32_t* block_hist;
   int32_t* rank;
+  uint8_t* xq;  // MXFP8 with a shared expert: x quantised, codes [T, d]
+  uint8_t* xs;  // and E8M0 scales [T, d/32]
   int32_t* tile_off[kNumTileBM];
   void* h_shared;
 };
@@ -81,6 +84,13 @@ size_t fwd_ws_layout(const moe_desc* d, char* base, FwdWs* w) {
   }
   if (w) w->h_shared = base + o;
   o = align_up(o + act_bytes(d->act_dtype) * (size_t)d->T * d->d_ff_shared);
+  if (d->gemm_dtype == MOE_MXFP8 && d->d_ff_shared > 0) {
+    const size_t n = (size_t)d->T * d->d_model;
+    if (w) w->xq = (uint8_t*)(base + o);
+    o = align_up(o + n);
+    if (w) w->xs = (uint8_t*)(base + o);
+    o = align_up(o + n / 32);
+  }
   return o;
 }
 
@@ -214,10 +224,14 @@ hipError_t do_gemm2(const moe_desc* d, const void* h, const int32_t* off,
 
 // MXFP8 expert GEMMs. h lives in the caller's h buffer as E4M3 codes
 // [T*K, d_ff] followed by E8M0 scales [T*K, d_ff/32].
+// With a shared expert, x is quantised into the workspace and the shared
+// GEMMs run as one dense group, h_shared holding codes then scales.
 hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
                          const uint8_t* x_perm_scales, const int32_t* offsets,
-                         const moe_expert_weights* rw, void* h, void* y_perm,
-                         const FwdWs& ws, hipStream_t s, void* ev_mid) {
+                         const moe_expert_weights* rw, const void* x_shared,
+                         const moe_expert_weights* sw, void* h, void* y_perm,
+                         void* y_shared, const FwdWs& ws, hipStream_t s,
+                         void* ev_mid) {
   const int TK = d->T * d->K, dm = d->d_model, f = d->d_ff;
   uint8_t* hq = (uint8_t*)h;
   uint8_t* hs = hq + (size_t)TK * f;
@@ -237,6 +251,27 @@ hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
   p.B = rw->w2; p.ldb = f; p.sB = (long)dm * f;
   p.Bs = rw->w2_scales; p.ld_s = f / 32; p.sBs = (long)dm * (f / 32);
   p.C = y_perm; p.ldc = dm;
+  e = gemm_mfma(kOpGemm2Mx, p, ws.tile_off, s);
+  if (e != hipSuccess || !x_shared || d->d_ff_shared == 0) return e;
+  const int T = d->T, fs = d->d_ff_shared;
+  e = launch_quantize_mxfp8(x_shared, T, dm, ws.xq, ws.xs, s);
+  if (e != hipSuccess) return e;
+  uint8_t* sq = (uint8_t*)ws.h_shared;
+  uint8_t* ss = sq + (size_t)T * fs;
+  p = gp();
+  p.M = T; p.N = fs; p.K = dm;
+  p.A = ws.xq; p.lda = dm; p.As = ws.xs;
+  p.B = sw->w1; p.B2 = sw->w3; p.ldb = dm;
+  p.Bs = sw->w1_scales; p.B2s = sw->w3_scales; p.ld_s = dm / 32;
+  p.C = sq; p.C2 = ss; p.ldc = fs;
+  e = gemm_mfma(kOpGemm1Mx, p, ws.tile_off, s);
+  if (e != hipSuccess) return e;
+  p = gp();
+  p.M = T; p.N = dm; p.K = fs;
+  p.A = sq; p.lda = fs; p.As = ss;
+  p.B = sw->w2; p.ldb = fs;
+  p.Bs = sw->w2_scales; p.ld_s = fs / 32;
+  p.C = y_shared; p.ldc = dm;
   return gemm_mfma(kOpGemm2Mx, p, ws.tile_off, s);
 }
 
@@ -444,9 +479,12 @@ moe_status moe_grouped_gemm_swiglu(const moe_desc* d, const void* x_perm,
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_tile_prefix(offsets, d->E, w.tile_off, s);
   if (e != hipSuccess) return MOE_EHIP;
-  if (mx)
+  if (mx) {
+    if (use_shared && !mx_weights_ok(shared)) return MOE_EINVAL;
     return hip_status(do_experts_mx(d, x_perm, x_perm_scales, offsets, routed,
-                                    h, y_perm, w, s, nullptr));
+                                    use_shared ? x_shared : nullptr, shared, h,
+                                    y_perm, y_shared, w, s, nullptr));
+  }
   const bool save = d->flags & MOE_FLAG_SAVE_ACTS;
   return hip_status(do_experts(d, x_perm, offsets, routed,
                                use_shared ? x_shared : nullptr, shared, h,
@@ -483,6 +521,7 @@ moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
   if (save && (!a->act_a || !a->act_b)) return MOE_EINVAL;
   const bool mx = d->gemm_dtype == MOE_MXFP8;
   if (mx && (!a->x_perm_scales || !mx_weights_ok(&a->routed))) return MOE_EINVAL;
+  if (mx && shared && !mx_weights_ok(&a->shared)) return MOE_EINVAL;
   if (ws_bytes < fwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
   FwdWs w;
   fwd_ws_layout(d, (char*)ws, &w);
@@ -498,7 +537,8 @@ moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
   record(a->events[2], s);
   if (mx)
     e = do_experts_mx(d, a->x_perm, a->x_perm_scales, a->offsets, &a->routed,
-                      a->h, a->y_perm, w, s, a->events[3]);
+                      shared ? a->x : nullptr, &a->shared, a->h, a->y_perm,
+                      a->y_shared, w, s, a->events[3]);
   else
     e = do_experts(d, a->x_perm, a->offsets, &a->routed,
                    shared ? a->x : nullptr, &a->shared, a->h, a->y_perm,

@@ -36,8 +36,9 @@ def quantize_expert_weights(inp: dict) -> dict:
     """MXFP8 copies of the routed expert weights (quantised once, along
     each matrix's rows = the contraction dimension of its GEMM)."""
     out = {}
-    for k in ("w1", "w3", "w2"):
-        out[k], out[k + "_s"] = quantize_mxfp8(inp[k])
+    for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2"):
+        if inp.get(k) is not None:
+            out[k], out[k + "_s"] = quantize_mxfp8(inp[k])
     return out
 
 
@@ -90,9 +91,13 @@ def fwd_args(inp: dict, bufs: dict,
         m = inp["mx"]
         a.routed = B.expert_weights(m["w1"], m["w3"], m["w2"], m["w1_s"],
                                     m["w3_s"], m["w2_s"])
+        a.shared = B.expert_weights(m.get("ws1"), m.get("ws3"), m.get("ws2"),
+                                    m.get("ws1_s"), m.get("ws3_s"),
+                                    m.get("ws2_s"))
     else:
         a.routed = B.expert_weights(inp["w1"], inp["w3"], inp["w2"])
-    a.shared = B.expert_weights(inp.get("ws1"), inp.get("ws3"), inp.get("ws2"))
+        a.shared = B.expert_weights(inp.get("ws1"), inp.get("ws3"),
+                                    inp.get("ws2"))
     for k in ("out", "logits", "topk_idx", "topk_w", "counts", "offsets",
               "sorted_src", "dest", "x_perm", "x_perm_scales", "h", "y_perm",
               "y_shared", "act_a", "act_b"):

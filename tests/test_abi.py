@@ -77,7 +77,7 @@ def test_workspace_size_host_only():
     (dict(flags=8), B.MOE_EINVAL),
     (dict(gemm_dtype=B.MOE_F32), B.MOE_EINVAL),             # bf16 act, f32 gemm
     (dict(gemm_dtype=B.MOE_MXFP8, d_model=160), B.MOE_EUNSUPPORTED),
-    (dict(gemm_dtype=B.MOE_MXFP8, d_ff_shared=128), B.MOE_EUNSUPPORTED),
+    (dict(gemm_dtype=B.MOE_MXFP8, d_ff_shared=96), B.MOE_EUNSUPPORTED),
     (dict(gemm_dtype=B.MOE_MXFP8, flags=B.MOE_FLAG_SAVE_ACTS),
      B.MOE_EUNSUPPORTED),
 ])

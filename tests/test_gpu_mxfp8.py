@@ -49,6 +49,8 @@ def test_quantizer_bit_exact():
 
 MX_SMALL = [
     mi.MoEConfig("mx_T1024_d256_f512_E8_K2", 1024, 256, 512, 8, 2),
+    mi.MoEConfig("mx_shared_sigmoid_T512_d256_f256_E16_K4_fs256", 512, 256,
+                 256, 16, 4, f_shared=256, gate="sigmoid", bias=True),
     mi.MoEConfig("mx_T256_d128_f256_E8_K2", 256, 128, 256, 8, 2),
     mi.MoEConfig("mx_skewed_T1024_d256_f256_E16_K4", 1024, 256, 256, 16, 4,
                  synth_logits=True, n_zero=3, zipf_s=1.2),
@@ -56,8 +58,8 @@ MX_SMALL = [
 
 
 def _mx_forward(cfg, ginp):
-    desc = B.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.K, gate=cfg.gate,
-                       mxfp8=True)
+    desc = B.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.K, cfg.f_shared,
+                       gate=cfg.gate, mxfp8=True)
     ginp = dict(ginp)
     ginp["mx"] = L.quantize_expert_weights(ginp)
     bufs = L.alloc_forward(desc, DEV)
@@ -79,10 +81,12 @@ def test_mxfp8_forward_parity(cfg):
     # weights quantised on the device agree with the oracle's rule
     q1, c1 = oracle.mx_quantize(cinp["w1"][0].double())
     assert torch.equal(mx["w1_s"][0].cpu(), c1)
+    sh = (cinp["ws1"], cinp["ws3"], cinp["ws2"])
     ref = oracle.forward_mxfp8(cinp["x"], cinp["w1"], cinp["w3"], cinp["w2"],
-                               idx, w)
+                               idx, w, *sh)
     err = rel_err(bufs["out"], ref)
-    exact = oracle.forward(cinp["x"], cinp["w1"], cinp["w3"], cinp["w2"], idx, w)
+    exact = oracle.forward(cinp["x"], cinp["w1"], cinp["w3"], cinp["w2"], idx, w,
+                           *sh)
     err_exact = rel_err(bufs["out"], exact)
     print(f"{cfg.name}: vs fp8-aware oracle {err:.3e}, vs exact oracle "
           f"{err_exact:.3e}")
