@@ -430,8 +430,70 @@ def gate_logit_grad(logits: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
     return out
 
 
-def router_backward(x, wr, logits, idx, w, d_w, gate: str):
+def router_backward(x, wr, logits, idx, w, d_w, gate: str,
+                    aux_coef: float = 0.0):
     """Gradients of the router: d_logits [T, E], d_wr = d_logits^T x
-    [E, d] and the router's share of dx, d_logits wr [T, d] (fp64)."""
+    [E, d] and the router's share of dx, d_logits wr [T, d] (fp64).
+    With aux_coef != 0 the loss also holds aux_coef times the balance loss
+    of load_balance_stats, whose logit gradient is added first."""
     dl = gate_logit_grad(logits, idx, w, d_w, gate)
+    if aux_coef != 0.0:
+        dl = dl + aux_coef * aux_loss_logit_grad(logits, idx, logits.shape[1],
+                                                 gate)
     return {"d_logits": dl, "d_wr": dl.T @ _f64(x), "dx": dl @ _f64(wr)}
+
+
+# --------------------------------------------------------------------------
+# Load-balance statistics [P3 §6.2, §9]: the GShard-style auxiliary loss
+# N * sum_i f_i P_i, with f_i the share of tokens whose top-K mask holds
+# expert i and P_i the mean gate probability of expert i over the tokens.
+# --------------------------------------------------------------------------
+
+def gate_probs(logits: torch.Tensor, gate: str) -> torch.Tensor:
+    """Per-token gate probabilities over all E experts [T, E] (fp64):
+    softmax of the logits (softmax gate), or the sigmoids normalised to sum
+    to one over all experts (sigmoid gate; raw logits, no route bias)."""
+    L = _f64(logits)
+    if gate == "softmax":
+        return torch.softmax(L, dim=1)
+    if gate == "sigmoid":
+        s = _sigmoid(L)
+        return s / s.sum(dim=1, keepdim=True)
+    raise ValueError(gate)
+
+
+def load_balance_stats(logits: torch.Tensor, idx: torch.Tensor, E: int,
+                       gate: str) -> dict:
+    """f [E] = mean over tokens of the top-K mask (sums to K), p_mean [E] =
+    mean over tokens of the gate probabilities (sums to 1), aux = E *
+    sum_i f_i p_mean_i. The load statistic of the layer [P3 §9] is f / K."""
+    T = logits.shape[0]
+    mask = torch.zeros(T, E, dtype=torch.float64)
+    mask.scatter_(1, idx.to(torch.int64), 1.0)
+    f = mask.mean(dim=0)
+    P = gate_probs(logits, gate).mean(dim=0)
+    return {"f": f, "p_mean": P, "aux": E * (f * P).sum()}
+
+
+def aux_loss_logit_grad(logits: torch.Tensor, idx: torch.Tensor, E: int,
+                        gate: str) -> torch.Tensor:
+    """d aux / d logits [T, E] (fp64), with the mask share f held constant
+    (it is piecewise constant in the logits).
+
+    aux = (E / T) sum_t sum_i f_i P_ti, so d aux / d L_tj =
+    (E / T) sum_i f_i dP_ti / dL_tj. Softmax: dP_ti / dL_tj =
+    P_ti (delta_ij - P_tj), giving (E / T) P_tj (f_j - sum_i f_i P_ti).
+    Normalised sigmoid, P_ti = s_ti / S_t: dP_ti / dL_tj =
+    s_tj (1 - s_tj) / S_t (delta_ij - P_ti), giving
+    (E / T) s_tj (1 - s_tj) / S_t (f_j - sum_i f_i P_ti)."""
+    L = _f64(logits)
+    T = L.shape[0]
+    f = load_balance_stats(L, idx, E, gate)["f"]
+    P = gate_probs(L, gate)
+    inner = (P * f).sum(dim=1, keepdim=True)
+    if gate == "softmax":
+        q = P
+    else:
+        s = _sigmoid(L)
+        q = s * (1.0 - s) / s.sum(dim=1, keepdim=True)
+    return (E / T) * q * (f - inner)

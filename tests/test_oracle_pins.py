@@ -455,3 +455,96 @@ def test_router_backward_invariants():
         dl = oracle.gate_logit_grad(L, idx, w, torch.full((T, K), 0.7,
                                     dtype=torch.float64), gate)
         assert torch.allclose(dl, torch.zeros_like(dl), atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Load-balance statistics [P3 §6.2, §9]
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gate", ["softmax", "sigmoid"])
+def test_balance_stats_closed_forms(gate):
+    """Uniform logits give P_i = 1/E for any routing, so aux = sum_i f_i =
+    K; top-1 routing spread evenly with uniform probabilities gives aux = 1,
+    the value the page scales the loss by E to reach [P3 §6.2]."""
+    T, E, K = 24, 6, 2
+    L = torch.zeros(T, E, dtype=torch.float64)
+    g = torch.Generator().manual_seed(21)
+    idx = torch.stack([torch.randperm(E, generator=g)[:K] for _ in range(T)])
+    r = oracle.load_balance_stats(L, idx, E, gate)
+    assert torch.allclose(r["p_mean"], torch.full((E,), 1.0 / E,
+                          dtype=torch.float64), atol=1e-15)
+    assert abs(float(r["aux"]) - K) < 1e-12
+    idx1 = (torch.arange(T) % E).unsqueeze(1)
+    r1 = oracle.load_balance_stats(L, idx1, E, gate)
+    assert torch.allclose(r1["f"], torch.full((E,), 1.0 / E,
+                          dtype=torch.float64), atol=1e-15)
+    assert abs(float(r1["aux"]) - 1.0) < 1e-12
+
+
+@pytest.mark.parametrize("gate", ["softmax", "sigmoid"])
+def test_balance_stats_invariants(gate):
+    """f equals bincount / T and sums to K; each token's probabilities sum
+    to one, so p_mean sums to one; evenly spread loads (every f_i = K/E)
+    make aux = K whatever the logits."""
+    g = torch.Generator().manual_seed(22)
+    T, E, K = 40, 8, 3
+    L = 2.0 * torch.randn(T, E, generator=g, dtype=torch.float64)
+    idx = oracle.topk_select(oracle.selection_keys(L), K)
+    r = oracle.load_balance_stats(L, idx, E, gate)
+    assert torch.equal(r["f"], torch.bincount(idx.reshape(-1), minlength=E)
+                       .to(torch.float64) / T)
+    assert abs(float(r["f"].sum()) - K) < 1e-12
+    assert abs(float(r["p_mean"].sum()) - 1.0) < 1e-12
+    # every token picks experts (t + j) mod E: each expert T*K/E times
+    idx_even = (torch.arange(T).unsqueeze(1) + torch.arange(K)) % E
+    r2 = oracle.load_balance_stats(L, idx_even, E, gate)
+    assert abs(float(r2["aux"]) - K) < 1e-12
+
+
+@pytest.mark.parametrize("gate", ["softmax", "sigmoid"])
+def test_aux_loss_grad_matches_autograd(gate):
+    """The closed-form logit gradient of the balance loss equals autograd
+    through softmax (or the normalised sigmoid) and the token mean, with
+    the mask share held fixed; added into the router backward it reaches
+    Wr and x as aux_coef times autograd of the balance loss."""
+    g = torch.Generator().manual_seed(23)
+    T, d, E, K = 14, 9, 7, 2
+    x = torch.randn(T, d, generator=g, dtype=torch.float64)
+    wr = torch.randn(E, d, generator=g, dtype=torch.float64)
+    L0 = x @ wr.T
+    idx = oracle.topk_select(oracle.selection_keys(L0), K)
+    f = torch.bincount(idx.reshape(-1), minlength=E).to(torch.float64) / T
+    xa, wra = x.clone().requires_grad_(), wr.clone().requires_grad_()
+    La = xa @ wra.T
+    if gate == "softmax":
+        P = torch.softmax(La, dim=1)
+    else:
+        s = torch.sigmoid(La)
+        P = s / s.sum(dim=1, keepdim=True)
+    aux = E * (f * P.mean(dim=0)).sum()
+    coef = 0.03
+    (coef * aux).backward()
+    dl = oracle.aux_loss_logit_grad(L0, idx, E, gate)
+    zero = torch.zeros(T, K, dtype=torch.float64)
+    w = oracle.gate_weights(L0, idx, gate)
+    r = oracle.router_backward(x, wr, L0, idx, w, zero, gate, aux_coef=coef)
+    assert torch.allclose(r["d_logits"], coef * dl, rtol=0, atol=1e-15)
+    assert torch.allclose(r["d_wr"], wra.grad, rtol=0, atol=1e-12)
+    assert torch.allclose(r["dx"], xa.grad, rtol=0, atol=1e-12)
+
+
+def test_aux_loss_grad_special_cases():
+    """Softmax: a token's gradient sums to zero (shift invariance); evenly
+    spread loads give zero gradient (aux is then K for every logit)."""
+    g = torch.Generator().manual_seed(24)
+    T, E, K = 16, 8, 2
+    L = torch.randn(T, E, generator=g, dtype=torch.float64)
+    idx = oracle.topk_select(oracle.selection_keys(L), K)
+    dl = oracle.aux_loss_logit_grad(L, idx, E, "softmax")
+    assert torch.allclose(dl.sum(dim=1), torch.zeros(T, dtype=torch.float64),
+                          atol=1e-15)
+    assert dl.abs().max() > 1e-3
+    idx_even = (torch.arange(T).unsqueeze(1) + torch.arange(K)) % E
+    for gate in ("softmax", "sigmoid"):
+        dz = oracle.aux_loss_logit_grad(L, idx_even, E, gate)
+        assert dz.abs().max() < 1e-15
