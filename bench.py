@@ -143,6 +143,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time a training step: forward (activations saved) "
                          "plus backward; FLOPs counted as 3x the forward")
+    ap.add_argument("--aux-coef", type=float, default=0.01,
+                    help="coefficient of the balance loss in the training "
+                         "step's router backward")
     ap.add_argument("--mxfp8", action="store_true",
                     help="expert GEMMs on MXFP8 operands (weights quantised "
                          "once, before timing)")
@@ -186,7 +189,7 @@ def main():
         gbufs = [L.alloc_backward(desc, dev) for _ in batches]
         rbufs = [L.alloc_router_backward(desc, dev) for _ in batches]
         bev = HipEvents(B.MOE_BWD_NEVENTS * max(args.steps, 1))
-        rev = HipEvents(2 * max(args.steps, 1))
+        rev = HipEvents(3 * max(args.steps, 1))
     if args.mxfp8:
         mx = L.quantize_expert_weights(base)
         for b in batches:
@@ -217,13 +220,18 @@ def main():
                   if timed else None)
             L.backward(desc, batches[j], bufs[j], batches[j]["dy"], gbufs[j],
                        events=be)
-            if not cfg.synth_logits:  # router backward: the gate to Wr and dx
+            if not cfg.synth_logits:
+                # balance statistics of the routing, then the router
+                # backward: the gate (and the balance loss) to Wr and dx
                 if timed:
-                    rev.record(2 * i, stream)
+                    rev.record(3 * i, stream)
+                L.load_balance_stats(desc, bufs[j], rbufs[j])
+                if timed:
+                    rev.record(3 * i + 1, stream)
                 L.router_backward(desc, batches[j], bufs[j], gbufs[j],
-                                  rbufs[j])
+                                  rbufs[j], aux_coef=args.aux_coef)
                 if timed:
-                    rev.record(2 * i + 1, stream)
+                    rev.record(3 * i + 2, stream)
 
     log("bench: warmup")
     for i in range(args.warmup):
@@ -259,8 +267,10 @@ def main():
             for q, nm in enumerate(names):
                 bstage[nm] += bev.ms(o + q, o + q + 1) / args.steps
         if not cfg.synth_logits:
+            bstage["balance_stats"] = sum(
+                rev.ms(3 * i, 3 * i + 1) for i in range(args.steps)) / args.steps
             bstage["router_backward"] = sum(
-                rev.ms(2 * i, 2 * i + 1) for i in range(args.steps)) / args.steps
+                rev.ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)) / args.steps
 
     TK = cfg.TK
     b = 4 if cfg.dtype == "f32" else 2

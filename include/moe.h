@@ -258,7 +258,8 @@ moe_status moe_forward(const moe_desc* desc, const moe_fwd_args* args,
 moe_status moe_backward(const moe_desc* desc, const moe_bwd_args* args,
                         void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes of moe_router_backward (independent of its pointers). */
+/* Workspace bytes of moe_router_backward and of moe_load_balance_stats
+ * (independent of their pointers). */
 moe_status moe_router_workspace_size(const moe_desc* desc, size_t* bytes);
 
 /* Router backward: the gate-weight gradient d_topk_w [T, K] (from
@@ -270,20 +271,52 @@ moe_status moe_router_workspace_size(const moe_desc* desc, size_t* bytes);
  *   sigmoid: d_logits[t, e_k] = s_k (1 - s_k) / S (d_w_k - sum_j w_j d_w_j),
  *            s = sigmoid(logit), S = sum of the selected s (0 if S == 0);
  * with w = topk_w and logits the forward's fp32 logits [T, E] (the raw
- * logits: a route bias only moves the selection). Writes d_logits [T, E]
- * fp32 (zero off the selection) and d_w_router [E, d_model] = d_logits^T x
- * in the activation dtype, and ADDS d_logits * w_router [T, d_model] into
- * dx (in/out, activation dtype: e.g. moe_backward's dx, so that dx becomes
- * the whole layer's input gradient). x and w_router are as in the forward.
- * d_w_router is the sum of fixed token-range partial sums taken in a fixed
- * order: deterministic. MOE_EINVAL on a NULL pointer, MOE_EWORKSPACE if
+ * logits: a route bias only moves the selection).
+ * With aux_coef != 0 the loss also holds aux_coef times the balance loss
+ * of moe_load_balance_stats [P3 §6.2]; its gradient at fixed
+ * f = counts / T (counts [E] from the forward, required then, ignored
+ * otherwise) is added to every logit j of token t:
+ *   aux_coef (E / T) q_tj (f_j - sum_i f_i P_ti),
+ *   q = P (softmax), q_tj = s_tj (1 - s_tj) / sum_i s_ti (sigmoid),
+ * with P the full-row gate probabilities defined there.
+ * Writes d_logits [T, E] fp32 (zero off the selection when aux_coef == 0)
+ * and d_w_router [E, d_model] = d_logits^T x in the activation dtype, and
+ * ADDS d_logits * w_router [T, d_model] into dx (in/out, activation dtype:
+ * e.g. moe_backward's dx, so that dx becomes the whole layer's input
+ * gradient). x and w_router are as in the forward. d_w_router is the sum
+ * of fixed token-range partial sums taken in a fixed order:
+ * deterministic. MOE_EINVAL on a NULL pointer, a NaN aux_coef or a
+ * nonzero aux_coef without counts; MOE_EWORKSPACE if
  * ws_bytes < moe_router_workspace_size. */
 moe_status moe_router_backward(const moe_desc* desc, const void* x,
                                const void* w_router, const float* logits,
                                const int32_t* topk_idx, const float* topk_w,
-                               const float* d_topk_w, float* d_logits,
+                               const float* d_topk_w, const int32_t* counts,
+                               float aux_coef, float* d_logits,
                                void* d_w_router, void* dx, void* ws,
                                size_t ws_bytes, void* stream);
+
+/* Load-balance statistics of one routing [P3 §6.2, §9], from the
+ * forward's fp32 logits [T, E] and counts [E]:
+ *   f[e]      = counts[e] / T, the share of tokens whose top-K holds e
+ *               (sums to K; the layer's load statistic counts / (T K) is
+ *               f / K);
+ *   p_mean[e] = (1 / T) sum_t P[t, e], the mean gate probability, with
+ *               P[t, :] = softmax(logits[t, :]) over all E experts
+ *               (softmax gate) or sigmoid(logits[t, :]) divided by its sum
+ *               over all E (sigmoid gate, raw logits; 1/E each if every
+ *               sigmoid of the row is zero in fp32);
+ *   aux[0]    = E sum_e f[e] p_mean[e], the auxiliary balance loss before
+ *               its coefficient (E scales it to 1 for top-1 routing that
+ *               is balanced in load and probability).
+ * All fp32 outputs on the device. The token sums run over fixed token
+ * ranges in a fixed order: deterministic. Logits are assumed finite.
+ * T == 0 writes nothing. ws: at least moe_router_workspace_size bytes.
+ * MOE_EINVAL on a NULL pointer, MOE_EWORKSPACE if ws is too small. */
+moe_status moe_load_balance_stats(const moe_desc* desc, const float* logits,
+                                  const int32_t* counts, float* f,
+                                  float* p_mean, float* aux, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 /* MX quantisation of a bf16 [rows, cols] matrix along its rows (cols a
  * multiple of 32), per the OCP MX v1.0 rule: X = floor(log2(amax)) - 8

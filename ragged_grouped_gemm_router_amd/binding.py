@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import c_int32, c_int64, c_size_t, c_void_p, POINTER
+from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p, POINTER
 from typing import Optional
 
 import torch
@@ -29,7 +29,8 @@ MOE_FWD_NEVENTS, MOE_BWD_NEVENTS = 6, 8
 EXPORTED = ["moe_status_str", "moe_workspace_size", "moe_route",
             "moe_permute", "moe_grouped_gemm_swiglu", "moe_unpermute_combine",
             "moe_forward", "moe_backward", "moe_router_workspace_size",
-            "moe_router_backward", "moe_quantize_mxfp8"]
+            "moe_router_backward", "moe_load_balance_stats",
+            "moe_quantize_mxfp8"]
 
 
 class MoeError(RuntimeError):
@@ -104,8 +105,10 @@ def load() -> ctypes.CDLL:
         "moe_quantize_mxfp8": (c_int32, [c_void_p, c_int64, c_int64,
                                          c_void_p, c_void_p, c_void_p]),
         "moe_router_workspace_size": (c_int32, [D, POINTER(c_size_t)]),
-        "moe_router_backward": (c_int32, [D] + [c_void_p] * 10 +
-                                [c_size_t, c_void_p]),
+        "moe_router_backward": (c_int32, [D] + [c_void_p] * 7 + [c_float] +
+                                [c_void_p] * 4 + [c_size_t, c_void_p]),
+        "moe_load_balance_stats": (c_int32, [D] + [c_void_p] * 6 +
+                                   [c_size_t, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -224,13 +227,24 @@ def moe_router_workspace_size(desc: MoeDesc) -> int:
 
 
 def moe_router_backward(desc, x, w_router, logits, topk_idx, topk_w,
-                        d_topk_w, d_logits, d_w_router, dx, ws, stream=None):
+                        d_topk_w, counts, aux_coef, d_logits, d_w_router, dx,
+                        ws, stream=None):
     check(load().moe_router_backward(
         ctypes.byref(desc), ptr(x), ptr(w_router), ptr(logits), ptr(topk_idx),
-        ptr(topk_w), ptr(d_topk_w), ptr(d_logits), ptr(d_w_router), ptr(dx),
+        ptr(topk_w), ptr(d_topk_w), ptr(counts), float(aux_coef),
+        ptr(d_logits), ptr(d_w_router), ptr(dx),
         ptr(ws), ws.numel() * ws.element_size(),
         stream if stream is not None else current_stream()),
         "moe_router_backward")
+
+
+def moe_load_balance_stats(desc, logits, counts, f, p_mean, aux, ws,
+                           stream=None):
+    check(load().moe_load_balance_stats(
+        ctypes.byref(desc), ptr(logits), ptr(counts), ptr(f), ptr(p_mean),
+        ptr(aux), ptr(ws), ws.numel() * ws.element_size(),
+        stream if stream is not None else current_stream()),
+        "moe_load_balance_stats")
 
 
 def moe_quantize_mxfp8(src, rows, cols, q, scales, stream=None):

@@ -1,6 +1,7 @@
 // C ABI of the MoE layer: argument validation, workspace carving and the
 // launch sequence of each entry point. No allocation, no synchronisation,
 // no state kept between calls.
+#include <algorithm>
 #include <climits>
 #include <cstdlib>
 #include <cstring>
@@ -314,31 +315,50 @@ bool weights_ok(const moe_expert_weights* w) {
 // token-range partial sums of the router-weight gradient [G, E, d] fp32,
 // the G + 1 range bounds, and the router's share of dx [T, d].
 struct RouterWs {
-  void* dl_a;
-  float* part;
+  void* dl_a;    // d_logits in the activation dtype, [T, ld_dl], zero padded
+  float* part;   // [G, E, d_model] token-range partial sums of d Wr
   int32_t* split;
   void* dx_router;
-  int G;
+  float* bpart;  // balance statistics: [Gb, E] token-range partial sums
+  int G, Gb, ld_dl;
 };
 
-int router_splits(int T) {
-  const int G = T / 256;
-  return G < 1 ? 1 : (G > 64 ? 64 : G);
+// Token ranges of the router-weight gradient: enough (tile, range) pairs
+// to cover the CUs about four times, ranges of at least 256 tokens, and
+// at most half as many bytes of fp32 partial sums as the x they read.
+int router_splits(const moe_desc* d) {
+  const long T = d->T, E = d->E, dm = d->d_model;
+  const long tiles = ((E + 127) / 128) * ((dm + 127) / 128);
+  long G = 1024 / (tiles > 0 ? tiles : 1);
+  G = std::min(G, T / 256);
+  G = std::min(G, T / (4 * E));
+  return (int)std::max(1L, std::min(G, 64L));
+}
+
+// token ranges of the balance statistics: about 32 tokens each, so that
+// even a few thousand tokens spread over every CU
+int balance_splits(int T) {
+  const int G = (T + 31) / 32;
+  return G < 1 ? 1 : (G > 1024 ? 1024 : G);
 }
 
 size_t router_ws_layout(const moe_desc* d, char* base, RouterWs* w) {
   const size_t b = act_bytes(d->act_dtype), T = d->T, E = d->E,
                dm = d->d_model;
-  const int G = router_splits(d->T);
+  const int G = router_splits(d);
+  const size_t ld_dl = (E + 63) / 64 * 64;
   size_t o = 0;
-  if (w) { w->dl_a = base + o; w->G = G; }
-  o = align_up(o + b * T * E);
+  if (w) { w->dl_a = base + o; w->G = G; w->ld_dl = (int)ld_dl; }
+  o = align_up(o + b * T * ld_dl);
   if (w) w->part = (float*)(base + o);
   o = align_up(o + sizeof(float) * (size_t)G * E * dm);
   if (w) w->split = (int32_t*)(base + o);
   o = align_up(o + sizeof(int32_t) * (size_t)(G + 1));
   if (w) w->dx_router = base + o;
   o = align_up(o + b * T * dm);
+  const int Gb = balance_splits(d->T);
+  if (w) { w->bpart = (float*)(base + o); w->Gb = Gb; }
+  o = align_up(o + sizeof(float) * (size_t)Gb * E);
   return o;
 }
 
@@ -373,10 +393,27 @@ moe_status moe_router_workspace_size(const moe_desc* desc, size_t* bytes) {
   return MOE_OK;
 }
 
+moe_status moe_load_balance_stats(const moe_desc* d, const float* logits,
+                                  const int32_t* counts, float* f,
+                                  float* p_mean, float* aux, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;  // nothing is accessed
+  if (!logits || !counts || !f || !p_mean || !aux || !ws) return MOE_EINVAL;
+  if (ws_bytes < router_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
+  RouterWs w;
+  router_ws_layout(d, (char*)ws, &w);
+  return hip_status(launch_balance_stats(logits, counts, d->T, d->E, d->gate,
+                                         w.Gb, w.bpart, f, p_mean, aux,
+                                         (hipStream_t)stream));
+}
+
 moe_status moe_router_backward(const moe_desc* d, const void* x,
                                const void* w_router, const float* logits,
                                const int32_t* topk_idx, const float* topk_w,
-                               const float* d_topk_w, float* d_logits,
+                               const float* d_topk_w, const int32_t* counts,
+                               float aux_coef, float* d_logits,
                                void* d_w_router, void* dx, void* ws,
                                size_t ws_bytes, void* stream) {
   moe_status st = check_desc(d);
@@ -384,6 +421,8 @@ moe_status moe_router_backward(const moe_desc* d, const void* x,
   if (d->T == 0) return MOE_OK;  // nothing is accessed
   if (!x || !w_router || !logits || !topk_idx || !topk_w || !d_topk_w ||
       !d_logits || !d_w_router || !dx || !ws)
+    return MOE_EINVAL;
+  if (!(aux_coef == aux_coef) || (aux_coef != 0.0f && !counts))
     return MOE_EINVAL;
   if (ws_bytes < router_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
   RouterWs w;
@@ -396,24 +435,36 @@ moe_status moe_router_backward(const moe_desc* d, const void* x,
     e = (x);                               \
     if (e != hipSuccess) return MOE_EHIP;  \
   } while (0)
-  MOE_TRY(launch_router_grad(dt, logits, topk_idx, topk_w, d_topk_w, T, E,
-                             d->K, d->gate, d_logits, w.dl_a, w.G, w.split, s));
+  MOE_TRY(launch_router_grad(dt, logits, topk_idx, topk_w, d_topk_w,
+                             aux_coef != 0.0f ? counts : nullptr, aux_coef, T,
+                             E, d->K, d->gate, d_logits, w.dl_a, w.ld_dl, w.G,
+                             w.split, s));
+  // bf16 products on MFMA; fp32 (or shapes the tiles do not take) on SIMT
+  const bool mfma = dt == MOE_BF16 && !force_simt();
   {  // the router's share of dx: d_logits Wr, added to dx
     GemmParams p = gp();
     p.M = T; p.N = dm; p.K = E;
-    p.A = w.dl_a; p.lda = E;
+    p.A = w.dl_a; p.lda = w.ld_dl;
     p.B = w_router; p.ldb = dm;
-    p.C = w.dx_router; p.ldc = dm;
-    MOE_TRY(run_gemm(kOpRouterDx, dt, p, nullptr, s));
-    MOE_TRY(launch_add_inplace(dt, dx, w.dx_router, (long)T * dm, s));
+    p.C = dx; p.ldc = dm;
+    if (mfma && mfma_supported(kOpRouterDx, p)) {
+      MOE_TRY(gemm_mfma(kOpRouterDx, p, nullptr, s));  // accumulates into dx
+    } else {
+      p.C = w.dx_router;
+      MOE_TRY(run_gemm(kOpRouterDx, dt, p, nullptr, s));
+      MOE_TRY(launch_add_inplace(dt, dx, w.dx_router, (long)T * dm, s));
+    }
   }
   {  // d Wr = d_logits^T x: partial sums over G token ranges, then their sum
     GemmParams p = gp();
     p.M = E; p.N = dm; p.G = w.G; p.off = w.split;
-    p.A = w.dl_a; p.lda = E;
+    p.A = w.dl_a; p.lda = w.ld_dl;
     p.B = x; p.ldb = dm;
     p.C = w.part; p.ldc = dm; p.sC = (long)E * dm;
-    MOE_TRY(run_gemm(kOpRouterDw, dt, p, nullptr, s));
+    if (mfma && mfma_supported(kOpRouterDw, p))
+      MOE_TRY(gemm_mfma(kOpRouterDw, p, nullptr, s));
+    else
+      MOE_TRY(run_gemm(kOpRouterDw, dt, p, nullptr, s));
     MOE_TRY(launch_reduce_parts(dt, w.part, (long)E * dm, w.G, d_w_router, s));
   }
 #undef MOE_TRY

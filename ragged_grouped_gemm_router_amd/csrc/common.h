@@ -70,6 +70,8 @@ enum : int {
   kEpiSwigluBwd = 2,  // dh = acc; C = dh * b * silu'(a), C2 = dh * silu(a)
   kEpiSwigluMx = 3,   // h = silu(acc) * acc2 as MXFP8: C = E4M3 codes [M, N],
                       // C2 = E8M0 scales [M, N/32] (blocks along N)
+  kEpiStoreF32 = 4,   // C = acc in fp32 (partial sums)
+  kEpiAccum = 5,      // C = C + acc (read, add in fp32, one rounding)
 };
 
 struct GemmParams {

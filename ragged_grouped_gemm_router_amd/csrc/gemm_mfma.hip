@@ -1000,7 +1000,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
     __builtin_amdgcn_s_waitcnt(0);  // no load may still target LDS at exit
   }
   // through LDS: ROWS rows per pass (the stages are free now)
-  bf16* C = (bf16*)p.C + (SCHED == kSchedK ? (long)t.g * p.sC : 0);
+  const long c_off = SCHED == kSchedK ? (long)t.g * p.sC : 0;
+  bf16* C = (bf16*)p.C + c_off;
   auto value = [&](int i, int j, int r) { return acc[0][i][j][r]; };
   auto store = [&](int row, int col, const float* v) {
     const int grow = t.m0 + row, gcol = t.n0 + col;
@@ -1008,6 +1009,16 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
     const long o = (long)grow * p.ldc + gcol;
     if constexpr (EPI == kEpiStore) {
       *(bf16x8*)(C + o) = pack8(v);
+    } else if constexpr (EPI == kEpiStoreF32) {
+      float* Cf = (float*)p.C + c_off + o;
+      *(f32x4*)Cf = f32x4{v[0], v[1], v[2], v[3]};
+      *(f32x4*)(Cf + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    } else if constexpr (EPI == kEpiAccum) {
+      const bf16x8 c8 = *(const bf16x8*)(C + o);
+      float s[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s[q] = (float)c8[q] + v[q];
+      *(bf16x8*)(C + o) = pack8(s);
     } else {  // SwiGLU backward from dh = v and the saved a, b
       const bf16x8 a8 = *(const bf16x8*)((const bf16*)p.aux_a + o);
       const bf16x8 b8 = *(const bf16x8*)((const bf16*)p.aux_b + o);
@@ -1151,6 +1162,10 @@ bool mfma_supported(GemmOp op, const GemmParams& p) {
   if (op == kOpDgrad1 && p.K1 % 64) return false;
   if ((op == kOpDgrad2 || op == kOpDgrad1) && p.N % 8) return false;
   if (op == kOpWgrad && (p.M % 8 || p.N % 8)) return false;
+  // router backward: d_logits rows padded to whole k-tiles (row-major A
+  // of the dx product), 16-byte aligned k-rows and output pieces
+  if (op == kOpRouterDx && (p.lda % 64 || p.ldb % 8 || p.N % 8)) return false;
+  if (op == kOpRouterDw && (p.lda % 8 || p.ldb % 8 || p.N % 8)) return false;
   return true;
 }
 
@@ -1160,8 +1175,11 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   p.group_n = tile_group_n();
   // Big tiles when the average group has enough rows to fill them.
   bool big;
-  if (op == kOpWgrad) {
+  if (op == kOpWgrad || op == kOpRouterDw) {
     big = p.M >= 256 && p.N >= 256;
+  } else if (op == kOpRouterDx) {
+    big = false;
+    p.tiles_m_max = (p.M + 127) / 128;
   } else {
     const long rows_per_group = p.off ? (long)p.M / (p.G > 0 ? p.G : 1) : p.M;
     big = rows_per_group >= 192 && p.N >= 256;
@@ -1206,6 +1224,13 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
       return !big ? launch_t<128, 128, 2, 2, true, true, false, kEpiStore, kSchedK>(p, s)
              : w4 ? launch_t<256, 256, 2, 2, true, true, false, kEpiStore, kSchedK>(p, s)
                   : launch_t<256, 256, 2, 4, true, true, false, kEpiStore, kSchedK>(p, s);
+    // router backward: dx += d_logits Wr (Wr read k-major as stored), and
+    // fp32 partial sums of d_logits^T x over token ranges
+    if (op == kOpRouterDx)
+      return launch_t<128, 128, 2, 2, false, true, false, kEpiAccum, kSchedM>(p, s);
+    if (op == kOpRouterDw)
+      return !big ? launch_t<128, 128, 2, 2, true, true, false, kEpiStoreF32, kSchedK>(p, s)
+                  : launch_t<256, 256, 2, 4, true, true, false, kEpiStoreF32, kSchedK>(p, s);
   }
   if (op == kOpGemm1Mx)
     return launch_dl_sized<true, kEpiSwigluMx, bf16, true>(big, p, s);

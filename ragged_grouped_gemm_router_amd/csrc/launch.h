@@ -45,12 +45,20 @@ hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y,
                               hipStream_t s);
 
 // Router backward. d_logits [T,E] fp32 and the same in the activation
-// dtype (d_logits_a); split [G+1] token ranges for the partial sums.
+// dtype (d_logits_a, rows of ld_a elements, zero past E); split [G+1]
+// token ranges for the partial sums.
 hipError_t launch_router_grad(int dtype, const float* logits,
                               const int32_t* idx, const float* w,
-                              const float* d_w, int T, int E, int K, int gate,
-                              float* d_logits, void* d_logits_a, int G,
-                              int32_t* split, hipStream_t s);
+                              const float* d_w, const int32_t* counts,
+                              float aux_coef, int T, int E, int K, int gate,
+                              float* d_logits, void* d_logits_a, int ld_a,
+                              int G, int32_t* split, hipStream_t s);
+// Balance statistics: f = counts / T, p_mean = mean gate probability,
+// aux = E sum f p_mean, through G token-range partial sums in part [G, E].
+hipError_t launch_balance_stats(const float* logits, const int32_t* counts,
+                                int T, int E, int gate, int G, float* part,
+                                float* f, float* p_mean, float* aux,
+                                hipStream_t s);
 // split[g] = g * T / G for g = 0..G (G <= 1023).
 hipError_t launch_split(int T, int G, int32_t* split, hipStream_t s);
 // out[i] = sum_{g < G} part[g * n + i] (fixed order), in dtype.

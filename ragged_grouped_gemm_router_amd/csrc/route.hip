@@ -123,28 +123,80 @@ hipError_t launch_topk(const float* logits, const float* bias, int T, int E,
 namespace moe {
 namespace {
 
+__device__ __forceinline__ float sigmoidf(float l) {
+  return 1.0f / (1.0f + expf(-l));
+}
+
+// The gate's probability of every expert for one token, as the balance
+// statistics define it: softmax over all E logits (softmax gate) or the
+// sigmoids over their sum (sigmoid gate; 1/E each if every sigmoid is
+// zero). Each lane visits experts lane, lane + 64, ...; the wave-wide
+// max and sum leave the same value in every lane. Returns the
+// normaliser; the probability of expert e is then prob(row[e]).
+struct GateProbs {
+  int gate;
+  float m, z;
+  __device__ GateProbs(const float* row, int E, int gate_, int lane)
+      : gate(gate_), m(0.0f), z(0.0f) {
+    if (gate == MOE_GATE_SOFTMAX) {
+      float mx = -INFINITY;
+      for (int e = lane; e < E; e += kWave) mx = fmaxf(mx, row[e]);
+      m = wave_max(mx);
+      float zz = 0.0f;
+      for (int e = lane; e < E; e += kWave) zz += expf(row[e] - m);
+      z = wave_sum(zz);
+    } else {
+      float zz = 0.0f;
+      for (int e = lane; e < E; e += kWave) zz += sigmoidf(row[e]);
+      z = wave_sum(zz);
+    }
+  }
+  __device__ float num(float l) const {
+    return gate == MOE_GATE_SOFTMAX ? expf(l - m) : sigmoidf(l);
+  }
+  __device__ float prob(float l, int E) const {
+    return z > 0.0f ? num(l) / z : 1.0f / (float)E;
+  }
+};
+
 // Gate backward, one wavefront per token: d loss / d logits from
 // d loss / d topk_w. Lane e writes logit e (and e + 64, ...) once: the
 // selected ones get w_k (d_w_k - <w, d_w>) (softmax) or
 // s_k (1 - s_k) / S (d_w_k - <w, d_w>) with s = sigmoid(logit), S the sum
 // of the selected s (sigmoid; zero if S == 0, where the weights were 1/K);
-// the rest get zero. Also the same values in the activation dtype.
+// the rest get zero. With counts given, every logit j also gets
+// aux_coef (E / T) q_j (f_j - sum_i f_i P_i), the gradient of the balance
+// loss E sum_i f_i mean_t P_ti at fixed f = counts / T, where P is the
+// full-row gate probability and q_j = P_j (softmax) or
+// s_j (1 - s_j) / sum_i s_i (sigmoid). Also the same values in the
+// activation dtype, in rows of ld_a >= E elements whose tail is zero.
 template <typename TA>
 __global__ __launch_bounds__(256) void router_grad_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ idx,
-    const float* __restrict__ w, const float* __restrict__ d_w, int T, int E,
-    int K, int gate, float* __restrict__ d_logits, TA* __restrict__ d_logits_a) {
+    const float* __restrict__ w, const float* __restrict__ d_w,
+    const int32_t* __restrict__ counts, float aux_coef, int T, int E, int K,
+    int gate, float* __restrict__ d_logits, TA* __restrict__ d_logits_a,
+    int ld_a) {
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
   const long r = (long)t * K;
+  const float* row = logits + (long)t * E;
   float inner = 0.0f, S = 0.0f;
   for (int k = 0; k < K; ++k) {
     inner = fmaf(w[r + k], d_w[r + k], inner);
-    if (gate == MOE_GATE_SIGMOID) {
-      const float l = logits[(long)t * E + idx[r + k]];
-      S += 1.0f / (1.0f + expf(-l));
-    }
+    if (gate == MOE_GATE_SIGMOID) S += sigmoidf(row[idx[r + k]]);
+  }
+  const bool aux = counts != nullptr;
+  const float invT = 1.0f / (float)T;
+  float aux_scale = 0.0f, aux_inner = 0.0f;
+  GateProbs gp(row, aux ? E : 0, gate, lane);
+  if (aux) {
+    aux_scale = aux_coef * (float)E * invT;
+    float in = 0.0f;
+    for (int e = lane; e < E; e += kWave)
+      in += ((float)counts[e] * invT) * gp.prob(row[e], E);
+    aux_inner = wave_sum(in);
   }
   for (int e = lane; e < E; e += kWave) {
     float g = 0.0f;
@@ -154,13 +206,99 @@ __global__ __launch_bounds__(256) void router_grad_kernel(
       if (gate == MOE_GATE_SOFTMAX) {
         g = w[r + k] * dd;
       } else if (S > 0.0f) {
-        const float s = 1.0f / (1.0f + expf(-logits[(long)t * E + e]));
+        const float s = sigmoidf(row[e]);
         g = s * (1.0f - s) / S * dd;
       }
     }
+    if (aux && gp.z > 0.0f) {
+      float q;
+      if (gate == MOE_GATE_SOFTMAX) {
+        q = gp.prob(row[e], E);
+      } else {
+        const float s = sigmoidf(row[e]);
+        q = s * (1.0f - s) / gp.z;
+      }
+      g += aux_scale * q * ((float)counts[e] * invT - aux_inner);
+    }
     d_logits[(long)t * E + e] = g;
-    d_logits_a[(long)t * E + e] = (TA)g;
+    d_logits_a[(long)t * ld_a + e] = (TA)g;
   }
+  for (int e = E + lane; e < ld_a; e += kWave)
+    d_logits_a[(long)t * ld_a + e] = (TA)0.0f;
+}
+
+// Balance statistics, pass 1: block g adds up the gate probabilities of
+// tokens [g T / G, (g + 1) T / G) per expert into part[g E + e]. Wave v
+// takes every fourth token of the range in order, each lane keeping the
+// running sums of its experts; the four waves' sums are then added in
+// wave order, so the result does not depend on scheduling.
+template <int CPL>
+__global__ __launch_bounds__(256) void balance_part_kernel(
+    const float* __restrict__ logits, int T, int E, int G, int gate,
+    float* __restrict__ part) {
+  __shared__ float wsum[4][MOE_E_MAX];
+  const int lane = threadIdx.x % kWave, v = threadIdx.x / kWave;
+  const int g = blockIdx.x;
+  const long t0 = (long)g * T / G, t1 = (long)(g + 1) * T / G;
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.0f;
+  for (long t = t0 + v; t < t1; t += 4) {
+    const float* row = logits + t * E;
+    const GateProbs gp(row, E, gate, lane);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int e = lane + kWave * c;
+      if (e < E) acc[c] += gp.prob(row[e], E);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int e = lane + kWave * c;
+    if (e < E) wsum[v][e] = acc[c];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256)
+    part[(long)g * E + e] = ((wsum[0][e] + wsum[1][e]) + wsum[2][e]) + wsum[3][e];
+}
+
+// Balance statistics, pass 2 (one block of 1024 threads): thread
+// (slice q, expert e) adds part[g E + e] for g = q, q + Q, ... with Q =
+// 1024 / Ep slices (Ep = E rounded up to a power of two); the Q slice sums
+// are then added in slice order. p_mean[e] = that sum / T,
+// f[e] = counts[e] / T and aux = E sum_e f[e] p_mean[e], the products
+// summed by a fixed tree, so the result does not depend on scheduling.
+__global__ __launch_bounds__(1024) void balance_finish_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ counts, int T,
+    int E, int Ep, int G, float* __restrict__ f, float* __restrict__ p_mean,
+    float* __restrict__ aux) {
+  __shared__ float red[1024];
+  const int tid = threadIdx.x, Q = 1024 / Ep;
+  {
+    const int e = tid % Ep, q = tid / Ep;
+    float s = 0.0f;
+    if (e < E)
+      for (int g = q; g < G; g += Q) s += part[(long)g * E + e];
+    red[tid] = s;
+  }
+  __syncthreads();
+  float prod = 0.0f;
+  if (tid < E) {
+    float s = 0.0f;
+    for (int q = 0; q < Q; ++q) s += red[q * Ep + tid];
+    const float P = s / (float)T, fe = (float)counts[tid] / (float)T;
+    p_mean[tid] = P;
+    f[tid] = fe;
+    prod = fe * P;
+  }
+  __syncthreads();
+  red[tid] = prod;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  if (tid == 0) aux[0] = (float)E * red[0];
 }
 
 // out[i] = sum_g part[g * n + i] in g order (fixed, so deterministic)
@@ -195,17 +333,43 @@ __global__ void split_kernel(int T, int G, int32_t* __restrict__ split) {
 
 hipError_t launch_router_grad(int dtype, const float* logits,
                               const int32_t* idx, const float* w,
-                              const float* d_w, int T, int E, int K, int gate,
-                              float* d_logits, void* d_logits_a, int G,
-                              int32_t* split, hipStream_t s) {
+                              const float* d_w, const int32_t* counts,
+                              float aux_coef, int T, int E, int K, int gate,
+                              float* d_logits, void* d_logits_a, int ld_a,
+                              int G, int32_t* split, hipStream_t s) {
   const dim3 grid((T + 3) / 4), block(256);
   if (dtype == MOE_F32)
     hipLaunchKernelGGL(router_grad_kernel<float>, grid, block, 0, s, logits,
-                       idx, w, d_w, T, E, K, gate, d_logits, (float*)d_logits_a);
+                       idx, w, d_w, counts, aux_coef, T, E, K, gate, d_logits,
+                       (float*)d_logits_a, ld_a);
   else
     hipLaunchKernelGGL(router_grad_kernel<bf16>, grid, block, 0, s, logits, idx,
-                       w, d_w, T, E, K, gate, d_logits, (bf16*)d_logits_a);
+                       w, d_w, counts, aux_coef, T, E, K, gate, d_logits,
+                       (bf16*)d_logits_a, ld_a);
   hipLaunchKernelGGL(split_kernel, dim3(1), dim3(1024), 0, s, T, G, split);
+  return hipGetLastError();
+}
+
+hipError_t launch_balance_stats(const float* logits, const int32_t* counts,
+                                int T, int E, int gate, int G, float* part,
+                                float* f, float* p_mean, float* aux,
+                                hipStream_t s) {
+  const int cpl = (E + kWave - 1) / kWave;
+  const dim3 grid(G), block(256);
+  if (cpl <= 1)
+    hipLaunchKernelGGL(balance_part_kernel<1>, grid, block, 0, s, logits, T, E, G, gate, part);
+  else if (cpl <= 2)
+    hipLaunchKernelGGL(balance_part_kernel<2>, grid, block, 0, s, logits, T, E, G, gate, part);
+  else if (cpl <= 4)
+    hipLaunchKernelGGL(balance_part_kernel<4>, grid, block, 0, s, logits, T, E, G, gate, part);
+  else if (cpl <= 8)
+    hipLaunchKernelGGL(balance_part_kernel<8>, grid, block, 0, s, logits, T, E, G, gate, part);
+  else
+    hipLaunchKernelGGL(balance_part_kernel<16>, grid, block, 0, s, logits, T, E, G, gate, part);
+  int Ep = 1;
+  while (Ep < E) Ep *= 2;
+  hipLaunchKernelGGL(balance_finish_kernel, dim3(1), dim3(1024), 0, s, part,
+                     counts, T, E, Ep, G, f, p_mean, aux);
   return hipGetLastError();
 }
 

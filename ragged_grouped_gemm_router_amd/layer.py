@@ -169,17 +169,31 @@ def alloc_router_backward(desc: B.MoeDesc, device="cuda") -> dict:
         "d_w_router": torch.empty(E, d, dtype=dt, device=device),
         "ws": torch.empty(max(B.moe_router_workspace_size(desc), 1),
                           dtype=torch.uint8, device=device),
+        "f": torch.empty(E, dtype=torch.float32, device=device),
+        "p_mean": torch.empty(E, dtype=torch.float32, device=device),
+        "aux": torch.empty(1, dtype=torch.float32, device=device),
     }
 
 
+def load_balance_stats(desc: B.MoeDesc, fbufs: dict, rbufs: dict,
+                       stream=None) -> dict:
+    """After forward(): the balance statistics of its routing into
+    rbufs["f"], rbufs["p_mean"] and rbufs["aux"]."""
+    B.moe_load_balance_stats(desc, fbufs["logits"], fbufs["counts"],
+                             rbufs["f"], rbufs["p_mean"], rbufs["aux"],
+                             rbufs["ws"], stream)
+    return rbufs
+
+
 def router_backward(desc: B.MoeDesc, inp: dict, fbufs: dict, gbufs: dict,
-                    rbufs: dict, stream=None) -> dict:
-    """After backward(): carries gbufs["d_topk_w"] through the gate into
-    rbufs["d_logits"] and rbufs["d_w_router"], and adds the router's share
-    of the input gradient into gbufs["dx"]."""
+                    rbufs: dict, aux_coef: float = 0.0, stream=None) -> dict:
+    """After backward(): carries gbufs["d_topk_w"] (and, with aux_coef,
+    the balance loss) through the gate into rbufs["d_logits"] and
+    rbufs["d_w_router"], and adds the router's share of the input
+    gradient into gbufs["dx"]."""
     B.moe_router_backward(desc, inp["x"], inp["wr"], fbufs["logits"],
                           fbufs["topk_idx"], fbufs["topk_w"],
-                          gbufs["d_topk_w"], rbufs["d_logits"],
-                          rbufs["d_w_router"], gbufs["dx"], rbufs["ws"],
-                          stream)
+                          gbufs["d_topk_w"], fbufs["counts"], aux_coef,
+                          rbufs["d_logits"], rbufs["d_w_router"], gbufs["dx"],
+                          rbufs["ws"], stream)
     return rbufs

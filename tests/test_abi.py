@@ -147,14 +147,40 @@ def test_router_backward_validation():
     n = ctypes.c_size_t(0)
     assert lib.moe_router_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_OK
     assert n.value >= 64 * 128 * 2  # the router's share of dx
-    args = [fake] * 9
-    # a missing d_topk_w
-    bad = list(args)
-    bad[5] = None
-    assert lib.moe_router_backward(ctypes.byref(d), *bad, fake, n.value,
-                                   None) == B.MOE_EINVAL
-    assert lib.moe_router_backward(ctypes.byref(d), *args, fake, 16,
-                                   None) == B.MOE_EWORKSPACE
+
+    def call(desc, ws_bytes=n.value, aux_coef=0.0, **null):
+        names = ["x", "w_router", "logits", "topk_idx", "topk_w", "d_topk_w",
+                 "counts"]
+        head = [None if k in null else fake for k in names]
+        tail = [None if k in null else fake
+                for k in ("d_logits", "d_w_router", "dx", "ws")]
+        return lib.moe_router_backward(ctypes.byref(desc), *head, aux_coef,
+                                       *tail, ws_bytes, None)
+
+    assert call(d, d_topk_w=1) == B.MOE_EINVAL
+    assert call(d, ws_bytes=16) == B.MOE_EWORKSPACE
+    # counts may be NULL only without the balance loss
+    assert call(d, aux_coef=0.01, counts=1) == B.MOE_EINVAL
+    assert call(d, aux_coef=float("nan")) == B.MOE_EINVAL
     z = B.make_desc(0, 128, 256, 8, 2)
-    assert lib.moe_router_backward(ctypes.byref(z), *([None] * 9), None, 0,
-                                   None) == B.MOE_OK
+    assert lib.moe_router_backward(ctypes.byref(z), *([None] * 7), 0.0,
+                                   *([None] * 4), 0, None) == B.MOE_OK
+
+
+def test_balance_stats_validation():
+    lib = B.load()
+    d = B.make_desc(64, 128, 256, 8, 2)
+    fake = 0x1000
+    n = ctypes.c_size_t(0)
+    assert lib.moe_router_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_OK
+    ok = [fake] * 6
+    for i in range(6):
+        bad = list(ok)
+        bad[i] = None
+        assert lib.moe_load_balance_stats(ctypes.byref(d), *bad, n.value,
+                                          None) == B.MOE_EINVAL
+    assert lib.moe_load_balance_stats(ctypes.byref(d), *ok, 16,
+                                      None) == B.MOE_EWORKSPACE
+    z = B.make_desc(0, 128, 256, 8, 2)
+    assert lib.moe_load_balance_stats(ctypes.byref(z), *([None] * 6), 0,
+                                      None) == B.MOE_OK

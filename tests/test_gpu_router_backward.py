@@ -85,3 +85,80 @@ def test_router_backward_full_size_mixtral():
     toks = torch.tensor([0, 1, 4095, cfg.T - 1])
     ref_dx = dl[toks] @ ginp["wr"].cpu().double()
     assert rel_err(gb["dx"][toks.to(DEV)], ref_dx) <= tol(cfg)
+
+
+# ------------------------------------------------ load-balance statistics
+
+def _stats_ref(logits, counts, idx, E, gate):
+    ref = oracle.load_balance_stats(logits, idx, E, gate)
+    # the oracle's share comes from the mask; counts must describe the same
+    assert torch.equal(torch.bincount(idx.reshape(-1), minlength=E),
+                       counts.long())
+    return ref
+
+
+def _check_stats(rb, ref):
+    # f = counts / T: one correctly rounded fp32 division of exact integers
+    assert torch.equal(rb["f"].cpu(), ref["f"].to(torch.float32))
+    assert rel_err(rb["p_mean"], ref["p_mean"]) <= 1e-5
+    assert abs(float(rb["aux"].cpu()[0]) - float(ref["aux"])) <= \
+        1e-5 * abs(float(ref["aux"]))
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
+def test_balance_stats_parity(cfg):
+    cinp, ginp = inputs(cfg, 8)
+    desc, fb = run_forward(cfg, ginp)
+    rb = L.alloc_router_backward(desc, DEV)
+    L.load_balance_stats(desc, fb, rb)
+    torch.cuda.synchronize()
+    idx = fb["topk_idx"].cpu().long()
+    ref = _stats_ref(fb["logits"].cpu(), fb["counts"].cpu(), idx, cfg.E,
+                     cfg.gate)
+    _check_stats(rb, ref)
+
+
+@pytest.mark.parametrize("T,E,K,gate", [(8192, 8, 2, "softmax"),
+                                        (4096, 256, 8, "sigmoid"),
+                                        (16384, 128, 8, "softmax"),
+                                        (3, 1024, 16, "sigmoid")])
+def test_balance_stats_full_size(T, E, K, gate):
+    """The statistics at the Mixtral-, DeepSeek-V3- and skewed-shaped
+    routing sizes (and the widest E with fewer tokens than waves), from
+    seeded logits with their own selection and counts."""
+    g = torch.Generator().manual_seed(T + E)
+    logits = 1.5 * torch.randn(T, E, generator=g)
+    idx = oracle.topk_select(oracle.selection_keys(logits), K)
+    counts = torch.bincount(idx.reshape(-1), minlength=E).to(torch.int32)
+    desc = L.B.make_desc(T, 256, 256, E, K, gate=gate)
+    rb = L.alloc_router_backward(desc, DEV)
+    fb = {"logits": logits.to(DEV), "counts": counts.to(DEV)}
+    L.load_balance_stats(desc, fb, rb)
+    torch.cuda.synchronize()
+    _check_stats(rb, _stats_ref(logits, counts, idx, E, gate))
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
+def test_aux_loss_backward_parity(cfg):
+    """With d_topk_w = 0 the logit gradient is the balance loss's alone
+    (its scale, coef * E / T, is far below the gate term, so it is checked
+    on its own); then both terms together."""
+    cinp, ginp = inputs(cfg, 9)
+    desc, fb = run_forward(cfg, ginp)
+    logits = fb["logits"].cpu()
+    idx = fb["topk_idx"].cpu().long()
+    w = fb["topk_w"].cpu()
+    for coef, dw_scale in ((1.0, 0.0), (0.05, 1.0)):
+        g = torch.Generator().manual_seed(10)
+        d_w = torch.randn(cfg.T, cfg.K, generator=g) * dw_scale
+        gb = {"d_topk_w": d_w.to(DEV),
+              "dx": torch.zeros(cfg.T, cfg.d, dtype=cfg.torch_dtype,
+                                device=DEV)}
+        rb = L.alloc_router_backward(desc, DEV)
+        L.router_backward(desc, ginp, fb, gb, rb, aux_coef=coef)
+        torch.cuda.synchronize()
+        ref = oracle.router_backward(cinp["x"], cinp["wr"], logits, idx, w,
+                                     d_w, cfg.gate, aux_coef=coef)
+        assert rel_err(rb["d_logits"], ref["d_logits"]) <= 1e-4
+        assert rel_err(rb["d_w_router"], ref["d_wr"]) <= tol(cfg)
+        assert rel_err(gb["dx"], ref["dx"]) <= tol(cfg)
