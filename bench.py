@@ -143,6 +143,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time a training step: forward (activations saved) "
                          "plus backward; FLOPs counted as 3x the forward")
+    ap.add_argument("--gather", action="store_true",
+                    help="forward only: leave x_perm out, GEMM 1 gathers its "
+                         "rows from x through sorted_src")
     ap.add_argument("--aux-coef", type=float, default=0.01,
                     help="coefficient of the balance loss in the training "
                          "step's router backward")
@@ -158,6 +161,8 @@ def main():
               "is not supported (the layer does not shard across GPUs here)",
               file=sys.stderr)
         sys.exit(2)
+    if args.gather and args.backward:
+        ap.error("--gather is forward only: the backward reads x_perm")
 
     import torch
     import moe_inputs as mi
@@ -195,7 +200,7 @@ def main():
         for b in batches:
             b["mx"] = mx
         torch.cuda.synchronize()
-    bufs = [L.alloc_forward(desc, dev) for _ in batches]
+    bufs = [L.alloc_forward(desc, dev, gather=args.gather) for _ in batches]
     n_steps = args.warmup + args.steps
     ev = HipEvents(B.MOE_FWD_NEVENTS * max(args.steps, 1))
     stream = torch.cuda.current_stream()
@@ -279,7 +284,11 @@ def main():
     step_flops = acc.train_flops(routed) if args.backward else routed
     value = step_flops / (ms_step * 1e-3) / 1e12
     gemm_s = (stage["gemm1_swiglu"] + stage["gemm2_shared"]) * 1e-3
-    perm_bytes = acc.permute_bytes(cfg.T, cfg.K, cfg.d, b)
+    if args.gather:  # indices only (and, under MXFP8, x quantised once)
+        perm_bytes = acc.permute_index_bytes(cfg.T, cfg.K) + (
+            acc.quantize_bytes(cfg.T * cfg.d) if args.mxfp8 else 0)
+    else:
+        perm_bytes = acc.permute_bytes(cfg.T, cfg.K, cfg.d, b)
     comb_bytes = acc.combine_bytes(cfg.T, cfg.K, cfg.d, b, cfg.f_shared > 0)
     k5_s = stage["gemm1_swiglu"] * 1e-3
     k5_tflops = g1 / k5_s / 1e12
@@ -321,6 +330,8 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d,
                    "d_ff": cfg.f, "E": cfg.E, "K": cfg.K,
                    "d_ff_shared": cfg.f_shared, "gate": cfg.gate,
+                   "x_perm": "gathered in GEMM 1" if args.gather else
+                             "materialised",
                    "parallelism": "single GPU"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "grouped_gemm_tflops": round(routed / gemm_s / 1e12, 2),
@@ -334,7 +345,8 @@ def main():
             **k5_roof,
             "algorithmic_bytes": int(g1_bytes),
             "algorithmic_flops": g1,
-            "traffic": gemm1_traffic(cfg, args.mxfp8),
+            "traffic": (None if args.gather
+                        else gemm1_traffic(cfg, args.mxfp8)),
         },
     }
     if not args.no_cpu_baseline:

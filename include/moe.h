@@ -128,8 +128,16 @@ typedef struct moe_fwd_args {
   int32_t* sorted_src;        /* [T*K] copy j = t*K+k at each sorted slot    */
   int32_t* dest;              /* [T*K] sorted slot of each copy j            */
   /* activations */
-  void* x_perm;               /* [T*K, d_model] act (MXFP8: E4M3 bytes)      */
-  uint8_t* x_perm_scales;     /* MXFP8 only: [T*K, d_model/32] E8M0          */
+  void* x_perm;               /* [T*K, d_model] act (MXFP8: E4M3 bytes), or
+                                 NULL: then GEMM 1 reads row p straight from
+                                 x[sorted_src[p] / K] (MXFP8: from x
+                                 quantised once in the workspace) and the
+                                 permute writes only the indices. NULL
+                                 needs bf16 act, d_model % 64 == 0 and
+                                 T * d_model * 2 < 2^31, else
+                                 MOE_EUNSUPPORTED. moe_backward still needs
+                                 a materialised x_perm.                     */
+  uint8_t* x_perm_scales;     /* MXFP8 with x_perm: [T*K, d_model/32] E8M0   */
   void* h;                    /* [T*K, d_ff] act. MXFP8: E4M3 codes [T*K,
                                  d_ff] then E8M0 scales [T*K, d_ff/32]
                                  (fits in a bf16-sized buffer)              */

@@ -55,6 +55,18 @@ def permute_bytes(T: int, K: int, d: int, b: int) -> int:
     return T * d * b + T * K * d * b + 12 * T * K
 
 
+def permute_index_bytes(T: int, K: int) -> int:
+    """The permute when GEMM 1 gathers its rows: read topk_idx, write
+    sorted_src and dest (three int32 per copy), no rows."""
+    return 12 * T * K
+
+
+def quantize_bytes(n: int) -> float:
+    """MX quantisation of n bf16 elements: read 2n, write n codes and n/32
+    scales."""
+    return 2 * n + n + n / 32
+
+
 def combine_bytes(T: int, K: int, d: int, b: int, shared: bool) -> int:
     """Read T*K rows of y_perm, (read y_shared,) write out; read dest and
     topk_w (int32 + fp32 per copy)."""

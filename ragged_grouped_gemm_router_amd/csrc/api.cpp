@@ -51,8 +51,8 @@ moe_status check_desc(const moe_desc* d) {
 struct FwdWs {
   int32_t* block_hist;
   int32_t* rank;
-  uint8_t* xq;  // MXFP8 with a shared expert: x quantised, codes [T, d]
-  uint8_t* xs;  // and E8M0 scales [T, d/32]
+  uint8_t* xq;  // MXFP8: x quantised once (shared expert, gathered GEMM 1):
+  uint8_t* xs;  // codes [T, d] and E8M0 scales [T, d/32]
   int32_t* tile_off[kNumTileBM];
   void* h_shared;
 };
@@ -85,7 +85,7 @@ size_t fwd_ws_layout(const moe_desc* d, char* base, FwdWs* w) {
   }
   if (w) w->h_shared = base + o;
   o = align_up(o + act_bytes(d->act_dtype) * (size_t)d->T * d->d_ff_shared);
-  if (d->gemm_dtype == MOE_MXFP8 && d->d_ff_shared > 0) {
+  if (d->gemm_dtype == MOE_MXFP8) {
     const size_t n = (size_t)d->T * d->d_model;
     if (w) w->xq = (uint8_t*)(base + o);
     o = align_up(o + n);
@@ -181,6 +181,8 @@ hipError_t do_route(const moe_desc* d, const void* x, const void* wr,
   return launch_topk(L, bias, d->T, d->E, d->K, d->gate, idx, w, s);
 }
 
+// x_perm == NULL: only the indices (the expert GEMM gathers its rows from
+// x; under MXFP8 x is quantised once into the workspace for it).
 hipError_t do_permute(const moe_desc* d, const void* x, const int32_t* idx,
                       int32_t* counts, int32_t* offsets, int32_t* src,
                       int32_t* dest, void* x_perm, uint8_t* x_perm_scales,
@@ -189,6 +191,11 @@ hipError_t do_permute(const moe_desc* d, const void* x, const int32_t* idx,
   hipError_t e = launch_hist_rank_scan(idx, TK, d->E, ws.block_hist, ws.rank,
                                        counts, offsets, ws.tile_off, s);
   if (e != hipSuccess) return e;
+  if (!x_perm) {
+    e = launch_slots(idx, ws.block_hist, ws.rank, TK, d->E, dest, src, s);
+    if (e != hipSuccess || d->gemm_dtype != MOE_MXFP8) return e;
+    return launch_quantize_mxfp8(x, d->T, d->d_model, ws.xq, ws.xs, s);
+  }
   if (d->gemm_dtype == MOE_MXFP8) {
     e = launch_slots(idx, ws.block_hist, ws.rank, TK, d->E, dest, src, s);
     if (e != hipSuccess) return e;
@@ -203,10 +210,11 @@ hipError_t do_permute(const moe_desc* d, const void* x, const int32_t* idx,
 hipError_t do_gemm1(const moe_desc* d, const void* A, const int32_t* off,
                     int rows, int G, const void* w1, const void* w3, int f,
                     void* h, void* a_out, void* b_out, int32_t* const* toff,
-                    hipStream_t s) {
+                    hipStream_t s, const int32_t* gsrc = nullptr) {
   GemmParams p = gp();
   p.M = rows; p.N = f; p.K = d->d_model; p.G = G; p.off = off;
   p.A = A; p.lda = d->d_model;
+  p.gsrc = gsrc; p.gdiv = d->K;
   p.B = w1; p.B2 = w3; p.ldb = d->d_model; p.sB = (long)f * d->d_model;
   p.C = h; p.C2 = a_out; p.C3 = b_out; p.ldc = f;
   return run_gemm(kOpGemm1, d->act_dtype, p, toff, s);
@@ -227,18 +235,22 @@ hipError_t do_gemm2(const moe_desc* d, const void* h, const int32_t* off,
 // [T*K, d_ff] followed by E8M0 scales [T*K, d_ff/32].
 // With a shared expert, x is quantised into the workspace and the shared
 // GEMMs run as one dense group, h_shared holding codes then scales.
+// gsrc != NULL: x_perm was not written; GEMM 1 gathers the rows of the
+// quantised x in the workspace through gsrc (sorted_src).
 hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
                          const uint8_t* x_perm_scales, const int32_t* offsets,
                          const moe_expert_weights* rw, const void* x_shared,
                          const moe_expert_weights* sw, void* h, void* y_perm,
                          void* y_shared, const FwdWs& ws, hipStream_t s,
-                         void* ev_mid) {
+                         void* ev_mid, const int32_t* gsrc = nullptr) {
   const int TK = d->T * d->K, dm = d->d_model, f = d->d_ff;
   uint8_t* hq = (uint8_t*)h;
   uint8_t* hs = hq + (size_t)TK * f;
   GemmParams p = gp();
   p.M = TK; p.N = f; p.K = dm; p.G = d->E; p.off = offsets;
-  p.A = x_perm; p.lda = dm; p.As = x_perm_scales;
+  p.A = gsrc ? ws.xq : x_perm; p.lda = dm;
+  p.As = gsrc ? ws.xs : x_perm_scales;
+  p.gsrc = gsrc; p.gdiv = d->K;
   p.B = rw->w1; p.B2 = rw->w3; p.ldb = dm; p.sB = (long)f * dm;
   p.Bs = rw->w1_scales; p.B2s = rw->w3_scales;
   p.ld_s = dm / 32; p.sBs = (long)f * (dm / 32);
@@ -255,8 +267,10 @@ hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
   e = gemm_mfma(kOpGemm2Mx, p, ws.tile_off, s);
   if (e != hipSuccess || !x_shared || d->d_ff_shared == 0) return e;
   const int T = d->T, fs = d->d_ff_shared;
-  e = launch_quantize_mxfp8(x_shared, T, dm, ws.xq, ws.xs, s);
-  if (e != hipSuccess) return e;
+  if (!gsrc) {  // (with gathered rows x is quantised already)
+    e = launch_quantize_mxfp8(x_shared, T, dm, ws.xq, ws.xs, s);
+    if (e != hipSuccess) return e;
+  }
   uint8_t* sq = (uint8_t*)ws.h_shared;
   uint8_t* ss = sq + (size_t)T * fs;
   p = gp();
@@ -281,15 +295,17 @@ bool mx_weights_ok(const moe_expert_weights* w) {
          w->w2_scales;
 }
 
+// gsrc != NULL: x_perm is x itself and GEMM 1 gathers its rows through
+// gsrc (sorted_src).
 hipError_t do_experts(const moe_desc* d, const void* x_perm,
                       const int32_t* offsets, const moe_expert_weights* rw,
                       const void* x_shared, const moe_expert_weights* sw,
                       void* h, void* y_perm, void* y_shared, void* act_a,
                       void* act_b, const FwdWs& ws, hipStream_t s,
-                      void* ev_mid) {
+                      void* ev_mid, const int32_t* gsrc = nullptr) {
   const int TK = d->T * d->K;
   hipError_t e = do_gemm1(d, x_perm, offsets, TK, d->E, rw->w1, rw->w3,
-                          d->d_ff, h, act_a, act_b, ws.tile_off, s);
+                          d->d_ff, h, act_a, act_b, ws.tile_off, s, gsrc);
   if (e != hipSuccess) return e;
   record(ev_mid, s);
   e = do_gemm2(d, h, offsets, TK, d->E, rw->w2, d->d_ff, y_perm, ws.tile_off, s);
@@ -564,14 +580,21 @@ moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
   if (!a || !ws || !a->x || !a->out || !weights_ok(&a->routed)) return MOE_EINVAL;
   if (!a->logits_in && (!a->w_router || !a->logits)) return MOE_EINVAL;
   if (!a->topk_idx || !a->topk_w || !a->counts || !a->offsets ||
-      !a->sorted_src || !a->dest || !a->x_perm || !a->h || !a->y_perm)
+      !a->sorted_src || !a->dest || !a->h || !a->y_perm)
     return MOE_EINVAL;
+  // no x_perm: GEMM 1 gathers its rows from x (direct-to-LDS kernel only)
+  const bool gather = a->x_perm == nullptr;
+  if (gather && (d->act_dtype != MOE_BF16 || force_simt() ||
+                 !gemm1_gather_supported(d->d_model) ||
+                 (long)d->T * d->d_model * 2 >= (1L << 31)))
+    return MOE_EUNSUPPORTED;
   const bool shared = d->d_ff_shared > 0;
   if (shared && (!weights_ok(&a->shared) || !a->y_shared)) return MOE_EINVAL;
   const bool save = d->flags & MOE_FLAG_SAVE_ACTS;
   if (save && (!a->act_a || !a->act_b)) return MOE_EINVAL;
   const bool mx = d->gemm_dtype == MOE_MXFP8;
-  if (mx && (!a->x_perm_scales || !mx_weights_ok(&a->routed))) return MOE_EINVAL;
+  if (mx && ((!gather && !a->x_perm_scales) || !mx_weights_ok(&a->routed)))
+    return MOE_EINVAL;
   if (mx && shared && !mx_weights_ok(&a->shared)) return MOE_EINVAL;
   if (ws_bytes < fwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
   FwdWs w;
@@ -586,15 +609,16 @@ moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
                  a->dest, a->x_perm, a->x_perm_scales, w, s);
   if (e != hipSuccess) return MOE_EHIP;
   record(a->events[2], s);
+  const int32_t* gsrc = gather ? a->sorted_src : nullptr;
   if (mx)
     e = do_experts_mx(d, a->x_perm, a->x_perm_scales, a->offsets, &a->routed,
                       shared ? a->x : nullptr, &a->shared, a->h, a->y_perm,
-                      a->y_shared, w, s, a->events[3]);
+                      a->y_shared, w, s, a->events[3], gsrc);
   else
-    e = do_experts(d, a->x_perm, a->offsets, &a->routed,
+    e = do_experts(d, gather ? a->x : a->x_perm, a->offsets, &a->routed,
                    shared ? a->x : nullptr, &a->shared, a->h, a->y_perm,
                    a->y_shared, save ? a->act_a : nullptr,
-                   save ? a->act_b : nullptr, w, s, a->events[3]);
+                   save ? a->act_b : nullptr, w, s, a->events[3], gsrc);
   if (e != hipSuccess) return MOE_EHIP;
   record(a->events[4], s);
   e = launch_combine(d->act_dtype, a->y_perm, a->dest, a->topk_w,

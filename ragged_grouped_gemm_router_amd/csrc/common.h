@@ -88,6 +88,9 @@ struct GemmParams {
   // bytes (= K/32); B scales have group stride sBs bytes.
   const uint8_t* As; const uint8_t* Bs; const uint8_t* B2s;
   long ld_s; long sBs;
+  // gathered A rows (direct-to-LDS GEMM 1 only): row i of A (and of As)
+  // is row gsrc[i] / gdiv of the A given, e.g. token t of copy j = t*K+k
+  const int32_t* gsrc; int gdiv;
 };
 
 }  // namespace moe

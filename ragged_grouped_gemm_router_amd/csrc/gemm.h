@@ -37,5 +37,8 @@ constexpr int kSimtBM = 64;
 hipError_t gemm_mfma(GemmOp op, GemmParams p,
                      const int32_t* const* tile_off_by_bm, hipStream_t s);
 bool mfma_supported(GemmOp op, const GemmParams& p);
+// Whether GEMM 1 can gather its A rows (direct-to-LDS kernel, bf16 or
+// MXFP8) for contraction length K.
+bool gemm1_gather_supported(int K);
 
 }  // namespace moe

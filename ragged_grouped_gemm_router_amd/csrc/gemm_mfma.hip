@@ -517,14 +517,19 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // per-lane offsets stay small at any problem size and the k-tile offset
   // rides in the scalar offset; each lane fetches the 16-byte chunk that
   // belongs at its (swizzled) LDS position.
+  // Gathered A: the resource spans the whole source matrix and each lane's
+  // offset is its row's source row (the host keeps it below 2^31 bytes).
   const int r_in = lane / CPR, phys = lane % CPR;
-  const Rsrc ra = make_rsrc((const char*)p.A + (long)t.m0 * p.lda * F::ES);
+  const bool gather = p.gsrc != nullptr;
+  const Rsrc ra = make_rsrc((const char*)p.A +
+                            (gather ? 0 : (long)t.m0 * p.lda * F::ES));
   int a_off[A_INS];
 #pragma unroll
   for (int j = 0; j < A_INS; ++j) {
     const int row = (j * NW + wave) * RPI + r_in;
     const int grow = min(t.m0 + row, t.m_end - 1);
-    a_off[j] = (grow - t.m0) * p.lda * F::ES + swz<CPR>(row, phys) * 16;
+    const int src = gather ? p.gsrc[grow] / p.gdiv : grow - t.m0;
+    a_off[j] = src * (int)p.lda * F::ES + swz<CPR>(row, phys) * 16;
   }
   Rsrc rb[NB_OPS];
   rb[0] = make_rsrc((const char*)p.B +
@@ -566,7 +571,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int row = min(t.m0 + wm * WM + i * 32 + lane % 32, t.m_end - 1);
-      sc_row[i] = p.As + (long)row * p.ld_s;
+      const long src = gather ? p.gsrc[row] / p.gdiv : row;
+      sc_row[i] = p.As + src * p.ld_s;
     }
 #pragma unroll
     for (int o = 0; o < NB_OPS; ++o)
@@ -1169,9 +1175,15 @@ bool mfma_supported(GemmOp op, const GemmParams& p) {
   return true;
 }
 
+bool gemm1_gather_supported(int K) { return K % 64 == 0 && !force_staged(); }
+
 hipError_t gemm_mfma(GemmOp op, GemmParams p,
                      const int32_t* const* tile_off_by_bm, hipStream_t s) {
   if (!mfma_supported(op, p)) return hipErrorNotSupported;
+  // gathered rows only on the direct-to-LDS GEMM 1
+  if (p.gsrc && !(op == kOpGemm1Mx ||
+                  (op == kOpGemm1 && gemm1_gather_supported(p.K))))
+    return hipErrorNotSupported;
   p.group_n = tile_group_n();
   // Big tiles when the average group has enough rows to fill them.
   bool big;

@@ -42,10 +42,12 @@ def quantize_expert_weights(inp: dict) -> dict:
     return out
 
 
-def alloc_forward(desc: B.MoeDesc, device="cuda") -> dict:
+def alloc_forward(desc: B.MoeDesc, device="cuda", gather=False) -> dict:
     """Every caller-owned forward buffer for ``desc`` plus the workspace.
     MXFP8: x_perm holds E4M3 codes with scales in x_perm_scales, and h
-    holds E4M3 codes [T*K, d_ff] followed by E8M0 scales."""
+    holds E4M3 codes [T*K, d_ff] followed by E8M0 scales. gather=True
+    leaves x_perm out: GEMM 1 then reads its rows from x through
+    sorted_src (the permute writes only the indices)."""
     T, d, f, E, K = desc.T, desc.d_model, desc.d_ff, desc.E, desc.K
     TK = T * K
     dt = act_torch_dtype(desc)
@@ -71,6 +73,8 @@ def alloc_forward(desc: B.MoeDesc, device="cuda") -> dict:
         bufs["x_perm"] = torch.empty(TK, d, dtype=u8, device=device)
         bufs["x_perm_scales"] = torch.empty(TK, d // 32, dtype=u8, device=device)
         bufs["h"] = torch.empty(TK * f + TK * (f // 32), dtype=u8, device=device)
+    if gather:
+        bufs["x_perm"] = bufs["x_perm_scales"] = None
     if desc.flags & B.MOE_FLAG_SAVE_ACTS:
         bufs["act_a"] = torch.empty(TK, f, dtype=dt, device=device)
         bufs["act_b"] = torch.empty(TK, f, dtype=dt, device=device)
