@@ -10,7 +10,7 @@ from .moe_oracle import (  # noqa: F401
     permute, swiglu, expert_ffn, forward, forward_gather, dense_masked_forward,
     stage_gemm1, stage_gemm2, stage_combine, backward, backward_sampled,
     gate_logit_grad, router_backward, gate_probs, load_balance_stats,
-    aux_loss_logit_grad,
+    aux_loss_logit_grad, update_route_bias, balance_monitor,
 )
 from .mxfp8 import (  # noqa: F401
     e4m3_values, e4m3_round, mx_quantize, mx_dequantize, mx_roundtrip,

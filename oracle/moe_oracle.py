@@ -497,3 +497,47 @@ def aux_loss_logit_grad(logits: torch.Tensor, idx: torch.Tensor, E: int,
         s = _sigmoid(L)
         q = s * (1.0 - s) / s.sum(dim=1, keepdim=True)
     return (E / T) * q * (f - inner)
+
+
+# --------------------------------------------------------------------------
+# Bias-balance update and load monitor [P3 §6.3, §9, §13 monitoring].
+# Computed in fp32, in the order the definitions give, because the sign of
+# (load - target) and the cold-expert count are decisions that must come
+# out the same as on the device.
+# --------------------------------------------------------------------------
+
+def update_route_bias(bias, counts, gamma: float, target: float = 0.0,
+                      rule: int = 0):
+    """One step of the auxiliary-loss-free balancing. load = counts /
+    sum(counts) (the layer's load statistic); target <= 0 means 1/E.
+    rule 0 [P3 §6.3 text]: an overloaded expert's bias drops by gamma, an
+    underloaded one's rises by gamma, one on target keeps it.
+    rule 1 [P3 §9 update_balance_bias]: the step is additionally scaled by
+    the load, clamped below at 1e-6.
+    Returns (new bias, load), fp32 numpy arrays."""
+    c = np.asarray(counts, dtype=np.int64)
+    E = c.shape[0]
+    load = c.astype(np.float32) / np.float32(c.sum())
+    tgt = np.float32(target) if target > 0 else np.float32(1.0) / np.float32(E)
+    sgn = np.sign(load - tgt).astype(np.float32)
+    step = np.float32(gamma) * sgn
+    if rule == 1:
+        step = step * np.maximum(load, np.float32(1e-6))
+    return (np.asarray(bias, dtype=np.float32) - step).astype(np.float32), load
+
+
+def balance_monitor(load_hist):
+    """Monitor figures from a window of load vectors [W, E] (oldest
+    first): the mean load r over the window (fp32, summed in row order),
+    its minimum, the entropy -sum r log(r + 1e-9) and the number of cold
+    experts (r < 0.3 / E). Returns (min, entropy, cold) as floats."""
+    h = np.asarray(load_hist, dtype=np.float32)
+    W, E = h.shape
+    s = np.zeros(E, dtype=np.float32)
+    for w in range(W):
+        s = (s + h[w]).astype(np.float32)
+    r = (s / np.float32(W)).astype(np.float32)
+    r64 = r.astype(np.float64)
+    entropy = float(-(r64 * np.log(r64 + 1e-9)).sum())
+    cold = int((r < np.float32(0.3) / np.float32(E)).sum())
+    return float(r.min()), entropy, cold

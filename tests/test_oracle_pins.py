@@ -548,3 +548,59 @@ def test_aux_loss_grad_special_cases():
     for gate in ("softmax", "sigmoid"):
         dz = oracle.aux_loss_logit_grad(L, idx_even, E, gate)
         assert dz.abs().max() < 1e-15
+
+
+# --------------------------------------------------------------------------
+# Bias-balance update and load monitor [P3 §6.3, §9, §13]
+# --------------------------------------------------------------------------
+
+def test_route_bias_update_page_rule():
+    """The stated rule: overloaded experts' bias drops by gamma,
+    underloaded ones' rises by gamma; the scaled variant moves each by
+    gamma times its load. Two experts at 3:1 against the 1/2 target."""
+    bias = np.array([0.25, -0.5], dtype=np.float32)
+    nb, load = oracle.update_route_bias(bias, [300, 100], 0.125)
+    assert load.tolist() == [0.75, 0.25]
+    assert nb.tolist() == [0.125, -0.375]
+    nb1, _ = oracle.update_route_bias(bias, [300, 100], 0.125, rule=1)
+    assert nb1.tolist() == [0.25 - 0.125 * 0.75, -0.5 + 0.125 * 0.25]
+
+
+def test_route_bias_update_invariants():
+    """Balanced loads leave the bias unchanged; an explicit target moves
+    experts on either side of it; an empty expert's scaled step uses the
+    1e-6 floor; the plain rule's steps sum to gamma * (#under - #over)."""
+    E = 8
+    bias = np.linspace(-1, 1, E).astype(np.float32)
+    nb, _ = oracle.update_route_bias(bias, [64] * E, 0.01)
+    assert np.array_equal(nb, bias)
+    counts = [0, 5, 10, 10, 10, 10, 20, 15]
+    nb, load = oracle.update_route_bias(bias, counts, 0.01, target=0.1)
+    assert np.array_equal(np.sign(bias - nb), np.sign(load - np.float32(0.1)))
+    nb1, _ = oracle.update_route_bias(bias, counts, 0.5, rule=1)
+    assert nb1[0] == np.float32(bias[0] - np.float32(-0.5) * np.float32(1e-6))
+    nb0, _ = oracle.update_route_bias(np.zeros(E, np.float32), counts, 0.5)
+    n_under = sum(c / 80 < 1 / E for c in counts)
+    n_over = sum(c / 80 > 1 / E for c in counts)
+    assert abs(float(nb0.sum()) - 0.5 * (n_under - n_over)) < 1e-6
+
+
+def test_balance_monitor_closed_forms():
+    """Uniform loads: min 1/E, entropy log E (up to the 1e-9 guard), no
+    cold expert. All load on one expert: entropy ~0, E - 1 cold experts.
+    A window averages its rows."""
+    E = 16
+    mn, ent, cold = oracle.balance_monitor(np.full((5, E), 1.0 / E))
+    assert abs(mn - 1.0 / E) < 1e-8
+    assert abs(ent - math.log(E)) < 1e-6
+    assert cold == 0
+    one = np.zeros((3, E))
+    one[:, 3] = 1.0
+    mn, ent, cold = oracle.balance_monitor(one)
+    assert mn == 0.0 and abs(ent) < 1e-8 and cold == E - 1
+    # two rows that average to uniform
+    a = np.zeros((2, E))
+    a[0, : E // 2] = 2.0 / E
+    a[1, E // 2:] = 2.0 / E
+    mn, ent, cold = oracle.balance_monitor(a)
+    assert abs(mn - 1.0 / E) < 1e-8 and cold == 0
