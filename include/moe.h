@@ -326,6 +326,31 @@ moe_status moe_load_balance_stats(const moe_desc* desc, const float* logits,
                                   float* p_mean, float* aux, void* ws,
                                   size_t ws_bytes, void* stream);
 
+/* Route-bias step of the auxiliary-loss-free balancing [P3 §6.3, §9],
+ * from one routing's counts [E] (e.g. moe_forward's): load[e] =
+ * counts[e] / sum(counts), then in fp32, each product and difference
+ * rounded once:
+ *   rule 0 (the stated rule): bias[e] -= gamma * sign(load[e] - target);
+ *   rule 1 (the layer's update_balance_bias variant):
+ *          bias[e] -= gamma * sign(load[e] - target) * max(load[e], 1e-6);
+ * target <= 0 means 1/E; sign(0) = 0. route_bias [E] fp32 is updated in
+ * place (it only moves the selection, see moe_route); load [E] fp32 is
+ * written if non-NULL. T == 0 changes nothing. MOE_EINVAL on a NULL
+ * counts or route_bias, a rule other than 0 or 1, or a NaN gamma or
+ * target. */
+moe_status moe_update_route_bias(const moe_desc* desc, const int32_t* counts,
+                                 float* route_bias, float gamma, float target,
+                                 int32_t rule, float* load, void* stream);
+
+/* Load monitor [P3 §13 monitoring]: from a window of W >= 1 load vectors
+ * load_hist [W, E] fp32 (e.g. successive moe_update_route_bias loads,
+ * oldest first; the pages average the latest 100), the mean load r (rows
+ * summed in order), and out[0] = min r, out[1] = -sum r log(r + 1e-9)
+ * (entropy), out[2] = number of experts with r < 0.3 / E (cold experts),
+ * all fp32 on the device. MOE_EINVAL on a NULL pointer or W < 1. */
+moe_status moe_balance_monitor(const moe_desc* desc, const float* load_hist,
+                               int32_t W, float* out, void* stream);
+
 /* MX quantisation of a bf16 [rows, cols] matrix along its rows (cols a
  * multiple of 32), per the OCP MX v1.0 rule: X = floor(log2(amax)) - 8
  * per 32-element block (clamped to [-127, 127]); scale code X + 127;

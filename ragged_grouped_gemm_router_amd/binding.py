@@ -30,6 +30,7 @@ EXPORTED = ["moe_status_str", "moe_workspace_size", "moe_route",
             "moe_permute", "moe_grouped_gemm_swiglu", "moe_unpermute_combine",
             "moe_forward", "moe_backward", "moe_router_workspace_size",
             "moe_router_backward", "moe_load_balance_stats",
+            "moe_update_route_bias", "moe_balance_monitor",
             "moe_quantize_mxfp8"]
 
 
@@ -109,6 +110,11 @@ def load() -> ctypes.CDLL:
                                 [c_void_p] * 4 + [c_size_t, c_void_p]),
         "moe_load_balance_stats": (c_int32, [D] + [c_void_p] * 6 +
                                    [c_size_t, c_void_p]),
+        "moe_update_route_bias": (c_int32, [D, c_void_p, c_void_p, c_float,
+                                            c_float, c_int32, c_void_p,
+                                            c_void_p]),
+        "moe_balance_monitor": (c_int32, [D, c_void_p, c_int32, c_void_p,
+                                          c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -245,6 +251,22 @@ def moe_load_balance_stats(desc, logits, counts, f, p_mean, aux, ws,
         ptr(aux), ptr(ws), ws.numel() * ws.element_size(),
         stream if stream is not None else current_stream()),
         "moe_load_balance_stats")
+
+
+def moe_update_route_bias(desc, counts, route_bias, gamma, target=0.0,
+                          rule=0, load_out=None, stream=None):
+    check(load().moe_update_route_bias(
+        ctypes.byref(desc), ptr(counts), ptr(route_bias), float(gamma),
+        float(target), int(rule), ptr(load_out),
+        stream if stream is not None else current_stream()),
+        "moe_update_route_bias")
+
+
+def moe_balance_monitor(desc, load_hist, out, stream=None):
+    check(load().moe_balance_monitor(
+        ctypes.byref(desc), ptr(load_hist), int(load_hist.shape[0]), ptr(out),
+        stream if stream is not None else current_stream()),
+        "moe_balance_monitor")
 
 
 def moe_quantize_mxfp8(src, rows, cols, q, scales, stream=None):

@@ -425,6 +425,28 @@ moe_status moe_load_balance_stats(const moe_desc* d, const float* logits,
                                          (hipStream_t)stream));
 }
 
+moe_status moe_update_route_bias(const moe_desc* d, const int32_t* counts,
+                                 float* route_bias, float gamma, float target,
+                                 int32_t rule, float* load, void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (!counts || !route_bias) return MOE_EINVAL;
+  if (rule != 0 && rule != 1) return MOE_EINVAL;
+  if (!(gamma == gamma) || !(target == target)) return MOE_EINVAL;
+  if (d->T == 0) return MOE_OK;  // no load to balance: nothing is accessed
+  return hip_status(launch_bias_update(counts, d->E, gamma, target, rule,
+                                       route_bias, load, (hipStream_t)stream));
+}
+
+moe_status moe_balance_monitor(const moe_desc* d, const float* load_hist,
+                               int32_t W, float* out, void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (!load_hist || !out || W < 1) return MOE_EINVAL;
+  return hip_status(launch_balance_monitor(load_hist, W, d->E, out,
+                                           (hipStream_t)stream));
+}
+
 moe_status moe_router_backward(const moe_desc* d, const void* x,
                                const void* w_router, const float* logits,
                                const int32_t* topk_idx, const float* topk_w,

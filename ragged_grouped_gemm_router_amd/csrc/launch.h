@@ -61,6 +61,12 @@ hipError_t launch_balance_stats(const float* logits, const int32_t* counts,
                                 hipStream_t s);
 // split[g] = g * T / G for g = 0..G (G <= 1023).
 hipError_t launch_split(int T, int G, int32_t* split, hipStream_t s);
+// Route-bias balance step and load monitor (one block each, E <= 1024).
+hipError_t launch_bias_update(const int32_t* counts, int E, float gamma,
+                              float target, int rule, float* bias,
+                              float* load, hipStream_t s);
+hipError_t launch_balance_monitor(const float* hist, int W, int E, float* out,
+                                  hipStream_t s);
 // out[i] = sum_{g < G} part[g * n + i] (fixed order), in dtype.
 hipError_t launch_reduce_parts(int dtype, const float* part, long n, int G,
                                void* out, hipStream_t s);

@@ -301,6 +301,67 @@ __global__ __launch_bounds__(1024) void balance_finish_kernel(
   if (tid == 0) aux[0] = (float)E * red[0];
 }
 
+// Route-bias balance step (one block of 1024 threads): load = counts /
+// sum(counts), the sum taken over 64-bit integers; each expert's bias
+// moves against the sign of load - target by gamma (rule 0), or by gamma
+// times the load clamped below at 1e-6 (rule 1). No contraction, so every
+// product and difference rounds once, as written.
+__global__ __launch_bounds__(1024) void bias_update_kernel(
+    const int32_t* __restrict__ counts, int E, float gamma, float target,
+    int rule, float* __restrict__ bias, float* __restrict__ load_out) {
+#pragma clang fp contract(off)
+  __shared__ long long red[1024];
+  const int e = threadIdx.x;
+  red[e] = e < E ? counts[e] : 0;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (e < off) red[e] += red[e + off];
+    __syncthreads();
+  }
+  if (e >= E) return;
+  const float load = (float)counts[e] / (float)red[0];
+  const float tgt = target > 0.0f ? target : 1.0f / (float)E;
+  const float sg = load > tgt ? 1.0f : (load < tgt ? -1.0f : 0.0f);
+  float step = gamma * sg;
+  if (rule == 1) step = step * fmaxf(load, 1e-6f);
+  bias[e] = bias[e] - step;
+  if (load_out) load_out[e] = load;
+}
+
+// Load monitor (one block of 1024 threads): r = mean of the W load rows
+// (summed in row order), then min r, the entropy -sum r log(r + 1e-9)
+// (fixed tree) and the number of experts with r < 0.3 / E.
+__global__ __launch_bounds__(1024) void balance_monitor_kernel(
+    const float* __restrict__ hist, int W, int E, float* __restrict__ out) {
+#pragma clang fp contract(off)
+  __shared__ float rmin[1024], ent[1024];
+  __shared__ int cold[1024];
+  const int e = threadIdx.x;
+  float r = 0.0f;
+  if (e < E) {
+    float s = 0.0f;
+    for (int w = 0; w < W; ++w) s = s + hist[(long)w * E + e];
+    r = s / (float)W;
+  }
+  rmin[e] = e < E ? r : INFINITY;
+  ent[e] = e < E ? -(r * logf(r + 1e-9f)) : 0.0f;
+  cold[e] = e < E && r < 0.3f / (float)E ? 1 : 0;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (e < off) {
+      rmin[e] = fminf(rmin[e], rmin[e + off]);
+      ent[e] += ent[e + off];
+      cold[e] += cold[e + off];
+    }
+    __syncthreads();
+  }
+  if (e == 0) {
+    out[0] = rmin[0];
+    out[1] = ent[0];
+    out[2] = (float)cold[0];
+  }
+}
+
 // out[i] = sum_g part[g * n + i] in g order (fixed, so deterministic)
 template <typename TO>
 __global__ __launch_bounds__(256) void reduce_parts_kernel(
@@ -370,6 +431,21 @@ hipError_t launch_balance_stats(const float* logits, const int32_t* counts,
   while (Ep < E) Ep *= 2;
   hipLaunchKernelGGL(balance_finish_kernel, dim3(1), dim3(1024), 0, s, part,
                      counts, T, E, Ep, G, f, p_mean, aux);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_update(const int32_t* counts, int E, float gamma,
+                              float target, int rule, float* bias,
+                              float* load, hipStream_t s) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3(1), dim3(1024), 0, s, counts, E,
+                     gamma, target, rule, bias, load);
+  return hipGetLastError();
+}
+
+hipError_t launch_balance_monitor(const float* hist, int W, int E, float* out,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(balance_monitor_kernel, dim3(1), dim3(1024), 0, s, hist,
+                     W, E, out);
   return hipGetLastError();
 }
 

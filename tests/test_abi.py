@@ -184,3 +184,20 @@ def test_balance_stats_validation():
     z = B.make_desc(0, 128, 256, 8, 2)
     assert lib.moe_load_balance_stats(ctypes.byref(z), *([None] * 6), 0,
                                       None) == B.MOE_OK
+
+def test_bias_update_and_monitor_validation():
+    lib = B.load()
+    d = B.make_desc(64, 128, 256, 8, 2)
+    fake = 0x1000
+    upd = lib.moe_update_route_bias
+    assert upd(ctypes.byref(d), None, fake, 0.01, 0.0, 0, None, None) == B.MOE_EINVAL
+    assert upd(ctypes.byref(d), fake, None, 0.01, 0.0, 0, None, None) == B.MOE_EINVAL
+    assert upd(ctypes.byref(d), fake, fake, 0.01, 0.0, 2, None, None) == B.MOE_EINVAL
+    assert upd(ctypes.byref(d), fake, fake, float("nan"), 0.0, 0, None,
+               None) == B.MOE_EINVAL
+    z = B.make_desc(0, 128, 256, 8, 2)
+    assert upd(ctypes.byref(z), fake, fake, 0.01, 0.0, 1, None, None) == B.MOE_OK
+    mon = lib.moe_balance_monitor
+    assert mon(ctypes.byref(d), fake, 0, fake, None) == B.MOE_EINVAL
+    assert mon(ctypes.byref(d), None, 4, fake, None) == B.MOE_EINVAL
+    assert mon(ctypes.byref(d), fake, 4, None, None) == B.MOE_EINVAL
