@@ -342,7 +342,7 @@ moe_status moe_update_route_bias(const moe_desc* desc, const int32_t* counts,
                                  float* route_bias, float gamma, float target,
                                  int32_t rule, float* load, void* stream);
 
-/* Load monitor [P3 §13 monitoring]: from a window of W >= 1 load vectors
+/* Load monitor [P3 §13.9]: from a window of W >= 1 load vectors
  * load_hist [W, E] fp32 (e.g. successive moe_update_route_bias loads,
  * oldest first; the pages average the latest 100), the mean load r (rows
  * summed in order), and out[0] = min r, out[1] = -sum r log(r + 1e-9)

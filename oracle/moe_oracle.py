@@ -500,7 +500,7 @@ def aux_loss_logit_grad(logits: torch.Tensor, idx: torch.Tensor, E: int,
 
 
 # --------------------------------------------------------------------------
-# Bias-balance update and load monitor [P3 §6.3, §9, §13 monitoring].
+# Bias-balance update and load monitor [P3 §6.3, §9, §13.9].
 # Computed in fp32, in the order the definitions give, because the sign of
 # (load - target) and the cold-expert count are decisions that must come
 # out the same as on the device.

@@ -551,7 +551,7 @@ def test_aux_loss_grad_special_cases():
 
 
 # --------------------------------------------------------------------------
-# Bias-balance update and load monitor [P3 §6.3, §9, §13]
+# Bias-balance update and load monitor [P3 §6.3, §9, §13.9]
 # --------------------------------------------------------------------------
 
 def test_route_bias_update_page_rule():
