@@ -14,5 +14,5 @@ from .moe_oracle import (  # noqa: F401
 )
 from .mxfp8 import (  # noqa: F401
     e4m3_values, e4m3_round, mx_quantize, mx_dequantize, mx_roundtrip,
-    forward_mxfp8,
+    forward_mxfp8, mx_roundtrip_cols, backward_mxfp8, backward_mxfp8_sampled,
 )

@@ -141,3 +141,123 @@ def forward_mxfp8(x, w1, w3, w2, idx, w, ws1=None, ws3=None, ws2=None,
         out += ffn(xq, wq("ws1", -1, ws1), wq("ws3", -1, ws3),
                    wq("ws2", -1, ws2))
     return out
+
+
+# --------------------------------------------------------------------------
+# MXFP8 backward. The pages give FP8 training as gradients times transposed
+# FP8 weights with fp32 accumulation and per-tile scales [P3 §13.6.2]. Read
+# with the forward's rule, both operands of each data-gradient product are
+# MX quantised along that product's contraction:
+#   dh = Q_d(g) . Q_d(W2)            (W2 [d, f] in blocks along d)
+#   dx_perm = Q_f(da) . Q_f(W1) + Q_f(db) . Q_f(W3)   (W1 [f, d] along f)
+# with g = w * dy and da, db held in the activation dtype (bf16) as stored,
+# a, b the forward's pre-activations, and fp64 products of the dequantised
+# values. The weight gradients take the operands the forward multiplied,
+# unquantised by the backward: dW2 = g^T Q_f(h), dW1 = da^T Q_d(x),
+# dW3 = db^T Q_d(x). quant=False turns every quantiser and the bf16
+# rounding into the identity, which must give the exact backward.
+# --------------------------------------------------------------------------
+
+def mx_roundtrip_cols(W: torch.Tensor, block: int = BLOCK) -> torch.Tensor:
+    """Quantise then dequantise a matrix in blocks of 32 along its first
+    dimension (the contraction of a product that reads it transposed)."""
+    return mx_roundtrip(_f64(W).T, block).T
+
+
+def _bf16r(v: torch.Tensor) -> torch.Tensor:
+    return v.to(torch.bfloat16).to(F64)
+
+
+def _mx_bwd_ops(quant: bool):
+    ident = lambda v: _f64(v)  # noqa: E731
+    if not quant:
+        return ident, ident, ident
+    return (lambda v: mx_roundtrip(_f64(v))), mx_roundtrip_cols, _bf16r
+
+
+def backward_mxfp8(x, w1, w3, w2, idx, w, dy, quant: bool = True) -> dict:
+    """Gradients of sum(dy * forward_mxfp8(...)) under the reading above,
+    routing fixed and the gate weights as leaves; experts with no token
+    get dW = 0."""
+    Q, Qc, R = _mx_bwd_ops(quant)
+    T, d = x.shape
+    E, f, _ = w1.shape
+    x64, dy64, w64 = _f64(x), _f64(dy), _f64(w)
+    dx = torch.zeros(T, d, dtype=F64)
+    dw1 = torch.zeros(E, f, d, dtype=F64)
+    dw3 = torch.zeros_like(dw1)
+    dw2 = torch.zeros(E, d, f, dtype=F64)
+    d_w = torch.zeros(w.shape, dtype=F64)
+    for e in range(E):
+        mask = idx == e
+        if not bool(mask.any()):
+            continue
+        rows, ks = mask.nonzero(as_tuple=True)
+        X = Q(x64[rows])
+        a = X @ Q(w1[e]).T
+        b = X @ Q(w3[e]).T
+        hq = Q(swiglu(a, b))
+        Y = hq @ Q(w2[e]).T
+        d_w[rows, ks] = (dy64[rows] * Y).sum(dim=1)
+        g = R(dy64[rows] * w64[rows, ks].unsqueeze(-1))
+        dh = Q(g) @ Qc(w2[e])
+        sg = torch.sigmoid(a)
+        da = R(dh * b * sg * (1.0 + a * (1.0 - sg)))
+        db = R(dh * a * sg)
+        dx.index_add_(0, rows, Q(da) @ Qc(w1[e]) + Q(db) @ Qc(w3[e]))
+        dw2[e] = g.T @ hq
+        dw1[e] = da.T @ X
+        dw3[e] = db.T @ X
+    return {"dx": dx, "dw1": dw1, "dw3": dw3, "dw2": dw2, "d_w": d_w}
+
+
+def backward_mxfp8_sampled(x, w1, w3, w2, idx, w, dy, tokens, cols) -> dict:
+    """backward_mxfp8 on a sample, for full-size shapes: dx and d_w of the
+    given tokens (each needs only its own K copies), and for (e, j) pairs
+    row j of dW1_e and dW3_e and column j of dW2_e (hidden unit j over the
+    expert's rows; Q_f(h) at j needs only j's 32-block of h). Weights are
+    quantised per expert as they are needed."""
+    Q, Qc, R = _mx_bwd_ops(True)
+    x64, dy64, w64 = _f64(x), _f64(dy), _f64(w)
+    K = idx.shape[1]
+    tokens = _token_subset(x.shape[0], tokens)
+    dx = torch.zeros(tokens.numel(), x.shape[1], dtype=F64)
+    d_w = torch.zeros(tokens.numel(), K, dtype=F64)
+    need = {}
+    for i, t in enumerate(tokens.tolist()):
+        for k in range(K):
+            need.setdefault(int(idx[t, k]), []).append((i, t, k))
+    for e, copies in sorted(need.items()):
+        W1f, W3f, W2f = Q(w1[e]), Q(w3[e]), Q(w2[e])
+        W1c, W3c, W2c = Qc(w1[e]), Qc(w3[e]), Qc(w2[e])
+        for i, t, k in copies:
+            X = Q(x64[t:t + 1])
+            a, b = X @ W1f.T, X @ W3f.T
+            Y = Q(swiglu(a, b)) @ W2f.T
+            d_w[i, k] = (dy64[t] * Y[0]).sum()
+            g = R(w64[t, k] * dy64[t:t + 1])
+            dh = Q(g) @ W2c
+            sg = torch.sigmoid(a)
+            da = R(dh * b * sg * (1.0 + a * (1.0 - sg)))
+            db = R(dh * a * sg)
+            dx[i] += (Q(da) @ W1c + Q(db) @ W3c)[0]
+        del W1f, W3f, W2f, W1c, W3c, W2c
+    dw1_rows, dw3_rows, dw2_cols = [], [], []
+    for e, j in cols:
+        rows, ks = (idx == e).nonzero(as_tuple=True)
+        X = Q(x64[rows])
+        blk = slice(j - j % BLOCK, j - j % BLOCK + BLOCK)
+        a = X @ Q(w1[e][blk]).T
+        b = X @ Q(w3[e][blk]).T
+        hq = Q(swiglu(a, b))[:, j % BLOCK]
+        g = R(dy64[rows] * w64[rows, ks].unsqueeze(-1))
+        dh = Q(g) @ mx_roundtrip(_f64(w2[e][:, j]))
+        aj, bj = a[:, j % BLOCK], b[:, j % BLOCK]
+        sg = torch.sigmoid(aj)
+        da = R(dh * bj * sg * (1.0 + aj * (1.0 - sg)))
+        db = R(dh * aj * sg)
+        dw1_rows.append(da @ X)
+        dw3_rows.append(db @ X)
+        dw2_cols.append(g.T @ hq)
+    return {"dx": dx, "d_w": d_w, "dw1_rows": dw1_rows,
+            "dw3_rows": dw3_rows, "dw2_cols": dw2_cols}

@@ -604,3 +604,68 @@ def test_balance_monitor_closed_forms():
     a[1, E // 2:] = 2.0 / E
     mn, ent, cold = oracle.balance_monitor(a)
     assert abs(mn - 1.0 / E) < 1e-8 and cold == 0
+
+
+# --------------------------------------------------------------------------
+# MXFP8 backward [P3 §13.6]
+# --------------------------------------------------------------------------
+
+def _mx_bwd_case(seed, T=40, d=64, f=96, E=4, K=2):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(T, d, generator=g, dtype=torch.float64)
+    w1 = torch.randn(E, f, d, generator=g, dtype=torch.float64) / d ** 0.5
+    w3 = torch.randn(E, f, d, generator=g, dtype=torch.float64) / d ** 0.5
+    w2 = torch.randn(E, d, f, generator=g, dtype=torch.float64) / f ** 0.5
+    L = torch.randn(T, E, generator=g, dtype=torch.float64)
+    idx = oracle.topk_select(oracle.selection_keys(L), K)
+    idx[0] = torch.arange(K)  # expert 3 may stay empty
+    w = oracle.gate_weights(L, idx, "softmax")
+    dy = torch.randn(T, d, generator=g, dtype=torch.float64)
+    return x, w1, w3, w2, idx, w, dy
+
+
+def test_mx_backward_without_quantisers_is_exact():
+    """With every quantiser (and the bf16 storage rounding) the identity,
+    the MXFP8 backward is the exact backward: which operand meets which,
+    signs and the SwiGLU derivative are those of the layer."""
+    x, w1, w3, w2, idx, w, dy = _mx_bwd_case(31)
+    got = oracle.backward_mxfp8(x, w1, w3, w2, idx, w, dy, quant=False)
+    ref = oracle.backward(x, w1, w3, w2, idx, w, dy)
+    for k in ("dx", "dw1", "dw3", "dw2", "d_w"):
+        assert torch.allclose(got[k], ref[k], rtol=0, atol=1e-12), k
+
+
+def test_mx_cols_quantiser_axis():
+    """A transposed operand is quantised in blocks along its first
+    dimension: a matrix whose 32-blocks down each column are exactly
+    representable (integers of magnitude <= 14 times a power of two per
+    column, so at most 448 after scaling) is left unchanged, while
+    quantising along rows, which mixes the columns' scales 2^0..2^20 and
+    so drops the small ones below E4M3's subnormal step, is not."""
+    g = torch.Generator().manual_seed(32)
+    ints = torch.randint(-14, 15, (64, 32), generator=g).to(torch.float64)
+    col_scale = torch.pow(2.0, torch.arange(32, dtype=torch.float64) % 21)
+    W = ints * col_scale
+    assert torch.equal(oracle.mx_roundtrip_cols(W), W)
+    assert not torch.equal(oracle.mx_roundtrip(W), W)
+
+
+def test_mx_backward_sampled_matches_full_and_is_near_exact():
+    """The sampled form reproduces the full MXFP8 backward on its sample,
+    and the MXFP8 gradients stay near the exact ones (a sanity bound: E4M3
+    keeps 3 mantissa bits, and these experts have few rows)."""
+    x, w1, w3, w2, idx, w, dy = _mx_bwd_case(33)
+    full = oracle.backward_mxfp8(x, w1, w3, w2, idx, w, dy)
+    toks = [0, 5, 39]
+    cols = [(0, 0), (1, 37), (2, 95)]
+    smp = oracle.backward_mxfp8_sampled(x, w1, w3, w2, idx, w, dy, toks, cols)
+    assert torch.allclose(smp["dx"], full["dx"][toks], rtol=0, atol=1e-12)
+    assert torch.allclose(smp["d_w"], full["d_w"][toks], rtol=0, atol=1e-12)
+    for i, (e, j) in enumerate(cols):
+        assert torch.allclose(smp["dw1_rows"][i], full["dw1"][e, j], atol=1e-12)
+        assert torch.allclose(smp["dw3_rows"][i], full["dw3"][e, j], atol=1e-12)
+        assert torch.allclose(smp["dw2_cols"][i], full["dw2"][e, :, j], atol=1e-12)
+    exact = oracle.backward(x, w1, w3, w2, idx, w, dy)
+    for k in ("dx", "dw1", "dw3", "dw2", "d_w"):
+        err = (full[k] - exact[k]).abs().max() / exact[k].abs().max()
+        assert 0 < err < 0.3, (k, float(err))
