@@ -156,7 +156,7 @@ typedef struct moe_fwd_args {
 typedef struct moe_bwd_args {
   const void* dy;             /* [T, d_model] act                            */
   const void* x;              /* [T, d_model] act                            */
-  moe_expert_weights routed;  /* act dtype (MXFP8 backward unsupported)      */
+  moe_expert_weights routed;  /* act dtype (MXFP8: the forward's MX weights)  */
   moe_expert_weights shared;
   /* saved forward state (as written by moe_forward) */
   const int32_t* topk_idx;
@@ -178,6 +178,17 @@ typedef struct moe_bwd_args {
   void* dws1;                 /* [d_ff_shared, d_model] act; iff shared      */
   void* dws3;                 /* [d_ff_shared, d_model] act; iff shared      */
   void* dws2;                 /* [d_model, d_ff_shared] act; iff shared      */
+  /* MXFP8 backward only (gemm_dtype MOE_MXFP8): the forward's MX state and
+     the weights quantised for the transposed products (moe_quantize_mxfp8_t):
+     x_perm and h then hold the forward's E4M3 codes (h: codes then scales),
+     routed the forward's MX weights (for the recomputed a, b). */
+  const uint8_t* x_perm_scales; /* [T*K, d_model/32] E8M0                    */
+  const uint8_t* w2t;         /* [E, d_ff, d_model] E4M3: W2^T, blocks along
+                                 d_model                                    */
+  const uint8_t* w2t_scales;  /* [E, d_ff, d_model/32]                       */
+  const uint8_t* w13t;        /* [E, d_model, 2*d_ff] E4M3: [W1^T | W3^T],
+                                 blocks along d_ff                          */
+  const uint8_t* w13t_scales; /* [E, d_model, 2*d_ff/32]                     */
   void* events[MOE_BWD_NEVENTS]; /* optional hipEvent_t stage boundaries     */
 } moe_bwd_args;
 
@@ -262,7 +273,18 @@ moe_status moe_forward(const moe_desc* desc, const moe_fwd_args* args,
  * owned tile by tile (no split-K atomics). The shared expert [P3 §5] is an
  * ungated SwiGLU FFN over every token: its pre-activations are recomputed,
  * its gradients written to dws1/dws3/dws2 and its share of dx added into
- * dx. MOE_EUNSUPPORTED for MXFP8 descriptors. */
+ * dx.
+ * MXFP8 descriptors [P3 §13.6]: the data-gradient products run on the
+ * scaled MFMA with both operands MX-quantised along their contraction:
+ *   dh = Q(dy_perm) . w2t  (dy_perm = w * dy in bf16, blocks along d_model)
+ *   dx_perm = Q([da | db]) . w13t  (da, db in bf16, blocks along d_ff)
+ * with a, b recomputed by the MX GEMM 1 from the forward's x_perm codes;
+ * the weight gradients are bf16 products of the operands the forward
+ * multiplied: dW2 = dy_perm^T h, dW1 = da^T x_perm, dW3 = db^T x_perm with
+ * h and x_perm dequantised from the forward's MX codes (exact in bf16).
+ * Needs x_perm_scales, w2t, w13t and their scales, the routed MX weights
+ * with scales, no saved activations; a shared expert is
+ * MOE_EUNSUPPORTED on this path. */
 moe_status moe_backward(const moe_desc* desc, const moe_bwd_args* args,
                         void* ws, size_t ws_bytes, void* stream);
 
@@ -350,6 +372,22 @@ moe_status moe_update_route_bias(const moe_desc* desc, const int32_t* counts,
  * all fp32 on the device. MOE_EINVAL on a NULL pointer or W < 1. */
 moe_status moe_balance_monitor(const moe_desc* desc, const float* load_hist,
                                int32_t W, float* out, void* stream);
+
+/* Transposing MX quantisation, for the weights of the MXFP8 backward's
+ * data-gradient products [P3 §13.6: gradient times transposed weight]:
+ * for each of `batch` bf16 [rows, cols] matrices src_b (contiguous),
+ *   q_b[c, col_off + r] = E4M3 code of src_b[r, c] in 32-blocks along r,
+ *   scales_b[c, (col_off + r) / 32] = the block's E8M0 code,
+ * with q_b of row stride ldq (batch stride cols * ldq) and scales_b of
+ * row stride ldq / 32 (batch stride cols * ldq / 32); same rule as
+ * moe_quantize_mxfp8. W2 [E, d, f] -> w2t: (E, d, f, ldq = d, col_off 0);
+ * W1, W3 [E, f, d] -> w13t: (E, f, d, ldq = 2 f, col_off 0 and f).
+ * rows % 32 == 0, cols % 64 == 0, ldq % 32 == 0, col_off % 32 == 0 and
+ * col_off + rows <= ldq, else MOE_EUNSUPPORTED / MOE_EINVAL. */
+moe_status moe_quantize_mxfp8_t(const void* src_bf16, int64_t batch,
+                                int64_t rows, int64_t cols, uint8_t* q,
+                                uint8_t* scales, int64_t ldq, int64_t col_off,
+                                void* stream);
 
 /* MX quantisation of a bf16 [rows, cols] matrix along its rows (cols a
  * multiple of 32), per the OCP MX v1.0 rule: X = floor(log2(amax)) - 8

@@ -150,9 +150,9 @@ def forward_mxfp8(x, w1, w3, w2, idx, w, ws1=None, ws3=None, ws2=None,
 # MX quantised along that product's contraction:
 #   dh = Q_d(g) . Q_d(W2)            (W2 [d, f] in blocks along d)
 #   dx_perm = Q_f(da) . Q_f(W1) + Q_f(db) . Q_f(W3)   (W1 [f, d] along f)
-# with g = w * dy and da, db held in the activation dtype (bf16) as stored,
-# a, b the forward's pre-activations, and fp64 products of the dequantised
-# values. The weight gradients take the operands the forward multiplied,
+# with g = w * dy, da, db and the forward's pre-activations a, b held in the
+# activation dtype (bf16), as the backward stores them (saved or
+# recomputed), and fp64 products of the dequantised values. The weight gradients take the operands the forward multiplied,
 # unquantised by the backward: dW2 = g^T Q_f(h), dW1 = da^T Q_d(x),
 # dW3 = db^T Q_d(x). quant=False turns every quantiser and the bf16
 # rounding into the identity, which must give the exact backward.
@@ -201,6 +201,7 @@ def backward_mxfp8(x, w1, w3, w2, idx, w, dy, quant: bool = True) -> dict:
         d_w[rows, ks] = (dy64[rows] * Y).sum(dim=1)
         g = R(dy64[rows] * w64[rows, ks].unsqueeze(-1))
         dh = Q(g) @ Qc(w2[e])
+        a, b = R(a), R(b)
         sg = torch.sigmoid(a)
         da = R(dh * b * sg * (1.0 + a * (1.0 - sg)))
         db = R(dh * a * sg)
@@ -237,6 +238,7 @@ def backward_mxfp8_sampled(x, w1, w3, w2, idx, w, dy, tokens, cols) -> dict:
             d_w[i, k] = (dy64[t] * Y[0]).sum()
             g = R(w64[t, k] * dy64[t:t + 1])
             dh = Q(g) @ W2c
+            a, b = R(a), R(b)
             sg = torch.sigmoid(a)
             da = R(dh * b * sg * (1.0 + a * (1.0 - sg)))
             db = R(dh * a * sg)
@@ -252,7 +254,7 @@ def backward_mxfp8_sampled(x, w1, w3, w2, idx, w, dy, tokens, cols) -> dict:
         hq = Q(swiglu(a, b))[:, j % BLOCK]
         g = R(dy64[rows] * w64[rows, ks].unsqueeze(-1))
         dh = Q(g) @ mx_roundtrip(_f64(w2[e][:, j]))
-        aj, bj = a[:, j % BLOCK], b[:, j % BLOCK]
+        aj, bj = R(a[:, j % BLOCK]), R(b[:, j % BLOCK])
         sg = torch.sigmoid(aj)
         da = R(dh * bj * sg * (1.0 + aj * (1.0 - sg)))
         db = R(dh * aj * sg)

@@ -31,7 +31,7 @@ EXPORTED = ["moe_status_str", "moe_workspace_size", "moe_route",
             "moe_forward", "moe_backward", "moe_router_workspace_size",
             "moe_router_backward", "moe_load_balance_stats",
             "moe_update_route_bias", "moe_balance_monitor",
-            "moe_quantize_mxfp8"]
+            "moe_quantize_mxfp8", "moe_quantize_mxfp8_t"]
 
 
 class MoeError(RuntimeError):
@@ -73,6 +73,9 @@ class MoeBwdArgs(ctypes.Structure):
         ("dx", c_void_p), ("dw1", c_void_p), ("dw3", c_void_p),
         ("dw2", c_void_p), ("d_topk_w", c_void_p),
         ("dws1", c_void_p), ("dws3", c_void_p), ("dws2", c_void_p),
+        ("x_perm_scales", c_void_p), ("w2t", c_void_p),
+        ("w2t_scales", c_void_p), ("w13t", c_void_p),
+        ("w13t_scales", c_void_p),
         ("events", c_void_p * MOE_BWD_NEVENTS)]
 
 
@@ -103,6 +106,9 @@ def load() -> ctypes.CDLL:
                                   c_void_p]),
         "moe_backward": (c_int32, [D, POINTER(MoeBwdArgs), c_void_p,
                                    c_size_t, c_void_p]),
+        "moe_quantize_mxfp8_t": (c_int32, [c_void_p, c_int64, c_int64,
+                                           c_int64, c_void_p, c_void_p,
+                                           c_int64, c_int64, c_void_p]),
         "moe_quantize_mxfp8": (c_int32, [c_void_p, c_int64, c_int64,
                                          c_void_p, c_void_p, c_void_p]),
         "moe_router_workspace_size": (c_int32, [D, POINTER(c_size_t)]),
@@ -274,3 +280,11 @@ def moe_quantize_mxfp8(src, rows, cols, q, scales, stream=None):
         ptr(src), rows, cols, ptr(q), ptr(scales),
         stream if stream is not None else current_stream()),
         "moe_quantize_mxfp8")
+
+
+def moe_quantize_mxfp8_t(src, batch, rows, cols, q, scales, ldq, col_off=0,
+                         stream=None):
+    check(load().moe_quantize_mxfp8_t(
+        ptr(src), batch, rows, cols, ptr(q), ptr(scales), ldq, col_off,
+        stream if stream is not None else current_stream()),
+        "moe_quantize_mxfp8_t")

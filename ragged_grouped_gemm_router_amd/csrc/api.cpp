@@ -69,6 +69,12 @@ struct BwdWs {
   void* sh;
   void* sdx;
   int32_t* srange;
+  // MXFP8: dy_perm and [da | db] quantised, h dequantised for dW2
+  uint8_t* dyq;
+  uint8_t* dys;
+  uint8_t* dgq;
+  uint8_t* dgs;
+  void* h_bf;
 };
 
 size_t fwd_ws_layout(const moe_desc* d, char* base, FwdWs* w) {
@@ -122,6 +128,18 @@ size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
     o = align_up(o + b * T * d->d_model);
     if (w) w->srange = (int32_t*)(base + o);
     o = align_up(o + 2 * sizeof(int32_t));
+  }
+  if (d->gemm_dtype == MOE_MXFP8) {
+    const size_t dm = d->d_model, f = d->d_ff;
+    uint8_t** u8s[4] = {w ? &w->dyq : nullptr, w ? &w->dys : nullptr,
+                        w ? &w->dgq : nullptr, w ? &w->dgs : nullptr};
+    const size_t n[4] = {TK * dm, TK * dm / 32, TK * 2 * f, TK * 2 * f / 32};
+    for (int i = 0; i < 4; ++i) {
+      if (u8s[i]) *u8s[i] = (uint8_t*)(base + o);
+      o = align_up(o + n[i]);
+    }
+    if (w) w->h_bf = base + o;
+    o = align_up(o + b * TK * f);
   }
   return o;
 }
@@ -324,6 +342,93 @@ bool weights_ok(const moe_expert_weights* w) {
   return w && w->w1 && w->w3 && w->w2;
 }
 
+// MXFP8 backward (validated by moe_backward): the data-gradient products on
+// MX operands, the weight gradients in bf16 from the forward's operands.
+hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
+                          hipStream_t s) {
+  BwdWs w;
+  bwd_ws_layout(d, (char*)ws, &w);
+  const int TK = d->T * d->K, dm = d->d_model, f = d->d_ff, E = d->E;
+  hipError_t e;
+#define MOE_TRY(x)                        \
+  do {                                    \
+    e = (x);                              \
+    if (e != hipSuccess) return e;        \
+  } while (0)
+  record(a->events[0], s);
+  MOE_TRY(launch_tile_prefix(a->offsets, E, w.tile_off, s));
+  MOE_TRY(launch_combine_bwd(MOE_BF16, a->dy, a->y_perm, a->dest, a->topk_w,
+                             w.dy_perm, a->d_topk_w, d->T, d->K, dm, s));
+  MOE_TRY(launch_quantize_mxfp8(w.dy_perm, TK, dm, w.dyq, w.dys, s));
+  record(a->events[1], s);
+  {  // a, b of the forward: GEMM 1 again on its MX operands, kept in bf16
+    GemmParams p = gp();
+    p.M = TK; p.N = f; p.K = dm; p.G = E; p.off = a->offsets;
+    p.A = a->x_perm; p.lda = dm; p.As = a->x_perm_scales;
+    p.B = a->routed.w1; p.B2 = a->routed.w3; p.ldb = dm; p.sB = (long)f * dm;
+    p.Bs = a->routed.w1_scales; p.B2s = a->routed.w3_scales;
+    p.ld_s = dm / 32; p.sBs = (long)f * (dm / 32);
+    p.C = nullptr; p.C2 = w.da; p.C3 = w.db; p.ldc = f;
+    MOE_TRY(gemm_mfma(kOpGemm1MxAct, p, w.tile_off, s));
+  }
+  record(a->events[2], s);
+  {  // dh = Q(dy_perm) W2t_e, then (da, db) in place of (a, b)
+    GemmParams p = gp();
+    p.M = TK; p.N = f; p.K = dm; p.G = E; p.off = a->offsets;
+    p.A = w.dyq; p.lda = dm; p.As = w.dys;
+    p.B = a->w2t; p.ldb = dm; p.sB = (long)f * dm;
+    p.Bs = a->w2t_scales; p.ld_s = dm / 32; p.sBs = (long)f * (dm / 32);
+    p.C = w.da; p.C2 = w.db; p.ldc = f;
+    p.aux_a = w.da; p.aux_b = w.db;
+    MOE_TRY(gemm_mfma(kOpDgrad2Mx, p, w.tile_off, s));
+    // [da | db] quantised along d_ff, side by side
+    MOE_TRY(launch_quantize_mxfp8_strided(w.da, TK, f, w.dgq, 2L * f, w.dgs,
+                                          2L * f / 32, s));
+    MOE_TRY(launch_quantize_mxfp8_strided(w.db, TK, f, w.dgq + f, 2L * f,
+                                          w.dgs + f / 32, 2L * f / 32, s));
+  }
+  record(a->events[3], s);
+  {  // dx_perm = Q([da | db]) W13t_e
+    GemmParams p = gp();
+    p.M = TK; p.N = dm; p.K = 2 * f; p.G = E; p.off = a->offsets;
+    p.A = w.dgq; p.lda = 2 * f; p.As = w.dgs;
+    p.B = a->w13t; p.ldb = 2 * f; p.sB = (long)dm * 2 * f;
+    p.Bs = a->w13t_scales; p.ld_s = 2 * f / 32; p.sBs = (long)dm * (2 * f / 32);
+    p.C = w.dx_perm; p.ldc = dm;
+    MOE_TRY(gemm_mfma(kOpGemm2Mx, p, w.tile_off, s));
+  }
+  record(a->events[4], s);
+  MOE_TRY(launch_combine(MOE_BF16, w.dx_perm, a->dest, nullptr, nullptr,
+                         a->dx, d->T, d->K, dm, s));
+  record(a->events[5], s);
+  {  // dW2_e = dy_perm^T h, h dequantised from the forward's codes
+    const uint8_t* hq = (const uint8_t*)a->h;
+    MOE_TRY(launch_dequantize_mxfp8(hq, hq + (size_t)TK * f, TK, f, w.h_bf, s));
+    GemmParams p = gp();
+    p.M = dm; p.N = f; p.G = E; p.off = a->offsets;
+    p.A = w.dy_perm; p.lda = dm;
+    p.B = w.h_bf; p.ldb = f;
+    p.C = a->dw2; p.ldc = f; p.sC = (long)dm * f;
+    MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
+  }
+  record(a->events[6], s);
+  // dW1_e = da^T x_perm, dW3_e = db^T x_perm, x_perm dequantised (into the
+  // dx_perm buffer, free after the gather-sum)
+  MOE_TRY(launch_dequantize_mxfp8((const uint8_t*)a->x_perm, a->x_perm_scales,
+                                  TK, dm, w.dx_perm, s));
+  for (int which = 0; which < 2; ++which) {
+    GemmParams p = gp();
+    p.M = f; p.N = dm; p.G = E; p.off = a->offsets;
+    p.A = which ? w.db : w.da; p.lda = f;
+    p.B = w.dx_perm; p.ldb = dm;
+    p.C = which ? a->dw3 : a->dw1; p.ldc = dm; p.sC = (long)f * dm;
+    MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
+  }
+  record(a->events[7], s);
+#undef MOE_TRY
+  return hipSuccess;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -445,6 +550,22 @@ moe_status moe_balance_monitor(const moe_desc* d, const float* load_hist,
   if (!load_hist || !out || W < 1) return MOE_EINVAL;
   return hip_status(launch_balance_monitor(load_hist, W, d->E, out,
                                            (hipStream_t)stream));
+}
+
+moe_status moe_quantize_mxfp8_t(const void* src, int64_t batch, int64_t rows,
+                                int64_t cols, uint8_t* q, uint8_t* scales,
+                                int64_t ldq, int64_t col_off, void* stream) {
+  if (batch < 0 || rows < 0 || cols < 0 || ldq < 0 || col_off < 0)
+    return MOE_EINVAL;
+  if (batch == 0 || rows == 0 || cols == 0) return MOE_OK;
+  if (!src || !q || !scales || col_off + rows > ldq) return MOE_EINVAL;
+  if (rows % 32 || cols % 64 || ldq % 32 || col_off % 32 || rows > INT_MAX ||
+      cols > INT_MAX || batch > 65535 || rows / 32 > 65535)
+    return MOE_EUNSUPPORTED;
+  return hip_status(launch_quantize_mxfp8_cols(src, batch, (int)rows,
+                                               (int)cols, q + col_off, ldq,
+                                               scales + col_off / 32,
+                                               (hipStream_t)stream));
 }
 
 moe_status moe_router_backward(const moe_desc* d, const void* x,
@@ -661,7 +782,14 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
       !a->dx || !a->dw1 || !a->dw3 || !a->dw2 || !a->d_topk_w)
     return MOE_EINVAL;
   if ((a->act_a == nullptr) != (a->act_b == nullptr)) return MOE_EINVAL;
-  if (d->gemm_dtype == MOE_MXFP8) return MOE_EUNSUPPORTED;
+  if (d->gemm_dtype == MOE_MXFP8) {
+    if (d->d_ff_shared > 0 || a->act_a) return MOE_EUNSUPPORTED;
+    if (!a->x_perm_scales || !a->w2t || !a->w2t_scales || !a->w13t ||
+        !a->w13t_scales || !a->routed.w1_scales || !a->routed.w3_scales)
+      return MOE_EINVAL;
+    if (ws_bytes < bwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
+    return hip_status(do_backward_mx(d, a, ws, (hipStream_t)stream));
+  }
   const bool shared = d->d_ff_shared > 0;
   if (shared && (!weights_ok(&a->shared) || !a->dws1 || !a->dws3 || !a->dws2))
     return MOE_EINVAL;

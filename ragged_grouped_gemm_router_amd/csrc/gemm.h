@@ -17,6 +17,8 @@ enum GemmOp : int {
   kOpGemm2Mx = 7, // GEMM 2 on MXFP8 operands; y_perm in bf16
   kOpRouterDx = 8,  // dx_router[T,d] = d_logits[T,E] Wr[E,d]   (1 group)
   kOpRouterDw = 9,  // part_g[E,d] = d_logits_g^T x_g over token range g (fp32)
+  kOpGemm1MxAct = 10,  // GEMM 1 on MXFP8 operands; bf16 h (optional), a, b
+  kOpDgrad2Mx = 11,    // dh = dy_perm W2_e on MXFP8 operands -> (da, db) bf16
 };
 
 // Row-tile heights for which the permute step publishes tile prefixes.

@@ -795,6 +795,28 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
         SO::run(lds, wm, wn, lane,
                 [&](int i, int j, int r) { return acc[NB_OPS - 1][i][j][r]; },
                 put((TO*)p.C3));
+    } else if constexpr (EPI == kEpiSwigluBwd) {
+      // dh = acc; (da, db) from the pre-activations a, b (bf16, ld = ldc),
+      // which may share their buffers with da, db
+      SO::run(lds, wm, wn, lane,
+              [&](int i, int j, int r) { return acc[0][i][j][r]; },
+              [&](int row, int col, const float* v) {
+                const int grow = t.m0 + row, gcol = t.n0 + col;
+                if (grow >= t.m_end || gcol >= p.N) return;
+                const long o = (long)grow * p.ldc + gcol;
+                const bf16x8 a8 = *(const bf16x8*)((const bf16*)p.aux_a + o);
+                const bf16x8 b8 = *(const bf16x8*)((const bf16*)p.aux_b + o);
+                float da[8], db[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                  const float a = (float)a8[q], b = (float)b8[q];
+                  const float sg = fast_sigmoid(a);
+                  da[q] = v[q] * b * sg * (1.0f + a * (1.0f - sg));
+                  db[q] = v[q] * a * sg;
+                }
+                *(bf16x8*)((bf16*)p.C + o) = pack8(da);
+                *(bf16x8*)((bf16*)p.C2 + o) = pack8(db);
+              });
     } else {
       SO::run(lds, wm, wn, lane,
               [&](int i, int j, int r) { return acc[0][i][j][r]; },
@@ -1163,7 +1185,8 @@ bool mfma_supported(GemmOp op, const GemmParams& p) {
   if (p.K % 8) return false;
   // MXFP8 products run only on the direct-to-LDS kernel: whole 128-byte
   // k-tiles (K % 128) and 32-column scale blocks in the output (N % 32)
-  if ((op == kOpGemm1Mx || op == kOpGemm2Mx) && (p.K % 128 || p.N % 32))
+  if ((op == kOpGemm1Mx || op == kOpGemm2Mx || op == kOpGemm1MxAct ||
+       op == kOpDgrad2Mx) && (p.K % 128 || p.N % 32))
     return false;
   if (op == kOpDgrad1 && p.K1 % 64) return false;
   if ((op == kOpDgrad2 || op == kOpDgrad1) && p.N % 8) return false;
@@ -1246,6 +1269,10 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   }
   if (op == kOpGemm1Mx)
     return launch_dl_sized<true, kEpiSwigluMx, bf16, true>(big, p, s);
+  if (op == kOpGemm1MxAct)
+    return launch_dl_sized<true, kEpiSwiglu, bf16, true>(big, p, s);
+  if (op == kOpDgrad2Mx)
+    return launch_dl_sized<false, kEpiSwigluBwd, bf16, true>(big, p, s);
   if (op == kOpGemm2Mx)
     return launch_dl_sized<false, kEpiStore, bf16, true>(big, p, s);
   switch (op) {

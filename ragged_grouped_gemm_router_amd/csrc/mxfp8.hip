@@ -6,17 +6,10 @@
 namespace moe {
 namespace {
 
-// Quantise 32 consecutive bf16 values (64 bytes at src, 16-byte aligned)
-// into 32 E4M3 codes packed in q[8] (4 per word, lowest address first);
-// returns the E8M0 scale code.
-__device__ __forceinline__ uint32_t quant32(const bf16* src, uint32_t q[8]) {
-  float v[32];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const bf16x8 x = *(const bf16x8*)(src + c * 8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[c * 8 + i] = (float)x[i];
-  }
+// Quantise 32 values into 32 E4M3 codes packed in q[8] (4 per word,
+// lowest index first); returns the E8M0 scale code.
+__device__ __forceinline__ uint32_t quant32v(const float (&v)[32],
+                                             uint32_t q[8]) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -30,6 +23,98 @@ __device__ __forceinline__ uint32_t quant32(const bf16* src, uint32_t q[8]) {
     q[w] = word;
   }
   return (uint32_t)(X + 127);
+}
+
+// The same for 32 consecutive bf16 values (64 bytes at src, 16-byte
+// aligned).
+__device__ __forceinline__ uint32_t quant32(const bf16* src, uint32_t q[8]) {
+  float v[32];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const bf16x8 x = *(const bf16x8*)(src + c * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[c * 8 + i] = (float)x[i];
+  }
+  return quant32v(v, q);
+}
+
+// Value of an E4M3 (e4m3fn) code: exponent bias 7, 3 mantissa bits,
+// subnormals m * 2^-9 (the saturating encoder never writes the NaN code).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e == 0 ? (float)m * 0x1p-9f
+                           : __uint_as_float((e + 120u) << 23) * (1.0f + (float)m * 0.125f);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Strided form: block b of 32 is row b / bpr, block b % bpr of a
+// contiguous [rows, bpr * 32] source; codes go to q + row * ldq and
+// scales to scales + row * lds (both already offset to the first column).
+__global__ __launch_bounds__(256) void quantize_rows_strided_kernel(
+    const bf16* __restrict__ src, long nblk, int bpr, uint8_t* __restrict__ q,
+    long ldq, uint8_t* __restrict__ scales, long lds) {
+  const long b = blockIdx.x * 256L + threadIdx.x;
+  if (b >= nblk) return;
+  const long r = b / bpr;
+  const int blk = (int)(b % bpr);
+  uint32_t w[8];
+  const uint32_t code = quant32(src + b * 32, w);
+  u32x4* dst = (u32x4*)(q + r * ldq + blk * 32);
+  dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+  dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+  scales[r * lds + blk] = (uint8_t)code;
+}
+
+// MX codes [rows, cols] with scales [rows, cols/32] back to bf16, one
+// thread per 32-block (exact: an E4M3 value times a power of two fits
+// bf16's 8-bit mantissa).
+__global__ __launch_bounds__(256) void dequantize_rows_kernel(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ scales,
+    long nblk, bf16* __restrict__ out) {
+  const long b = blockIdx.x * 256L + threadIdx.x;
+  if (b >= nblk) return;
+  const float sc = ldexpf(1.0f, (int)scales[b] - 127);
+  const u32x4* src = (const u32x4*)(q + b * 32);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const u32x4 w = src[h];
+    bf16x8 o[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      o[i / 8][i % 8] = (bf16)(e4m3_decode((w[i / 4] >> (8 * (i % 4))) & 0xffu) * sc);
+    *(bf16x8*)(out + b * 32 + h * 16) = o[0];
+    *(bf16x8*)(out + b * 32 + h * 16 + 8) = o[1];
+  }
+}
+
+// Transposing quantisation: batch b of a [R, C] bf16 source becomes
+// [C, ldq] codes with element (c, r) = Q(src[r][c]), in 32-blocks along r,
+// scales [C, ldq / 32]. A workgroup stages a 32 x 64 tile in LDS; thread
+// c < 64 then quantises column c's 32 values. (Used once per weight set.)
+__global__ __launch_bounds__(256) void quantize_cols_kernel(
+    const bf16* __restrict__ src, int R, int C, uint8_t* __restrict__ q,
+    long ldq, long q_bstride, uint8_t* __restrict__ scales, long s_bstride) {
+  __shared__ float tile[32][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 32, b = blockIdx.z;
+  const bf16* sb = src + (long)b * R * C;
+  {
+    const int r = threadIdx.x / 8, c = (threadIdx.x % 8) * 8;
+    const bf16x8 x = *(const bf16x8*)(sb + (long)(r0 + r) * C + c0 + c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[r][c + i] = (float)x[i];
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int c = threadIdx.x;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = tile[i][c];
+  uint32_t w[8];
+  const uint32_t code = quant32v(v, w);
+  u32x4* dst = (u32x4*)(q + b * q_bstride + (long)(c0 + c) * ldq + r0);
+  dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+  dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+  scales[b * s_bstride + (long)(c0 + c) * (ldq / 32) + r0 / 32] = (uint8_t)code;
 }
 
 __global__ __launch_bounds__(256) void quantize_rows_kernel(
@@ -76,6 +161,42 @@ hipError_t launch_quantize_mxfp8(const void* src, long rows, long cols,
   hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)((nblk + 255) / 256)),
                      dim3(256), 0, s, (const bf16*)src, nblk, (int)(cols / 32),
                      q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp8_strided(const void* src, long rows,
+                                         long cols, uint8_t* q, long ldq,
+                                         uint8_t* scales, long lds,
+                                         hipStream_t s) {
+  const long nblk = rows * (cols / 32);
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_rows_strided_kernel,
+                     dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s,
+                     (const bf16*)src, nblk, (int)(cols / 32), q, ldq, scales,
+                     lds);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_mxfp8(const uint8_t* q, const uint8_t* scales,
+                                   long rows, long cols, void* out,
+                                   hipStream_t s) {
+  const long nblk = rows * (cols / 32);
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequantize_rows_kernel,
+                     dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s, q,
+                     scales, nblk, (bf16*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp8_cols(const void* src, long batch, int R,
+                                      int C, uint8_t* q, long ldq,
+                                      uint8_t* scales, hipStream_t s) {
+  if (batch == 0 || R == 0 || C == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_cols_kernel,
+                     dim3((unsigned)(C / 64), (unsigned)(R / 32),
+                          (unsigned)batch),
+                     dim3(256), 0, s, (const bf16*)src, R, C, q, ldq,
+                     (long)C * ldq, scales, (long)C * (ldq / 32));
   return hipGetLastError();
 }
 

@@ -42,6 +42,25 @@ def quantize_expert_weights(inp: dict) -> dict:
     return out
 
 
+def quantize_expert_weights_bwd(inp: dict) -> dict:
+    """MXFP8 copies of the routed weights for the backward's transposed
+    products: w2t [E, f, d] (W2^T, blocks along d) and w13t [E, d, 2f]
+    ([W1^T | W3^T], blocks along f), with their E8M0 scales."""
+    w1, w3, w2 = inp["w1"], inp["w3"], inp["w2"]
+    E, f, d = w1.shape
+    dev, u8 = w1.device, torch.uint8
+    out = {"w2t": torch.empty(E, f, d, dtype=u8, device=dev),
+           "w2t_s": torch.empty(E, f, d // 32, dtype=u8, device=dev),
+           "w13t": torch.empty(E, d, 2 * f, dtype=u8, device=dev),
+           "w13t_s": torch.empty(E, d, 2 * f // 32, dtype=u8, device=dev)}
+    B.moe_quantize_mxfp8_t(w2.contiguous(), E, d, f, out["w2t"], out["w2t_s"],
+                           d)
+    for col, w in ((0, w1), (f, w3)):
+        B.moe_quantize_mxfp8_t(w.contiguous(), E, f, d, out["w13t"],
+                               out["w13t_s"], 2 * f, col)
+    return out
+
+
 def alloc_forward(desc: B.MoeDesc, device="cuda", gather=False) -> dict:
     """Every caller-owned forward buffer for ``desc`` plus the workspace.
     MXFP8: x_perm holds E4M3 codes with scales in x_perm_scales, and h
@@ -145,10 +164,18 @@ def bwd_args(inp: dict, fbufs: dict, dy: torch.Tensor, gbufs: dict,
     p = B.ptr
     a.dy = p(dy)
     a.x = p(inp["x"])
-    a.routed = B.expert_weights(inp["w1"], inp["w3"], inp["w2"])
+    mx = inp.get("mx")
+    if mx is not None:  # MXFP8: the forward's MX weights and the backward's
+        a.routed = B.expert_weights(mx["w1"], mx["w3"], mx["w2"], mx["w1_s"],
+                                    mx["w3_s"], mx["w2_s"])
+        bw = inp["mx_bwd"]
+        a.w2t, a.w2t_scales = p(bw["w2t"]), p(bw["w2t_s"])
+        a.w13t, a.w13t_scales = p(bw["w13t"]), p(bw["w13t_s"])
+    else:
+        a.routed = B.expert_weights(inp["w1"], inp["w3"], inp["w2"])
     a.shared = B.expert_weights(inp.get("ws1"), inp.get("ws3"), inp.get("ws2"))
     for k in ("topk_idx", "topk_w", "offsets", "sorted_src", "dest", "x_perm",
-              "h", "y_perm", "act_a", "act_b"):
+              "h", "y_perm", "act_a", "act_b", "x_perm_scales"):
         setattr(a, k, p(fbufs.get(k)))
     for k in ("dx", "dw1", "dw3", "dw2", "d_topk_w", "dws1", "dws3", "dws2"):
         setattr(a, k, p(gbufs.get(k)))

@@ -43,7 +43,7 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.MoeExpertWeights) == 48
     n_ptr_fwd = 4 + 1 + 14 + B.MOE_FWD_NEVENTS
     assert ctypes.sizeof(B.MoeFwdArgs) == 8 * n_ptr_fwd + 2 * 48
-    n_ptr_bwd = 2 + 18 + B.MOE_BWD_NEVENTS
+    n_ptr_bwd = 2 + 18 + 5 + B.MOE_BWD_NEVENTS
     assert ctypes.sizeof(B.MoeBwdArgs) == 8 * n_ptr_bwd + 2 * 48
 
 
@@ -201,3 +201,43 @@ def test_bias_update_and_monitor_validation():
     assert mon(ctypes.byref(d), fake, 0, fake, None) == B.MOE_EINVAL
     assert mon(ctypes.byref(d), None, 4, fake, None) == B.MOE_EINVAL
     assert mon(ctypes.byref(d), fake, 4, None, None) == B.MOE_EINVAL
+
+
+def test_mxfp8_backward_validation():
+    lib = B.load()
+    fake = 0x1000
+    d = B.make_desc(64, 128, 256, 8, 2, mxfp8=True)
+    nb = _ws(d, True)
+    a = B.MoeBwdArgs()
+    for k in ("dy", "x", "topk_idx", "topk_w", "offsets", "sorted_src", "dest",
+              "x_perm", "h", "y_perm", "dx", "dw1", "dw3", "dw2", "d_topk_w",
+              "x_perm_scales", "w2t", "w2t_scales", "w13t", "w13t_scales"):
+        setattr(a, k, fake)
+    a.routed = B.MoeExpertWeights(fake, fake, fake, fake, fake, fake)
+    assert lib.moe_backward(ctypes.byref(d), ctypes.byref(a), fake, 16,
+                            None) == B.MOE_EWORKSPACE
+    a.w13t = None
+    assert lib.moe_backward(ctypes.byref(d), ctypes.byref(a), fake, nb,
+                            None) == B.MOE_EINVAL
+    a.w13t = fake
+    a.act_a = a.act_b = fake  # the MX forward keeps no pre-activations
+    assert lib.moe_backward(ctypes.byref(d), ctypes.byref(a), fake, nb,
+                            None) == B.MOE_EUNSUPPORTED
+    a.act_a = a.act_b = None
+    ds = B.make_desc(64, 128, 256, 8, 2, d_ff_shared=128, mxfp8=True)
+    assert lib.moe_backward(ctypes.byref(ds), ctypes.byref(a), fake,
+                            _ws(ds, True), None) == B.MOE_EUNSUPPORTED
+    # the MX backward's workspace holds the quantised dy_perm and [da | db]
+    assert nb > _ws(B.make_desc(64, 128, 256, 8, 2), True) + 128 * 3 * 256
+
+
+def test_quantize_t_validation():
+    lib = B.load()
+    fake = 0x1000
+    q = lib.moe_quantize_mxfp8_t
+    assert q(None, 2, 64, 128, fake, fake, 64, 0, None) == B.MOE_EINVAL
+    assert q(fake, 2, 64, 128, fake, fake, 96, 64, None) == B.MOE_EINVAL
+    assert q(fake, 2, 48, 128, fake, fake, 64, 0, None) == B.MOE_EUNSUPPORTED
+    assert q(fake, 2, 64, 96, fake, fake, 64, 0, None) == B.MOE_EUNSUPPORTED
+    assert q(fake, 0, 64, 128, None, None, 64, 0, None) == B.MOE_OK
+    assert q(fake, -1, 64, 128, fake, fake, 64, 0, None) == B.MOE_EINVAL
