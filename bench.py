@@ -171,6 +171,8 @@ def main():
     from ragged_grouped_gemm_router_amd import layer as L
 
     cfg = workload(args.workload)
+    if args.mxfp8 and args.backward and cfg.f_shared:
+        ap.error("the MXFP8 backward takes no shared expert")
     dev = "cuda"
     log(f"bench: workload {cfg.name}")
     base = mi.make_inputs(cfg, 0, device=dev)
@@ -197,8 +199,10 @@ def main():
         rev = HipEvents(3 * max(args.steps, 1))
     if args.mxfp8:
         mx = L.quantize_expert_weights(base)
+        mxb = L.quantize_expert_weights_bwd(base) if args.backward else None
         for b in batches:
             b["mx"] = mx
+            b["mx_bwd"] = mxb
         torch.cuda.synchronize()
     bufs = [L.alloc_forward(desc, dev, gather=args.gather) for _ in batches]
     n_steps = args.warmup + args.steps

@@ -89,9 +89,9 @@ typedef struct moe_desc {
   int32_t d_ff_shared;  /* shared expert hidden size, 0 = none [P3 §5]     */
   int32_t gate;         /* MOE_GATE_SOFTMAX | MOE_GATE_SIGMOID             */
   int32_t act_dtype;    /* MOE_F32 | MOE_BF16                              */
-  int32_t gemm_dtype;   /* = act_dtype, or MOE_MXFP8 (forward only, bf16
-                           act, d_model, d_ff and d_ff_shared multiples of
-                           128, no MOE_FLAG_SAVE_ACTS)                     */
+  int32_t gemm_dtype;   /* = act_dtype, or MOE_MXFP8 (bf16 act; d_model,
+                           d_ff and d_ff_shared multiples of 128; the
+                           backward without a shared expert)              */
   int32_t flags;        /* MOE_FLAG_*                                      */
 } moe_desc;
 
@@ -278,13 +278,14 @@ moe_status moe_forward(const moe_desc* desc, const moe_fwd_args* args,
  * scaled MFMA with both operands MX-quantised along their contraction:
  *   dh = Q(dy_perm) . w2t  (dy_perm = w * dy in bf16, blocks along d_model)
  *   dx_perm = Q([da | db]) . w13t  (da, db in bf16, blocks along d_ff)
- * with a, b recomputed by the MX GEMM 1 from the forward's x_perm codes;
+ * with a, b saved by the forward (MOE_FLAG_SAVE_ACTS: the MX GEMM 1 keeps
+ * its fp32 accumulators in bf16) or else recomputed by it from x_perm;
  * the weight gradients are bf16 products of the operands the forward
  * multiplied: dW2 = dy_perm^T h, dW1 = da^T x_perm, dW3 = db^T x_perm with
  * h and x_perm dequantised from the forward's MX codes (exact in bf16).
- * Needs x_perm_scales, w2t, w13t and their scales, the routed MX weights
- * with scales, no saved activations; a shared expert is
- * MOE_EUNSUPPORTED on this path. */
+ * Needs x_perm_scales, w2t, w13t and their scales and the routed MX
+ * weights with scales; a shared expert is MOE_EUNSUPPORTED on this
+ * path. */
 moe_status moe_backward(const moe_desc* desc, const moe_bwd_args* args,
                         void* ws, size_t ws_bytes, void* stream);
 

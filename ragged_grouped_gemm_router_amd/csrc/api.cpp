@@ -37,11 +37,9 @@ moe_status check_desc(const moe_desc* d) {
     return MOE_EINVAL;
   if (d->d_model % 8 || d->d_ff % 8 || d->d_ff_shared % 8) return MOE_EUNSUPPORTED;
   if (d->gemm_dtype == MOE_MXFP8) {
-    // whole 128-element k-tiles for every GEMM; no saved pre-activations
-    // on this path
+    // whole 128-element k-tiles for every GEMM
     if (d->d_model % 128 || d->d_ff % 128 || d->d_ff_shared % 128)
       return MOE_EUNSUPPORTED;
-    if (d->flags & MOE_FLAG_SAVE_ACTS) return MOE_EUNSUPPORTED;
   }
   if ((long)d->T * d->K > kMaxCopies) return MOE_EUNSUPPORTED;
   return MOE_OK;
@@ -260,7 +258,8 @@ hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
                          const moe_expert_weights* rw, const void* x_shared,
                          const moe_expert_weights* sw, void* h, void* y_perm,
                          void* y_shared, const FwdWs& ws, hipStream_t s,
-                         void* ev_mid, const int32_t* gsrc = nullptr) {
+                         void* ev_mid, const int32_t* gsrc = nullptr,
+                         void* act_a = nullptr, void* act_b = nullptr) {
   const int TK = d->T * d->K, dm = d->d_model, f = d->d_ff;
   uint8_t* hq = (uint8_t*)h;
   uint8_t* hs = hq + (size_t)TK * f;
@@ -273,6 +272,7 @@ hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
   p.Bs = rw->w1_scales; p.B2s = rw->w3_scales;
   p.ld_s = dm / 32; p.sBs = (long)f * (dm / 32);
   p.C = hq; p.C2 = hs; p.ldc = f;
+  p.Sa = act_a; p.Sb = act_b;
   hipError_t e = gemm_mfma(kOpGemm1Mx, p, ws.tile_off, s);
   if (e != hipSuccess) return e;
   record(ev_mid, s);
@@ -361,7 +361,12 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
                              w.dy_perm, a->d_topk_w, d->T, d->K, dm, s));
   MOE_TRY(launch_quantize_mxfp8(w.dy_perm, TK, dm, w.dyq, w.dys, s));
   record(a->events[1], s);
-  {  // a, b of the forward: GEMM 1 again on its MX operands, kept in bf16
+  // a, b of the forward: saved, or GEMM 1 again on its MX operands (bf16)
+  const void* sa = a->act_a;
+  const void* sb = a->act_b;
+  if (!sa) {
+    sa = w.da;
+    sb = w.db;
     GemmParams p = gp();
     p.M = TK; p.N = f; p.K = dm; p.G = E; p.off = a->offsets;
     p.A = a->x_perm; p.lda = dm; p.As = a->x_perm_scales;
@@ -379,7 +384,7 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.B = a->w2t; p.ldb = dm; p.sB = (long)f * dm;
     p.Bs = a->w2t_scales; p.ld_s = dm / 32; p.sBs = (long)f * (dm / 32);
     p.C = w.da; p.C2 = w.db; p.ldc = f;
-    p.aux_a = w.da; p.aux_b = w.db;
+    p.aux_a = sa; p.aux_b = sb;
     MOE_TRY(gemm_mfma(kOpDgrad2Mx, p, w.tile_off, s));
     // [da | db] quantised along d_ff, side by side
     MOE_TRY(launch_quantize_mxfp8_strided(w.da, TK, f, w.dgq, 2L * f, w.dgs,
@@ -756,7 +761,8 @@ moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
   if (mx)
     e = do_experts_mx(d, a->x_perm, a->x_perm_scales, a->offsets, &a->routed,
                       shared ? a->x : nullptr, &a->shared, a->h, a->y_perm,
-                      a->y_shared, w, s, a->events[3], gsrc);
+                      a->y_shared, w, s, a->events[3], gsrc,
+                      save ? a->act_a : nullptr, save ? a->act_b : nullptr);
   else
     e = do_experts(d, gather ? a->x : a->x_perm, a->offsets, &a->routed,
                    shared ? a->x : nullptr, &a->shared, a->h, a->y_perm,
@@ -783,7 +789,7 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     return MOE_EINVAL;
   if ((a->act_a == nullptr) != (a->act_b == nullptr)) return MOE_EINVAL;
   if (d->gemm_dtype == MOE_MXFP8) {
-    if (d->d_ff_shared > 0 || a->act_a) return MOE_EUNSUPPORTED;
+    if (d->d_ff_shared > 0) return MOE_EUNSUPPORTED;
     if (!a->x_perm_scales || !a->w2t || !a->w2t_scales || !a->w13t ||
         !a->w13t_scales || !a->routed.w1_scales || !a->routed.w3_scales)
       return MOE_EINVAL;

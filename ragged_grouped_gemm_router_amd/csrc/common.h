@@ -91,6 +91,8 @@ struct GemmParams {
   // gathered A rows (direct-to-LDS GEMM 1 only): row i of A (and of As)
   // is row gsrc[i] / gdiv of the A given, e.g. token t of copy j = t*K+k
   const int32_t* gsrc; int gdiv;
+  // kEpiSwigluMx: optional bf16 copies of the pre-activations (ld = ldc)
+  void* Sa; void* Sb;
 };
 
 }  // namespace moe

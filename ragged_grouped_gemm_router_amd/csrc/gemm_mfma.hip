@@ -497,12 +497,11 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
                 "power-of-two stage count, even substep count");
   static_assert((S - 1) * (A_INS + (DUAL ? 2 : 1) * B_INS) <= 63, "vmcnt range");
 
-  // the epilogue stages 128 rows at a time (all but the quantising one)
+  // the epilogue stages 128 rows at a time (the quantising one only for
+  // the optional pre-activation copies)
   constexpr int kEpiRows = BM > 128 ? 128 : BM;
   constexpr int EPI_BYTES =
-      EPI == kEpiSwigluMx
-          ? 0
-          : StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>::BYTES;
+      StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>::BYTES;
   __shared__ __attribute__((aligned(1024))) char lds[S * STAGE > EPI_BYTES ? S * STAGE : EPI_BYTES];
 
   Tile t;
@@ -760,12 +759,27 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   }
 #undef MOE_FENCE
   __builtin_amdgcn_s_waitcnt(0);  // no load may still target LDS at exit
+  // through LDS in 16-byte row pieces: the output (SwiGLU of the two
+  // accumulators, or the plain product), then any saved pre-activations
+  using SO = StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>;
   if constexpr (EPI == kEpiSwigluMx) {
     epilogue_swiglu_mx<WM, WN, MB, NB>(p, t, acc, wm, wn, lane);
+    auto put_bf16 = [&](void* dst) {
+      return [=](int row, int col, const float* v) {
+        const int grow = t.m0 + row, gcol = t.n0 + col;
+        if (grow >= t.m_end || gcol >= p.N) return;
+        *(bf16x8*)((bf16*)dst + (long)grow * p.ldc + gcol) = pack8(v);
+      };
+    };
+    if (p.Sa)
+      SO::run(lds, wm, wn, lane,
+              [&](int i, int j, int r) { return acc[0][i][j][r]; },
+              put_bf16(p.Sa));
+    if (p.Sb)
+      SO::run(lds, wm, wn, lane,
+              [&](int i, int j, int r) { return acc[NB_OPS - 1][i][j][r]; },
+              put_bf16(p.Sb));
   } else {
-    // through LDS in 16-byte row pieces: the output (SwiGLU of the two
-    // accumulators, or the plain product), then any saved pre-activations
-    using SO = StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>;
     auto put = [&](TO* dst) {
       return [=](int row, int col, const float* v) {
         const int grow = t.m0 + row, gcol = t.n0 + col;

@@ -78,8 +78,7 @@ def test_workspace_size_host_only():
     (dict(gemm_dtype=B.MOE_F32), B.MOE_EINVAL),             # bf16 act, f32 gemm
     (dict(gemm_dtype=B.MOE_MXFP8, d_model=160), B.MOE_EUNSUPPORTED),
     (dict(gemm_dtype=B.MOE_MXFP8, d_ff_shared=96), B.MOE_EUNSUPPORTED),
-    (dict(gemm_dtype=B.MOE_MXFP8, flags=B.MOE_FLAG_SAVE_ACTS),
-     B.MOE_EUNSUPPORTED),
+    (dict(gemm_dtype=B.MOE_MXFP8, act_dtype=B.MOE_F32), B.MOE_EINVAL),
 ])
 def test_bad_descriptor(fields, code):
     d = B.make_desc(64, 128, 256, 8, 2)
@@ -220,10 +219,10 @@ def test_mxfp8_backward_validation():
     assert lib.moe_backward(ctypes.byref(d), ctypes.byref(a), fake, nb,
                             None) == B.MOE_EINVAL
     a.w13t = fake
-    a.act_a = a.act_b = fake  # the MX forward keeps no pre-activations
+    a.act_a = fake  # saved pre-activations come in pairs
     assert lib.moe_backward(ctypes.byref(d), ctypes.byref(a), fake, nb,
-                            None) == B.MOE_EUNSUPPORTED
-    a.act_a = a.act_b = None
+                            None) == B.MOE_EINVAL
+    a.act_a = None
     ds = B.make_desc(64, 128, 256, 8, 2, d_ff_shared=128, mxfp8=True)
     assert lib.moe_backward(ctypes.byref(ds), ctypes.byref(a), fake,
                             _ws(ds, True), None) == B.MOE_EUNSUPPORTED

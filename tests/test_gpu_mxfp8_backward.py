@@ -44,9 +44,9 @@ def test_transposing_quantiser_exact():
         assert (q[e, :, :col] == 0).all() and (sc[e, :, :col // 32] == 0).all()
 
 
-def _mx_train(cfg, ginp):
+def _mx_train(cfg, ginp, save_acts=False):
     desc = B.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.K, 0, gate=cfg.gate,
-                       mxfp8=True)
+                       mxfp8=True, save_acts=save_acts)
     ginp = dict(ginp)
     ginp["mx"] = L.quantize_expert_weights(ginp)
     ginp["mx_bwd"] = L.quantize_expert_weights_bwd(ginp)
@@ -58,10 +58,12 @@ def _mx_train(cfg, ginp):
     return fb, gb
 
 
+@pytest.mark.parametrize("save_acts", [False, True],
+                         ids=["recompute", "saved"])
 @pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
-def test_mxfp8_backward_parity(cfg):
+def test_mxfp8_backward_parity(cfg, save_acts):
     cinp, ginp = inputs(cfg, seed=6, with_dy=True)
-    fb, gb = _mx_train(cfg, ginp)
+    fb, gb = _mx_train(cfg, ginp, save_acts)
     idx, w, counts, *_ = check_routing_exact(cfg, cinp, fb)
     ref = oracle.backward_mxfp8(cinp["x"], cinp["w1"], cinp["w3"], cinp["w2"],
                                 idx, w, cinp["dy"])
@@ -82,7 +84,7 @@ def test_mxfp8_backward_full_size_sampled():
     tokens, dW1/dW3 rows and dW2 columns on sampled hidden units."""
     cfg = mi.MIXTRAL_TRAIN
     ginp = mi.make_inputs(cfg, 0, device=DEV, with_dy=True)
-    fb, gb = _mx_train(cfg, ginp)
+    fb, gb = _mx_train(cfg, ginp, save_acts=True)
     idx, w, *_ = check_routing_exact(cfg, {"logits_in": None, "bias": None},
                                      fb)
     g = torch.Generator().manual_seed(1)
@@ -100,3 +102,16 @@ def test_mxfp8_backward_full_size_sampled():
         assert rel_err(gb["dw1"][e, j], ref["dw1_rows"][i]) <= MX_TOL, (e, j)
         assert rel_err(gb["dw3"][e, j], ref["dw3_rows"][i]) <= MX_TOL, (e, j)
         assert rel_err(gb["dw2"][e, :, j], ref["dw2_cols"][i]) <= MX_TOL, (e, j)
+
+
+def test_mxfp8_saved_acts_match_recompute():
+    """The pre-activations the MX forward saves are the ones the backward
+    recomputes: both backward paths give identical gradients, and the
+    forward's output does not change when it saves them."""
+    cfg = CASES[0]
+    _, ginp = inputs(cfg, seed=7, with_dy=True)
+    fr, gr = _mx_train(cfg, ginp, False)
+    fs, gs = _mx_train(cfg, ginp, True)
+    assert torch.equal(fr["out"], fs["out"])
+    for k in ("dx", "dw1", "dw3", "dw2", "d_topk_w"):
+        assert torch.equal(gr[k], gs[k]), k
