@@ -34,6 +34,13 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return (b % kNumXcd) * (n / kNumXcd) + b / kNumXcd;
 }
 
+// The same for any n: a bijection of [0, n) that hands each XCD a
+// contiguous range of logical indices whose sizes differ by at most one.
+__device__ __forceinline__ int xcd_remap_n(int b, int n) {
+  const int x = b % kNumXcd, q = n / kNumXcd, r = n % kNumXcd;
+  return x * q + (x < r ? x : r) + b / kNumXcd;
+}
+
 // Largest g in [0, G) with pre[g] <= v (pre is non-decreasing, pre[0] = 0).
 __device__ __forceinline__ int upper_group(const int32_t* pre, int G, int v) {
   int lo = 0, hi = G - 1;

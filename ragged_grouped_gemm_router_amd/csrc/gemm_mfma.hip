@@ -166,33 +166,40 @@ struct Tile {
 
 // Decode this workgroup's output tile. Returns false for surplus
 // workgroups (beyond the device-side tile count).
+//
+// Row-grouped products: the grid is sized by an upper bound, and the real
+// row tiles (mt, from the device tile prefix) are enumerated densely in
+// n-group-major order (GN column tiles, every row tile of every group,
+// then the GN column tiles within), so that consecutive tiles share weight
+// and row panels. The first mt * tiles_n workgroups take them, each XCD a
+// contiguous share of equal size; the rest exit.
 template <int BM, int BN, int SCHED>
 __device__ __forceinline__ bool lookup_tile(const GemmParams& p, Tile& t) {
   const int tiles_n = (p.N + BN - 1) / BN;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
   t.g = 0;
   t.k_beg = 0;
   t.k_end = p.K;
   if (SCHED == kSchedM) {
+    const int mt = p.off ? p.tile_off[p.G] : (p.M + BM - 1) / BM;
+    const int n_tiles = mt * tiles_n;
+    if ((int)blockIdx.x >= n_tiles) return false;
+    const int idx = xcd_remap_n(blockIdx.x, n_tiles);
     const int GN = p.group_n;
-    const int MT = p.tiles_m_max;
-    const int ng = L / (MT * GN);
-    const int within = L % (MT * GN);
+    const int ng = idx / (mt * GN), within = idx % (mt * GN);
     const int gsz = min(GN, tiles_n - ng * GN);
-    if (gsz <= 0 || within >= MT * gsz) return false;
-    const int mt = within / gsz;
+    const int m = within / gsz;
     t.n0 = (ng * GN + within % gsz) * BN;
     if (p.off == nullptr) {
-      t.m0 = mt * BM;
+      t.m0 = m * BM;
       t.m_end = p.M;
-      return t.m0 < t.m_end;
+      return true;
     }
-    if (mt >= p.tile_off[p.G]) return false;
-    t.g = upper_group(p.tile_off, p.G, mt);
-    t.m0 = p.off[t.g] + (mt - p.tile_off[t.g]) * BM;
+    t.g = upper_group(p.tile_off, p.G, m);
+    t.m0 = p.off[t.g] + (m - p.tile_off[t.g]) * BM;
     t.m_end = p.off[t.g + 1];
     return true;
   }
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int tiles_m = (p.M + BM - 1) / BM;
   if (L >= p.G * tiles_m * tiles_n) return false;
   t.g = L / (tiles_m * tiles_n);
