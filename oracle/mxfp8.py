@@ -175,10 +175,28 @@ def _mx_bwd_ops(quant: bool):
     return (lambda v: mx_roundtrip(_f64(v))), mx_roundtrip_cols, _bf16r
 
 
-def backward_mxfp8(x, w1, w3, w2, idx, w, dy, quant: bool = True) -> dict:
+def _mx_ffn_bwd(X, W1, W3, W2, g, Q, Qc, R):
+    """One SwiGLU FFN's MXFP8 backward over rows X (already quantised) with
+    output gradient g (held in bf16): (dX, dW1, dW3, dW2, Y)."""
+    a = X @ Q(W1).T
+    b = X @ Q(W3).T
+    hq = Q(swiglu(a, b))
+    Y = hq @ Q(W2).T
+    dh = Q(g) @ Qc(W2)
+    a, b = R(a), R(b)
+    sg = torch.sigmoid(a)
+    da = R(dh * b * sg * (1.0 + a * (1.0 - sg)))
+    db = R(dh * a * sg)
+    dX = Q(da) @ Qc(W1) + Q(db) @ Qc(W3)
+    return dX, da.T @ X, db.T @ X, g.T @ hq, Y
+
+
+def backward_mxfp8(x, w1, w3, w2, idx, w, dy, ws1=None, ws3=None, ws2=None,
+                   quant: bool = True) -> dict:
     """Gradients of sum(dy * forward_mxfp8(...)) under the reading above,
     routing fixed and the gate weights as leaves; experts with no token
-    get dW = 0."""
+    get dW = 0. With a shared expert (ws1, ws3, ws2) it is one more FFN over
+    every token, ungated (g = dy), added into dx."""
     Q, Qc, R = _mx_bwd_ops(quant)
     T, d = x.shape
     E, f, _ = w1.shape
@@ -193,23 +211,17 @@ def backward_mxfp8(x, w1, w3, w2, idx, w, dy, quant: bool = True) -> dict:
         if not bool(mask.any()):
             continue
         rows, ks = mask.nonzero(as_tuple=True)
-        X = Q(x64[rows])
-        a = X @ Q(w1[e]).T
-        b = X @ Q(w3[e]).T
-        hq = Q(swiglu(a, b))
-        Y = hq @ Q(w2[e]).T
-        d_w[rows, ks] = (dy64[rows] * Y).sum(dim=1)
         g = R(dy64[rows] * w64[rows, ks].unsqueeze(-1))
-        dh = Q(g) @ Qc(w2[e])
-        a, b = R(a), R(b)
-        sg = torch.sigmoid(a)
-        da = R(dh * b * sg * (1.0 + a * (1.0 - sg)))
-        db = R(dh * a * sg)
-        dx.index_add_(0, rows, Q(da) @ Qc(w1[e]) + Q(db) @ Qc(w3[e]))
-        dw2[e] = g.T @ hq
-        dw1[e] = da.T @ X
-        dw3[e] = db.T @ X
-    return {"dx": dx, "dw1": dw1, "dw3": dw3, "dw2": dw2, "d_w": d_w}
+        dX, dw1[e], dw3[e], dw2[e], Y = _mx_ffn_bwd(
+            Q(x64[rows]), w1[e], w3[e], w2[e], g, Q, Qc, R)
+        d_w[rows, ks] = (dy64[rows] * Y).sum(dim=1)
+        dx.index_add_(0, rows, dX)
+    res = {"dx": dx, "dw1": dw1, "dw3": dw3, "dw2": dw2, "d_w": d_w}
+    if ws1 is not None:
+        dX, res["dws1"], res["dws3"], res["dws2"], _ = _mx_ffn_bwd(
+            Q(x64), ws1, ws3, ws2, R(dy64), Q, Qc, R)
+        dx += dX
+    return res
 
 
 def backward_mxfp8_sampled(x, w1, w3, w2, idx, w, dy, tokens, cols) -> dict:

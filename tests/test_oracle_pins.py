@@ -669,3 +669,24 @@ def test_mx_backward_sampled_matches_full_and_is_near_exact():
     for k in ("dx", "dw1", "dw3", "dw2", "d_w"):
         err = (full[k] - exact[k]).abs().max() / exact[k].abs().max()
         assert 0 < err < 0.3, (k, float(err))
+
+
+def test_mx_backward_shared_expert_reduces():
+    """With identity quantisers the shared expert's MXFP8 backward is the
+    exact shared-expert backward; a zero shared expert adds nothing."""
+    x, w1, w3, w2, idx, w, dy = _mx_bwd_case(34, f=64)
+    g = torch.Generator().manual_seed(35)
+    d, fs = x.shape[1], 96
+    ws1 = torch.randn(fs, d, generator=g, dtype=torch.float64) / d ** 0.5
+    ws3 = torch.randn(fs, d, generator=g, dtype=torch.float64) / d ** 0.5
+    ws2 = torch.randn(d, fs, generator=g, dtype=torch.float64) / fs ** 0.5
+    got = oracle.backward_mxfp8(x, w1, w3, w2, idx, w, dy, ws1, ws3, ws2,
+                                quant=False)
+    ref = oracle.backward(x, w1, w3, w2, idx, w, dy, ws1, ws3, ws2)
+    for k in ("dx", "dw1", "dw3", "dw2", "d_w", "dws1", "dws3", "dws2"):
+        assert torch.allclose(got[k], ref[k], rtol=0, atol=1e-12), k
+    z = torch.zeros_like
+    with_zero = oracle.backward_mxfp8(x, w1, w3, w2, idx, w, dy, z(ws1),
+                                      z(ws3), z(ws2))
+    without = oracle.backward_mxfp8(x, w1, w3, w2, idx, w, dy)
+    assert torch.equal(with_zero["dx"], without["dx"])
