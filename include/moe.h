@@ -90,8 +90,7 @@ typedef struct moe_desc {
   int32_t gate;         /* MOE_GATE_SOFTMAX | MOE_GATE_SIGMOID             */
   int32_t act_dtype;    /* MOE_F32 | MOE_BF16                              */
   int32_t gemm_dtype;   /* = act_dtype, or MOE_MXFP8 (bf16 act; d_model,
-                           d_ff and d_ff_shared multiples of 128; the
-                           backward without a shared expert)              */
+                           d_ff and d_ff_shared multiples of 128)         */
   int32_t flags;        /* MOE_FLAG_*                                      */
 } moe_desc;
 
@@ -189,6 +188,13 @@ typedef struct moe_bwd_args {
   const uint8_t* w13t;        /* [E, d_model, 2*d_ff] E4M3: [W1^T | W3^T],
                                  blocks along d_ff                          */
   const uint8_t* w13t_scales; /* [E, d_model, 2*d_ff/32]                     */
+  /* the same for the shared expert (MXFP8 with d_ff_shared > 0): shared
+     holds its forward MX weights; ws2t [d_ff_shared, d_model],
+     ws13t [d_model, 2*d_ff_shared], as w2t and w13t with E = 1 */
+  const uint8_t* ws2t;
+  const uint8_t* ws2t_scales;
+  const uint8_t* ws13t;
+  const uint8_t* ws13t_scales;
   void* events[MOE_BWD_NEVENTS]; /* optional hipEvent_t stage boundaries     */
 } moe_bwd_args;
 
@@ -284,8 +290,10 @@ moe_status moe_forward(const moe_desc* desc, const moe_fwd_args* args,
  * multiplied: dW2 = dy_perm^T h, dW1 = da^T x_perm, dW3 = db^T x_perm with
  * h and x_perm dequantised from the forward's MX codes (exact in bf16).
  * Needs x_perm_scales, w2t, w13t and their scales and the routed MX
- * weights with scales; a shared expert is MOE_EUNSUPPORTED on this
- * path. */
+ * weights with scales. A shared expert runs the same way as one dense
+ * group over every token (dy ungated; x and dy quantised into the
+ * workspace; its a, b and MX h recomputed by the MX GEMM 1) and needs the
+ * shared MX weights and ws2t, ws13t with their scales. */
 moe_status moe_backward(const moe_desc* desc, const moe_bwd_args* args,
                         void* ws, size_t ws_bytes, void* stream);
 

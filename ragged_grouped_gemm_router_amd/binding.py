@@ -75,7 +75,9 @@ class MoeBwdArgs(ctypes.Structure):
         ("dws1", c_void_p), ("dws3", c_void_p), ("dws2", c_void_p),
         ("x_perm_scales", c_void_p), ("w2t", c_void_p),
         ("w2t_scales", c_void_p), ("w13t", c_void_p),
-        ("w13t_scales", c_void_p),
+        ("w13t_scales", c_void_p), ("ws2t", c_void_p),
+        ("ws2t_scales", c_void_p), ("ws13t", c_void_p),
+        ("ws13t_scales", c_void_p),
         ("events", c_void_p * MOE_BWD_NEVENTS)]
 
 

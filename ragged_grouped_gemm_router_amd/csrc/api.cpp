@@ -73,6 +73,17 @@ struct BwdWs {
   uint8_t* dgq;
   uint8_t* dgs;
   void* h_bf;
+  // MXFP8 shared expert: x and dy quantised, its h (codes, scales) and
+  // [da | db] quantised, x dequantised for its weight gradients
+  uint8_t* sxq;
+  uint8_t* sxs;
+  uint8_t* sdyq;
+  uint8_t* sdys;
+  uint8_t* shq;
+  uint8_t* shs;
+  uint8_t* sdgq;
+  uint8_t* sdgs;
+  void* sx_bf;
 };
 
 size_t fwd_ws_layout(const moe_desc* d, char* base, FwdWs* w) {
@@ -138,6 +149,21 @@ size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
     }
     if (w) w->h_bf = base + o;
     o = align_up(o + b * TK * f);
+    if (d->d_ff_shared > 0) {
+      const size_t T = d->T, fs = d->d_ff_shared;
+      uint8_t** q[8] = {w ? &w->sxq : nullptr,  w ? &w->sxs : nullptr,
+                        w ? &w->sdyq : nullptr, w ? &w->sdys : nullptr,
+                        w ? &w->shq : nullptr,  w ? &w->shs : nullptr,
+                        w ? &w->sdgq : nullptr, w ? &w->sdgs : nullptr};
+      const size_t m[8] = {T * dm, T * dm / 32, T * dm, T * dm / 32,
+                           T * fs, T * fs / 32, T * 2 * fs, T * 2 * fs / 32};
+      for (int i = 0; i < 8; ++i) {
+        if (q[i]) *q[i] = (uint8_t*)(base + o);
+        o = align_up(o + m[i]);
+      }
+      if (w) w->sx_bf = base + o;
+      o = align_up(o + b * T * dm);
+    }
   }
   return o;
 }
@@ -360,6 +386,12 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
   MOE_TRY(launch_combine_bwd(MOE_BF16, a->dy, a->y_perm, a->dest, a->topk_w,
                              w.dy_perm, a->d_topk_w, d->T, d->K, dm, s));
   MOE_TRY(launch_quantize_mxfp8(w.dy_perm, TK, dm, w.dyq, w.dys, s));
+  const bool shared = d->d_ff_shared > 0;
+  const int T = d->T, fs = d->d_ff_shared;
+  if (shared) {  // x and the (ungated) dy of the shared expert, quantised
+    MOE_TRY(launch_quantize_mxfp8(a->x, T, dm, w.sxq, w.sxs, s));
+    MOE_TRY(launch_quantize_mxfp8(a->dy, T, dm, w.sdyq, w.sdys, s));
+  }
   record(a->events[1], s);
   // a, b of the forward: saved, or GEMM 1 again on its MX operands (bf16)
   const void* sa = a->act_a;
@@ -375,6 +407,17 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.ld_s = dm / 32; p.sBs = (long)f * (dm / 32);
     p.C = nullptr; p.C2 = w.da; p.C3 = w.db; p.ldc = f;
     MOE_TRY(gemm_mfma(kOpGemm1MxAct, p, w.tile_off, s));
+  }
+  if (shared) {  // its a, b (bf16) and MX h, as the forward made them
+    MOE_TRY(launch_split(T, 1, w.srange, s));
+    GemmParams p = gp();
+    p.M = T; p.N = fs; p.K = dm;
+    p.A = w.sxq; p.lda = dm; p.As = w.sxs;
+    p.B = a->shared.w1; p.B2 = a->shared.w3; p.ldb = dm;
+    p.Bs = a->shared.w1_scales; p.B2s = a->shared.w3_scales; p.ld_s = dm / 32;
+    p.C = w.shq; p.C2 = w.shs; p.ldc = fs;
+    p.Sa = w.sa; p.Sb = w.sb;
+    MOE_TRY(gemm_mfma(kOpGemm1Mx, p, w.tile_off, s));
   }
   record(a->events[2], s);
   {  // dh = Q(dy_perm) W2t_e, then (da, db) in place of (a, b)
@@ -392,6 +435,19 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     MOE_TRY(launch_quantize_mxfp8_strided(w.db, TK, f, w.dgq + f, 2L * f,
                                           w.dgs + f / 32, 2L * f / 32, s));
   }
+  if (shared) {  // dh_s = Q(dy) Ws2t, (da_s, db_s) in place, quantised
+    GemmParams p = gp();
+    p.M = T; p.N = fs; p.K = dm;
+    p.A = w.sdyq; p.lda = dm; p.As = w.sdys;
+    p.B = a->ws2t; p.ldb = dm; p.Bs = a->ws2t_scales; p.ld_s = dm / 32;
+    p.C = w.sa; p.C2 = w.sb; p.ldc = fs;
+    p.aux_a = w.sa; p.aux_b = w.sb;
+    MOE_TRY(gemm_mfma(kOpDgrad2Mx, p, w.tile_off, s));
+    MOE_TRY(launch_quantize_mxfp8_strided(w.sa, T, fs, w.sdgq, 2L * fs, w.sdgs,
+                                          2L * fs / 32, s));
+    MOE_TRY(launch_quantize_mxfp8_strided(w.sb, T, fs, w.sdgq + fs, 2L * fs,
+                                          w.sdgs + fs / 32, 2L * fs / 32, s));
+  }
   record(a->events[3], s);
   {  // dx_perm = Q([da | db]) W13t_e
     GemmParams p = gp();
@@ -402,9 +458,17 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.C = w.dx_perm; p.ldc = dm;
     MOE_TRY(gemm_mfma(kOpGemm2Mx, p, w.tile_off, s));
   }
+  if (shared) {  // dx_s = Q([da_s | db_s]) Ws13t
+    GemmParams p = gp();
+    p.M = T; p.N = dm; p.K = 2 * fs;
+    p.A = w.sdgq; p.lda = 2 * fs; p.As = w.sdgs;
+    p.B = a->ws13t; p.ldb = 2 * fs; p.Bs = a->ws13t_scales; p.ld_s = 2 * fs / 32;
+    p.C = w.sdx; p.ldc = dm;
+    MOE_TRY(gemm_mfma(kOpGemm2Mx, p, w.tile_off, s));
+  }
   record(a->events[4], s);
-  MOE_TRY(launch_combine(MOE_BF16, w.dx_perm, a->dest, nullptr, nullptr,
-                         a->dx, d->T, d->K, dm, s));
+  MOE_TRY(launch_combine(MOE_BF16, w.dx_perm, a->dest, nullptr,
+                         shared ? w.sdx : nullptr, a->dx, d->T, d->K, dm, s));
   record(a->events[5], s);
   {  // dW2_e = dy_perm^T h, h dequantised from the forward's codes
     const uint8_t* hq = (const uint8_t*)a->h;
@@ -414,6 +478,16 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.A = w.dy_perm; p.lda = dm;
     p.B = w.h_bf; p.ldb = f;
     p.C = a->dw2; p.ldc = f; p.sC = (long)dm * f;
+    MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
+  }
+  if (shared) {  // dWs2 = dy^T h_s, h_s dequantised; x dequantised too
+    MOE_TRY(launch_dequantize_mxfp8(w.shq, w.shs, T, fs, w.sh, s));
+    MOE_TRY(launch_dequantize_mxfp8(w.sxq, w.sxs, T, dm, w.sx_bf, s));
+    GemmParams p = gp();
+    p.M = dm; p.N = fs; p.G = 1; p.off = w.srange;
+    p.A = a->dy; p.lda = dm;
+    p.B = w.sh; p.ldb = fs;
+    p.C = a->dws2; p.ldc = fs;
     MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
   }
   record(a->events[6], s);
@@ -428,6 +502,14 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.B = w.dx_perm; p.ldb = dm;
     p.C = which ? a->dw3 : a->dw1; p.ldc = dm; p.sC = (long)f * dm;
     MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
+    if (shared) {  // dWs1 = da_s^T x, dWs3 = db_s^T x (x as quantised)
+      GemmParams q = gp();
+      q.M = fs; q.N = dm; q.G = 1; q.off = w.srange;
+      q.A = which ? w.sb : w.sa; q.lda = fs;
+      q.B = w.sx_bf; q.ldb = dm;
+      q.C = which ? a->dws3 : a->dws1; q.ldc = dm;
+      MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, q, w.tile_off, s));
+    }
   }
   record(a->events[7], s);
 #undef MOE_TRY
@@ -789,9 +871,12 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     return MOE_EINVAL;
   if ((a->act_a == nullptr) != (a->act_b == nullptr)) return MOE_EINVAL;
   if (d->gemm_dtype == MOE_MXFP8) {
-    if (d->d_ff_shared > 0) return MOE_EUNSUPPORTED;
     if (!a->x_perm_scales || !a->w2t || !a->w2t_scales || !a->w13t ||
         !a->w13t_scales || !a->routed.w1_scales || !a->routed.w3_scales)
+      return MOE_EINVAL;
+    if (d->d_ff_shared > 0 &&
+        (!mx_weights_ok(&a->shared) || !a->dws1 || !a->dws3 || !a->dws2 ||
+         !a->ws2t || !a->ws2t_scales || !a->ws13t || !a->ws13t_scales))
       return MOE_EINVAL;
     if (ws_bytes < bwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
     return hip_status(do_backward_mx(d, a, ws, (hipStream_t)stream));

@@ -42,22 +42,38 @@ def quantize_expert_weights(inp: dict) -> dict:
     return out
 
 
-def quantize_expert_weights_bwd(inp: dict) -> dict:
-    """MXFP8 copies of the routed weights for the backward's transposed
-    products: w2t [E, f, d] (W2^T, blocks along d) and w13t [E, d, 2f]
-    ([W1^T | W3^T], blocks along f), with their E8M0 scales."""
-    w1, w3, w2 = inp["w1"], inp["w3"], inp["w2"]
+def _quantize_t(w1, w3, w2):
+    """w2t [E, f, d] (W2^T, blocks along d) and w13t [E, d, 2f]
+    ([W1^T | W3^T], blocks along f) with their E8M0 scales."""
     E, f, d = w1.shape
     dev, u8 = w1.device, torch.uint8
-    out = {"w2t": torch.empty(E, f, d, dtype=u8, device=dev),
-           "w2t_s": torch.empty(E, f, d // 32, dtype=u8, device=dev),
-           "w13t": torch.empty(E, d, 2 * f, dtype=u8, device=dev),
-           "w13t_s": torch.empty(E, d, 2 * f // 32, dtype=u8, device=dev)}
-    B.moe_quantize_mxfp8_t(w2.contiguous(), E, d, f, out["w2t"], out["w2t_s"],
-                           d)
+    w2t = torch.empty(E, f, d, dtype=u8, device=dev)
+    w2t_s = torch.empty(E, f, d // 32, dtype=u8, device=dev)
+    w13t = torch.empty(E, d, 2 * f, dtype=u8, device=dev)
+    w13t_s = torch.empty(E, d, 2 * f // 32, dtype=u8, device=dev)
+    B.moe_quantize_mxfp8_t(w2.contiguous(), E, d, f, w2t, w2t_s, d)
     for col, w in ((0, w1), (f, w3)):
-        B.moe_quantize_mxfp8_t(w.contiguous(), E, f, d, out["w13t"],
-                               out["w13t_s"], 2 * f, col)
+        B.moe_quantize_mxfp8_t(w.contiguous(), E, f, d, w13t, w13t_s, 2 * f,
+                               col)
+    return w2t, w2t_s, w13t, w13t_s
+
+
+def quantize_expert_weights_bwd(inp: dict) -> dict:
+    """MXFP8 copies of the weights for the backward's transposed products:
+    w2t, w13t (routed) and, with a shared expert, ws2t, ws13t (E = 1), each
+    with its E8M0 scales (key + "_s")."""
+    out = {}
+    keys = [("", "w1", "w3", "w2"), ("s", "ws1", "ws3", "ws2")]
+    for tag, k1, k3, k2 in keys:
+        if inp.get(k1) is None:
+            continue
+        w1, w3, w2 = inp[k1], inp[k3], inp[k2]
+        if w1.dim() == 2:
+            w1, w3, w2 = w1[None], w3[None], w2[None]
+        w2t, w2t_s, w13t, w13t_s = _quantize_t(w1, w3, w2)
+        sq = (lambda t: t[0]) if tag else (lambda t: t)
+        out[f"w{tag}2t"], out[f"w{tag}2t_s"] = sq(w2t), sq(w2t_s)
+        out[f"w{tag}13t"], out[f"w{tag}13t_s"] = sq(w13t), sq(w13t_s)
     return out
 
 
@@ -171,9 +187,15 @@ def bwd_args(inp: dict, fbufs: dict, dy: torch.Tensor, gbufs: dict,
         bw = inp["mx_bwd"]
         a.w2t, a.w2t_scales = p(bw["w2t"]), p(bw["w2t_s"])
         a.w13t, a.w13t_scales = p(bw["w13t"]), p(bw["w13t_s"])
+        if "ws1" in mx:
+            a.shared = B.expert_weights(mx["ws1"], mx["ws3"], mx["ws2"],
+                                        mx["ws1_s"], mx["ws3_s"], mx["ws2_s"])
+            a.ws2t, a.ws2t_scales = p(bw["ws2t"]), p(bw["ws2t_s"])
+            a.ws13t, a.ws13t_scales = p(bw["ws13t"]), p(bw["ws13t_s"])
     else:
         a.routed = B.expert_weights(inp["w1"], inp["w3"], inp["w2"])
-    a.shared = B.expert_weights(inp.get("ws1"), inp.get("ws3"), inp.get("ws2"))
+        a.shared = B.expert_weights(inp.get("ws1"), inp.get("ws3"),
+                                    inp.get("ws2"))
     for k in ("topk_idx", "topk_w", "offsets", "sorted_src", "dest", "x_perm",
               "h", "y_perm", "act_a", "act_b", "x_perm_scales"):
         setattr(a, k, p(fbufs.get(k)))

@@ -43,7 +43,7 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.MoeExpertWeights) == 48
     n_ptr_fwd = 4 + 1 + 14 + B.MOE_FWD_NEVENTS
     assert ctypes.sizeof(B.MoeFwdArgs) == 8 * n_ptr_fwd + 2 * 48
-    n_ptr_bwd = 2 + 18 + 5 + B.MOE_BWD_NEVENTS
+    n_ptr_bwd = 2 + 18 + 5 + 4 + B.MOE_BWD_NEVENTS
     assert ctypes.sizeof(B.MoeBwdArgs) == 8 * n_ptr_bwd + 2 * 48
 
 
@@ -223,9 +223,11 @@ def test_mxfp8_backward_validation():
     assert lib.moe_backward(ctypes.byref(d), ctypes.byref(a), fake, nb,
                             None) == B.MOE_EINVAL
     a.act_a = None
+    # a shared expert needs its MX weights and transposed copies
     ds = B.make_desc(64, 128, 256, 8, 2, d_ff_shared=128, mxfp8=True)
     assert lib.moe_backward(ctypes.byref(ds), ctypes.byref(a), fake,
-                            _ws(ds, True), None) == B.MOE_EUNSUPPORTED
+                            _ws(ds, True), None) == B.MOE_EINVAL
+    assert _ws(ds, True) > nb
     # the MX backward's workspace holds the quantised dy_perm and [da | db]
     assert nb > _ws(B.make_desc(64, 128, 256, 8, 2), True) + 128 * 3 * 256
 

@@ -23,6 +23,8 @@ CASES = [
     mi.MoEConfig("mxb_tail_T333_d384_f256_E16_K3", 333, 384, 256, 16, 3),
     mi.MoEConfig("mxb_skewed_T1024_d256_f256_E16_K4", 1024, 256, 256, 16, 4,
                  synth_logits=True, n_zero=3, zipf_s=1.2),
+    mi.MoEConfig("mxb_shared_sigmoid_T512_d256_f128_E16_K4_fs256", 512, 256,
+                 128, 16, 4, f_shared=256, gate="sigmoid", bias=True),
 ]
 
 
@@ -45,8 +47,8 @@ def test_transposing_quantiser_exact():
 
 
 def _mx_train(cfg, ginp, save_acts=False):
-    desc = B.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.K, 0, gate=cfg.gate,
-                       mxfp8=True, save_acts=save_acts)
+    desc = B.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.K, cfg.f_shared,
+                       gate=cfg.gate, mxfp8=True, save_acts=save_acts)
     ginp = dict(ginp)
     ginp["mx"] = L.quantize_expert_weights(ginp)
     ginp["mx_bwd"] = L.quantize_expert_weights_bwd(ginp)
@@ -65,12 +67,16 @@ def test_mxfp8_backward_parity(cfg, save_acts):
     cinp, ginp = inputs(cfg, seed=6, with_dy=True)
     fb, gb = _mx_train(cfg, ginp, save_acts)
     idx, w, counts, *_ = check_routing_exact(cfg, cinp, fb)
+    sh = (cinp["ws1"], cinp["ws3"], cinp["ws2"])
     ref = oracle.backward_mxfp8(cinp["x"], cinp["w1"], cinp["w3"], cinp["w2"],
-                                idx, w, cinp["dy"])
+                                idx, w, cinp["dy"], *sh)
     exact = oracle.backward(cinp["x"], cinp["w1"], cinp["w3"], cinp["w2"],
-                            idx, w, cinp["dy"])
-    for k, rk in (("dx", "dx"), ("dw1", "dw1"), ("dw3", "dw3"),
-                  ("dw2", "dw2"), ("d_topk_w", "d_w")):
+                            idx, w, cinp["dy"], *sh)
+    keys = [("dx", "dx"), ("dw1", "dw1"), ("dw3", "dw3"), ("dw2", "dw2"),
+            ("d_topk_w", "d_w")]
+    if cfg.f_shared:
+        keys += [("dws1", "dws1"), ("dws3", "dws3"), ("dws2", "dws2")]
+    for k, rk in keys:
         err = rel_err(gb[k], ref[rk])
         print(f"{cfg.name} {k}: vs fp8-aware oracle {err:.3e}, vs exact "
               f"{rel_err(gb[k], exact[rk]):.3e}")
