@@ -100,6 +100,8 @@ struct GemmParams {
   const int32_t* gsrc; int gdiv;
   // kEpiSwigluMx: optional bf16 copies of the pre-activations (ld = ldc)
   void* Sa; void* Sb;
+  // kSchedK: the group ranges are off[g] * kmul (0 means 1)
+  int kmul;
 };
 
 }  // namespace moe

@@ -19,6 +19,8 @@ enum GemmOp : int {
   kOpRouterDw = 9,  // part_g[E,d] = d_logits_g^T x_g over token range g (fp32)
   kOpGemm1MxAct = 10,  // GEMM 1 on MXFP8 operands; bf16 h (optional), a, b
   kOpDgrad2Mx = 11,    // dh = dy_perm W2_e on MXFP8 operands -> (da, db) bf16
+  kOpWgradT = 12,      // dW_e = L_e R_e^T with L, R transposed and each
+                       // group's columns padded to 64 (zeros): k contiguous
 };
 
 // Row-tile heights for which the permute step publishes tile prefixes.
@@ -39,6 +41,8 @@ constexpr int kSimtBM = 64;
 hipError_t gemm_mfma(GemmOp op, GemmParams p,
                      const int32_t* const* tile_off_by_bm, hipStream_t s);
 bool mfma_supported(GemmOp op, const GemmParams& p);
+// Whether the direct-to-LDS kernels are in use (not forced off).
+bool gemm_direct_ok();
 // Whether GEMM 1 can gather its A rows (direct-to-LDS kernel, bf16 or
 // MXFP8) for contraction length K.
 bool gemm1_gather_supported(int K);

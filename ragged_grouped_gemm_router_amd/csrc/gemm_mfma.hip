@@ -207,8 +207,9 @@ __device__ __forceinline__ bool lookup_tile(const GemmParams& p, Tile& t) {
   t.m0 = (rem / tiles_n) * BM;
   t.n0 = (rem % tiles_n) * BN;
   t.m_end = p.M;
-  t.k_beg = p.off[t.g];
-  t.k_end = p.off[t.g + 1];
+  const int km = p.kmul > 0 ? p.kmul : 1;
+  t.k_beg = p.off[t.g] * km;
+  t.k_end = p.off[t.g + 1] * km;
   return true;
 }
 
@@ -482,7 +483,7 @@ template <> struct Fmt<true> {
 };
 
 template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
-          typename TO, bool MX>
+          typename TO, bool MX, int SCHED = kSchedM>
 __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) {
   using F = Fmt<MX>;
   typedef typename F::Frag Frag;
@@ -511,8 +512,12 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
       StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>::BYTES;
   __shared__ __attribute__((aligned(1024))) char lds[S * STAGE > EPI_BYTES ? S * STAGE : EPI_BYTES];
 
+  // the tile; grouped contraction (SCHED K): k-tiles [kt0, kt0 + nk) of
+  // the group's range, which the host pads to whole k-tiles
   Tile t;
-  if (!lookup_tile<BM, BN, kSchedM>(p, t)) return;
+  if (!lookup_tile<BM, BN, SCHED>(p, t)) return;
+  const int kt0 = SCHED == kSchedK ? t.k_beg / BK : 0;
+  const int nk = SCHED == kSchedK ? (t.k_end - t.k_beg) / BK : p.K / BK;
   const int tid = threadIdx.x, lane = tid % kWave;
   // wave-uniform, so every LDS destination below is a scalar (M0) value
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -554,7 +559,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // DMA instruction d of a k-tile (d < A_INS: operand A, then each B)
   auto issue_one = [&](int kt, int stage, int d) {
     char* base = lds + stage * STAGE;
-    const int k0 = kt * RB;
+    const int k0 = (kt0 + kt) * RB;
     if (d < A_INS) {
       dma16(ra, base + (d * NW + wave) * 1024, a_off[d], k0);
     } else {
@@ -603,8 +608,6 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[o][i][j] = f32x16{};
-
-  const int nk = p.K / BK;
 
   // fragments of one k-substep
   struct Frags {
@@ -680,6 +683,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // Prologue: (scales of k-tile 0,) k-tiles 0 .. S-1 in flight (past the
   // last tile, the last one again, into stages nobody reads); wait for
   // tile 0.
+  if (nk > 0) {  // (an empty group's tile writes zeros)
   load_scales(0);
 #pragma unroll
   for (int i = 0; i < S; ++i) issue(min(i, nk - 1), i);
@@ -765,6 +769,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     }
   }
 #undef MOE_FENCE
+  }
   __builtin_amdgcn_s_waitcnt(0);  // no load may still target LDS at exit
   // through LDS in 16-byte row pieces: the output (SwiGLU of the two
   // accumulators, or the plain product), then any saved pre-activations
@@ -841,7 +846,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     } else {
       SO::run(lds, wm, wn, lane,
               [&](int i, int j, int r) { return acc[0][i][j][r]; },
-              put((TO*)p.C));
+              put((TO*)p.C + (SCHED == kSchedK ? (long)t.g * p.sC : 0)));
     }
   }
 }
@@ -1125,14 +1130,17 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 }
 
 template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
-          typename TO, bool MX>
+          typename TO, bool MX, int SCHED = kSchedM>
 hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
   const long tiles_n = (p.N + BN - 1) / BN;
-  long tiles = (tiles_n + p.group_n - 1) / p.group_n * p.tiles_m_max * p.group_n;
+  long tiles = SCHED == kSchedK
+                   ? (long)p.G * ((p.M + BM - 1) / BM) * tiles_n
+                   : (tiles_n + p.group_n - 1) / p.group_n * p.tiles_m_max *
+                         p.group_n;
   if (tiles <= 0) return hipSuccess;
   tiles = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, S, WGM, WGN, DUAL, EPI, TO, MX>),
+  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, S, WGM, WGN, DUAL, EPI, TO, MX, SCHED>),
                      dim3((unsigned)tiles), dim3(WGM * WGN * kWave), 0, s, p);
   return hipGetLastError();
 }
@@ -1212,6 +1220,7 @@ bool mfma_supported(GemmOp op, const GemmParams& p) {
   if (op == kOpDgrad1 && p.K1 % 64) return false;
   if ((op == kOpDgrad2 || op == kOpDgrad1) && p.N % 8) return false;
   if (op == kOpWgrad && (p.M % 8 || p.N % 8)) return false;
+  if (op == kOpWgradT && (p.lda % 64 || p.ldb % 64 || p.N % 8)) return false;
   // router backward: d_logits rows padded to whole k-tiles (row-major A
   // of the dx product), 16-byte aligned k-rows and output pieces
   if (op == kOpRouterDx && (p.lda % 64 || p.ldb % 8 || p.N % 8)) return false;
@@ -1220,6 +1229,8 @@ bool mfma_supported(GemmOp op, const GemmParams& p) {
 }
 
 bool gemm1_gather_supported(int K) { return K % 64 == 0 && !force_staged(); }
+
+bool gemm_direct_ok() { return !force_staged(); }
 
 hipError_t gemm_mfma(GemmOp op, GemmParams p,
                      const int32_t* const* tile_off_by_bm, hipStream_t s) {
@@ -1231,7 +1242,7 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   p.group_n = tile_group_n();
   // Big tiles when the average group has enough rows to fill them.
   bool big;
-  if (op == kOpWgrad || op == kOpRouterDw) {
+  if (op == kOpWgrad || op == kOpRouterDw || op == kOpWgradT) {
     big = p.M >= 256 && p.N >= 256;
   } else if (op == kOpRouterDx) {
     big = false;
@@ -1288,6 +1299,11 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
       return !big ? launch_t<128, 128, 2, 2, true, true, false, kEpiStoreF32, kSchedK>(p, s)
                   : launch_t<256, 256, 2, 4, true, true, false, kEpiStoreF32, kSchedK>(p, s);
   }
+  // weight gradients from transposed, group-padded operands: both k
+  // contiguous, so the forward's direct-to-LDS kernel takes them
+  if (op == kOpWgradT)
+    return big ? launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false, kSchedK>(p, s)
+               : launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false, kSchedK>(p, s);
   if (op == kOpGemm1Mx)
     return launch_dl_sized<true, kEpiSwigluMx, bf16, true>(big, p, s);
   if (op == kOpGemm1MxAct)

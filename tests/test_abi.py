@@ -228,8 +228,10 @@ def test_mxfp8_backward_validation():
     assert lib.moe_backward(ctypes.byref(ds), ctypes.byref(a), fake,
                             _ws(ds, True), None) == B.MOE_EINVAL
     assert _ws(ds, True) > nb
-    # the MX backward's workspace holds the quantised dy_perm and [da | db]
-    assert nb > _ws(B.make_desc(64, 128, 256, 8, 2), True) + 128 * 3 * 256
+    # the MX backward's workspace holds the quantised dy_perm [T*K, d] and
+    # [da | db] [T*K, 2 f] besides the bf16 buffers
+    TK, d, f = 128, 128, 256
+    assert nb > 2 * TK * (2 * d + 2 * f) + TK * d + TK * 2 * f
 
 
 def test_quantize_t_validation():
@@ -242,3 +244,13 @@ def test_quantize_t_validation():
     assert q(fake, 2, 64, 96, fake, fake, 64, 0, None) == B.MOE_EUNSUPPORTED
     assert q(fake, 0, 64, 128, None, None, 64, 0, None) == B.MOE_OK
     assert q(fake, -1, 64, 128, fake, fake, 64, 0, None) == B.MOE_EINVAL
+
+
+def test_transposed_wgrad_workspace():
+    """bf16 backward with widths that are multiples of 64 and experts of at
+    least 512 rows on average reserves the transposed, group-padded
+    operands of the weight gradients: (2 d + 3 f) x 64 (T K / 64 + E + 1)
+    bf16 elements."""
+    d = B.make_desc(2048, 128, 192, 8, 2)  # 512 rows per expert on average
+    ldT = 64 * (4096 // 64 + 8 + 1)
+    assert _ws(d, True) >= 2 * (2 * 128 + 3 * 192) * ldT

@@ -20,6 +20,12 @@ CASES = [
                  dtype="f32"),
     mi.MoEConfig("skewed_like_T1024_d128_f192_E16_K4", 1024, 128, 192, 16, 4,
                  synth_logits=True, n_zero=3, zipf_s=1.2),
+    # >= 512 rows per expert on average: weight gradients from the
+    # transposed, group-padded operands (ragged N with f = 192; empty
+    # experts in the skewed case)
+    mi.MoEConfig("wgrad_t_T2048_d256_f192_E4_K2", 2048, 256, 192, 4, 2),
+    mi.MoEConfig("wgrad_t_skewed_T4096_d128_f256_E16_K4", 4096, 128, 256, 16,
+                 4, synth_logits=True, n_zero=3, zipf_s=1.2),
     mi.MoEConfig("many_experts_T256_d256_f128_E64_K8_sigmoid", 256, 256, 128,
                  64, 8, gate="sigmoid", bias=True),
 ]
