@@ -467,6 +467,28 @@ __device__ __forceinline__ void epilogue_swiglu_mx(const GemmParams& p,
   }
 }
 
+// Fragment read order of a k-substep: the order in which its MFMAs, q =
+// (o * MB + i) * NB + j taking A block i and B block (o, j), first use
+// them (FIRST_USE), else A blocks then B blocks. Index r < MB is A block r,
+// else B block (r - MB) / NB, (r - MB) % NB.
+template <int MB, int NB, int NOPS, bool FIRST_USE>
+struct ReadOrder {
+  int r[MB + NOPS * NB];
+  constexpr ReadOrder() : r{} {
+    bool seen[MB + NOPS * NB] = {};
+    int n = 0;
+    if (!FIRST_USE) {
+      for (; n < MB + NOPS * NB; ++n) r[n] = n;
+      return;
+    }
+    for (int q = 0; q < NOPS * MB * NB; ++q) {
+      const int ra = (q / NB) % MB, rb = MB + q / (MB * NB) * NB + q % NB;
+      if (!seen[rb]) seen[rb] = true, r[n++] = rb;
+      if (!seen[ra]) seen[ra] = true, r[n++] = ra;
+    }
+  }
+};
+
 // Operand formats of the direct-to-LDS kernel.
 //   bf16 : v_mfma_f32_32x32x16_bf16, 8 bf16 per lane per fragment
 //   MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3, 32 bytes per lane per
@@ -501,8 +523,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   constexpr int A_INS = BM / RPI / NW, B_INS = BN / RPI / NW;
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile shape");
   static_assert(MB >= 1 && NB >= 1, "tile shape");
-  static_assert(S >= 2 && (S & (S - 1)) == 0 && KS % 2 == 0,
-                "power-of-two stage count, even substep count");
+  static_assert(S >= 2 && KS % 2 == 0, "stage count, even substep count");
   static_assert((S - 1) * (A_INS + (DUAL ? 2 : 1) * B_INS) <= 63, "vmcnt range");
 
   // the epilogue stages 128 rows at a time (the quantising one only for
@@ -619,7 +640,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // Fragment rows differ from the lane's first row by multiples of 32, so
   // they share its swizzle: the chunk position depends on the lane and the
   // substep only, and the block offset is an immediate of the LDS read.
-  const int lrow = lane % 32, half = lane / 32, sw = (lrow >> 1) & 7;
+  const int lrow = lane % 32, half = lane / 32, sw = swz<CPR>(lrow, 0);
   const int a_row0 = (wm * WM + lrow) * RB;
   const int b_row0 = A_BYTES + (wn * WN + lrow) * RB;
   auto read_frag = [&](const char* rowp, int ks) {
@@ -638,8 +659,15 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
       return *(const Frag*)(rowp + ((ks * 2 + half) ^ sw) * 16);
     }
   };
-  // fragment r of substep ks (r < MB: A block r, else B block)
-  auto read_one = [&](const char* sb, int ks, Frags& f, int r) {
+  // Fragment reads follow the order in which the MFMAs of the substep
+  // first use them (MFMA q takes A block i and B block (o, j)), so the
+  // first MFMAs of a region wait only for the first reads of the region
+  // before it. The dual MXFP8 tile keeps A-then-B order: its longer-lived
+  // 32-byte fragments would spill.
+  constexpr ReadOrder<MB, NB, NB_OPS, !(MX && DUAL)> kOrder{};
+  // fragment kOrder.r[m] of substep ks (r < MB: A block r, else B block)
+  auto read_one = [&](const char* sb, int ks, Frags& f, int m) {
+    const int r = kOrder.r[m];
     if (r < MB) {
       f.a[r] = read_frag(sb + a_row0 + r * 32 * RB, ks);
     } else {
@@ -710,9 +738,11 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // free.)
   constexpr int H = N_MFMA >= 8 ? 2 : N_MFMA >= 2 ? 1 : 0;
 #define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
+  // stage of k-tile kt (kt mod S) and of k-tile kt + 1, kept as counters
+  int st = 0, st_next = S > 1 ? 1 : 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const char* sb = lds + (kt & (S - 1)) * STAGE;
-    const char* sb_next = lds + ((kt + 1) & (S - 1)) * STAGE;
+    const char* sb = lds + st * STAGE;
+    const char* sb_next = lds + st_next * STAGE;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       Frags& cur = (ks & 1) ? fb : fa;
@@ -758,7 +788,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
             if ((mm + 1) * N_READ / NM_MAX != rb)
               read_one(sb_next, 0, nxt, rb);
             else
-              issue_one(min(kt + S, nk - 1), kt & (S - 1), mm - rb);
+              issue_one(min(kt + S, nk - 1), st, mm - rb);
           }
           MOE_FENCE();
         }
@@ -767,6 +797,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
         MOE_FENCE();
       }
     }
+    st = st_next;
+    st_next = st_next + 1 == S ? 0 : st_next + 1;
   }
 #undef MOE_FENCE
   }
@@ -967,7 +999,11 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
   };
   constexpr int N_READ = MB + NB;
   constexpr int N_MFMA = MB * NB;
-  auto read_one = [&](const char* sb, int ks, Frags& f, int r) {
+  // reads in the order the substep's MFMAs first use the fragments, on
+  // the big tiles (measured: the 2 x 2 block tiles run faster A then B)
+  constexpr ReadOrder<MB, NB, 1, (N_MFMA >= 8)> kOrder{};
+  auto read_one = [&](const char* sb, int ks, Frags& f, int m) {
+    const int r = kOrder.r[m];
     if (r < MB) {
       const int row0 = wm * WM + r * 32;
       f.a[r] = A_KM ? read_km(sb, BM, row0, ks) : read_rm(sb, row0, ks);
