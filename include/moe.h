@@ -71,6 +71,11 @@ typedef int32_t moe_status;
 
 /* flags */
 #define MOE_FLAG_SAVE_ACTS 1  /* forward stores the pre-activations a, b */
+/* The bf16 expert GEMMs run a partial last round of 256-row tiles (at most
+   a quarter of the CUs' worth of tiles) as 128 x 128 quarter tiles by
+   default; this flag keeps every tile at full size. Results are
+   bit-identical either way (same accumulation order per output). */
+#define MOE_FLAG_NO_TAIL_SPLIT 2
 
 /* limits of this build */
 #define MOE_K_MAX 16

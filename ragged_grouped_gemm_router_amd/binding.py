@@ -23,6 +23,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID = 0, 1
 MOE_FLAG_SAVE_ACTS = 1
+MOE_FLAG_NO_TAIL_SPLIT = 2
 MOE_K_MAX, MOE_E_MAX = 16, 1024
 MOE_FWD_NEVENTS, MOE_BWD_NEVENTS = 6, 8
 

@@ -30,7 +30,7 @@ moe_status check_desc(const moe_desc* d) {
   if (d->K > d->E) return MOE_EINVAL;
   if (d->gate != MOE_GATE_SOFTMAX && d->gate != MOE_GATE_SIGMOID) return MOE_EINVAL;
   if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_EINVAL;
-  if (d->flags & ~MOE_FLAG_SAVE_ACTS) return MOE_EINVAL;
+  if (d->flags & ~(MOE_FLAG_SAVE_ACTS | MOE_FLAG_NO_TAIL_SPLIT)) return MOE_EINVAL;
   if (d->K > MOE_K_MAX || d->E > MOE_E_MAX) return MOE_EUNSUPPORTED;
   if (d->gemm_dtype != d->act_dtype &&
       !(d->gemm_dtype == MOE_MXFP8 && d->act_dtype == MOE_BF16))
@@ -299,6 +299,7 @@ hipError_t do_gemm1(const moe_desc* d, const void* A, const int32_t* off,
   p.gsrc = gsrc; p.gdiv = d->K;
   p.B = w1; p.B2 = w3; p.ldb = d->d_model; p.sB = (long)f * d->d_model;
   p.C = h; p.C2 = a_out; p.C3 = b_out; p.ldc = f;
+  p.slots = d->flags & MOE_FLAG_NO_TAIL_SPLIT ? 0 : -1;
   return run_gemm(kOpGemm1, d->act_dtype, p, toff, s);
 }
 
@@ -310,6 +311,7 @@ hipError_t do_gemm2(const moe_desc* d, const void* h, const int32_t* off,
   p.A = h; p.lda = f;
   p.B = w2; p.ldb = f; p.sB = (long)d->d_model * f;
   p.C = y; p.ldc = d->d_model;
+  p.slots = d->flags & MOE_FLAG_NO_TAIL_SPLIT ? 0 : -1;
   return run_gemm(kOpGemm2, d->act_dtype, p, toff, s);
 }
 

@@ -102,6 +102,10 @@ struct GemmParams {
   void* Sa; void* Sb;
   // kSchedK: the group ranges are off[g] * kmul (0 means 1)
   int kmul;
+  // kSchedM big tiles: row x column tiles that run at once (one per CU),
+  // for the split of a partial last round into quarter tiles; 0 = no
+  // split, -1 = the device's CU count (resolved by the launcher)
+  int slots;
 };
 
 }  // namespace moe

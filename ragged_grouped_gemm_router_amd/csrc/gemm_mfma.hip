@@ -173,30 +173,59 @@ struct Tile {
 // then the GN column tiles within), so that consecutive tiles share weight
 // and row panels. The first mt * tiles_n workgroups take them, each XCD a
 // contiguous share of equal size; the rest exit.
-template <int BM, int BN, int SCHED>
+//
+// Split last round (TAIL, row-grouped only). With S = p.slots big tiles
+// running at once, n_tiles big tiles take full rounds plus a last round of
+// r = n_tiles mod S tiles. When 0 < 4 r <= S and there is a full round,
+// the big-tile launch (TAIL 1) runs only the full rounds, and a second
+// launch of half-size tiles (TAIL 2: BM x BN = half the big tile each
+// way) runs the last round's tiles as four quarters each, so that round
+// spreads over 4 r CUs instead of r. Both launches decide from the same
+// device tile prefix; otherwise TAIL 1 runs every tile and TAIL 2 nothing.
+template <int BM, int BN, int SCHED, int TAIL = 0>
 __device__ __forceinline__ bool lookup_tile(const GemmParams& p, Tile& t) {
-  const int tiles_n = (p.N + BN - 1) / BN;
+  // tile size of the enumeration: the big tile in the quarter launch
+  constexpr int DM = TAIL == 2 ? 2 * BM : BM, DN = TAIL == 2 ? 2 * BN : BN;
+  const int tiles_n = (p.N + DN - 1) / DN;
   t.g = 0;
   t.k_beg = 0;
   t.k_end = p.K;
   if (SCHED == kSchedM) {
-    const int mt = p.off ? p.tile_off[p.G] : (p.M + BM - 1) / BM;
+    const int mt = p.off ? p.tile_off[p.G] : (p.M + DM - 1) / DM;
     const int n_tiles = mt * tiles_n;
-    if ((int)blockIdx.x >= n_tiles) return false;
-    const int idx = xcd_remap_n(blockIdx.x, n_tiles);
+    // this launch's logical tiles: [lo, lo + n) (quarters: 4 per tile)
+    int lo = 0, n = n_tiles;
+    if (TAIL != 0) {
+      const int full = n_tiles / p.slots * p.slots, r = n_tiles - full;
+      const bool split = full > 0 && r > 0 && 4 * r <= p.slots;
+      if (TAIL == 1 && split) n = full;
+      if (TAIL == 2) {
+        if (!split) return false;
+        lo = full;
+        n = 4 * r;
+      }
+    }
+    if ((int)blockIdx.x >= n) return false;
+    const int li = xcd_remap_n(blockIdx.x, n);
+    const int idx = lo + (TAIL == 2 ? li / 4 : li), q = li % 4;
     const int GN = p.group_n;
     const int ng = idx / (mt * GN), within = idx % (mt * GN);
     const int gsz = min(GN, tiles_n - ng * GN);
     const int m = within / gsz;
-    t.n0 = (ng * GN + within % gsz) * BN;
+    t.n0 = (ng * GN + within % gsz) * DN;
     if (p.off == nullptr) {
-      t.m0 = m * BM;
+      t.m0 = m * DM;
       t.m_end = p.M;
-      return true;
+    } else {
+      t.g = upper_group(p.tile_off, p.G, m);
+      t.m0 = p.off[t.g] + (m - p.tile_off[t.g]) * DM;
+      t.m_end = p.off[t.g + 1];
     }
-    t.g = upper_group(p.tile_off, p.G, m);
-    t.m0 = p.off[t.g] + (m - p.tile_off[t.g]) * BM;
-    t.m_end = p.off[t.g + 1];
+    if (TAIL == 2) {  // quarter q of the big tile; none past its rows
+      t.m0 += (q / 2) * BM;
+      t.n0 += (q % 2) * BN;
+      if (t.m0 >= t.m_end || t.n0 >= p.N) return false;
+    }
     return true;
   }
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -505,7 +534,7 @@ template <> struct Fmt<true> {
 };
 
 template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
-          typename TO, bool MX, int SCHED = kSchedM>
+          typename TO, bool MX, int SCHED = kSchedM, int TAIL = 0>
 __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) {
   using F = Fmt<MX>;
   typedef typename F::Frag Frag;
@@ -536,7 +565,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // the tile; grouped contraction (SCHED K): k-tiles [kt0, kt0 + nk) of
   // the group's range, which the host pads to whole k-tiles
   Tile t;
-  if (!lookup_tile<BM, BN, SCHED>(p, t)) return;
+  if (!lookup_tile<BM, BN, SCHED, TAIL>(p, t)) return;
   const int kt0 = SCHED == kSchedK ? t.k_beg / BK : 0;
   const int nk = SCHED == kSchedK ? (t.k_end - t.k_beg) / BK : p.K / BK;
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -1166,17 +1195,18 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 }
 
 template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
-          typename TO, bool MX, int SCHED = kSchedM>
+          typename TO, bool MX, int SCHED = kSchedM, int TAIL = 0>
 hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
   const long tiles_n = (p.N + BN - 1) / BN;
   long tiles = SCHED == kSchedK
                    ? (long)p.G * ((p.M + BM - 1) / BM) * tiles_n
                    : (tiles_n + p.group_n - 1) / p.group_n * p.tiles_m_max *
                          p.group_n;
+  if (TAIL == 2) tiles = p.slots;  // at most 4 r <= slots quarter tiles
   if (tiles <= 0) return hipSuccess;
   tiles = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, S, WGM, WGN, DUAL, EPI, TO, MX, SCHED>),
+  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, S, WGM, WGN, DUAL, EPI, TO, MX, SCHED, TAIL>),
                      dim3((unsigned)tiles), dim3(WGM * WGN * kWave), 0, s, p);
   return hipGetLastError();
 }
@@ -1194,6 +1224,21 @@ int big_tile_waves() {
 }
 
 
+// compute units of the current device (cached per device)
+int num_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <bool DUAL, int EPI, typename TO, bool MX = false>
 hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
   // big: 256 x 256 outputs (256 x 128 x 2 dual), either over 8 waves, two
@@ -1205,6 +1250,19 @@ hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
     const int forced = big_tile_waves();
     if (forced == 4 || (forced == 0 && MX && !DUAL))
       return launch_dl<256, DUAL ? 128 : 256, 2, 2, 2, DUAL, EPI, TO, MX>(p, s);
+    // bf16 row-grouped products: a partial last round of big tiles runs
+    // as quarter tiles (128 x 128, or 128 x 64 x 2 dual) in a second launch
+    if constexpr (!MX) {
+      if (p.slots != 0 && p.off) {
+        GemmParams q = p;
+        if (q.slots < 0) q.slots = num_cus();
+        hipError_t e = launch_dl<256, DUAL ? 128 : 256, 2, 2, 4, DUAL, EPI, TO,
+                                 MX, kSchedM, 1>(q, s);
+        if (e != hipSuccess) return e;
+        return launch_dl<128, DUAL ? 64 : 128, 2, 2, 2, DUAL, EPI, TO, MX,
+                         kSchedM, 2>(q, s);
+      }
+    }
     return launch_dl<256, DUAL ? 128 : 256, 2, 2, 4, DUAL, EPI, TO, MX>(p, s);
   }
   return launch_dl<128, DUAL ? 64 : 128, 2, 2, 2, DUAL, EPI, TO, MX>(p, s);

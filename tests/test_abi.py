@@ -65,6 +65,15 @@ def test_workspace_size_host_only():
     assert nb >= 2 * 32768 * (2 * 7168 + 2 * 2048)
 
 
+def test_flags_accepted():
+    """Every defined flag bit is a valid descriptor."""
+    d = B.make_desc(64, 128, 256, 8, 2)
+    for fl in (B.MOE_FLAG_SAVE_ACTS, B.MOE_FLAG_NO_TAIL_SPLIT,
+               B.MOE_FLAG_SAVE_ACTS | B.MOE_FLAG_NO_TAIL_SPLIT):
+        d.flags = fl
+        assert _ws(d) > 0
+
+
 @pytest.mark.parametrize("fields,code", [
     (dict(K=3, E=2), B.MOE_EINVAL),              # K > E
     (dict(K=0), B.MOE_EINVAL),
@@ -75,6 +84,7 @@ def test_workspace_size_host_only():
     (dict(gate=7), B.MOE_EINVAL),
     (dict(act_dtype=5), B.MOE_EINVAL),
     (dict(flags=8), B.MOE_EINVAL),
+    (dict(flags=4), B.MOE_EINVAL),               # no such flag
     (dict(gemm_dtype=B.MOE_F32), B.MOE_EINVAL),             # bf16 act, f32 gemm
     (dict(gemm_dtype=B.MOE_MXFP8, d_model=160), B.MOE_EUNSUPPORTED),
     (dict(gemm_dtype=B.MOE_MXFP8, d_ff_shared=96), B.MOE_EUNSUPPORTED),
