@@ -68,3 +68,37 @@ def test_tail_split_bit_identical_and_matches_oracle():
     y_ref = oracle.stage_gemm2(h_split.cpu(), offc, w2.cpu(), rows=rows)
     assert rel_err(y_split[rows].cpu(), y_ref) <= 1e-2
 
+
+
+def test_tail_split_training_step_bit_identical():
+    """Mixtral-shaped training step with and without the split: every
+    output and gradient bit-identical. (With 8 experts of ~2048 rows the
+    256-row tiles number 64-72; GEMM 2, 16 column tiles, splits its last
+    round when that round holds at most 64 tiles.)"""
+    from moe_testlib import desc_of, inputs
+    from ragged_grouped_gemm_router_amd import layer as L
+    import moe_inputs as mi
+    cfg = mi.MIXTRAL_TRAIN
+    _, ginp = inputs(cfg, seed=3, with_dy=True, device_gen=True)
+    res = []
+    for flags in (0, B.MOE_FLAG_NO_TAIL_SPLIT):
+        desc = desc_of(cfg, save_acts=True)
+        desc.flags |= flags
+        fb = L.alloc_forward(desc, DEV)
+        L.forward(desc, ginp, fb)
+        gb = L.alloc_backward(desc, DEV)
+        L.backward(desc, ginp, fb, ginp["dy"], gb)
+        torch.cuda.synchronize()
+        res.append((fb, gb))
+    counts = res[0][0]["counts"].cpu()
+    mt = int(((counts + 255) // 256).sum())
+    S = torch.cuda.get_device_properties(0).multi_processor_count
+    r = mt * 16 % S
+    split = mt * 16 >= S and 0 < 4 * r <= S
+    print(f"row tiles {mt}: last round {r} of GEMM 2's tiles "
+          f"({'split' if split else 'not split'})", flush=True)
+    (f0, g0), (f1, g1) = res
+    for k in ("h", "y_perm", "out"):
+        assert torch.equal(f0[k], f1[k]), k
+    for k in ("dx", "dw1", "dw3", "dw2", "d_topk_w"):
+        assert torch.equal(g0[k], g1[k]), k
