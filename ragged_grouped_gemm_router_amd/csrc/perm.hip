@@ -347,6 +347,60 @@ __global__ __launch_bounds__(kScatterThreads) void combine_kernel(
   }
 }
 
+// The same for a compile-time K: the U * KT row loads of a thread's items
+// are issued together (indices clamped instead of branched on, so the
+// code is straight-line), then summed in k order as above.
+template <typename T, int U, int KT>
+__global__ __launch_bounds__(kScatterThreads) void combine_k_kernel(
+    const T* __restrict__ y, const int32_t* __restrict__ dest,
+    const float* __restrict__ w, const T* __restrict__ add, T* __restrict__ out,
+    int Ttok, int d, int tpb) {
+  __shared__ int32_t sd[kScatterThreads];
+  __shared__ float sw[kScatterThreads];
+  const long t0 = (long)blockIdx.x * tpb;
+  const int ntok = (int)min((long)tpb, Ttok - t0);
+  for (int i = threadIdx.x; i < ntok * KT; i += kScatterThreads) {
+    sd[i] = dest[t0 * KT + i];
+    sw[i] = w ? w[t0 * KT + i] : 1.0f;
+  }
+  __syncthreads();
+  const int cpr = d / 8, n = ntok * cpr;
+  for (int i0 = threadIdx.x; i0 < n; i0 += U * kScatterThreads) {
+    float v[U][KT][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = min(i0 + u * kScatterThreads, n - 1);
+      const int tl = i / cpr, c = (i % cpr) * 8;
+#pragma unroll
+      for (int k = 0; k < KT; ++k)
+        load8(y + (long)sd[tl * KT + k] * d + c, v[u][k]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kScatterThreads;
+      if (i >= n) continue;
+      const int tl = i / cpr, c = (i % cpr) * 8;
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        const float wk = sw[tl * KT + k];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(wk, v[u][k][q], acc[q]);
+      }
+      const long o = (t0 + tl) * d + c;
+      if (add) {
+        float a8[8];
+        load8(add + o, a8);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += a8[q];
+      }
+      store8(out + o, acc);
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy,
                                                           const T* __restrict__ y,
@@ -509,7 +563,16 @@ hipError_t launch_combine_t(const T* y, const int32_t* dest, const float* w,
                             hipStream_t s) {
   const int tpb = scatter_tokens_per_block(K, (long)d * sizeof(T));
   const dim3 grid((unsigned)((Ttok + tpb - 1) / tpb)), block(kScatterThreads);
-  if (K >= 8)
+  if (K == 2)
+    hipLaunchKernelGGL((combine_k_kernel<T, 4, 2>), grid, block, 0, s, y, dest, w,
+                       add, out, Ttok, d, tpb);
+  else if (K == 4)
+    hipLaunchKernelGGL((combine_k_kernel<T, 2, 4>), grid, block, 0, s, y, dest, w,
+                       add, out, Ttok, d, tpb);
+  else if (K == 8)
+    hipLaunchKernelGGL((combine_k_kernel<T, 1, 8>), grid, block, 0, s, y, dest, w,
+                       add, out, Ttok, d, tpb);
+  else if (K >= 8)
     hipLaunchKernelGGL((combine_kernel<T, 1>), grid, block, 0, s, y, dest, w, add,
                        out, Ttok, K, d, tpb);
   else if (K >= 4)
