@@ -270,8 +270,12 @@ hipError_t do_permute(const moe_desc* d, const void* x, const int32_t* idx,
                       int32_t* dest, void* x_perm, uint8_t* x_perm_scales,
                       const FwdWs& ws, hipStream_t s) {
   const int TK = d->T * d->K;
+  // materialised bf16/fp32 rows with few experts: the scatter scans the
+  // chunk histograms itself (one launch fewer)
+  const bool fused = x_perm && d->gemm_dtype != MOE_MXFP8 &&
+                     scan_in_scatter(TK, d->E);
   hipError_t e = launch_hist_rank_scan(idx, TK, d->E, ws.block_hist, ws.rank,
-                                       counts, offsets, ws.tile_off, s);
+                                       counts, offsets, ws.tile_off, s, !fused);
   if (e != hipSuccess) return e;
   if (!x_perm) {
     e = launch_slots(idx, ws.block_hist, ws.rank, TK, d->E, dest, src, s);
@@ -286,7 +290,8 @@ hipError_t do_permute(const moe_desc* d, const void* x, const int32_t* idx,
   }
   return launch_scatter(x, idx, ws.block_hist, ws.rank, d->T, d->E, d->K,
                         (long)d->d_model * act_bytes(d->act_dtype), dest, src,
-                        x_perm, s);
+                        x_perm, s, fused ? counts : nullptr,
+                        fused ? offsets : nullptr, ws.tile_off);
 }
 
 hipError_t do_gemm1(const moe_desc* d, const void* A, const int32_t* off,

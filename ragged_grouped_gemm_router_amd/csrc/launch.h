@@ -16,20 +16,30 @@ hipError_t launch_topk(const float* logits, const float* bias, int T, int E,
 // block_hist: [nblk, E] int32 scratch, nblk = ceil(TK / kPermChunk), left
 // holding the first slot of every (chunk, expert); rank: [TK] int32, each
 // copy's rank among its chunk's copies of the same expert; tile_off:
-// kNumTileBM arrays of E+1 (row-tile prefix per tile height).
+// kNumTileBM arrays of E+1 (row-tile prefix per tile height). scan ==
+// false stops after the histograms (block_hist then holds the counts of
+// every (chunk, expert)), for launch_scatter to scan them itself.
 hipError_t launch_hist_rank_scan(const int32_t* idx, int TK, int E,
                                  int32_t* block_hist, int32_t* rank,
                                  int32_t* counts, int32_t* offsets,
-                                 int32_t* const* tile_off, hipStream_t s);
+                                 int32_t* const* tile_off, hipStream_t s,
+                                 bool scan = true);
+// Whether the scatter can scan the chunk histograms itself (E * chunks
+// small enough for one workgroup of the scatter).
+bool scan_in_scatter(int TK, int E);
 // tile_off[i][e] = sum_{e' < e} ceil(count_e' / kTileBM[i]) from offsets.
 hipError_t launch_tile_prefix(const int32_t* offsets, int E,
                               int32_t* const* tile_off, hipStream_t s);
 // dest / sorted_src of every copy from the sort above, and x_perm[dest[j]]
-// = x[j / K] (row_bytes % 16 == 0).
+// = x[j / K] (row_bytes % 16 == 0). With counts given and
+// scan_in_scatter(T * K, E), `first` holds the unscanned histograms, and
+// the scatter scans them and writes counts, offsets and tile_off too.
 hipError_t launch_scatter(const void* x, const int32_t* idx,
                           const int32_t* first, const int32_t* rank, int T,
                           int E, int K, long row_bytes, int32_t* dest,
-                          int32_t* sorted_src, void* x_perm, hipStream_t s);
+                          int32_t* sorted_src, void* x_perm, hipStream_t s,
+                          int32_t* counts = nullptr, int32_t* offsets = nullptr,
+                          int32_t* const* tile_off = nullptr);
 // dest / sorted_src only.
 hipError_t launch_slots(const int32_t* idx, const int32_t* first,
                         const int32_t* rank, int TK, int E, int32_t* dest,

@@ -81,12 +81,13 @@ __global__ __launch_bounds__(kRankWaves * kWave) void hist_rank_kernel(
   }
 }
 
-// Exclusive scan over a 1024-thread block of N values per thread at once
-// (v[i] of thread t scanned across threads): an inclusive scan inside each
-// wave by shuffles, then one pass over the 16 wave totals. wsum holds
-// 16 * N ints of LDS.
-template <int N>
+// Exclusive scan over a block of NW waves (1024 threads by default) of N
+// values per thread at once (v[i] of thread t scanned across threads): an
+// inclusive scan inside each wave by shuffles, then one pass over the NW
+// wave totals. wsum holds 16 * N ints of LDS.
+template <int N, int NW = 16>
 __device__ void block_exclusive_scan(int (&v)[N], int32_t* wsum) {
+  static_assert(NW <= 16, "wave totals");
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   int x[N];
 #pragma unroll
@@ -106,14 +107,14 @@ __device__ void block_exclusive_scan(int (&v)[N], int32_t* wsum) {
   if (wv == 0) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      int s = lane < 16 ? wsum[i * 16 + lane] : 0;
+      int s = lane < NW ? wsum[i * 16 + lane] : 0;
       const int own = s;
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
+      for (int off = 1; off < NW; off <<= 1) {
         const int y = __shfl_up(s, off);
         if (lane >= off) s += y;
       }
-      if (lane < 16) wsum[i * 16 + lane] = s - own;  // exclusive wave base
+      if (lane < NW) wsum[i * 16 + lane] = s - own;  // exclusive wave base
     }
   }
   __syncthreads();
@@ -124,7 +125,9 @@ __device__ void block_exclusive_scan(int (&v)[N], int32_t* wsum) {
 
 struct TileOffPtrs { int32_t* p[kNumTileBM]; };
 
-// Row-tile prefix of every tile height, from expert counts (thread e).
+// Row-tile prefix of every tile height, from expert counts (thread e of a
+// block of NW waves, E <= 64 * NW).
+template <int NW = 16>
 __device__ void write_tile_prefix(int cnt, int E, const TileOffPtrs& toff,
                                   int32_t* wsum) {
   const int e = threadIdx.x;
@@ -134,7 +137,7 @@ __device__ void write_tile_prefix(int cnt, int E, const TileOffPtrs& toff,
     tiles[s] = e < E ? (cnt + kTileBM[s] - 1) / kTileBM[s] : 0;
     tx[s] = tiles[s];
   }
-  block_exclusive_scan(tx, wsum);
+  block_exclusive_scan<kNumTileBM, NW>(tx, wsum);
 #pragma unroll
   for (int s = 0; s < kNumTileBM; ++s) {
     if (e < E) toff.p[s][e] = tx[s];
@@ -244,14 +247,46 @@ __global__ __launch_bounds__(256) void slots_kernel(
 
 // x_perm[slot(t, k)] = x[t] for the workgroup's tpb tokens; cpr 16-byte
 // chunks per row.
+// SCAN (E * nblk <= kScatterThreads): `first` still holds the chunk
+// histograms; every workgroup scans them in LDS (expert-major order, as
+// the scan kernel does) instead of a separate single-workgroup launch,
+// and workgroup 0 writes counts, offsets and the row-tile prefixes.
+template <bool SCAN>
 __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ first, const int32_t* __restrict__ rank,
     int T, int E, int K, int cpr, int tpb, int32_t* __restrict__ dest,
-    int32_t* __restrict__ sorted_src, u32x4* __restrict__ xp) {
+    int32_t* __restrict__ sorted_src, u32x4* __restrict__ xp, int nblk,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    TileOffPtrs toff) {
   __shared__ int32_t slot[kScatterThreads];
+  __shared__ int32_t sfirst[SCAN ? kScatterThreads : 1];
+  __shared__ int32_t wsum[16 * kNumTileBM];
+  constexpr int NW = kScatterThreads / kWave;
+  const int32_t* fst = first;
+  if constexpr (SCAN) {
+    const int tid = threadIdx.x, ne = E * nblk;
+    const int e = tid / nblk, c = tid % nblk;
+    int v[1] = {tid < ne ? first[(long)c * E + e] : 0};
+    block_exclusive_scan<1, NW>(v, wsum);
+    if (tid < ne) sfirst[c * E + e] = v[0];
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      const int TK = T * K;
+      int cnt = 0;
+      if (tid < E) {  // chunk 0 of expert e: its first slot
+        const int o = sfirst[tid];
+        cnt = (tid + 1 < E ? sfirst[tid + 1] : TK) - o;
+        counts[tid] = cnt;
+        offsets[tid] = o;
+      }
+      if (tid == 0) offsets[E] = TK;
+      write_tile_prefix<NW>(cnt, E, toff, wsum);
+    }
+    fst = sfirst;
+  }
   const long t0 = (long)blockIdx.x * tpb;
-  const int ntok = block_slots(idx, first, rank, E, K, t0, tpb, T, dest,
+  const int ntok = block_slots(idx, fst, rank, E, K, t0, tpb, T, dest,
                                sorted_src, slot);
   const int n = ntok * cpr;
   constexpr int U = 4;  // chunks in flight per thread
@@ -511,13 +546,19 @@ int scatter_tokens_per_block(int K, long row_bytes) {
   return (int)tpb;
 }
 
+bool scan_in_scatter(int TK, int E) {
+  return (long)E * ((TK + kPermChunk - 1) / kPermChunk) <= kScatterThreads;
+}
+
 hipError_t launch_hist_rank_scan(const int32_t* idx, int TK, int E,
                                  int32_t* block_hist, int32_t* rank,
                                  int32_t* counts, int32_t* offsets,
-                                 int32_t* const* tile_off, hipStream_t s) {
+                                 int32_t* const* tile_off, hipStream_t s,
+                                 bool scan) {
   const int nblk = (TK + kPermChunk - 1) / kPermChunk;
   hipLaunchKernelGGL(hist_rank_kernel, dim3(nblk), dim3(kRankWaves * kWave), 0,
                      s, idx, TK, E, perm_nbits(E), block_hist, rank);
+  if (!scan) return hipGetLastError();
   TileOffPtrs tp;
   for (int i = 0; i < kNumTileBM; ++i) tp.p[i] = tile_off[i];
   int ep = 1;
@@ -547,13 +588,26 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int E,
 hipError_t launch_scatter(const void* x, const int32_t* idx,
                           const int32_t* first, const int32_t* rank, int T,
                           int E, int K, long row_bytes, int32_t* dest,
-                          int32_t* sorted_src, void* x_perm, hipStream_t s) {
+                          int32_t* sorted_src, void* x_perm, hipStream_t s,
+                          int32_t* counts, int32_t* offsets,
+                          int32_t* const* tile_off) {
   const int tpb = scatter_tokens_per_block(K, row_bytes);
   const long blocks = (T + tpb - 1) / tpb;
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)blocks), dim3(kScatterThreads),
-                     0, s, (const u32x4*)x, idx, first, rank, T, E, K,
-                     (int)(row_bytes / 16), tpb, dest, sorted_src,
-                     (u32x4*)x_perm);
+  const int TK = T * K;
+  TileOffPtrs tp{};
+  if (counts)
+    for (int i = 0; i < kNumTileBM; ++i) tp.p[i] = tile_off[i];
+  if (counts && scan_in_scatter(TK, E))
+    hipLaunchKernelGGL(scatter_kernel<true>, dim3((unsigned)blocks),
+                       dim3(kScatterThreads), 0, s, (const u32x4*)x, idx, first,
+                       rank, T, E, K, (int)(row_bytes / 16), tpb, dest,
+                       sorted_src, (u32x4*)x_perm,
+                       (TK + kPermChunk - 1) / kPermChunk, counts, offsets, tp);
+  else
+    hipLaunchKernelGGL(scatter_kernel<false>, dim3((unsigned)blocks),
+                       dim3(kScatterThreads), 0, s, (const u32x4*)x, idx, first,
+                       rank, T, E, K, (int)(row_bytes / 16), tpb, dest,
+                       sorted_src, (u32x4*)x_perm, 0, nullptr, nullptr, tp);
   return hipGetLastError();
 }
 
