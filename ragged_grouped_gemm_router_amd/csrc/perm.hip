@@ -407,8 +407,18 @@ __global__ __launch_bounds__(kScatterThreads) void combine_k_kernel(
       const int i = min(i0 + u * kScatterThreads, n - 1);
       const int tl = i / cpr, c = (i % cpr) * 8;
 #pragma unroll
-      for (int k = 0; k < KT; ++k)
-        load8(y + (long)sd[tl * KT + k] * d + c, v[u][k]);
+      for (int k = 0; k < KT; ++k) {
+        const T* row = y + (long)sd[tl * KT + k] * d + c;
+        if constexpr (sizeof(T) == 2 && KT >= 8) {
+          // many rows gathered per token, each read once: streaming
+          // loads (measured: K = 8 combine 126 -> 107 us at d = 7168)
+          const bf16x8 a = __builtin_nontemporal_load((const bf16x8*)row);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[u][k][q] = (float)a[q];
+        } else {
+          load8(row, v[u][k]);
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -618,7 +628,7 @@ hipError_t launch_combine_t(const T* y, const int32_t* dest, const float* w,
   const int tpb = scatter_tokens_per_block(K, (long)d * sizeof(T));
   const dim3 grid((unsigned)((Ttok + tpb - 1) / tpb)), block(kScatterThreads);
   if (K == 2)
-    hipLaunchKernelGGL((combine_k_kernel<T, 4, 2>), grid, block, 0, s, y, dest, w,
+    hipLaunchKernelGGL((combine_k_kernel<T, 8, 2>), grid, block, 0, s, y, dest, w,
                        add, out, Ttok, d, tpb);
   else if (K == 4)
     hipLaunchKernelGGL((combine_k_kernel<T, 2, 4>), grid, block, 0, s, y, dest, w,
