@@ -1291,14 +1291,19 @@ bool force_staged() {
   return v;
 }
 
-// n-tiles per rasterization group (MOE_TILE_GROUP_N overrides, for tuning)
-int tile_group_n() {
+// n-tiles per rasterization group for a product of tiles_n column tiles:
+// all of them when there are at most 8 (the row tiles of an expert then
+// run back to back over its whole weight panel: skewed shape, GEMM 1
+// 0.898 -> 0.867 ms), else 4 (Mixtral and DeepSeek-V3 shapes, where wider
+// groups measured slower). MOE_TILE_GROUP_N overrides, for tuning.
+int tile_group_n(int tiles_n) {
   static const int v = [] {
     const char* e = getenv("MOE_TILE_GROUP_N");
     const int n = e ? atoi(e) : 0;
-    return n > 0 ? n : 4;
+    return n > 0 ? n : 0;
   }();
-  return v;
+  if (v > 0) return v;
+  return tiles_n <= 8 ? (tiles_n > 0 ? tiles_n : 1) : 4;
 }
 
 bool mfma_supported(GemmOp op, const GemmParams& p) {
@@ -1333,7 +1338,6 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   if (p.gsrc && !(op == kOpGemm1Mx ||
                   (op == kOpGemm1 && gemm1_gather_supported(p.K))))
     return hipErrorNotSupported;
-  p.group_n = tile_group_n();
   // Big tiles when the average group has enough rows to fill them.
   bool big;
   if (op == kOpWgrad || op == kOpRouterDw || op == kOpWgradT) {
@@ -1352,6 +1356,14 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
     } else {
       p.tiles_m_max = (p.M + bm - 1) / bm;
     }
+  }
+  {  // column tile width of the kernel chosen below; the backward
+     // products keep groups of 4 (wider ones measured slower for dgrad1)
+    const bool dual = op == kOpGemm1 || op == kOpGemm1Mx || op == kOpGemm1MxAct;
+    const bool fwd = dual || op == kOpGemm2 || op == kOpGemm2Mx || op == kOpRouter;
+    const int bn = op == kOpRouter && p.N <= 32 ? 32
+                   : dual ? (big ? 128 : 64) : (big ? 256 : 128);
+    p.group_n = tile_group_n(fwd ? (p.N + bn - 1) / bn : 1 << 30);
   }
   // k-contiguous operands with whole k-tiles go straight to LDS
   if (p.K % 64 == 0 && !force_staged()) {
