@@ -23,6 +23,7 @@ SMALL = [
     mi.MoEConfig("g_skewed_like_T2048_d256_f128_E32_K4", 2048, 256, 128, 32,
                  4, synth_logits=True, n_zero=4, zipf_s=1.2),
     mi.MoEConfig("g_tail_T333_d192_f256_E16_K3", 333, 192, 256, 16, 3),
+    mi.MoEConfig("g_mid_rows_T1024_d256_f256_E16_K2", 1024, 256, 256, 16, 2),
 ]
 MX_SMALL = [
     mi.MoEConfig("gmx_T1024_d256_f512_E8_K2", 1024, 256, 512, 8, 2),

@@ -27,6 +27,10 @@ SMALL = [
                  64, 8, f_shared=256, gate="sigmoid", bias=True),
     mi.MoEConfig("skewed_like_T2048_d256_f128_E32_K4", 2048, 256, 128, 32, 4,
                  synth_logits=True, n_zero=4, zipf_s=1.2),
+    # ~128 rows per expert, as in the DeepSeek-V3 shape: one 256-row tile
+    # per expert with the empty 32-row blocks' MFMAs skipped
+    mi.MoEConfig("deepseek_mid_rows_T1024_d256_f256_E64_K8_shared", 1024, 256,
+                 256, 64, 8, f_shared=256, gate="sigmoid", bias=True),
 ]
 IDS = [c.name for c in SMALL]
 
