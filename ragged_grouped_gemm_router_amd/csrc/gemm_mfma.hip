@@ -940,7 +940,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 // every k-tile's buffer resource ends at the range end. KCAT contracts over
 // the concatenation [A | A2] . [B ; B2] with K1 rows in the first part.
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, bool KCAT,
-          int EPI, int SCHED>
+          int EPI, int SCHED, bool SKIP = false>
 __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
   typedef bf16x8 Frag;
   constexpr int NW = WGM * WGN, S = 2;
@@ -1060,8 +1060,14 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[0][i][j] = f32x16{};
+  // SKIP: as in the forward kernel, the MFMAs of 32-row blocks wholly
+  // past the group's end are skipped (groups of about half a tile)
+  constexpr bool kSkipTail = SKIP && SCHED == kSchedM && N_MFMA * 16 <= 128;
+  const int act_mb = __builtin_amdgcn_readfirstlane(
+      min(MB, max(0, (t.m_end - t.m0 - wm * WM + 31) / 32)));
   auto mfma_one = [&](const Frags& f, int q) {
     const int i = q / NB, j = q % NB;
+    if (kSkipTail && i >= act_mb) return;
     acc[0][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j],
                                                            acc[0][i][j], 0, 0, 0);
   };
@@ -1170,7 +1176,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
 }
 
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, bool KCAT,
-          int EPI, int SCHED>
+          int EPI, int SCHED, bool SKIP = false>
 hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   const long tiles_n = (p.N + BN - 1) / BN;
   long tiles;
@@ -1181,7 +1187,7 @@ hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
   tiles = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mfma_gemm_t<BM, BN, WGM, WGN, A_KM, B_KM, KCAT, EPI, SCHED>),
+  hipLaunchKernelGGL((mfma_gemm_t<BM, BN, WGM, WGN, A_KM, B_KM, KCAT, EPI, SCHED, SKIP>),
                      dim3((unsigned)tiles), dim3(WGM * WGN * kWave), 0, s, p);
   return hipGetLastError();
 }
@@ -1370,7 +1376,7 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
     // tiles give ~half the experts a second, nearly empty tile, and
     // 64-row tiles measured slower still)
     if (!big && p.off && rows_per_group >= 96 && p.N >= 256 &&
-        (op == kOpGemm1 || op == kOpGemm2))
+        (op == kOpGemm1 || op == kOpGemm2 || op == kOpDgrad2 || op == kOpDgrad1))
       big = skip = true;
     const int bm = op == kOpRouter && p.N <= 32 ? 32 : big ? 256 : 128;
     if (p.off) {
@@ -1415,6 +1421,10 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   // backward products on the direct-to-LDS kernel with k-major operands
   if (!force_staged()) {
     const bool w4 = big_tile_waves() == 4;
+    if (skip && op == kOpDgrad2 && p.K % 64 == 0)
+      return launch_t<256, 256, 2, 4, false, true, false, kEpiSwigluBwd, kSchedM, true>(p, s);
+    if (skip && op == kOpDgrad1 && p.K1 % 64 == 0 && p.K == 2 * p.K1)
+      return launch_t<256, 256, 2, 4, false, true, true, kEpiStore, kSchedM, true>(p, s);
     if (op == kOpDgrad2 && p.K % 64 == 0)
       return !big ? launch_t<128, 128, 2, 2, false, true, false, kEpiSwigluBwd, kSchedM>(p, s)
              : w4 ? launch_t<256, 256, 2, 2, false, true, false, kEpiSwigluBwd, kSchedM>(p, s)

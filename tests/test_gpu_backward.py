@@ -28,6 +28,9 @@ CASES = [
                  4, synth_logits=True, n_zero=3, zipf_s=1.2),
     mi.MoEConfig("many_experts_T256_d256_f128_E64_K8_sigmoid", 256, 256, 128,
                  64, 8, gate="sigmoid", bias=True),
+    # ~128 rows per expert: the data-gradient products run one 256-row
+    # tile per expert with the empty 32-row blocks' MFMAs skipped
+    mi.MoEConfig("mid_rows_T1024_d256_f256_E16_K2", 1024, 256, 256, 16, 2),
 ]
 
 
