@@ -1376,7 +1376,8 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
     // tiles give ~half the experts a second, nearly empty tile, and
     // 64-row tiles measured slower still)
     if (!big && p.off && rows_per_group >= 96 && p.N >= 256 &&
-        (op == kOpGemm1 || op == kOpGemm2 || op == kOpDgrad2 || op == kOpDgrad1))
+        (op == kOpGemm1 || op == kOpGemm2 || op == kOpDgrad2 || op == kOpDgrad1 ||
+         op == kOpGemm1Mx || op == kOpGemm1MxAct))
       big = skip = true;
     const int bm = op == kOpRouter && p.N <= 32 ? 32 : big ? 256 : 128;
     if (p.off) {
@@ -1451,9 +1452,11 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
     return big ? launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false, kSchedK>(p, s)
                : launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false, kSchedK>(p, s);
   if (op == kOpGemm1Mx)
-    return launch_dl_sized<true, kEpiSwigluMx, bf16, true>(big, p, s);
+    return skip ? launch_dl_sized<true, kEpiSwigluMx, bf16, true, true>(big, p, s)
+                : launch_dl_sized<true, kEpiSwigluMx, bf16, true>(big, p, s);
   if (op == kOpGemm1MxAct)
-    return launch_dl_sized<true, kEpiSwiglu, bf16, true>(big, p, s);
+    return skip ? launch_dl_sized<true, kEpiSwiglu, bf16, true, true>(big, p, s)
+                : launch_dl_sized<true, kEpiSwiglu, bf16, true>(big, p, s);
   if (op == kOpDgrad2Mx)
     return launch_dl_sized<false, kEpiSwigluBwd, bf16, true>(big, p, s);
   if (op == kOpGemm2Mx)
