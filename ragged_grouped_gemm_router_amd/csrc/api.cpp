@@ -76,6 +76,7 @@ struct BwdWs {
   void* daT;
   void* dbT;
   long ldT;
+  void* w2t;  // W2 transposed, [E, d_ff, d_model], for the dgrad2 product
   // MXFP8: dy_perm and [da | db] quantised, h dequantised for dW2
   uint8_t* dyq;
   uint8_t* dys;
@@ -177,6 +178,8 @@ size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
       if (t[i]) *t[i] = base + o;
       o = align_up(o + b * rows[i] * ldT);
     }
+    if (w) w->w2t = base + o;
+    o = align_up(o + b * (size_t)d->E * f * dm);
   }
   if (d->gemm_dtype == MOE_MXFP8) {
     const size_t dm = d->d_model, f = d->d_ff;
@@ -972,7 +975,14 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.B = a->routed.w2; p.ldb = f; p.sB = (long)dm * f;
     p.C = w.da; p.C2 = w.db; p.ldc = f;
     p.aux_a = sa; p.aux_b = sb;
-    MOE_TRY(run_gemm(kOpDgrad2, dt, p, w.tile_off, s));
+    if (wgrad_t_ok(d)) {  // experts of 512+ rows: W2 transposed once per
+                          // step, so the product reads it k-contiguous
+      MOE_TRY(launch_transpose_batched(a->routed.w2, E, dm, f, w.w2t, s));
+      p.B = w.w2t; p.ldb = dm; p.sB = (long)f * dm;
+      MOE_TRY(gemm_mfma(kOpDgrad2T, p, w.tile_off, s));
+    } else {
+      MOE_TRY(run_gemm(kOpDgrad2, dt, p, w.tile_off, s));
+    }
   }
   if (shared) {  // ungated: dh_s = dy Ws2, (da_s, db_s) in place of (a_s, b_s)
     GemmParams p = gp();

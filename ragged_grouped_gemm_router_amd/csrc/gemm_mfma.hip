@@ -1415,6 +1415,8 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
         if (skip)
           return launch_dl_sized<false, kEpiStore, bf16, false, true>(big, p, s);
         return launch_dl_sized<false, kEpiStore, bf16>(big, p, s);
+      case kOpDgrad2T:
+        return launch_dl_sized<false, kEpiSwigluBwd, bf16>(big, p, s);
       default:
         break;
     }

@@ -503,6 +503,30 @@ int perm_nbits(int E) {
   return nbits;
 }
 
+// dst[b, c, r] = src[b, r, c]: matrix blockIdx.z, the 64 x 64 block at
+// rows 64 * blockIdx.y and columns 64 * blockIdx.x through LDS, in 16-byte
+// row pieces both ways (R, C multiples of 64).
+__global__ __launch_bounds__(256) void transpose_batched_kernel(
+    const bf16* __restrict__ src, int R, int C, bf16* __restrict__ dst) {
+  __shared__ bf16 tile[64][72];
+  const long base = (long)blockIdx.z * R * C;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  for (int q = threadIdx.x; q < 64 * 8; q += 256) {
+    const int r = q / 8, cc = (q % 8) * 8;
+    const bf16x8 v = *(const bf16x8*)(src + base + (long)(r0 + r) * C + c0 + cc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[r][cc + i] = v[i];
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < 64 * 8; q += 256) {
+    const int c = q / 8, rr = (q % 8) * 8;
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = tile[rr + i][c];
+    *(bf16x8*)(dst + base + (long)(c0 + c) * R + r0 + rr) = o;
+  }
+}
+
 // Transpose with per-group padding: for each expert e with rows
 // [off[e], off[e+1]) of src [rows, C] (bf16), dst[c, 64 * t64[e] + i] =
 // src[off[e] + i, c] for i < count_e, and zero up to the next multiple of
@@ -536,6 +560,15 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(
 }
 
 }  // namespace
+
+hipError_t launch_transpose_batched(const void* src, int B, int R, int C,
+                                    void* dst, hipStream_t s) {
+  if (B <= 0 || R <= 0 || C <= 0) return hipSuccess;
+  if (R % 64 || C % 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_batched_kernel, dim3(C / 64, R / 64, B), dim3(256),
+                     0, s, (const bf16*)src, R, C, (bf16*)dst);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose_pad(const void* src, int rows_max, int C,
                                 const int32_t* off, const int32_t* t64, int E,
