@@ -76,7 +76,11 @@ struct BwdWs {
   void* daT;
   void* dbT;
   long ldT;
-  void* w2t;  // W2 transposed, [E, d_ff, d_model], for the dgrad2 product
+  // weights transposed for the data-gradient products: W2^T [E, d_ff,
+  // d_model], then (reusing its space) W1^T and W3^T [E, d_model, d_ff]
+  void* w2t;
+  void* w1t;
+  void* w3t;
   // MXFP8: dy_perm and [da | db] quantised, h dequantised for dW2
   uint8_t* dyq;
   uint8_t* dys;
@@ -178,7 +182,9 @@ size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
       if (t[i]) *t[i] = base + o;
       o = align_up(o + b * rows[i] * ldT);
     }
-    if (w) w->w2t = base + o;
+    if (w) w->w2t = w->w1t = base + o;
+    o = align_up(o + b * (size_t)d->E * f * dm);
+    if (w) w->w3t = base + o;
     o = align_up(o + b * (size_t)d->E * f * dm);
   }
   if (d->gemm_dtype == MOE_MXFP8) {
@@ -1000,7 +1006,14 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.A = w.da; p.A2 = w.db; p.lda = f;
     p.B = a->routed.w1; p.B2 = a->routed.w3; p.ldb = dm; p.sB = (long)f * dm;
     p.C = w.dx_perm; p.ldc = dm;
-    MOE_TRY(run_gemm(kOpDgrad1, dt, p, w.tile_off, s));
+    if (wgrad_t_ok(d)) {  // W1, W3 transposed (into the space of W2^T)
+      MOE_TRY(launch_transpose_batched(a->routed.w1, E, f, dm, w.w1t, s));
+      MOE_TRY(launch_transpose_batched(a->routed.w3, E, f, dm, w.w3t, s));
+      p.B = w.w1t; p.B2 = w.w3t; p.ldb = f; p.sB = (long)dm * f;
+      MOE_TRY(gemm_mfma(kOpDgrad1T, p, w.tile_off, s));
+    } else {
+      MOE_TRY(run_gemm(kOpDgrad1, dt, p, w.tile_off, s));
+    }
   }
   if (shared) {  // dx_s = da_s Ws1 + db_s Ws3
     GemmParams p = gp();

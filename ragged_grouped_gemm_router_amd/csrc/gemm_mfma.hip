@@ -535,7 +535,7 @@ template <> struct Fmt<true> {
 
 template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
           typename TO, bool MX, int SCHED = kSchedM, int TAIL = 0,
-          bool SKIP = false>
+          bool SKIP = false, bool KCAT = false>
 __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) {
   using F = Fmt<MX>;
   typedef typename F::Frag Frag;
@@ -606,17 +606,29 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     const int grow = min(t.n0 + row, p.N - 1);
     b_off[j] = (grow - t.n0) * p.ldb * F::ES + swz<CPR>(row, phys) * 16;
   }
+  // KCAT: the contraction runs over [A | A2] . [B ; B2], the first K1
+  // indices from A, B (k-tiles below nk1) and the rest from A2, B2, all
+  // with the same strides, so the lane offsets serve both parts
+  static_assert(!KCAT || (!DUAL && !MX && SCHED == kSchedM), "K-concatenation");
+  const int nk1 = KCAT ? p.K1 / BK : 0;
+  Rsrc ra2 = ra, rb2 = rb[0];
+  if (KCAT) {
+    ra2 = make_rsrc((const char*)p.A2 + (long)t.m0 * p.lda * F::ES);
+    rb2 = make_rsrc((const char*)p.B2 +
+                    ((long)t.g * p.sB + (long)t.n0 * p.ldb) * F::ES);
+  }
 
   // DMA instruction d of a k-tile (d < A_INS: operand A, then each B)
   auto issue_one = [&](int kt, int stage, int d) {
     char* base = lds + stage * STAGE;
-    const int k0 = (kt0 + kt) * RB;
+    const bool second = KCAT && kt >= nk1;
+    const int k0 = (kt0 + kt - (second ? nk1 : 0)) * RB;
     if (d < A_INS) {
-      dma16(ra, base + (d * NW + wave) * 1024, a_off[d], k0);
+      dma16(second ? ra2 : ra, base + (d * NW + wave) * 1024, a_off[d], k0);
     } else {
       const int o = (d - A_INS) / B_INS, j = (d - A_INS) % B_INS;
-      dma16(rb[o], base + A_BYTES + o * B_BYTES + (j * NW + wave) * 1024,
-            b_off[j], k0);
+      dma16(second ? rb2 : rb[o],
+            base + A_BYTES + o * B_BYTES + (j * NW + wave) * 1024, b_off[j], k0);
     }
   };
   auto issue = [&](int kt, int stage) {
@@ -1214,7 +1226,7 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 
 template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
           typename TO, bool MX, int SCHED = kSchedM, int TAIL = 0,
-          bool SKIP = false>
+          bool SKIP = false, bool KCAT = false>
 hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
   const long tiles_n = (p.N + BN - 1) / BN;
   long tiles = SCHED == kSchedK
@@ -1225,7 +1237,7 @@ hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
   tiles = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, S, WGM, WGN, DUAL, EPI, TO, MX, SCHED, TAIL, SKIP>),
+  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, S, WGM, WGN, DUAL, EPI, TO, MX, SCHED, TAIL, SKIP, KCAT>),
                      dim3((unsigned)tiles), dim3(WGM * WGN * kWave), 0, s, p);
   return hipGetLastError();
 }
@@ -1417,6 +1429,12 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
         return launch_dl_sized<false, kEpiStore, bf16>(big, p, s);
       case kOpDgrad2T:
         return launch_dl_sized<false, kEpiSwigluBwd, bf16>(big, p, s);
+      case kOpDgrad1T:
+        if (p.K1 % 64 || p.K != 2 * p.K1) return hipErrorNotSupported;
+        return big ? launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
+                               kSchedM, 0, false, true>(p, s)
+                   : launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false,
+                               kSchedM, 0, false, true>(p, s);
       default:
         break;
     }
