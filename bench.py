@@ -157,7 +157,7 @@ def main():
                          "(a known-size kernel to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} "
+        print(f"bench.py: this implementation runs on one GPU only; --gpus {args.gpus} "
               "is not supported (the layer does not shard across GPUs here)",
               file=sys.stderr)
         sys.exit(2)

@@ -56,7 +56,7 @@ extern "C" {
 typedef int32_t moe_status;
 #define MOE_OK            0
 #define MOE_EINVAL        1  /* NULL pointer, negative or inconsistent size */
-#define MOE_EUNSUPPORTED  2  /* valid but outside this build's limits     */
+#define MOE_EUNSUPPORTED  2  /* valid but outside this library's limits   */
 #define MOE_EWORKSPACE    3  /* workspace smaller than moe_workspace_size */
 #define MOE_EHIP          4  /* HIP runtime reported an error             */
 
@@ -77,7 +77,7 @@ typedef int32_t moe_status;
    bit-identical either way (same accumulation order per output). */
 #define MOE_FLAG_NO_TAIL_SPLIT 2
 
-/* limits of this build */
+/* limits of this library */
 #define MOE_K_MAX 16
 #define MOE_E_MAX 1024
 

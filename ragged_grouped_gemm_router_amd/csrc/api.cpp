@@ -632,7 +632,7 @@ const char* moe_status_str(moe_status st) {
   switch (st) {
     case MOE_OK: return "MOE_OK";
     case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
-    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: outside this build's limits";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: outside this library's limits";
     case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
     case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
   }
