@@ -126,8 +126,9 @@ size_t fwd_ws_layout(const moe_desc* d, char* base, FwdWs* w) {
 
 bool force_simt();
 
-// The bf16 weight gradients run on the direct-to-LDS kernel from transposed
-// operands when the widths allow and the experts average at least 512
+// The weight gradients (bf16, in the MXFP8 backward too) run on the
+// direct-to-LDS kernel from transposed operands when the widths allow and
+// the experts average at least 512
 // rows (eight k-tiles; with fewer, the transposes and the pipeline fill
 // cost more than the faster loop saves). MOE_WGRAD_T=0 keeps the
 // transposing-read kernel, for comparison.
@@ -136,10 +137,18 @@ bool wgrad_t_ok(const moe_desc* d) {
     const char* e = getenv("MOE_WGRAD_T");
     return e && strcmp(e, "0") == 0;
   }();
-  return d->act_dtype == MOE_BF16 && d->gemm_dtype == MOE_BF16 &&
+  return d->act_dtype == MOE_BF16 &&
+         (d->gemm_dtype == MOE_BF16 || d->gemm_dtype == MOE_MXFP8) &&
          d->d_model % 64 == 0 && d->d_ff % 64 == 0 &&
          (long)d->T * d->K >= 512L * d->E && !env_off && !force_simt() &&
          gemm_direct_ok();
+}
+
+// bf16 backward with experts of 512+ rows: the data-gradient products read
+// the weights transposed once per step (the MXFP8 backward takes them
+// transposed and quantised from the caller)
+bool dgrad_t_ok(const moe_desc* d) {
+  return wgrad_t_ok(d) && d->gemm_dtype == MOE_BF16;
 }
 
 size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
@@ -182,10 +191,12 @@ size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
       if (t[i]) *t[i] = base + o;
       o = align_up(o + b * rows[i] * ldT);
     }
-    if (w) w->w2t = w->w1t = base + o;
-    o = align_up(o + b * (size_t)d->E * f * dm);
-    if (w) w->w3t = base + o;
-    o = align_up(o + b * (size_t)d->E * f * dm);
+    if (dgrad_t_ok(d)) {
+      if (w) w->w2t = w->w1t = base + o;
+      o = align_up(o + b * (size_t)d->E * f * dm);
+      if (w) w->w3t = base + o;
+      o = align_up(o + b * (size_t)d->E * f * dm);
+    }
   }
   if (d->gemm_dtype == MOE_MXFP8) {
     const size_t dm = d->d_model, f = d->d_ff;
@@ -526,15 +537,31 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
   MOE_TRY(launch_combine(MOE_BF16, w.dx_perm, a->dest, nullptr,
                          shared ? w.sdx : nullptr, a->dx, d->T, d->K, dm, s));
   record(a->events[5], s);
+  // weight gradients in bf16; with experts of 512+ rows from transposed,
+  // group-padded operands as in the bf16 backward
+  const bool wt = wgrad_t_ok(d);
+  const int32_t* t64 = w.tile_off[tile_bm_slot(64)];
   {  // dW2_e = dy_perm^T h, h dequantised from the forward's codes
     const uint8_t* hq = (const uint8_t*)a->h;
     MOE_TRY(launch_dequantize_mxfp8(hq, hq + (size_t)TK * f, TK, f, w.h_bf, s));
     GemmParams p = gp();
-    p.M = dm; p.N = f; p.G = E; p.off = a->offsets;
-    p.A = w.dy_perm; p.lda = dm;
-    p.B = w.h_bf; p.ldb = f;
+    p.M = dm; p.N = f; p.G = E;
     p.C = a->dw2; p.ldc = f; p.sC = (long)dm * f;
-    MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
+    if (wt) {
+      MOE_TRY(launch_transpose_pad(w.dy_perm, TK, dm, a->offsets, t64, E,
+                                   w.dyT, w.ldT, s));
+      MOE_TRY(launch_transpose_pad(w.h_bf, TK, f, a->offsets, t64, E, w.hT,
+                                   w.ldT, s));
+      p.off = t64; p.kmul = 64;
+      p.A = w.dyT; p.lda = w.ldT;
+      p.B = w.hT; p.ldb = w.ldT;
+      MOE_TRY(gemm_mfma(kOpWgradT, p, w.tile_off, s));
+    } else {
+      p.off = a->offsets;
+      p.A = w.dy_perm; p.lda = dm;
+      p.B = w.h_bf; p.ldb = f;
+      MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
+    }
   }
   if (shared) {  // dWs2 = dy^T h_s, h_s dequantised; x dequantised too
     MOE_TRY(launch_dequantize_mxfp8(w.shq, w.shs, T, fs, w.sh, s));
@@ -551,13 +578,29 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
   // dx_perm buffer, free after the gather-sum)
   MOE_TRY(launch_dequantize_mxfp8((const uint8_t*)a->x_perm, a->x_perm_scales,
                                   TK, dm, w.dx_perm, s));
+  if (wt) {
+    MOE_TRY(launch_transpose_pad(w.dx_perm, TK, dm, a->offsets, t64, E, w.xT,
+                                 w.ldT, s));
+    MOE_TRY(launch_transpose_pad(w.da, TK, f, a->offsets, t64, E, w.daT,
+                                 w.ldT, s));
+    MOE_TRY(launch_transpose_pad(w.db, TK, f, a->offsets, t64, E, w.dbT,
+                                 w.ldT, s));
+  }
   for (int which = 0; which < 2; ++which) {
     GemmParams p = gp();
-    p.M = f; p.N = dm; p.G = E; p.off = a->offsets;
-    p.A = which ? w.db : w.da; p.lda = f;
-    p.B = w.dx_perm; p.ldb = dm;
+    p.M = f; p.N = dm; p.G = E;
     p.C = which ? a->dw3 : a->dw1; p.ldc = dm; p.sC = (long)f * dm;
-    MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
+    if (wt) {
+      p.off = t64; p.kmul = 64;
+      p.A = which ? w.dbT : w.daT; p.lda = w.ldT;
+      p.B = w.xT; p.ldb = w.ldT;
+      MOE_TRY(gemm_mfma(kOpWgradT, p, w.tile_off, s));
+    } else {
+      p.off = a->offsets;
+      p.A = which ? w.db : w.da; p.lda = f;
+      p.B = w.dx_perm; p.ldb = dm;
+      MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
+    }
     if (shared) {  // dWs1 = da_s^T x, dWs3 = db_s^T x (x as quantised)
       GemmParams q = gp();
       q.M = fs; q.N = dm; q.G = 1; q.off = w.srange;
@@ -981,7 +1024,7 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.B = a->routed.w2; p.ldb = f; p.sB = (long)dm * f;
     p.C = w.da; p.C2 = w.db; p.ldc = f;
     p.aux_a = sa; p.aux_b = sb;
-    if (wgrad_t_ok(d)) {  // experts of 512+ rows: W2 transposed once per
+    if (dgrad_t_ok(d)) {  // experts of 512+ rows: W2 transposed once per
                           // step, so the product reads it k-contiguous
       MOE_TRY(launch_transpose_batched(a->routed.w2, E, dm, f, w.w2t, s));
       p.B = w.w2t; p.ldb = dm; p.sB = (long)f * dm;
@@ -1006,7 +1049,7 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.A = w.da; p.A2 = w.db; p.lda = f;
     p.B = a->routed.w1; p.B2 = a->routed.w3; p.ldb = dm; p.sB = (long)f * dm;
     p.C = w.dx_perm; p.ldc = dm;
-    if (wgrad_t_ok(d)) {  // W1, W3 transposed (into the space of W2^T)
+    if (dgrad_t_ok(d)) {  // W1, W3 transposed (into the space of W2^T)
       MOE_TRY(launch_transpose_batched(a->routed.w1, E, f, dm, w.w1t, s));
       MOE_TRY(launch_transpose_batched(a->routed.w3, E, f, dm, w.w3t, s));
       p.B = w.w1t; p.B2 = w.w3t; p.ldb = f; p.sB = (long)dm * f;
