@@ -1053,6 +1053,7 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
       MOE_TRY(launch_transpose_batched(a->routed.w1, E, f, dm, w.w1t, s));
       MOE_TRY(launch_transpose_batched(a->routed.w3, E, f, dm, w.w3t, s));
       p.B = w.w1t; p.B2 = w.w3t; p.ldb = f; p.sB = (long)dm * f;
+      p.slots = d->flags & MOE_FLAG_NO_TAIL_SPLIT ? 0 : -1;
       MOE_TRY(gemm_mfma(kOpDgrad1T, p, w.tile_off, s));
     } else {
       MOE_TRY(run_gemm(kOpDgrad1, dt, p, w.tile_off, s));

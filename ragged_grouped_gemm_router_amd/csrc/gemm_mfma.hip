@@ -1431,6 +1431,15 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
         return launch_dl_sized<false, kEpiSwigluBwd, bf16>(big, p, s);
       case kOpDgrad1T:
         if (p.K1 % 64 || p.K != 2 * p.K1) return hipErrorNotSupported;
+        if (big && p.slots != 0 && p.off) {  // split last round, as GEMM 2
+          GemmParams q = p;
+          if (q.slots < 0) q.slots = num_cus();
+          hipError_t e = launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
+                                   kSchedM, 1, false, true>(q, s);
+          if (e != hipSuccess) return e;
+          return launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false,
+                           kSchedM, 2, false, true>(q, s);
+        }
         return big ? launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
                                kSchedM, 0, false, true>(p, s)
                    : launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false,
