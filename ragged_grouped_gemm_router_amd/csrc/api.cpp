@@ -375,6 +375,7 @@ hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
   p.B = rw->w2; p.ldb = f; p.sB = (long)dm * f;
   p.Bs = rw->w2_scales; p.ld_s = f / 32; p.sBs = (long)dm * (f / 32);
   p.C = y_perm; p.ldc = dm;
+  p.slots = d->flags & MOE_FLAG_NO_TAIL_SPLIT ? 0 : -1;
   e = gemm_mfma(kOpGemm2Mx, p, ws.tile_off, s);
   if (e != hipSuccess || !x_shared || d->d_ff_shared == 0) return e;
   const int T = d->T, fs = d->d_ff_shared;
@@ -523,6 +524,7 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.B = a->w13t; p.ldb = 2 * f; p.sB = (long)dm * 2 * f;
     p.Bs = a->w13t_scales; p.ld_s = 2 * f / 32; p.sBs = (long)dm * (2 * f / 32);
     p.C = w.dx_perm; p.ldc = dm;
+    p.slots = d->flags & MOE_FLAG_NO_TAIL_SPLIT ? 0 : -1;
     MOE_TRY(gemm_mfma(kOpGemm2Mx, p, w.tile_off, s));
   }
   if (shared) {  // dx_s = Q([da_s | db_s]) Ws13t

@@ -1279,8 +1279,20 @@ hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
   // takes four (its 8-wave form runs out of registers and spills).
   if (big) {
     const int forced = big_tile_waves();
-    if (forced == 4 || (forced == 0 && MX && !DUAL))
+    if (forced == 4 || (forced == 0 && MX && !DUAL)) {
+      // (the single-B MXFP8 product: its partial last round split as below)
+      if constexpr (MX && !DUAL) {
+        if (forced == 0 && p.slots != 0 && p.off) {
+          GemmParams q = p;
+          if (q.slots < 0) q.slots = num_cus();
+          hipError_t e = launch_dl<256, 256, 2, 2, 2, false, EPI, TO, MX,
+                                   kSchedM, 1>(q, s);
+          if (e != hipSuccess) return e;
+          return launch_dl<128, 128, 2, 2, 2, false, EPI, TO, MX, kSchedM, 2>(q, s);
+        }
+      }
       return launch_dl<256, DUAL ? 128 : 256, 2, 2, 2, DUAL, EPI, TO, MX>(p, s);
+    }
     // bf16 row-grouped products: a partial last round of big tiles runs
     // as quarter tiles (128 x 128, or 128 x 64 x 2 dual) in a second launch
     if constexpr (!MX) {

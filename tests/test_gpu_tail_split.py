@@ -102,3 +102,33 @@ def test_tail_split_training_step_bit_identical():
         assert torch.equal(f0[k], f1[k]), k
     for k in ("dx", "dw1", "dw3", "dw2", "d_topk_w"):
         assert torch.equal(g0[k], g1[k]), k
+
+
+def test_tail_split_mxfp8_training_step_bit_identical():
+    """The same for the MXFP8 training step: its single-B products (GEMM 2
+    and the backward's dx_perm product, 16 column tiles each) split their
+    last round like the bf16 GEMM 2."""
+    from moe_testlib import inputs
+    from ragged_grouped_gemm_router_amd import layer as L
+    import moe_inputs as mi
+    cfg = mi.MIXTRAL_TRAIN
+    _, ginp = inputs(cfg, seed=4, with_dy=True, device_gen=True)
+    ginp = dict(ginp)
+    ginp["mx"] = L.quantize_expert_weights(ginp)
+    ginp["mx_bwd"] = L.quantize_expert_weights_bwd(ginp)
+    res = []
+    for flags in (0, B.MOE_FLAG_NO_TAIL_SPLIT):
+        desc = B.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.K, cfg.f_shared,
+                           gate=cfg.gate, mxfp8=True, save_acts=True)
+        desc.flags |= flags
+        fb = L.alloc_forward(desc, DEV)
+        L.forward(desc, ginp, fb)
+        gb = L.alloc_backward(desc, DEV)
+        L.backward(desc, ginp, fb, ginp["dy"], gb)
+        torch.cuda.synchronize()
+        res.append((fb, gb))
+    (f0, g0), (f1, g1) = res
+    for k in ("y_perm", "out"):
+        assert torch.equal(f0[k], f1[k]), k
+    for k in ("dx", "dw1", "dw3", "dw2", "d_topk_w"):
+        assert torch.equal(g0[k], g1[k]), k
