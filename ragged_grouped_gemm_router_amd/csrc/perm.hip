@@ -503,27 +503,30 @@ int perm_nbits(int E) {
   return nbits;
 }
 
-// dst[b, c, r] = src[b, r, c]: matrix blockIdx.z, the 64 x 64 block at
-// rows 64 * blockIdx.y and columns 64 * blockIdx.x through LDS, in 16-byte
-// row pieces both ways (R, C multiples of 64).
+// dst[b, c, r] = src[b, r, c] (R, C multiples of 64). Each wave moves a
+// 64 x 64 block of matrix blockIdx.z (rows 64 * blockIdx.y, columns
+// 64 * (4 * blockIdx.x + wave)): lane l loads the 8 x 8 piece at rows
+// 8 (l % 8), columns 8 (l / 8) as eight 16-byte row pieces, transposes it
+// in registers and stores eight 16-byte pieces, so every load and store
+// instruction of the wave covers 128-byte contiguous segments.
 __global__ __launch_bounds__(256) void transpose_batched_kernel(
     const bf16* __restrict__ src, int R, int C, bf16* __restrict__ dst) {
-  __shared__ bf16 tile[64][72];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int cblk = blockIdx.x * 4 + wave;
+  if (cblk * 64 >= C) return;
   const long base = (long)blockIdx.z * R * C;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  for (int q = threadIdx.x; q < 64 * 8; q += 256) {
-    const int r = q / 8, cc = (q % 8) * 8;
-    const bf16x8 v = *(const bf16x8*)(src + base + (long)(r0 + r) * C + c0 + cc);
+  const int r = blockIdx.y * 64 + (lane % 8) * 8;
+  const int c = cblk * 64 + (lane / 8) * 8;
+  bf16x8 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tile[r][cc + i] = v[i];
-  }
-  __syncthreads();
-  for (int q = threadIdx.x; q < 64 * 8; q += 256) {
-    const int c = q / 8, rr = (q % 8) * 8;
+  for (int i = 0; i < 8; ++i)
+    v[i] = *(const bf16x8*)(src + base + (long)(r + i) * C + c);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
     bf16x8 o;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = tile[rr + i][c];
-    *(bf16x8*)(dst + base + (long)(c0 + c) * R + r0 + rr) = o;
+    for (int i = 0; i < 8; ++i) o[i] = v[i][j];
+    *(bf16x8*)(dst + base + (long)(c + j) * R + r) = o;
   }
 }
 
@@ -565,7 +568,7 @@ hipError_t launch_transpose_batched(const void* src, int B, int R, int C,
                                     void* dst, hipStream_t s) {
   if (B <= 0 || R <= 0 || C <= 0) return hipSuccess;
   if (R % 64 || C % 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(transpose_batched_kernel, dim3(C / 64, R / 64, B), dim3(256),
+  hipLaunchKernelGGL(transpose_batched_kernel, dim3((C / 64 + 3) / 4, R / 64, B), dim3(256),
                      0, s, (const bf16*)src, R, C, (bf16*)dst);
   return hipGetLastError();
 }
