@@ -535,7 +535,7 @@ template <> struct Fmt<true> {
 
 template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
           typename TO, bool MX, int SCHED = kSchedM, int TAIL = 0,
-          bool SKIP = false, bool KCAT = false>
+          bool SKIP = false, bool KCAT = false, int SB = 0>
 __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) {
   using F = Fmt<MX>;
   typedef typename F::Frag Frag;
@@ -551,17 +551,28 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
   constexpr int STAGE = A_BYTES + NB_OPS * B_BYTES;
   constexpr int A_INS = BM / RPI / NW, B_INS = BN / RPI / NW;
+  // SB > S: the B operands run in a ring of SB stages of their own, so a
+  // weight-streaming product keeps SB - 1 k-tiles of B in flight while A
+  // (re-read by every column tile, so mostly an L2 hit) keeps S - 1
+  constexpr bool RING_B = SB > S;
+  static_assert(!RING_B || (!MX && !KCAT), "deeper B ring: bf16 operands");
+  constexpr int S_B = RING_B ? SB : S;
+  constexpr int A_STRIDE = RING_B ? A_BYTES : STAGE;
+  constexpr int B_STRIDE = RING_B ? NB_OPS * B_BYTES : STAGE;
+  constexpr int B_BASE = RING_B ? S * A_BYTES : A_BYTES;
+  constexpr int RING_BYTES = RING_B ? S * A_BYTES + SB * NB_OPS * B_BYTES : S * STAGE;
+  constexpr int NBL = NB_OPS * B_INS;  // B DMA instructions per k-tile
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile shape");
   static_assert(MB >= 1 && NB >= 1, "tile shape");
   static_assert(S >= 2 && KS % 2 == 0, "stage count, even substep count");
-  static_assert((S - 1) * (A_INS + (DUAL ? 2 : 1) * B_INS) <= 63, "vmcnt range");
+  static_assert((S - 1) * (A_INS + NBL) + (S_B - S) * NBL <= 63, "vmcnt range");
 
   // the epilogue stages 128 rows at a time (the quantising one only for
   // the optional pre-activation copies)
   constexpr int kEpiRows = BM > 128 ? 128 : BM;
   constexpr int EPI_BYTES =
       StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>::BYTES;
-  __shared__ __attribute__((aligned(1024))) char lds[S * STAGE > EPI_BYTES ? S * STAGE : EPI_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES];
 
   // the tile; grouped contraction (SCHED K): k-tiles [kt0, kt0 + nk) of
   // the group's range, which the host pads to whole k-tiles
@@ -618,22 +629,22 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
                     ((long)t.g * p.sB + (long)t.n0 * p.ldb) * F::ES);
   }
 
-  // DMA instruction d of a k-tile (d < A_INS: operand A, then each B)
-  auto issue_one = [&](int kt, int stage, int d) {
-    char* base = lds + stage * STAGE;
-    const bool second = KCAT && kt >= nk1;
-    const int k0 = (kt0 + kt - (second ? nk1 : 0)) * RB;
+  // DMA instruction d of a k-tile (d < A_INS: operand A of k-tile kt
+  // into A stage sa, then each B of k-tile ktb into B stage sbs)
+  auto issue_one = [&](int kt, int sa, int ktb, int sbs, int d) {
     if (d < A_INS) {
-      dma16(second ? ra2 : ra, base + (d * NW + wave) * 1024, a_off[d], k0);
+      const bool second = KCAT && kt >= nk1;
+      const int k0 = (kt0 + kt - (second ? nk1 : 0)) * RB;
+      dma16(second ? ra2 : ra, lds + sa * A_STRIDE + (d * NW + wave) * 1024,
+            a_off[d], k0);
     } else {
+      const bool second = KCAT && ktb >= nk1;
+      const int k0 = (kt0 + ktb - (second ? nk1 : 0)) * RB;
       const int o = (d - A_INS) / B_INS, j = (d - A_INS) % B_INS;
       dma16(second ? rb2 : rb[o],
-            base + A_BYTES + o * B_BYTES + (j * NW + wave) * 1024, b_off[j], k0);
+            lds + B_BASE + sbs * B_STRIDE + o * B_BYTES + (j * NW + wave) * 1024,
+            b_off[j], k0);
     }
-  };
-  auto issue = [&](int kt, int stage) {
-#pragma unroll
-    for (int d = 0; d < A_INS + NB_OPS * B_INS; ++d) issue_one(kt, stage, d);
   };
 
   // MXFP8: the 4 E8M0 codes of a row for one k-tile are one aligned dword;
@@ -684,7 +695,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // substep only, and the block offset is an immediate of the LDS read.
   const int lrow = lane % 32, half = lane / 32, sw = swz<CPR>(lrow, 0);
   const int a_row0 = (wm * WM + lrow) * RB;
-  const int b_row0 = A_BYTES + (wn * WN + lrow) * RB;
+  const int b_row0 = (wn * WN + lrow) * RB;
   auto read_frag = [&](const char* rowp, int ks) {
     if constexpr (MX) {
       // The scaled MFMA takes bytes 0-15 of a lane from the substep's first
@@ -708,13 +719,14 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // 32-byte fragments would spill.
   constexpr ReadOrder<MB, NB, NB_OPS, !(MX && DUAL)> kOrder{};
   // fragment kOrder.r[m] of substep ks (r < MB: A block r, else B block)
-  auto read_one = [&](const char* sb, int ks, Frags& f, int m) {
+  // from the A stage at sa and the B stage at sbb
+  auto read_one = [&](const char* sa, const char* sbb, int ks, Frags& f, int m) {
     const int r = kOrder.r[m];
     if (r < MB) {
-      f.a[r] = read_frag(sb + a_row0 + r * 32 * RB, ks);
+      f.a[r] = read_frag(sa + a_row0 + r * 32 * RB, ks);
     } else {
       const int o = (r - MB) / NB, j = (r - MB) % NB;
-      f.b[o][j] = read_frag(sb + b_row0 + o * B_BYTES + j * 32 * RB, ks);
+      f.b[o][j] = read_frag(sbb + b_row0 + o * B_BYTES + j * 32 * RB, ks);
     }
   };
   // per-lane E8M0 scale operands of one substep: block ks*2 + lane/32
@@ -761,21 +773,28 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
-  // Prologue: (scales of k-tile 0,) k-tiles 0 .. S-1 in flight (past the
-  // last tile, the last one again, into stages nobody reads); wait for
-  // tile 0.
+  // Prologue: (scales of k-tile 0,) k-tiles 0 .. S-1 in flight, and the
+  // B operands of k-tiles S .. S_B-1 (past the last tile, the last one
+  // again, into stages nobody reads); wait for tile 0.
   if (nk > 0) {  // (an empty group's tile writes zeros)
   load_scales(0);
 #pragma unroll
-  for (int i = 0; i < S; ++i) issue(min(i, nk - 1), i);
-  barrier_after(std::integral_constant<int, (S - 1) * N_LOAD>{});
+  for (int i = 0; i < S; ++i)
+#pragma unroll
+    for (int d = 0; d < N_LOAD; ++d)
+      issue_one(min(i, nk - 1), i, min(i, nk - 1), i, d);
+#pragma unroll
+  for (int i = S; i < S_B; ++i)
+#pragma unroll
+    for (int d = A_INS; d < N_LOAD; ++d) issue_one(0, 0, min(i, nk - 1), i, d);
+  barrier_after(std::integral_constant<int, (S - 1) * N_LOAD + (S_B - S) * NBL>{});
   if constexpr (MX) {
 #pragma unroll
     for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
   }
   Frags fa, fb;
 #pragma unroll
-  for (int r = 0; r < N_READ; ++r) read_one(lds, 0, fa, r);
+  for (int r = 0; r < N_READ; ++r) read_one(lds, lds + B_BASE, 0, fa, r);
 
   // One region per k-substep. The MFMAs run on fragments read a region
   // earlier; the memory instructions of the region (the next substep's
@@ -783,7 +802,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // kt+S into the stage tile kt used) sit between them, at most a few per
   // MFMA, so the in-order issue of a long memory burst never leaves the
   // matrix pipe idle. The tile barrier waits until only the S-2 newest
-  // tiles' DMA is outstanding, i.e. for tile kt+1. The first H MFMAs
+  // tiles' DMA (and, with a deeper B ring, the B DMA of the S_B-S newest
+  // B tiles) is outstanding, i.e. for tile kt+1. The first H MFMAs
   // precede every new read: their wait for the current fragments then
   // covers no read issued here. Every step is fenced with sched_barrier to
   // keep this order. (MXFP8: the next tile's scales are fetched in the
@@ -793,9 +813,12 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 #define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
   // stage of k-tile kt (kt mod S) and of k-tile kt + 1, kept as counters
   int st = 0, st_next = S > 1 ? 1 : 0;
+  int sbt = 0, sbt_next = 1;  // the same for the B ring
   for (int kt = 0; kt < nk; ++kt) {
-    const char* sb = lds + st * STAGE;
-    const char* sb_next = lds + st_next * STAGE;
+    const char* sa = lds + st * A_STRIDE;
+    const char* sa_next = lds + st_next * A_STRIDE;
+    const char* sbb = lds + B_BASE + sbt * B_STRIDE;
+    const char* sbb_next = lds + B_BASE + sbt_next * B_STRIDE;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       Frags& cur = (ks & 1) ? fb : fa;
@@ -817,7 +840,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
         // Branch-free so the wait counters stay exact: past the last tile
         // the reads return unused data and the DMA fetches the last k-tile
         // again into a stage that is no longer read.
-        barrier_after(std::integral_constant<int, (S - 2) * N_LOAD>{});
+        barrier_after(std::integral_constant<int, (S - 2) * N_LOAD + (S_B - S) * NBL>{});
         if constexpr (MX) {
 #pragma unroll
           for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
@@ -833,15 +856,16 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
         for (int mm = 0; mm < NM_MAX; ++mm) {
           if (mm < m || mm >= m_end) continue;
           if (!last) {
-            read_one(sb, ks + 1, nxt, mm);
+            read_one(sa, sbb, ks + 1, nxt, mm);
           } else {
             // reads spread evenly among the DMAs: op mm is a read iff the
             // running read quota floor(x * N_READ / NM_MAX) steps at it
             const int rb = mm * N_READ / NM_MAX;
             if ((mm + 1) * N_READ / NM_MAX != rb)
-              read_one(sb_next, 0, nxt, rb);
+              read_one(sa_next, sbb_next, 0, nxt, rb);
             else
-              issue_one(min(kt + S, nk - 1), st, mm - rb);
+              issue_one(min(kt + S, nk - 1), st, min(kt + S_B, nk - 1), sbt,
+                        mm - rb);
           }
           MOE_FENCE();
         }
@@ -852,6 +876,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     }
     st = st_next;
     st_next = st_next + 1 == S ? 0 : st_next + 1;
+    sbt = sbt_next;
+    sbt_next = sbt_next + 1 == S_B ? 0 : sbt_next + 1;
   }
 #undef MOE_FENCE
   }
@@ -1226,7 +1252,7 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 
 template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
           typename TO, bool MX, int SCHED = kSchedM, int TAIL = 0,
-          bool SKIP = false, bool KCAT = false>
+          bool SKIP = false, bool KCAT = false, int SB = 0>
 hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
   const long tiles_n = (p.N + BN - 1) / BN;
   long tiles = SCHED == kSchedK
@@ -1237,7 +1263,7 @@ hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
   tiles = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, S, WGM, WGN, DUAL, EPI, TO, MX, SCHED, TAIL, SKIP, KCAT>),
+  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, S, WGM, WGN, DUAL, EPI, TO, MX, SCHED, TAIL, SKIP, KCAT, SB>),
                      dim3((unsigned)tiles), dim3(WGM * WGN * kWave), 0, s, p);
   return hipGetLastError();
 }
@@ -1295,19 +1321,25 @@ hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
     }
     // bf16 row-grouped products: a partial last round of big tiles runs
     // as quarter tiles (128 x 128, or 128 x 64 x 2 dual) in a second launch
+    // Groups of about half a tile (SKIP) stream their weights with about
+    // half a tile of MFMA work per k-tile, too little to cover one k-tile
+    // of HBM latency: B runs in a 3-stage ring of its own (A in 2, all
+    // 160 KB of LDS), so two k-tiles of weights are in flight (measured on
+    // the DeepSeek-V3 shape: GEMM 1 3.37 -> 3.12 ms)
+    constexpr int SB = SKIP && !MX ? 3 : 0;
     if constexpr (!MX) {
       if (p.slots != 0 && p.off) {
         GemmParams q = p;
         if (q.slots < 0) q.slots = num_cus();
         hipError_t e = launch_dl<256, DUAL ? 128 : 256, 2, 2, 4, DUAL, EPI, TO,
-                                 MX, kSchedM, 1, SKIP>(q, s);
+                                 MX, kSchedM, 1, SKIP, false, SB>(q, s);
         if (e != hipSuccess) return e;
         return launch_dl<128, DUAL ? 64 : 128, 2, 2, 2, DUAL, EPI, TO, MX,
                          kSchedM, 2, SKIP>(q, s);
       }
     }
     return launch_dl<256, DUAL ? 128 : 256, 2, 2, 4, DUAL, EPI, TO, MX, kSchedM,
-                     0, SKIP>(p, s);
+                     0, SKIP, false, SB>(p, s);
   }
   return launch_dl<128, DUAL ? 64 : 128, 2, 2, 2, DUAL, EPI, TO, MX>(p, s);
 }
@@ -1418,6 +1450,15 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
     const int bn = op == kOpRouter && p.N <= 32 ? 32
                    : dual ? (big ? 128 : 64) : (big ? 256 : 128);
     p.group_n = tile_group_n(fwd ? (p.N + bn - 1) / bn : 1 << 30);
+    // one row tile per group (skip): nothing re-reads B, while every
+    // column tile of a group reads the same A rows, so all of a group's
+    // column tiles run side by side and A leaves HBM once
+    // (measured on the DeepSeek-V3 shape: GEMM 2 2.15 -> 2.04 ms, the
+    // backward dgrad1 4.95 -> 4.85 ms)
+    if (skip) {
+      const int bns = fwd ? bn : 256;  // the backward's skip tiles: 256 x 256
+      p.group_n = (p.N + bns - 1) / bns;
+    }
   }
   // k-contiguous operands with whole k-tiles go straight to LDS
   if (p.K % 64 == 0 && !force_staged()) {
