@@ -555,7 +555,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // weight-streaming product keeps SB - 1 k-tiles of B in flight while A
   // (re-read by every column tile, so mostly an L2 hit) keeps S - 1
   constexpr bool RING_B = SB > S;
-  static_assert(!RING_B || (!MX && !KCAT), "deeper B ring: bf16 operands");
+  static_assert(!RING_B || !MX, "deeper B ring: bf16 operands");
   constexpr int S_B = RING_B ? SB : S;
   constexpr int A_STRIDE = RING_B ? A_BYTES : STAGE;
   constexpr int B_STRIDE = RING_B ? NB_OPS * B_BYTES : STAGE;
@@ -1321,12 +1321,13 @@ hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
     }
     // bf16 row-grouped products: a partial last round of big tiles runs
     // as quarter tiles (128 x 128, or 128 x 64 x 2 dual) in a second launch
-    // Groups of about half a tile (SKIP) stream their weights with about
-    // half a tile of MFMA work per k-tile, too little to cover one k-tile
-    // of HBM latency: B runs in a 3-stage ring of its own (A in 2, all
-    // 160 KB of LDS), so two k-tiles of weights are in flight (measured on
-    // the DeepSeek-V3 shape: GEMM 1 3.37 -> 3.12 ms)
-    constexpr int SB = SKIP && !MX ? 3 : 0;
+    // B runs in a 3-stage ring of its own (A in 2, all 160 KB of LDS), so
+    // two k-tiles of weights are in flight. Groups of about half a tile
+    // (SKIP) stream their weights with too little MFMA work per k-tile to
+    // cover one k-tile of HBM latency (measured on the DeepSeek-V3 shape:
+    // GEMM 1 3.37 -> 3.12 ms); the full tiles gain less (Mixtral-shaped
+    // GEMM 2 1.75 -> 1.69 ms, GEMM 1 3.38 -> 3.36 ms)
+    constexpr int SB = MX ? 0 : 3;
     if constexpr (!MX) {
       if (p.slots != 0 && p.off) {
         GemmParams q = p;
@@ -1488,13 +1489,13 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
           GemmParams q = p;
           if (q.slots < 0) q.slots = num_cus();
           hipError_t e = launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
-                                   kSchedM, 1, false, true>(q, s);
+                                   kSchedM, 1, false, true, 3>(q, s);
           if (e != hipSuccess) return e;
           return launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false,
                            kSchedM, 2, false, true>(q, s);
         }
         return big ? launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
-                               kSchedM, 0, false, true>(p, s)
+                               kSchedM, 0, false, true, 3>(p, s)
                    : launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false,
                                kSchedM, 0, false, true>(p, s);
       default:
@@ -1530,8 +1531,11 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   }
   // weight gradients from transposed, group-padded operands: both k
   // contiguous, so the forward's direct-to-LDS kernel takes them
+  // (B in its own 3-stage ring, as the forward's big tiles: Mixtral-shaped
+  // dW2 2.37 -> 2.23 ms, dW1/dW3 unchanged)
   if (op == kOpWgradT)
-    return big ? launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false, kSchedK>(p, s)
+    return big ? launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false, kSchedK,
+                           0, false, false, 3>(p, s)
                : launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false, kSchedK>(p, s);
   if (op == kOpGemm1Mx)
     return skip ? launch_dl_sized<true, kEpiSwigluMx, bf16, true, true>(big, p, s)
