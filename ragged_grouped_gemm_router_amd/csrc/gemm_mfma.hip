@@ -555,7 +555,6 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // weight-streaming product keeps SB - 1 k-tiles of B in flight while A
   // (re-read by every column tile, so mostly an L2 hit) keeps S - 1
   constexpr bool RING_B = SB > S;
-  static_assert(!RING_B || !MX, "deeper B ring: bf16 operands");
   constexpr int S_B = RING_B ? SB : S;
   constexpr int A_STRIDE = RING_B ? A_BYTES : STAGE;
   constexpr int B_STRIDE = RING_B ? NB_OPS * B_BYTES : STAGE;
@@ -565,7 +564,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile shape");
   static_assert(MB >= 1 && NB >= 1, "tile shape");
   static_assert(S >= 2 && KS % 2 == 0, "stage count, even substep count");
-  static_assert((S - 1) * (A_INS + NBL) + (S_B - S) * NBL <= 63, "vmcnt range");
+  static_assert((S - 1) * (A_INS + NBL) + (S_B - S) * NBL + (MX ? MB + NB_OPS * NB : 0) <= 63,
+                "vmcnt range");
 
   // the epilogue stages 128 rows at a time (the quantising one only for
   // the optional pre-activation copies)
@@ -668,10 +668,10 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
             (o ? p.B2s : p.Bs) + (long)t.g * p.sBs + (long)row * p.ld_s;
       }
   }
-  auto load_scales = [&](int kt) {
+  auto load_scales = [&](uint32_t* dst, int kt) {
     if constexpr (MX) {
 #pragma unroll
-      for (int q = 0; q < NSC; ++q) s_nxt[q] = *(const uint32_t*)(sc_row[q] + kt * 4);
+      for (int q = 0; q < NSC; ++q) dst[q] = *(const uint32_t*)(sc_row[q] + kt * 4);
     }
   };
 
@@ -775,20 +775,25 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 
   // Prologue: (scales of k-tile 0,) k-tiles 0 .. S-1 in flight, and the
   // B operands of k-tiles S .. S_B-1 (past the last tile, the last one
-  // again, into stages nobody reads); wait for tile 0.
+  // again, into stages nobody reads); wait for tile 0. With a deeper B
+  // ring, MXFP8 scales run two tiles ahead: those of tile kt+1 are issued
+  // before the B DMA of tile kt+2 (here: of tile 2), so that one is still
+  // the newest outstanding load at the tile barrier.
+  constexpr int NSC_RING = RING_B && MX ? NSC : 0;
   if (nk > 0) {  // (an empty group's tile writes zeros)
-  load_scales(0);
+  load_scales(RING_B ? s_cur : s_nxt, 0);
 #pragma unroll
   for (int i = 0; i < S; ++i)
 #pragma unroll
     for (int d = 0; d < N_LOAD; ++d)
       issue_one(min(i, nk - 1), i, min(i, nk - 1), i, d);
+  if constexpr (RING_B) load_scales(s_nxt, min(1, nk - 1));
 #pragma unroll
   for (int i = S; i < S_B; ++i)
 #pragma unroll
     for (int d = A_INS; d < N_LOAD; ++d) issue_one(0, 0, min(i, nk - 1), i, d);
-  barrier_after(std::integral_constant<int, (S - 1) * N_LOAD + (S_B - S) * NBL>{});
-  if constexpr (MX) {
+  barrier_after(std::integral_constant<int, (S - 1) * N_LOAD + NSC_RING + (S_B - S) * NBL>{});
+  if constexpr (MX && !RING_B) {
 #pragma unroll
     for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
   }
@@ -832,8 +837,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 #pragma unroll
       for (int q = 0; q < H; ++q) mfma_one(cur, q);
       MOE_FENCE();
-      if (ks == 0) {
-        load_scales(min(kt + 1, nk - 1));
+      if (ks == 0 && !RING_B) {
+        load_scales(s_nxt, min(kt + 1, nk - 1));
         MOE_FENCE();
       }
       if (last) {
@@ -844,6 +849,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
         if constexpr (MX) {
 #pragma unroll
           for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
+          if constexpr (RING_B) load_scales(s_nxt, min(kt + 2, nk - 1));
         }
         MOE_FENCE();
       }
@@ -1312,7 +1318,7 @@ hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
           GemmParams q = p;
           if (q.slots < 0) q.slots = num_cus();
           hipError_t e = launch_dl<256, 256, 2, 2, 2, false, EPI, TO, MX,
-                                   kSchedM, 1>(q, s);
+                                   kSchedM, 1, false, false, 3>(q, s);
           if (e != hipSuccess) return e;
           return launch_dl<128, 128, 2, 2, 2, false, EPI, TO, MX, kSchedM, 2>(q, s);
         }
@@ -1326,8 +1332,9 @@ hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
     // (SKIP) stream their weights with too little MFMA work per k-tile to
     // cover one k-tile of HBM latency (measured on the DeepSeek-V3 shape:
     // GEMM 1 3.37 -> 3.12 ms); the full tiles gain less (Mixtral-shaped
-    // GEMM 2 1.75 -> 1.69 ms, GEMM 1 3.38 -> 3.36 ms)
-    constexpr int SB = MX ? 0 : 3;
+    // GEMM 2 1.75 -> 1.69 ms, GEMM 1 3.38 -> 3.36 ms; MXFP8 GEMM 2
+    // 1.24 -> 1.18 ms, with the single-B 4-wave tile above)
+    constexpr int SB = 3;
     if constexpr (!MX) {
       if (p.slots != 0 && p.off) {
         GemmParams q = p;
