@@ -256,14 +256,19 @@ struct StageOut {
   static constexpr int BYTES = ROWS * PITCH * 4;
   static_assert(BM % ROWS == 0, "pass rows");
 
+  // rows: the tile's rows that are stored (a workgroup-uniform count);
+  // passes wholly past them are skipped, since every store there would
+  // be masked (a ragged group's tile that ends in its first pass)
   template <typename V, typename St>
   __device__ __forceinline__ static void run(char* lds, int wm, int wn,
-                                             int lane, V value, St store) {
+                                             int lane, V value, St store,
+                                             int rows) {
     float* st = (float*)lds;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int pass = 0; pass < BM / ROWS; ++pass) {
       const int r0 = pass * ROWS;
+      if (r0 >= rows) break;
       __syncthreads();  // LDS free (operands read, or previous pass out)
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
@@ -280,7 +285,7 @@ struct StageOut {
         }
       }
       __syncthreads();
-      constexpr int CH = ROWS * (BN / 8);
+      const int CH = min(ROWS, rows - r0) * (BN / 8);
 #pragma unroll 2
       for (int c = tid; c < CH; c += NT) {
         const int row = c / (BN / 8), col = (c % (BN / 8)) * 8;
@@ -903,11 +908,11 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     if (p.Sa)
       SO::run(lds, wm, wn, lane,
               [&](int i, int j, int r) { return acc[0][i][j][r]; },
-              put_bf16(p.Sa));
+              put_bf16(p.Sa), t.m_end - t.m0);
     if (p.Sb)
       SO::run(lds, wm, wn, lane,
               [&](int i, int j, int r) { return acc[NB_OPS - 1][i][j][r]; },
-              put_bf16(p.Sb));
+              put_bf16(p.Sb), t.m_end - t.m0);
   } else {
     auto put = [&](TO* dst) {
       return [=](int row, int col, const float* v) {
@@ -929,15 +934,15 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
                   const float a = acc[0][i][j][r], b = acc[NB_OPS - 1][i][j][r];
                   return a * fast_sigmoid(a) * b;
                 },
-                put((TO*)p.C));
+                put((TO*)p.C), t.m_end - t.m0);
       if (p.C2)
         SO::run(lds, wm, wn, lane,
                 [&](int i, int j, int r) { return acc[0][i][j][r]; },
-                put((TO*)p.C2));
+                put((TO*)p.C2), t.m_end - t.m0);
       if (p.C3)
         SO::run(lds, wm, wn, lane,
                 [&](int i, int j, int r) { return acc[NB_OPS - 1][i][j][r]; },
-                put((TO*)p.C3));
+                put((TO*)p.C3), t.m_end - t.m0);
     } else if constexpr (EPI == kEpiSwigluBwd) {
       // dh = acc; (da, db) from the pre-activations a, b (bf16, ld = ldc),
       // which may share their buffers with da, db
@@ -959,11 +964,11 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
                 }
                 *(bf16x8*)((bf16*)p.C + o) = pack8(da);
                 *(bf16x8*)((bf16*)p.C2 + o) = pack8(db);
-              });
+              }, t.m_end - t.m0);
     } else {
       SO::run(lds, wm, wn, lane,
               [&](int i, int j, int r) { return acc[0][i][j][r]; },
-              put((TO*)p.C + (SCHED == kSchedK ? (long)t.g * p.sC : 0)));
+              put((TO*)p.C + (SCHED == kSchedK ? (long)t.g * p.sC : 0)), t.m_end - t.m0);
     }
   }
 }
@@ -1216,7 +1221,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
     }
   };
   StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>::run(lds, wm, wn, lane,
-                                                              value, store);
+                                                              value, store, t.m_end - t.m0);
 }
 
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, bool KCAT,
