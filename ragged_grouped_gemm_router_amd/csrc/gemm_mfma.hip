@@ -1448,7 +1448,7 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
         (op == kOpGemm1 || op == kOpGemm2 || op == kOpDgrad2 || op == kOpDgrad1 ||
          op == kOpGemm1Mx || op == kOpGemm1MxAct))
       big = skip = true;
-    const int bm = op == kOpRouter && p.N <= 32 ? 32 : big ? 256 : 128;
+    const int bm = op == kOpRouter ? 32 : big ? 256 : 128;
     if (p.off) {
       p.tile_off = tile_off_by_bm[tile_bm_slot(bm)];
       p.tiles_m_max = (p.M + bm - 1) / bm + (p.G < p.M ? p.G : p.M);
@@ -1460,7 +1460,7 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
      // products keep groups of 4 (wider ones measured slower for dgrad1)
     const bool dual = op == kOpGemm1 || op == kOpGemm1Mx || op == kOpGemm1MxAct;
     const bool fwd = dual || op == kOpGemm2 || op == kOpGemm2Mx || op == kOpRouter;
-    const int bn = op == kOpRouter && p.N <= 32 ? 32
+    const int bn = op == kOpRouter ? 32
                    : dual ? (big ? 128 : 64) : (big ? 256 : 128);
     p.group_n = tile_group_n(fwd ? (p.N + bn - 1) / bn : 1 << 30);
     // one row tile per group (skip): nothing re-reads B, while every
@@ -1477,14 +1477,11 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   if (p.K % 64 == 0 && !force_staged()) {
     switch (op) {
       case kOpRouter:
-        // few experts: one wave per 32 x 32 tile, eight k-tiles in flight,
-        // so the skinny product spreads over every CU and hides latency
-        if (p.N <= 32)
-          return launch_dl<32, 32, 8, 1, 1, false, kEpiStore, float, false>(p, s);
-        // more experts (E = 256: 64 tiles of 128 x 128 over a long k):
-        // three k-tiles in flight (measured: route stage 0.122 -> 0.089 ms
-        // on the DeepSeek-V3 shape; more stages slow the expert GEMMs)
-        return launch_dl<128, 128, 3, 2, 2, false, kEpiStore, float, false>(p, s);
+        // one wave per 32 x 32 tile, eight k-tiles in flight, so the
+        // skinny product spreads over every CU and hides latency (E = 256
+        // on the DeepSeek-V3 shape: 1024 tiles; route stage 0.093 ->
+        // 0.084 ms against 64 tiles of 128 x 128 in 3 stages)
+        return launch_dl<32, 32, 8, 1, 1, false, kEpiStore, float, false>(p, s);
       case kOpGemm1:
         if (skip)
           return launch_dl_sized<true, kEpiSwiglu, bf16, false, true>(big, p, s);
