@@ -97,7 +97,7 @@ class HipEvents:
 def workload(name):
     import moe_inputs as mi
     table = {"mixtral": mi.MIXTRAL, "deepseek": mi.DEEPSEEK_V3,
-             "skewed": mi.SKEWED, "tiny": mi.TINY_FP32}
+             "skewed": mi.SKEWED, "qwen": mi.QWEN_MOE, "tiny": mi.TINY_FP32}
     return table[name]
 
 
@@ -106,8 +106,11 @@ def cpu_baseline(cfg, ginp, logits_gpu, n_tokens):
     n_tokens tokens, on the host cores. D2H copies happen before timing."""
     import torch
     import oracle
-    threads = min(len(os.sched_getaffinity(0)),
-                  int(os.environ.get("OMP_NUM_THREADS", "16")))
+    affinity = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    # threads: every CPU this process may run on, capped by OMP_NUM_THREADS
+    # when the host sets it (the CPU share of one GPU on a shared host)
+    threads = min(affinity, int(omp)) if omp else affinity
     torch.set_num_threads(threads)
     toks = list(range(n_tokens))
     c = {k: (v.cpu() if isinstance(v, torch.Tensor) else v)
@@ -123,10 +126,51 @@ def cpu_baseline(cfg, ginp, logits_gpu, n_tokens):
     from ragged_grouped_gemm_router_amd import accounting as acc
     flops = acc.routed_fwd_flops(cfg.d, cfg.f, n_tokens * cfg.K)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "threads": torch.get_num_threads(), "host_cores": os.cpu_count(),
+            "affinity_cpus": affinity,
+            "threads_cap": ("OMP_NUM_THREADS=" + omp) if omp else None,
             "kind": "oracle",
             "sample": (f"first {n_tokens} tokens ({n_tokens * cfg.K} routed "
                        f"copies) of {cfg.name}; fp64 torch CPU per-expert "
                        f"loop incl. weight upcast; {dt:.1f} s")}
+
+
+def graph_replay(step, stream, n_rep):
+    """The same step captured once per input batch in a HIP graph, then
+    replayed n_rep times in batch rotation; each replay timed with HIP
+    events on the launch stream. Returns the replay times' median and
+    p10 / p90 in ms."""
+    import numpy as np
+    import torch
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for j in range(3):
+            step(0, False, j=j)  # warm the side stream (no events)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    for j in range(3):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(0, False, j=j)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for j in range(3):  # untimed first replays
+        graphs[j].replay()
+    torch.cuda.synchronize()
+    gev = HipEvents(2 * n_rep)
+    for r in range(n_rep):
+        gev.record(2 * r, stream)
+        graphs[r % 3].replay()
+        gev.record(2 * r + 1, stream)
+    torch.cuda.synchronize()
+    t = np.array([gev.ms(2 * r, 2 * r + 1) for r in range(n_rep)])
+    q = np.percentile(t, [10, 50, 90])
+    return {"median_ms": round(float(q[1]), 4), "p10_ms": round(float(q[0]), 4),
+            "p90_ms": round(float(q[2]), 4), "replays": n_rep,
+            "what": "the whole step captured once per input batch in a HIP "
+                    "graph and replayed in rotation"}
 
 
 def main():
@@ -135,11 +179,14 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral",
-                    choices=["mixtral", "deepseek", "skewed", "tiny"])
+                    choices=["mixtral", "deepseek", "skewed", "qwen", "tiny"])
     ap.add_argument("--cpu-tokens", type=int, default=6144,
                     help="tokens of the workload the fp64 oracle runs for the "
                          "CPU baseline (about 10 s on 16 host cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph-replays", type=int, default=20,
+                    help="after the timed steps, replay the step captured in "
+                         "a HIP graph this many times (0: skip)")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step: forward (activations saved) "
                          "plus backward; FLOPs counted as 3x the forward")
@@ -217,28 +264,35 @@ def main():
         log(f"bench: calibration copy of {args.copy_calibration_mib} MiB done")
         del src, dst
 
-    def step(i, timed):
-        j = i % 3
+    sev = HipEvents(2 * max(args.steps, 1))  # around each whole step
+
+    def step(i, timed, j=None, stage_events=True):
+        j = i % 3 if j is None else j
+        timed_stages = timed and stage_events
+        if timed:
+            sev.record(2 * i, stream)
         e = (ev.ev[i * B.MOE_FWD_NEVENTS:(i + 1) * B.MOE_FWD_NEVENTS]
-             if timed else None)
+             if timed_stages else None)
         L.forward(desc, batches[j], bufs[j], events=e)
         if args.backward:
             be = (bev.ev[i * B.MOE_BWD_NEVENTS:(i + 1) * B.MOE_BWD_NEVENTS]
-                  if timed else None)
+                  if timed_stages else None)
             L.backward(desc, batches[j], bufs[j], batches[j]["dy"], gbufs[j],
                        events=be)
             if not cfg.synth_logits:
                 # balance statistics of the routing, then the router
                 # backward: the gate (and the balance loss) to Wr and dx
-                if timed:
+                if timed_stages:
                     rev.record(3 * i, stream)
                 L.load_balance_stats(desc, bufs[j], rbufs[j])
-                if timed:
+                if timed_stages:
                     rev.record(3 * i + 1, stream)
                 L.router_backward(desc, batches[j], bufs[j], gbufs[j],
                                   rbufs[j], aux_coef=args.aux_coef)
-                if timed:
+                if timed_stages:
                     rev.record(3 * i + 2, stream)
+        if timed:
+            sev.record(2 * i + 1, stream)
 
     log("bench: warmup")
     for i in range(args.warmup):
@@ -252,6 +306,9 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall / max(args.steps, 1) * 1e3
     log(f"bench: {ms_step:.3f} ms/step")
+    step_ms = [sev.ms(2 * i, 2 * i + 1) for i in range(args.steps)]
+    graph = graph_replay(step, stream, args.graph_replays) \
+        if args.graph_replays > 0 else None
 
     n = B.MOE_FWD_NEVENTS
     stage = {"route": 0.0, "permute": 0.0, "gemm1_swiglu": 0.0,
@@ -351,6 +408,14 @@ def main():
                         else gemm1_traffic(cfg, args.mxfp8)),
         },
     }
+    if step_ms:
+        import numpy as np
+        q = np.percentile(np.array(step_ms), [10, 50, 90])
+        line["step_ms_events"] = {"p10": round(float(q[0]), 4),
+                                  "median": round(float(q[1]), 4),
+                                  "p90": round(float(q[2]), 4),
+                                  "n": len(step_ms)}
+    line["graph_replay"] = graph
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(cfg, base, bufs[0]["logits"],

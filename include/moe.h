@@ -276,7 +276,19 @@ moe_status moe_unpermute_combine(const moe_desc* desc, const void* y_perm,
                                  const void* y_shared, void* out,
                                  void* stream);
 
-/* Whole forward: route, permute, grouped GEMMs (+ shared), combine. */
+/* Whole forward of the layer [P3 §9, the MoE layer and its forward; §5
+ * shared expert; P2 section on the TE mechanisms: routing, dispatch, the
+ * grouped GEMM and the combine in one device-resident pass]: moe_route,
+ * moe_permute, moe_grouped_gemm_swiglu (+ shared expert) and
+ * moe_unpermute_combine in sequence on one stream, with the same argument
+ * meanings (see moe_fwd_args). The caller owns every buffer in args and
+ * the workspace (>= moe_workspace_size(desc, 0)). args->x_perm == NULL
+ * (bf16 or MXFP8, d_model % 64 == 0, T * d_model * 2 < 2^31) selects the
+ * gathered GEMM 1: the permute writes only the indices and GEMM 1 reads
+ * its rows from x through sorted_src [P3 §9, its engineering notes on
+ * grouped GEMMs over per-expert row groups]; otherwise MOE_EUNSUPPORTED.
+ * Errors: NULL required pointers -> MOE_EINVAL; workspace too small ->
+ * MOE_EWORKSPACE; nothing is enqueued on error. */
 moe_status moe_forward(const moe_desc* desc, const moe_fwd_args* args,
                        void* ws, size_t ws_bytes, void* stream);
 
@@ -404,10 +416,15 @@ moe_status moe_quantize_mxfp8_t(const void* src_bf16, int64_t batch,
                                 void* stream);
 
 /* MX quantisation of a bf16 [rows, cols] matrix along its rows (cols a
- * multiple of 32), per the OCP MX v1.0 rule: X = floor(log2(amax)) - 8
+ * multiple of 32) [P2 section on the TE mechanisms: MXFP8 grouped GEMM
+ * operands; P3 §13.6: fp8 with per-tile rather than per-tensor scales].
+ * The pages fix no bit-level rule; this is the OCP MX v1.0 one: X = floor(log2(amax)) - 8
  * per 32-element block (clamped to [-127, 127]); scale code X + 127;
  * element = E4M3 round-to-nearest-even of v / 2^X, saturated to +-448.
- * Writes q [rows, cols] E4M3 bytes and scales [rows, cols/32]. */
+ * Writes q [rows, cols] E4M3 bytes and scales [rows, cols/32] (device
+ * pointers owned by the caller). NULL pointers, rows < 0 or cols <= 0 ->
+ * MOE_EINVAL; cols % 32 != 0 -> MOE_EUNSUPPORTED; rows == 0 -> MOE_OK
+ * with nothing enqueued. */
 moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows,
                               int64_t cols, uint8_t* q, uint8_t* scales,
                               void* stream);

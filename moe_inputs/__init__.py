@@ -6,8 +6,10 @@ of the layer itself (no gating, no permutation, no expert FFN).
 
 Workload shapes follow the models named on the pages: a tiny fp32 layer, a
 Mixtral-8x7B-shaped layer, a DeepSeek-V3-shaped layer (sigmoid gating with a
-route bias and one shared expert), and a skewed layer whose router logits are
-synthesised so that expert loads follow a Zipf law with some experts empty.
+route bias and one shared expert), a Qwen-MoE-like fine-grained layer (60
+narrow experts, top-4, an ungated shared expert), and a skewed layer whose
+router logits are synthesised so that expert loads follow a Zipf law with
+some experts empty.
 The pages measure no public dataset; these seeded tensors stand in for it.
 
 Seeding: every tensor has its own generator seeded with
@@ -67,6 +69,13 @@ DEEPSEEK_V3 = MoEConfig("deepseekv3_T4096_d7168_f2048_E256_K8_sigmoid_bias_share
 SKEWED = MoEConfig("skewed_zipf1.2_T16384_d2048_f768_E128_K8", 16384, 2048,
                    768, 128, 8, synth_logits=True, n_zero=10, zipf_s=1.2)
 MIXTRAL_TRAIN = MIXTRAL.replace(name="mixtral8x7b_train_fwd_bwd_T8192_d4096_f14336_E8_K2")
+# A Qwen-MoE-like fine-grained layer: many narrow experts, softmax top-4,
+# and one ungated shared expert twice the routed width (the pages put
+# shared experts at 1-2x a routed expert's size and print no Qwen
+# dimensions; d_model 2048, 60 experts of d_ff 1408 and top-4 are the
+# public Qwen1.5-MoE-A2.7B layer's).
+QWEN_MOE = MoEConfig("qwen_moe_like_T8192_d2048_f1408_E60_K4_shared2816",
+                     8192, 2048, 1408, 60, 4, f_shared=2816)
 
 CONFIGS = [TINY_FP32, MIXTRAL, DEEPSEEK_V3, SKEWED, MIXTRAL_TRAIN]
 

@@ -104,28 +104,32 @@ def mx_roundtrip(v: torch.Tensor, block: int = BLOCK) -> torch.Tensor:
 
 def forward_mxfp8(x, w1, w3, w2, idx, w, ws1=None, ws3=None, ws2=None,
                   tokens: Optional[Sequence[int]] = None,
-                  weight_cache: Optional[dict] = None) -> torch.Tensor:
+                  weight_cache: Optional[dict] = None,
+                  quant: bool = True) -> torch.Tensor:
     """The [P3 §9] per-expert layer with every expert GEMM operand MX
-    quantised: x and W1/W3 along d_model, h and W2 along d_ff. h is
-    quantised from its fp64 value. Gate weights and the combine stay in
-    fp64. ``weight_cache`` (a dict) keeps dequantised weights between
-    calls."""
+    quantised: x and W1/W3 along d_model, h and W2 along d_ff (each along
+    its GEMM's contraction, which is the last dimension of every operand
+    in the [out, in] weight layout). h is quantised from its fp64 value.
+    Gate weights and the combine stay in fp64. ``weight_cache`` (a dict)
+    keeps dequantised weights between calls. quant=False makes every
+    quantiser the identity, which must give the exact layer."""
     cache = {} if weight_cache is None else weight_cache
+    Q = mx_roundtrip if quant else _f64
 
     def wq(name, e, t):
-        key = (name, e)
+        key = (name, e, quant)
         if key not in cache:
-            cache[key] = mx_roundtrip(t)
+            cache[key] = Q(t)
         return cache[key]
 
     def ffn(X, W1, W3, W2):
         a = X @ W1.T
         b = X @ W3.T
-        h = mx_roundtrip(swiglu(a, b))
+        h = Q(swiglu(a, b))
         return h @ W2.T
 
     sel = _token_subset(x.shape[0], tokens)
-    xq = mx_roundtrip(_f64(x[sel]))
+    xq = Q(_f64(x[sel]))
     idx_s = idx[sel]
     w_s = _f64(w[sel])
     out = torch.zeros(xq.shape, dtype=F64)
@@ -150,12 +154,19 @@ def forward_mxfp8(x, w1, w3, w2, idx, w, ws1=None, ws3=None, ws2=None,
 # MX quantised along that product's contraction:
 #   dh = Q_d(g) . Q_d(W2)            (W2 [d, f] in blocks along d)
 #   dx_perm = Q_f(da) . Q_f(W1) + Q_f(db) . Q_f(W3)   (W1 [f, d] along f)
-# with g = w * dy, da, db and the forward's pre-activations a, b held in the
-# activation dtype (bf16), as the backward stores them (saved or
-# recomputed), and fp64 products of the dequantised values. The weight gradients take the operands the forward multiplied,
-# unquantised by the backward: dW2 = g^T Q_f(h), dW1 = da^T Q_d(x),
-# dW3 = db^T Q_d(x). quant=False turns every quantiser and the bf16
-# rounding into the identity, which must give the exact backward.
+# and fp64 products of the dequantised values. The operands that are MX
+# quantised here (g = w * dy, da, db) have E8M0 codes and E4M3 elements:
+# integers decided by floating point, so both sides take that decision in
+# the same precision. The layer holds its intermediates in the activation
+# dtype (bf16), so g, da and db are rounded to bf16 before they are
+# quantised, and da, db are formed from the pre-activations a, b as the
+# layer holds them, in bf16: a 2^-9 difference in a or b moves da, db
+# across an E4M3 rounding boundary for about one element in 30 (one E4M3
+# step, 2^-3 relative, each), about 0.03 of max|dx| in all. The weight
+# gradients take the operands the forward multiplied, unquantised by the
+# backward: dW2 = g^T Q_f(h), dW1 = da^T Q_d(x), dW3 = db^T Q_d(x).
+# quant=False turns every quantiser and the bf16 rounding into the
+# identity, which must give the exact backward.
 # --------------------------------------------------------------------------
 
 def mx_roundtrip_cols(W: torch.Tensor, block: int = BLOCK) -> torch.Tensor:

@@ -134,7 +134,7 @@ bool force_simt();
 // transposing-read kernel, for comparison.
 bool wgrad_t_ok(const moe_desc* d) {
   static const bool env_off = [] {
-    const char* e = getenv("MOE_WGRAD_T");
+    const char* e = tuning_env("MOE_WGRAD_T");
     return e && strcmp(e, "0") == 0;
   }();
   return d->act_dtype == MOE_BF16 &&
@@ -230,7 +230,7 @@ size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
 
 bool force_simt() {
   static const int v = [] {
-    const char* s = getenv("MOE_GEMM_BACKEND");
+    const char* s = tuning_env("MOE_GEMM_BACKEND");
     return (s && strcmp(s, "simt") == 0) ? 1 : 0;
   }();
   return v != 0;
@@ -903,12 +903,13 @@ moe_status moe_unpermute_combine(const moe_desc* d, const void* y_perm,
                                    (hipStream_t)stream));
 }
 
-moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
-                       size_t ws_bytes, void* stream) {
-  moe_status st = check_desc(d);
-  if (st != MOE_OK) return st;
-  if (d->T == 0) return MOE_OK;  // nothing is accessed
-  if (!a || !ws || !a->x || !a->out || !weights_ok(&a->routed)) return MOE_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// Arguments of the whole forward (everything but the workspace).
+moe_status check_fwd_args(const moe_desc* d, const moe_fwd_args* a) {
+  if (!a || !a->x || !a->out || !weights_ok(&a->routed)) return MOE_EINVAL;
   if (!a->logits_in && (!a->w_router || !a->logits)) return MOE_EINVAL;
   if (!a->topk_idx || !a->topk_w || !a->counts || !a->offsets ||
       !a->sorted_src || !a->dest || !a->h || !a->y_perm)
@@ -927,10 +928,18 @@ moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
   if (mx && ((!gather && !a->x_perm_scales) || !mx_weights_ok(&a->routed)))
     return MOE_EINVAL;
   if (mx && shared && !mx_weights_ok(&a->shared)) return MOE_EINVAL;
-  if (ws_bytes < fwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+// The whole forward in a validated workspace of the required size.
+moe_status forward_in(const moe_desc* d, const moe_fwd_args* a, void* ws,
+                      hipStream_t s) {
+  const bool gather = a->x_perm == nullptr;
+  const bool shared = d->d_ff_shared > 0;
+  const bool save = d->flags & MOE_FLAG_SAVE_ACTS;
+  const bool mx = d->gemm_dtype == MOE_MXFP8;
   FwdWs w;
   fwd_ws_layout(d, (char*)ws, &w);
-  hipStream_t s = (hipStream_t)stream;
   record(a->events[0], s);
   hipError_t e = do_route(d, a->x, a->w_router, a->route_bias, a->logits_in,
                           a->logits, a->topk_idx, a->topk_w, s);
@@ -960,6 +969,23 @@ moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
   record(a->events[5], s);
   return MOE_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
+                       size_t ws_bytes, void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;  // nothing is accessed
+  if (!ws) return MOE_EINVAL;
+  st = check_fwd_args(d, a);
+  if (st != MOE_OK) return st;
+  if (ws_bytes < fwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
+  return forward_in(d, a, ws, (hipStream_t)stream);
+}
+
 
 moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
                         size_t ws_bytes, void* stream) {

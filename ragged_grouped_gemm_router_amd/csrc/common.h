@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "../../include/moe.h"
 
@@ -15,6 +16,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// Kernel-choice switches read from the environment (MOE_GEMM_BACKEND,
+// MOE_BIG_TILE_WAVES, MOE_TILE_GROUP_N, MOE_WGRAD_T) exist only in builds
+// compiled with -DMOE_TUNING, which serve to measure alternatives; the
+// library otherwise ignores the environment and always makes its own
+// choices.
+inline const char* tuning_env(const char* name) {
+#ifdef MOE_TUNING
+  return getenv(name);
+#else
+  (void)name;
+  return nullptr;
+#endif
+}
 constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
@@ -30,19 +45,19 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) {
 // Remap a workgroup id so that each XCD receives one contiguous range of
 // logical ids: workgroup b runs on XCD b % 8, so logical id =
 // (b % 8) * (n / 8) + b / 8. n must be a multiple of 8.
-__device__ __forceinline__ int xcd_remap(int b, int n) {
+__host__ __device__ inline int xcd_remap(int b, int n) {
   return (b % kNumXcd) * (n / kNumXcd) + b / kNumXcd;
 }
 
 // The same for any n: a bijection of [0, n) that hands each XCD a
 // contiguous range of logical indices whose sizes differ by at most one.
-__device__ __forceinline__ int xcd_remap_n(int b, int n) {
+__host__ __device__ inline int xcd_remap_n(int b, int n) {
   const int x = b % kNumXcd, q = n / kNumXcd, r = n % kNumXcd;
   return x * q + (x < r ? x : r) + b / kNumXcd;
 }
 
 // Largest g in [0, G) with pre[g] <= v (pre is non-decreasing, pre[0] = 0).
-__device__ __forceinline__ int upper_group(const int32_t* pre, int G, int v) {
+__host__ __device__ inline int upper_group(const int32_t* pre, int G, int v) {
   int lo = 0, hi = G - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;

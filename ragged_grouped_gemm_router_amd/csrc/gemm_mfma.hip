@@ -24,6 +24,7 @@
 
 #include "gemm.h"
 #include "mx.h"
+#include "tile_map.h"
 
 namespace moe {
 namespace {
@@ -33,19 +34,11 @@ namespace {
 // pass; those lanes read the same logical chunk of 16 consecutive rows,
 // which lie two (CPR = 8) or four (CPR = 4) to a 256-byte bank line. The
 // XOR with the row's line index gives each of them its own 16-byte bank
-// group. (MOE_LDS_SWZ=0 selects the 32-bank form, kept for comparison.)
-#ifndef MOE_LDS_SWZ
-#define MOE_LDS_SWZ 1
-#endif
+// group.
 template <int CPR>
 __device__ __forceinline__ int swz(int row, int c) {
-#if MOE_LDS_SWZ == 1
   if constexpr (CPR == 8) return c ^ ((row >> 1) & 7);
   else return c ^ ((row >> 2) & 3);
-#else
-  if constexpr (CPR == 8) return c ^ (row & 7);
-  else return c ^ ((row >> 1) & 3);
-#endif
 }
 
 // Raw (untyped, unswizzled) buffer resource starting at `base`, with the
@@ -160,86 +153,11 @@ __device__ __forceinline__ float fast_sigmoid(float a) {
   return 1.0f / (1.0f + __expf(-a));
 }
 
-struct Tile {
-  int g, m0, m_end, n0, k_beg, k_end;
-};
-
-// Decode this workgroup's output tile. Returns false for surplus
-// workgroups (beyond the device-side tile count).
-//
-// Row-grouped products: the grid is sized by an upper bound, and the real
-// row tiles (mt, from the device tile prefix) are enumerated densely in
-// n-group-major order (GN column tiles, every row tile of every group,
-// then the GN column tiles within), so that consecutive tiles share weight
-// and row panels. The first mt * tiles_n workgroups take them, each XCD a
-// contiguous share of equal size; the rest exit.
-//
-// Split last round (TAIL, row-grouped only). With S = p.slots big tiles
-// running at once, n_tiles big tiles take full rounds plus a last round of
-// r = n_tiles mod S tiles. When 0 < 4 r <= S and there is a full round,
-// the big-tile launch (TAIL 1) runs only the full rounds, and a second
-// launch of half-size tiles (TAIL 2: BM x BN = half the big tile each
-// way) runs the last round's tiles as four quarters each, so that round
-// spreads over 4 r CUs instead of r. Both launches decide from the same
-// device tile prefix; otherwise TAIL 1 runs every tile and TAIL 2 nothing.
+// This workgroup's output tile (the decode and its order are described
+// with decode_tile); false for surplus workgroups.
 template <int BM, int BN, int SCHED, int TAIL = 0>
 __device__ __forceinline__ bool lookup_tile(const GemmParams& p, Tile& t) {
-  // tile size of the enumeration: the big tile in the quarter launch
-  constexpr int DM = TAIL == 2 ? 2 * BM : BM, DN = TAIL == 2 ? 2 * BN : BN;
-  const int tiles_n = (p.N + DN - 1) / DN;
-  t.g = 0;
-  t.k_beg = 0;
-  t.k_end = p.K;
-  if (SCHED == kSchedM) {
-    const int mt = p.off ? p.tile_off[p.G] : (p.M + DM - 1) / DM;
-    const int n_tiles = mt * tiles_n;
-    // this launch's logical tiles: [lo, lo + n) (quarters: 4 per tile)
-    int lo = 0, n = n_tiles;
-    if (TAIL != 0) {
-      const int full = n_tiles / p.slots * p.slots, r = n_tiles - full;
-      const bool split = full > 0 && r > 0 && 4 * r <= p.slots;
-      if (TAIL == 1 && split) n = full;
-      if (TAIL == 2) {
-        if (!split) return false;
-        lo = full;
-        n = 4 * r;
-      }
-    }
-    if ((int)blockIdx.x >= n) return false;
-    const int li = xcd_remap_n(blockIdx.x, n);
-    const int idx = lo + (TAIL == 2 ? li / 4 : li), q = li % 4;
-    const int GN = p.group_n;
-    const int ng = idx / (mt * GN), within = idx % (mt * GN);
-    const int gsz = min(GN, tiles_n - ng * GN);
-    const int m = within / gsz;
-    t.n0 = (ng * GN + within % gsz) * DN;
-    if (p.off == nullptr) {
-      t.m0 = m * DM;
-      t.m_end = p.M;
-    } else {
-      t.g = upper_group(p.tile_off, p.G, m);
-      t.m0 = p.off[t.g] + (m - p.tile_off[t.g]) * DM;
-      t.m_end = p.off[t.g + 1];
-    }
-    if (TAIL == 2) {  // quarter q of the big tile; none past its rows
-      t.m0 += (q / 2) * BM;
-      t.n0 += (q % 2) * BN;
-      if (t.m0 >= t.m_end || t.n0 >= p.N) return false;
-    }
-    return true;
-  }
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int tiles_m = (p.M + BM - 1) / BM;
-  if (L >= p.G * tiles_m * tiles_n) return false;
-  t.g = L / (tiles_m * tiles_n);
-  const int rem = L % (tiles_m * tiles_n);
-  t.m0 = (rem / tiles_n) * BM;
-  t.n0 = (rem % tiles_n) * BN;
-  t.m_end = p.M;
-  const int km = p.kmul > 0 ? p.kmul : 1;
-  t.k_beg = p.off[t.g] * km;
-  t.k_end = p.off[t.g + 1] * km;
-  return true;
+  return decode_tile<BM, BN, SCHED, TAIL>(p, (int)blockIdx.x, (int)gridDim.x, t);
 }
 
 // Tile output through LDS: the fp32 values of the wave's 32x32 blocks
@@ -571,6 +489,11 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   static_assert(S >= 2 && KS % 2 == 0, "stage count, even substep count");
   static_assert((S - 1) * (A_INS + NBL) + (S_B - S) * NBL + (MX ? MB + NB_OPS * NB : 0) <= 63,
                 "vmcnt range");
+  // The tile barrier's wait leaves the newest (S_B - S) * NBL loads in
+  // flight. Only NBL B loads of one k-tile follow the A loads of tile
+  // kt + 1 in issue order, so that count covers no A load only when the B
+  // ring is exactly one stage deeper than A's.
+  static_assert(!RING_B || SB == S + 1, "B ring depth must be S + 1");
 
   // the epilogue stages 128 rows at a time (the quantising one only for
   // the optional pre-activation copies)
@@ -919,6 +842,14 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
         const int grow = t.m0 + row, gcol = t.n0 + col;
         if (grow >= t.m_end || gcol >= p.N) return;
         TO* o = dst + (long)grow * p.ldc + gcol;
+        // a piece that ends past N (N = E of the router, any count), or
+        // whose rows are not 16-byte aligned, is stored element by element:
+        // its tail columns would land in the next row
+        if (gcol + 8 > p.N || (p.ldc * (long)sizeof(TO)) % 16 != 0) {
+          const int n = min(8, p.N - gcol);
+          for (int q = 0; q < n; ++q) o[q] = from_f32<TO>(v[q]);
+          return;
+        }
         if constexpr (sizeof(TO) == 2) {
           *(bf16x8*)o = pack8(v);
         } else {
@@ -1227,14 +1158,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, bool KCAT,
           int EPI, int SCHED, bool SKIP = false>
 hipError_t launch_t(const GemmParams& p, hipStream_t s) {
-  const long tiles_n = (p.N + BN - 1) / BN;
-  long tiles;
-  if (SCHED == kSchedM)
-    tiles = (tiles_n + p.group_n - 1) / p.group_n * p.tiles_m_max * p.group_n;
-  else
-    tiles = (long)p.G * ((p.M + BM - 1) / BM) * tiles_n;
+  const long tiles = launch_grid<BM, BN, SCHED>(p);
   if (tiles <= 0) return hipSuccess;
-  tiles = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((mfma_gemm_t<BM, BN, WGM, WGN, A_KM, B_KM, KCAT, EPI, SCHED, SKIP>),
                      dim3((unsigned)tiles), dim3(WGM * WGN * kWave), 0, s, p);
@@ -1244,16 +1169,8 @@ hipError_t launch_t(const GemmParams& p, hipStream_t s) {
 template <int BM, int BN, int BK, int WGM, int WGN, bool A_KC, bool B_KC,
           bool DUAL, int EPI, int SCHED, typename TO>
 hipError_t launch(const GemmParams& p, hipStream_t s) {
-  const long tiles_n = (p.N + BN - 1) / BN;
-  long tiles;
-  if (SCHED == kSchedM) {
-    const long ngroups = (tiles_n + p.group_n - 1) / p.group_n;
-    tiles = ngroups * p.tiles_m_max * p.group_n;
-  } else {
-    tiles = (long)p.G * ((p.M + BM - 1) / BM) * tiles_n;
-  }
+  const long tiles = launch_grid<BM, BN, SCHED>(p);
   if (tiles <= 0) return hipSuccess;
-  tiles = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(
       (mfma_gemm<BM, BN, BK, WGM, WGN, A_KC, B_KC, DUAL, EPI, SCHED, TO>),
@@ -1265,14 +1182,8 @@ template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
           typename TO, bool MX, int SCHED = kSchedM, int TAIL = 0,
           bool SKIP = false, bool KCAT = false, int SB = 0>
 hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
-  const long tiles_n = (p.N + BN - 1) / BN;
-  long tiles = SCHED == kSchedK
-                   ? (long)p.G * ((p.M + BM - 1) / BM) * tiles_n
-                   : (tiles_n + p.group_n - 1) / p.group_n * p.tiles_m_max *
-                         p.group_n;
-  if (TAIL == 2) tiles = p.slots;  // at most 4 r <= slots quarter tiles
+  const long tiles = launch_grid<BM, BN, SCHED, TAIL>(p);
   if (tiles <= 0) return hipSuccess;
-  tiles = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, S, WGM, WGN, DUAL, EPI, TO, MX, SCHED, TAIL, SKIP, KCAT, SB>),
                      dim3((unsigned)tiles), dim3(WGM * WGN * kWave), 0, s, p);
@@ -1284,7 +1195,7 @@ hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
 // for tuning), else 0
 int big_tile_waves() {
   static const int v = [] {
-    const char* e = getenv("MOE_BIG_TILE_WAVES");
+    const char* e = tuning_env("MOE_BIG_TILE_WAVES");
     const int n = e ? atoi(e) : 0;
     return n == 4 || n == 8 ? n : 0;
   }();
@@ -1374,7 +1285,7 @@ hipError_t launch_sized(bool big, const GemmParams& p, hipStream_t s) {
 // product (a testing aid: both kernels must agree with the oracle).
 bool force_staged() {
   static const bool v = [] {
-    const char* e = getenv("MOE_GEMM_BACKEND");
+    const char* e = tuning_env("MOE_GEMM_BACKEND");
     return e && strcmp(e, "staged") == 0;
   }();
   return v;
@@ -1387,7 +1298,7 @@ bool force_staged() {
 // groups measured slower). MOE_TILE_GROUP_N overrides, for tuning.
 int tile_group_n(int tiles_n) {
   static const int v = [] {
-    const char* e = getenv("MOE_TILE_GROUP_N");
+    const char* e = tuning_env("MOE_TILE_GROUP_N");
     const int n = e ? atoi(e) : 0;
     return n > 0 ? n : 0;
   }();

@@ -63,7 +63,22 @@ def oracle_routing(cfg, cinp, bufs):
     return oracle.route(logits, cfg.K, cfg.gate, cinp.get("bias"))
 
 
+def check_logits(cinp, bufs):
+    """The device router logits against fp64 x Wr^T (the routing checks
+    below route the oracle on the device's own logits, so they alone
+    cannot see a wrong router GEMM)."""
+    ref = oracle.router_logits(cinp["x"], cinp["wr"])
+    err = rel_err(bufs["logits"], ref)
+    assert err <= 1e-4, f"router logits rel err {err}"
+
+
 def check_routing_exact(cfg, cinp, bufs):
+    """Routing bit-exact against the oracle routed on the same logits; the
+    logits themselves are checked whenever the router GEMM made them (every
+    caller passes x and wr then)."""
+    if cinp.get("logits_in") is None:
+        assert "x" in cinp and "wr" in cinp, "pass x and wr to check the logits"
+        check_logits(cinp, bufs)
     idx, w = oracle_routing(cfg, cinp, bufs)
     g_idx = bufs["topk_idx"].cpu().to(torch.int64)
     assert torch.equal(g_idx, idx), "topk_idx differs"

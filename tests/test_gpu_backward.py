@@ -31,6 +31,14 @@ CASES = [
     # ~128 rows per expert: the data-gradient products run one 256-row
     # tile per expert with the empty 32-row blocks' MFMAs skipped
     mi.MoEConfig("mid_rows_T1024_d256_f256_E16_K2", 1024, 256, 256, 16, 2),
+    # widths that are multiples of 8 but not of 64: register-staged MFMA
+    # products, and the SIMT kernel for dgrad1 (d_ff % 64 != 0)
+    mi.MoEConfig("narrow_T512_d200_f328_E8_K2", 512, 200, 328, 8, 2),
+    # the library's limits: E = 1024, K = 16 (some experts empty)
+    mi.MoEConfig("max_experts_T256_d128_f64_E1024_K16", 256, 128, 64, 1024,
+                 16),
+    # E = 6: the router's output rows are not 16-byte aligned
+    mi.MoEConfig("six_experts_T1024_d128_f192_E6_K2", 1024, 128, 192, 6, 2),
 ]
 
 
@@ -66,6 +74,13 @@ SHARED = [
                  128, 16, 4, f_shared=256, gate="sigmoid", bias=True),
     mi.MoEConfig("shared_f32_T128_d64_f64_E4_K2_fs96", 128, 64, 64, 4, 2,
                  f_shared=96, dtype="f32"),
+    # Qwen-MoE-like structure: 60 fine-grained experts, top-4 softmax, an
+    # ungated shared expert twice the routed width
+    mi.MoEConfig("qwen_like_T1024_d256_f192_E60_K4_fs384", 1024, 256, 192, 60,
+                 4, f_shared=384),
+    # odd widths with a shared expert (staged MFMA and SIMT products)
+    mi.MoEConfig("narrow_shared_T256_d136_f200_E6_K2_fs72", 256, 136, 200, 6,
+                 2, f_shared=72),
 ]
 
 
@@ -106,8 +121,9 @@ def test_training_step_full_size_sampled():
     gb = L.alloc_backward(desc, DEV)
     L.backward(desc, ginp, fb, ginp["dy"], gb)
     torch.cuda.synchronize()
-    idx, w, counts, *_ = check_routing_exact(cfg, {"logits_in": None,
-                                                   "bias": None}, fb)
+    idx, w, counts, *_ = check_routing_exact(cfg, {"logits_in": None, "bias": None,
+                                                   "x": ginp["x"],
+                                                   "wr": ginp["wr"]}, fb)
     g = torch.Generator().manual_seed(0)
     toks = sorted(set(torch.randint(0, cfg.T, (6,), generator=g).tolist()))
     cols = [(int(torch.randint(0, cfg.E, (1,), generator=g)),

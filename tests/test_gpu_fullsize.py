@@ -12,14 +12,15 @@ from moe_testlib import DEV, check_routing_exact, rel_err, run_forward
 
 pytestmark = pytest.mark.gpu
 
-FULL = [mi.MIXTRAL, mi.DEEPSEEK_V3, mi.SKEWED]
+FULL = [mi.MIXTRAL, mi.DEEPSEEK_V3, mi.SKEWED, mi.QWEN_MOE]
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
 def test_full_size_forward_sampled(cfg):
     ginp = mi.make_inputs(cfg, 0, device=DEV)
     desc, bufs = run_forward(cfg, ginp, save_acts=False)
-    small = {"logits_in": None if ginp["logits_in"] is None
+    small = {"x": ginp["x"], "wr": ginp["wr"],
+             "logits_in": None if ginp["logits_in"] is None
              else ginp["logits_in"].cpu(),
              "bias": None if ginp["bias"] is None else ginp["bias"].cpu()}
     idx, w, counts, offsets, src, dest = check_routing_exact(cfg, small, bufs)

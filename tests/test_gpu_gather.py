@@ -79,7 +79,7 @@ def test_gather_forward_full_size(cfg):
     forward bit for bit."""
     ginp = mi.make_inputs(cfg, 0, device=DEV)
     mat, gat = _both(desc_of(cfg), ginp)
-    small = {"logits_in": None,
+    small = {"logits_in": None, "x": ginp["x"], "wr": ginp["wr"],
              "bias": None if ginp["bias"] is None else ginp["bias"].cpu()}
     idx, w, *_ = check_routing_exact(cfg, small, gat)
     toks = [0, 1, cfg.T // 2, cfg.T - 1]

@@ -2,6 +2,8 @@
 permute bit-exact (codes and scales), the MXFP8 forward within 2e-2 of
 max|ref| of the oracle that applies the same E8M0-scaled E4M3 rule; its
 error against the exact (bf16-input) oracle is reported."""
+import warnings
+
 import pytest
 import torch
 
@@ -12,6 +14,20 @@ from ragged_grouped_gemm_router_amd import binding as B
 from ragged_grouped_gemm_router_amd import layer as L
 
 pytestmark = pytest.mark.gpu
+
+# Bound on the MXFP8 forward's error against the exact (bf16-input) layer,
+# max|err| / max|ref|. E4M3 keeps 3 mantissa bits, so each MX-quantised
+# element carries a relative rounding error of at most 2^-4, about uniform,
+# rms 2^-4 / sqrt(3) = 0.036. A product of two quantised operands then has
+# a relative error of rms about 0.051 per term, and with many independent
+# terms the output error is about 0.051 of the output's rms. GEMM 2 adds
+# the same again on top of GEMM 1's (h and W2 quantised): rms about 0.07
+# of the output's rms, and the maxima of error and output over the sample
+# are both a few times their rms, so max|err| / max|ref| lands near 0.07
+# (measured: 0.067-0.084 on the small layers, 0.075 on the full-size
+# Mixtral-shaped one). The bound is twice the largest relative rounding
+# error of one E4M3 element, 2 * 2^-4.
+MX_VS_EXACT = 0.125
 F64 = torch.float64
 
 
@@ -88,10 +104,11 @@ def test_mxfp8_forward_parity(cfg):
     exact = oracle.forward(cinp["x"], cinp["w1"], cinp["w3"], cinp["w2"], idx, w,
                            *sh)
     err_exact = rel_err(bufs["out"], exact)
-    print(f"{cfg.name}: vs fp8-aware oracle {err:.3e}, vs exact oracle "
-          f"{err_exact:.3e}")
+    warnings.warn(f"MXFP8 forward {cfg.name}: max|err|/max|ref| vs the "
+                  f"fp8-aware oracle {err:.3e}, vs the bf16 (exact) oracle "
+                  f"{err_exact:.3e}")
     assert err <= 2e-2, err
-    assert err_exact <= 0.25, err_exact
+    assert err_exact <= MX_VS_EXACT, err_exact
 
 
 def test_mxfp8_forward_full_size_sampled():
@@ -100,8 +117,8 @@ def test_mxfp8_forward_full_size_sampled():
     cfg = mi.MIXTRAL_TRAIN
     ginp = mi.make_inputs(cfg, 0, device=DEV)
     desc, bufs, mx = _mx_forward(cfg, ginp)
-    idx, w, *_ = check_routing_exact(cfg, {"logits_in": None, "bias": None},
-                                     bufs)
+    idx, w, *_ = check_routing_exact(cfg, {"logits_in": None, "bias": None,
+                                      "x": ginp["x"], "wr": ginp["wr"]}, bufs)
     toks = [0, 17, 4095, cfg.T - 1]
     cache = {}
     ref = oracle.forward_mxfp8(ginp["x"], ginp["w1"], ginp["w3"], ginp["w2"],
@@ -110,5 +127,8 @@ def test_mxfp8_forward_full_size_sampled():
     exact = oracle.forward(ginp["x"], ginp["w1"], ginp["w3"], ginp["w2"], idx,
                            w, tokens=toks)
     err_exact = rel_err(bufs["out"][torch.tensor(toks, device=DEV)], exact)
-    print(f"full size: vs fp8-aware oracle {err:.3e}, vs exact {err_exact:.3e}")
+    warnings.warn(f"MXFP8 forward {cfg.name} (full size, tokens {toks}): "
+                  f"max|err|/max|ref| vs the fp8-aware oracle {err:.3e}, vs "
+                  f"the bf16 (exact) oracle {err_exact:.3e}")
     assert err <= 2e-2, err
+    assert err_exact <= MX_VS_EXACT, err_exact

@@ -96,8 +96,8 @@ def test_mxfp8_backward_full_size_sampled():
     cfg = mi.MIXTRAL_TRAIN
     ginp = mi.make_inputs(cfg, 0, device=DEV, with_dy=True)
     fb, gb = _mx_train(cfg, ginp, save_acts=True)
-    idx, w, *_ = check_routing_exact(cfg, {"logits_in": None, "bias": None},
-                                     fb)
+    idx, w, *_ = check_routing_exact(cfg, {"logits_in": None, "bias": None,
+                                      "x": ginp["x"], "wr": ginp["wr"]}, fb)
     g = torch.Generator().manual_seed(1)
     toks = [0, cfg.T - 1]
     e0 = int(idx[0, 0])

@@ -31,6 +31,23 @@ SMALL = [
     # per expert with the empty 32-row blocks' MFMAs skipped
     mi.MoEConfig("deepseek_mid_rows_T1024_d256_f256_E64_K8_shared", 1024, 256,
                  256, 64, 8, f_shared=256, gate="sigmoid", bias=True),
+    # expert counts that are not a multiple of 8: the router GEMM's last
+    # 8-column output piece of a row is partial (E = 4, 60) or its rows
+    # are not 16-byte aligned (E = 6); E = 60 with a shared expert is the
+    # Qwen-MoE-like structure
+    mi.MoEConfig("four_experts_T1024_d128_f128_E4_K2", 1024, 128, 128, 4, 2),
+    mi.MoEConfig("six_experts_T1024_d256_f256_E6_K2", 1024, 256, 256, 6, 2),
+    mi.MoEConfig("qwen_like_T1024_d256_f192_E60_K4_shared384", 1024, 256, 192,
+                 60, 4, f_shared=384),
+    # widths that are multiples of 8 but not of 64: the register-staged
+    # MFMA kernel (k-tiles zero-filled past K) for every forward product
+    mi.MoEConfig("narrow_T512_d200_f328_E8_K2", 512, 200, 328, 8, 2),
+    mi.MoEConfig("narrow_shared_T256_d136_f200_E6_K2_fs72", 256, 136, 200, 6,
+                 2, f_shared=72),
+    # the library's limits: E = 1024 experts, K = 16 per token (about 8
+    # rows per expert, some experts empty)
+    mi.MoEConfig("max_experts_T512_d128_f64_E1024_K16", 512, 128, 64, 1024,
+                 16),
 ]
 IDS = [c.name for c in SMALL]
 

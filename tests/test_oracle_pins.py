@@ -690,3 +690,164 @@ def test_mx_backward_shared_expert_reduces():
                                       z(ws3), z(ws2))
     without = oracle.backward_mxfp8(x, w1, w3, w2, idx, w, dy)
     assert torch.equal(with_zero["dx"], without["dx"])
+
+
+# --------------------------------------------------------------------------
+# MXFP8 forward: which operand is blocked along which axis [P2, section on
+# the TE mechanisms: MXFP8 grouped GEMM operands; P3 §13.6 per-tile scales]
+# --------------------------------------------------------------------------
+
+def test_mxfp8_forward_without_quantisers_is_exact():
+    """With every quantiser the identity the MXFP8 forward is the exact
+    layer, shared expert included: no other arithmetic differs."""
+    cfg, inp, logits, idx, w = _rand_layer(24, 64, 96, 4, 2, seed=41, shared=64)
+    args = (inp["x"], inp["w1"], inp["w3"], inp["w2"], idx, w,
+            inp["ws1"], inp["ws3"], inp["ws2"])
+    got = oracle.forward_mxfp8(*args, quant=False)
+    ref = oracle.forward(*args)
+    assert (got - ref).abs().max() <= 1e-12 * ref.abs().max()
+
+
+def _mx_exact_rows(rows, cols, scale_of_row, g):
+    """A matrix whose 32-blocks along each row are exactly representable
+    in MX (E4M3 values times 2^X, each block's largest magnitude 448 so
+    that X = floor(log2 amax) - 8 is the X used), with row r scaled by
+    scale_of_row(r). Rows with different scales make the 32-blocks down a
+    column mix magnitudes 2^8 apart and more, which E4M3's 3 mantissa bits
+    and subnormal floor cannot hold: those blocks are not exact."""
+    vals = oracle.e4m3_values()
+    fin = vals[~torch.isnan(vals)]
+    m = fin[torch.randint(0, fin.numel(), (rows, cols), generator=g)]
+    m.view(rows, cols // 32, 32)[:, :, 0] = 448.0 * torch.where(
+        torch.rand(rows, cols // 32, generator=g) < 0.5, -1.0, 1.0).to(F64)
+    s = torch.tensor([float(scale_of_row(r)) for r in range(rows)], dtype=F64)
+    return m * s.unsqueeze(1)
+
+
+def test_mxfp8_forward_quantiser_axes():
+    """Inputs exact in 32-blocks along each GEMM's contraction axis (x and
+    W1/W3 along d_model, W2 along d_ff) and not along the other axis: the
+    MXFP8 forward must then equal the exact GEMM 1, h MX-rounded along
+    d_ff, the exact GEMM 2 and the combine, composed from the stage
+    functions (to rounding). An oracle that left h unquantised, or blocked
+    x, W1/W3 or W2 along their other axis, differs by far more; the test
+    shows that too, so the construction discriminates."""
+    g = torch.Generator().manual_seed(42)
+    T, d, f, E, K = 64, 64, 96, 3, 2
+    x = _mx_exact_rows(T, d, lambda r: 2.0 ** (r % 9 - 12), g)
+    w1 = torch.stack([_mx_exact_rows(f, d, lambda r: 2.0 ** (-(r % 11) - 10), g)
+                      for _ in range(E)])
+    w3 = torch.stack([_mx_exact_rows(f, d, lambda r: 2.0 ** (-(r % 7) - 10), g)
+                      for _ in range(E)])
+    w2 = torch.stack([_mx_exact_rows(d, f, lambda r: 2.0 ** (-(r % 10) - 10), g)
+                      for _ in range(E)])
+    assert torch.equal(oracle.mx_roundtrip(x), x)
+    for W in (w1, w3, w2):
+        assert torch.equal(oracle.mx_roundtrip(W), W)
+        assert not torch.equal(oracle.mx_roundtrip_cols(W[0]), W[0])
+    assert not torch.equal(oracle.mx_roundtrip(x.T).T, x)
+    L = torch.randn(T, E, generator=g, dtype=F64).float()
+    idx, w = oracle.route(L, K, "softmax")
+    counts, offsets, src, dest = oracle.permute(idx, E)
+    assert (counts > 0).all()
+
+    def composed(xx, W1, W3, W2, hq=oracle.mx_roundtrip):
+        _, _, h = oracle.stage_gemm1(xx[src // K], offsets, W1, W3)
+        return oracle.stage_combine(oracle.stage_gemm2(hq(h), offsets, W2),
+                                    dest, w)
+
+    got = oracle.forward_mxfp8(x, w1, w3, w2, idx, w)
+    ref = composed(x, w1, w3, w2)
+    scale = ref.abs().max()
+    assert (got - ref).abs().max() <= 1e-12 * scale
+    cols = lambda W: torch.stack([oracle.mx_roundtrip_cols(m) for m in W])  # noqa: E731
+    wrong = {
+        "h unquantised": composed(x, w1, w3, w2, hq=lambda h: h),
+        "h along tokens": composed(x, w1, w3, w2,
+                                   hq=lambda h: oracle.mx_roundtrip_cols(h)),
+        "x along tokens": composed(oracle.mx_roundtrip(x.T).T, w1, w3, w2),
+        "W1 along d_ff": composed(x, cols(w1), w3, w2),
+        "W3 along d_ff": composed(x, w1, cols(w3), w2),
+        "W2 along d_model": composed(x, w1, w3, cols(w2)),
+    }
+    for name, v in wrong.items():
+        assert (v - ref).abs().max() > 1e-6 * scale, name
+
+
+def test_mx_backward_quantiser_placement():
+    """Which quantiser meets which operand in the MXFP8 backward of one
+    expert: identity quantisers that record what they are applied to show
+    the data-gradient products take W2, W1 and W3 through the column
+    quantiser (blocks along their first dimension: d_model for W2 [d, f],
+    d_ff for W1, W3 [f, d], the contraction of dh = g W2 and of
+    dx = da W1 + db W3), and that the forward's weights, its h, the output
+    gradient g and da, db go through the row quantiser (blocks along their
+    last dimension). With the column quantiser's axis pinned separately,
+    this fixes every block axis of the backward."""
+    from oracle import mxfp8 as M
+    g = torch.Generator().manual_seed(43)
+    n, d, f = 20, 64, 96
+    X = torch.randn(n, d, generator=g, dtype=F64)
+    W1 = torch.randn(f, d, generator=g, dtype=F64)
+    W3 = torch.randn(f, d, generator=g, dtype=F64)
+    W2 = torch.randn(d, f, generator=g, dtype=F64)
+    G = torch.randn(n, d, generator=g, dtype=F64)
+    rows, colq = [], []
+
+    def Q(v):
+        rows.append(v.clone())
+        return v
+
+    def Qc(v):
+        colq.append(v.clone())
+        return v
+
+    dX, dW1, dW3, dW2, Y = M._mx_ffn_bwd(X, W1, W3, W2, G, Q, Qc, lambda v: v)
+
+    def count(lst, t):
+        return sum(1 for v in lst if v.shape == t.shape and torch.equal(v, t))
+
+    for W in (W1, W3, W2):
+        assert count(colq, W) == 1 and count(rows, W) == 1
+    assert len(colq) == 3
+    assert count(rows, G) == 1
+    a, b = X @ W1.T, X @ W3.T
+    h = oracle.swiglu(a, b)
+    assert count(rows, h) == 1
+    # da and db are the row-quantised [n, f] operands other than h
+    others = [v for v in rows if v.shape == (n, f) and not torch.equal(v, h)]
+    assert len(others) == 2 and len(rows) == 7
+    ref = oracle.backward(X, W1.unsqueeze(0), W3.unsqueeze(0), W2.unsqueeze(0),
+                          torch.zeros(n, 1, dtype=torch.long),
+                          torch.ones(n, 1, dtype=F64), G)
+    assert torch.allclose(dX, ref["dx"], rtol=0, atol=1e-10)
+    assert torch.allclose(dW1, ref["dw1"][0], rtol=0, atol=1e-10)
+    assert torch.allclose(dW2, ref["dw2"][0], rtol=0, atol=1e-10)
+
+
+def test_backward_gradcheck():
+    """torch.autograd.gradcheck on the oracle's closed-form backward: a
+    function whose forward is oracle.forward and whose backward is
+    oracle.backward must agree with central finite differences of the
+    forward in every input (x, W1, W3, W2, the gate weights, shared
+    expert weights), routing fixed."""
+    T, d, f, E, K, fs = 6, 4, 5, 3, 2, 3
+    cfg, inp, logits, idx, w = _rand_layer(T, d, f, E, K, seed=44, shared=fs)
+
+    class Layer(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, w1, w3, w2, ww, ws1, ws3, ws2):
+            ctx.save_for_backward(x, w1, w3, w2, ww, ws1, ws3, ws2)
+            return oracle.forward(x, w1, w3, w2, idx, ww, ws1, ws3, ws2)
+
+        @staticmethod
+        def backward(ctx, dy):
+            x, w1, w3, w2, ww, ws1, ws3, ws2 = ctx.saved_tensors
+            r = oracle.backward(x, w1, w3, w2, idx, ww, dy, ws1, ws3, ws2)
+            return (r["dx"], r["dw1"], r["dw3"], r["dw2"], r["d_w"],
+                    r["dws1"], r["dws3"], r["dws2"])
+
+    ins = tuple(t.double().clone().requires_grad_() for t in
+                (inp["x"], inp["w1"], inp["w3"], inp["w2"], w,
+                 inp["ws1"], inp["ws3"], inp["ws2"]))
+    assert torch.autograd.gradcheck(Layer.apply, ins, eps=1e-6, atol=1e-7)
