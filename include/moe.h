@@ -80,6 +80,8 @@ typedef int32_t moe_status;
 /* limits of this library */
 #define MOE_K_MAX 16
 #define MOE_E_MAX 1024
+/* size of the static device scratch moe_forward_noalloc works in */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Number of stage-boundary events moe_forward / moe_backward can record. */
 #define MOE_FWD_NEVENTS 6
@@ -291,6 +293,27 @@ moe_status moe_unpermute_combine(const moe_desc* desc, const void* y_perm,
  * MOE_EWORKSPACE; nothing is enqueued on error. */
 moe_status moe_forward(const moe_desc* desc, const moe_fwd_args* args,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* Allocation-free whole forward, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same computation, arguments and errors as
+ * moe_forward, except that the workspace is not passed in: it is a static
+ * device array of MOE_STATIC_SCRATCH_BYTES (64 MiB) that the library holds
+ * on every GPU it runs on, from the first call there until the process
+ * ends. The caller still owns every buffer in args. The call allocates and
+ * frees nothing. The stream must belong to the current device.
+ *   - MOE_EUNSUPPORTED when moe_workspace_size(desc, 0) exceeds
+ *     MOE_STATIC_SCRATCH_BYTES (e.g. a shared expert's T x d_ff_shared
+ *     hidden, or under MXFP8 the quantised x, beyond it);
+ *   - MOE_EHIP when the device address of the array cannot be obtained;
+ *   - otherwise as moe_forward.
+ * Every call on one GPU works in that GPU's one array, which keeps the
+ * previous call's contents (no part of it needs to start at zero: each
+ * kernel writes what it later reads). Calls on one stream are ordered;
+ * calls that overlap in time on one GPU (different streams, or different
+ * host threads) race on the array and must not be made. */
+moe_status moe_forward_noalloc(const moe_desc* desc, const moe_fwd_args* args,
+                               void* stream);
 
 /* Whole backward (see moe_bwd_args). Deterministic: weight gradients are
  * owned tile by tile (no split-K atomics). The shared expert [P3 §5] is an

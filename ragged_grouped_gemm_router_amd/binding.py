@@ -26,13 +26,15 @@ MOE_FLAG_SAVE_ACTS = 1
 MOE_FLAG_NO_TAIL_SPLIT = 2
 MOE_K_MAX, MOE_E_MAX = 16, 1024
 MOE_FWD_NEVENTS, MOE_BWD_NEVENTS = 6, 8
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = ["moe_status_str", "moe_workspace_size", "moe_route",
             "moe_permute", "moe_grouped_gemm_swiglu", "moe_unpermute_combine",
             "moe_forward", "moe_backward", "moe_router_workspace_size",
             "moe_router_backward", "moe_load_balance_stats",
             "moe_update_route_bias", "moe_balance_monitor",
-            "moe_quantize_mxfp8", "moe_quantize_mxfp8_t"]
+            "moe_quantize_mxfp8", "moe_quantize_mxfp8_t",
+            "moe_forward_noalloc"]
 
 
 class MoeError(RuntimeError):
@@ -107,6 +109,7 @@ def load() -> ctypes.CDLL:
         "moe_unpermute_combine": (c_int32, [D] + [c_void_p] * 6),
         "moe_forward": (c_int32, [D, POINTER(MoeFwdArgs), c_void_p, c_size_t,
                                   c_void_p]),
+        "moe_forward_noalloc": (c_int32, [D, POINTER(MoeFwdArgs), c_void_p]),
         "moe_backward": (c_int32, [D, POINTER(MoeBwdArgs), c_void_p,
                                    c_size_t, c_void_p]),
         "moe_quantize_mxfp8_t": (c_int32, [c_void_p, c_int64, c_int64,
@@ -225,6 +228,13 @@ def moe_forward(desc, args: MoeFwdArgs, ws, stream=None):
                              ws.numel() * ws.element_size(),
                              stream if stream is not None else current_stream()),
           "moe_forward")
+
+
+def moe_forward_noalloc(desc, args: MoeFwdArgs, stream=None):
+    check(load().moe_forward_noalloc(
+        ctypes.byref(desc), ctypes.byref(args),
+        stream if stream is not None else current_stream()),
+        "moe_forward_noalloc")
 
 
 def moe_backward(desc, args: MoeBwdArgs, ws, stream=None):

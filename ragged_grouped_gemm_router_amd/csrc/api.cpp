@@ -5,6 +5,7 @@
 #include <climits>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "gemm.h"
 #include "launch.h"
@@ -972,6 +973,39 @@ moe_status forward_in(const moe_desc* d, const moe_fwd_args* a, void* ws,
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Static device scratch of the allocation-free forward. In host code the
+// name `scratch` is only a stand-in for the symbol: its device address (one
+// per GPU) comes from hipGetSymbolAddress with that GPU current, and only
+// that address is handed to kernels.
+static __device__ __align__(256) char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per GPU
+
+// This GPU's copy of the scratch (looked up on the first call on each
+// device, with that device current); nullptr if HIP cannot provide it.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();  // leave no sticky error for the next call
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
@@ -986,6 +1020,19 @@ moe_status moe_forward(const moe_desc* d, const moe_fwd_args* a, void* ws,
   return forward_in(d, a, ws, (hipStream_t)stream);
 }
 
+moe_status moe_forward_noalloc(const moe_desc* d, const moe_fwd_args* a,
+                               void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;  // nothing is accessed
+  st = check_fwd_args(d, a);
+  if (st != MOE_OK) return st;
+  if (fwd_ws_layout(d, nullptr, nullptr) > MOE_STATIC_SCRATCH_BYTES)
+    return MOE_EUNSUPPORTED;
+  void* ws = device_scratch();
+  if (!ws) return MOE_EHIP;
+  return forward_in(d, a, ws, (hipStream_t)stream);
+}
 
 moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
                         size_t ws_bytes, void* stream) {

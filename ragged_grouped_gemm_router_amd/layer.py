@@ -155,6 +155,14 @@ def forward(desc: B.MoeDesc, inp: dict, bufs: dict, events=None,
     return bufs["out"]
 
 
+def forward_noalloc(desc: B.MoeDesc, inp: dict, bufs: dict, events=None,
+                    stream=None) -> torch.Tensor:
+    """forward() without a workspace: the library's static device scratch
+    serves instead (bufs["ws"] is not used)."""
+    B.moe_forward_noalloc(desc, fwd_args(inp, bufs, events), stream)
+    return bufs["out"]
+
+
 def alloc_backward(desc: B.MoeDesc, device="cuda") -> dict:
     T, d, f, E, K = desc.T, desc.d_model, desc.d_ff, desc.E, desc.K
     fs = desc.d_ff_shared
