@@ -267,9 +267,13 @@ void record(void* ev, hipStream_t s) {
 }
 
 // --- building blocks shared by the entry points --------------------------
+// ws != NULL (the whole forward): where the shape allows, the top-K kernel
+// also ranks the permute's chunks into ws (see launch_topk_rank), and
+// *ranked says so.
 hipError_t do_route(const moe_desc* d, const void* x, const void* wr,
                     const float* bias, const float* logits_in,
-                    float* logits_out, int32_t* idx, float* w, hipStream_t s) {
+                    float* logits_out, int32_t* idx, float* w, hipStream_t s,
+                    const FwdWs* ws = nullptr, bool* ranked = nullptr) {
   const float* L = logits_in;
   if (!L) {
     GemmParams p = gp();
@@ -281,22 +285,30 @@ hipError_t do_route(const moe_desc* d, const void* x, const void* wr,
     if (e != hipSuccess) return e;
     L = logits_out;
   }
+  if (ranked) *ranked = false;
+  if (ws && ranked && topk_rank_supported(d->E, d->K)) {
+    *ranked = true;
+    return launch_topk_rank(L, bias, d->T, d->E, d->K, d->gate, idx, w,
+                            ws->block_hist, ws->rank, s);
+  }
   return launch_topk(L, bias, d->T, d->E, d->K, d->gate, idx, w, s);
 }
 
 // x_perm == NULL: only the indices (the expert GEMM gathers its rows from
 // x; under MXFP8 x is quantised once into the workspace for it).
+// ranked: the top-K kernel wrote the chunk histograms and ranks already.
 hipError_t do_permute(const moe_desc* d, const void* x, const int32_t* idx,
                       int32_t* counts, int32_t* offsets, int32_t* src,
                       int32_t* dest, void* x_perm, uint8_t* x_perm_scales,
-                      const FwdWs& ws, hipStream_t s) {
+                      const FwdWs& ws, hipStream_t s, bool ranked = false) {
   const int TK = d->T * d->K;
   // materialised bf16/fp32 rows with few experts: the scatter scans the
   // chunk histograms itself (one launch fewer)
   const bool fused = x_perm && d->gemm_dtype != MOE_MXFP8 &&
                      scan_in_scatter(TK, d->E);
   hipError_t e = launch_hist_rank_scan(idx, TK, d->E, ws.block_hist, ws.rank,
-                                       counts, offsets, ws.tile_off, s, !fused);
+                                       counts, offsets, ws.tile_off, s, !fused,
+                                       !ranked);
   if (e != hipSuccess) return e;
   if (!x_perm) {
     e = launch_slots(idx, ws.block_hist, ws.rank, TK, d->E, dest, src, s);
@@ -942,12 +954,13 @@ moe_status forward_in(const moe_desc* d, const moe_fwd_args* a, void* ws,
   FwdWs w;
   fwd_ws_layout(d, (char*)ws, &w);
   record(a->events[0], s);
+  bool ranked = false;
   hipError_t e = do_route(d, a->x, a->w_router, a->route_bias, a->logits_in,
-                          a->logits, a->topk_idx, a->topk_w, s);
+                          a->logits, a->topk_idx, a->topk_w, s, &w, &ranked);
   if (e != hipSuccess) return MOE_EHIP;
   record(a->events[1], s);
   e = do_permute(d, a->x, a->topk_idx, a->counts, a->offsets, a->sorted_src,
-                 a->dest, a->x_perm, a->x_perm_scales, w, s);
+                 a->dest, a->x_perm, a->x_perm_scales, w, s, ranked);
   if (e != hipSuccess) return MOE_EHIP;
   record(a->events[2], s);
   const int32_t* gsrc = gather ? a->sorted_src : nullptr;

@@ -149,8 +149,12 @@ struct TileLoader {
   }
 };
 
+// sigmoid of the SwiGLU epilogues: hardware exp2 and reciprocal (about 1
+// ulp each), far inside the bf16 rounding of the stored result, instead of
+// an IEEE division (ten instructions per element in an epilogue that no
+// other work overlaps: one workgroup per CU)
 __device__ __forceinline__ float fast_sigmoid(float a) {
-  return 1.0f / (1.0f + __expf(-a));
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
 // This workgroup's output tile (the decode and its order are described
@@ -701,26 +705,63 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
+  // DMA batches. Batch b = {A of k-tile b+S-1, B of k-tile b+S_B-1} fills
+  // the stages that the tile barrier ending k-tile b-1 frees: its first D1
+  // instructions are issued right after that barrier (in the last substep
+  // of tile b-1), the other N_LOAD - D1 spread over substeps 0 .. NSP-1 of
+  // tile b, so that the eight waves' DMA issue does not all fall into one
+  // substep. Every batch is issued whole between two consecutive tile
+  // barriers, in the same order, so the barriers' wait counts do not
+  // depend on the split. (MXFP8 products issue whole batches after the
+  // barrier: their scale loads share the wait count.)
+#ifndef MOE_DMA_AFTER_BAR
+#define MOE_DMA_AFTER_BAR 8  // eighths of a batch issued after the barrier
+#endif
+#ifndef MOE_DMA_SPREAD
+#define MOE_DMA_SPREAD 1     // substeps of the next tile taking the rest
+#endif
+  constexpr int D1 = MX ? N_LOAD : N_LOAD * MOE_DMA_AFTER_BAR / 8;
+  constexpr int NSP = D1 == N_LOAD ? 0 : (MOE_DMA_SPREAD < KS - 1 ? MOE_DMA_SPREAD : KS - 1);
+  static_assert(D1 == N_LOAD || NSP >= 1, "a split batch needs a substep for its rest");
+
   // Prologue: (scales of k-tile 0,) k-tiles 0 .. S-1 in flight, and the
   // B operands of k-tiles S .. S_B-1 (past the last tile, the last one
   // again, into stages nobody reads); wait for tile 0. With a deeper B
   // ring, MXFP8 scales run two tiles ahead: those of tile kt+1 are issued
   // before the B DMA of tile kt+2 (here: of tile 2), so that one is still
-  // the newest outstanding load at the tile barrier.
+  // the newest outstanding load at the tile barrier. With split batches
+  // the prologue issues k-tiles 0 .. S-2, the B of tiles S-1 .. S_B-2 and
+  // the first part of batch 0; batch 0's rest follows in tile 0.
   constexpr int NSC_RING = RING_B && MX ? NSC : 0;
   if (nk > 0) {  // (an empty group's tile writes zeros)
-  load_scales(RING_B ? s_cur : s_nxt, 0);
+  if constexpr (D1 == N_LOAD) {
+    load_scales(RING_B ? s_cur : s_nxt, 0);
 #pragma unroll
-  for (int i = 0; i < S; ++i)
+    for (int i = 0; i < S; ++i)
 #pragma unroll
-    for (int d = 0; d < N_LOAD; ++d)
-      issue_one(min(i, nk - 1), i, min(i, nk - 1), i, d);
-  if constexpr (RING_B) load_scales(s_nxt, min(1, nk - 1));
+      for (int d = 0; d < N_LOAD; ++d)
+        issue_one(min(i, nk - 1), i, min(i, nk - 1), i, d);
+    if constexpr (RING_B) load_scales(s_nxt, min(1, nk - 1));
 #pragma unroll
-  for (int i = S; i < S_B; ++i)
+    for (int i = S; i < S_B; ++i)
 #pragma unroll
-    for (int d = A_INS; d < N_LOAD; ++d) issue_one(0, 0, min(i, nk - 1), i, d);
-  barrier_after(std::integral_constant<int, (S - 1) * N_LOAD + NSC_RING + (S_B - S) * NBL>{});
+      for (int d = A_INS; d < N_LOAD; ++d) issue_one(0, 0, min(i, nk - 1), i, d);
+    barrier_after(std::integral_constant<int, (S - 1) * N_LOAD + NSC_RING + (S_B - S) * NBL>{});
+  } else {
+#pragma unroll
+    for (int i = 0; i + 1 < S; ++i)
+#pragma unroll
+      for (int d = 0; d < N_LOAD; ++d)
+        issue_one(min(i, nk - 1), i, min(i, nk - 1), i, d);
+#pragma unroll
+    for (int i = S - 1; i + 1 < S_B; ++i)
+#pragma unroll
+      for (int d = A_INS; d < N_LOAD; ++d) issue_one(0, 0, min(i, nk - 1), i, d);
+#pragma unroll
+    for (int d = 0; d < D1; ++d)
+      issue_one(min(S - 1, nk - 1), S - 1, min(S_B - 1, nk - 1), S_B - 1, d);
+    barrier_after(std::integral_constant<int, (S - 2) * N_LOAD + (S_B - S) * NBL + D1>{});
+  }
   if constexpr (MX && !RING_B) {
 #pragma unroll
     for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
@@ -731,22 +772,22 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 
   // One region per k-substep. The MFMAs run on fragments read a region
   // earlier; the memory instructions of the region (the next substep's
-  // fragment reads and, at the last substep of a k-tile, the DMA of k-tile
-  // kt+S into the stage tile kt used) sit between them, at most a few per
-  // MFMA, so the in-order issue of a long memory burst never leaves the
-  // matrix pipe idle. The tile barrier waits until only the S-2 newest
-  // tiles' DMA (and, with a deeper B ring, the B DMA of the S_B-S newest
-  // B tiles) is outstanding, i.e. for tile kt+1. The first H MFMAs
-  // precede every new read: their wait for the current fragments then
-  // covers no read issued here. Every step is fenced with sched_barrier to
-  // keep this order. (MXFP8: the next tile's scales are fetched in the
-  // first region and swapped in after the tile barrier, once their wait is
-  // free.)
+  // fragment reads and the DMA instructions assigned to it) sit between
+  // them, at most a few per MFMA, so the in-order issue of a long memory
+  // burst never leaves the matrix pipe idle. The tile barrier waits until
+  // only the S-2 newest tiles' DMA (and, with a deeper B ring, the B DMA
+  // of the S_B-S newest B tiles) is outstanding, i.e. for tile kt+1. The
+  // first H MFMAs precede every new read: their wait for the current
+  // fragments then covers no read issued here. Every step is fenced with
+  // sched_barrier to keep this order. (MXFP8: the next tile's scales are
+  // fetched in the first region and swapped in after the tile barrier,
+  // once their wait is free.)
   constexpr int H = N_MFMA >= 8 ? 2 : N_MFMA >= 2 ? 1 : 0;
 #define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
-  // stage of k-tile kt (kt mod S) and of k-tile kt + 1, kept as counters
-  int st = 0, st_next = S > 1 ? 1 : 0;
-  int sbt = 0, sbt_next = 1;  // the same for the B ring
+  // stage of k-tile kt (kt mod S), of k-tile kt + 1 and of k-tile kt - 1,
+  // kept as counters
+  int st = 0, st_next = S > 1 ? 1 : 0, st_prev = S - 1;
+  int sbt = 0, sbt_next = 1, sbt_prev = S_B - 1;  // the same for the B ring
   for (int kt = 0; kt < nk; ++kt) {
     const char* sa = lds + st * A_STRIDE;
     const char* sa_next = lds + st_next * A_STRIDE;
@@ -757,9 +798,13 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
       Frags& cur = (ks & 1) ? fb : fa;
       Frags& nxt = (ks & 1) ? fa : fb;
       const bool last = ks + 1 == KS;
-      // memory ops of this region: N_READ reads (+ N_LOAD DMAs if last)
+      // memory ops of this region: N_READ reads, plus D1 DMAs of batch
+      // kt+1 after the barrier (last substep) or DMAs [d_lo, d_hi) of
+      // batch kt (substeps below NSP)
       constexpr int NM_MAX = N_READ + N_LOAD;
-      const int nm = last ? NM_MAX : N_READ;
+      const int d_lo = ks < NSP ? D1 + (N_LOAD - D1) * ks / (NSP > 0 ? NSP : 1) : 0;
+      const int d_hi = ks < NSP ? D1 + (N_LOAD - D1) * (ks + 1) / (NSP > 0 ? NSP : 1) : 0;
+      const int nm = N_READ + (last ? D1 : 0) + (d_hi - d_lo);
       substep_scales(ks);
       MOE_FENCE();
 #pragma unroll
@@ -789,17 +834,20 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 #pragma unroll
         for (int mm = 0; mm < NM_MAX; ++mm) {
           if (mm < m || mm >= m_end) continue;
-          if (!last) {
-            read_one(sa, sbb, ks + 1, nxt, mm);
-          } else {
-            // reads spread evenly among the DMAs: op mm is a read iff the
-            // running read quota floor(x * N_READ / NM_MAX) steps at it
-            const int rb = mm * N_READ / NM_MAX;
-            if ((mm + 1) * N_READ / NM_MAX != rb)
+          // reads spread evenly among the DMAs: op mm is a read iff the
+          // running read quota floor(x * N_READ / nm) steps at it
+          const int rb = mm * N_READ / nm;
+          if ((mm + 1) * N_READ / nm != rb) {
+            if (last)
               read_one(sa_next, sbb_next, 0, nxt, rb);
             else
-              issue_one(min(kt + S, nk - 1), st, min(kt + S_B, nk - 1), sbt,
-                        mm - rb);
+              read_one(sa, sbb, ks + 1, nxt, rb);
+          } else if (last) {
+            issue_one(min(kt + S, nk - 1), st, min(kt + S_B, nk - 1), sbt,
+                      mm - rb);
+          } else {
+            issue_one(min(kt + S - 1, nk - 1), st_prev,
+                      min(kt + S_B - 1, nk - 1), sbt_prev, d_lo + mm - rb);
           }
           MOE_FENCE();
         }
@@ -808,8 +856,10 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
         MOE_FENCE();
       }
     }
+    st_prev = st;
     st = st_next;
     st_next = st_next + 1 == S ? 0 : st_next + 1;
+    sbt_prev = sbt;
     sbt = sbt_next;
     sbt_next = sbt_next + 1 == S_B ? 0 : sbt_next + 1;
   }

@@ -12,6 +12,15 @@ hipError_t launch_topk(const float* logits, const float* bias, int T, int E,
                        int K, int gate, int32_t* idx, float* w,
                        hipStream_t s);
 
+// Top-K fused with the permute's chunk ranking (E <= 32, K a divisor of
+// kPermChunk with at least 64 tokens per chunk): idx, w as launch_topk,
+// plus block_hist [nblk, E] (each chunk's expert counts, unscanned) and
+// rank [T*K], as the histogram pass of launch_hist_rank_scan writes them.
+bool topk_rank_supported(int E, int K);
+hipError_t launch_topk_rank(const float* logits, const float* bias, int T,
+                            int E, int K, int gate, int32_t* idx, float* w,
+                            int32_t* block_hist, int32_t* rank, hipStream_t s);
+
 // Counting sort of the T*K copies by expert (stable in the copy index).
 // block_hist: [nblk, E] int32 scratch, nblk = ceil(TK / kPermChunk), left
 // holding the first slot of every (chunk, expert); rank: [TK] int32, each
@@ -19,11 +28,13 @@ hipError_t launch_topk(const float* logits, const float* bias, int T, int E,
 // kNumTileBM arrays of E+1 (row-tile prefix per tile height). scan ==
 // false stops after the histograms (block_hist then holds the counts of
 // every (chunk, expert)), for launch_scatter to scan them itself.
+// hist == false: block_hist and rank hold the histogram pass's results
+// already (launch_topk_rank), and only the scan runs.
 hipError_t launch_hist_rank_scan(const int32_t* idx, int TK, int E,
                                  int32_t* block_hist, int32_t* rank,
                                  int32_t* counts, int32_t* offsets,
                                  int32_t* const* tile_off, hipStream_t s,
-                                 bool scan = true);
+                                 bool scan = true, bool hist = true);
 // Whether the scatter can scan the chunk histograms itself (E * chunks
 // small enough for one workgroup of the scatter).
 bool scan_in_scatter(int TK, int E);

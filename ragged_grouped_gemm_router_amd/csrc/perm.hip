@@ -20,65 +20,22 @@
 // The order within an expert follows the copy index, so the sort is stable.
 #include "gemm.h"
 #include "launch.h"
+#include "rank.h"
 
 namespace moe {
 namespace {
 
 constexpr int kRankWaves = 4;
-constexpr int kRankPerWave = kPermChunk / kRankWaves;
-static_assert(kRankPerWave % kWave == 0, "chunk split");
 
 __global__ __launch_bounds__(kRankWaves * kWave) void hist_rank_kernel(
     const int32_t* __restrict__ idx, int TK, int E, int nbits,
     int32_t* __restrict__ block_hist, int32_t* __restrict__ rank) {
   __shared__ int32_t cnt[kRankWaves][MOE_E_MAX];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int w = tid / kWave, lane = tid % kWave;
-  for (int i = tid; i < kRankWaves * E; i += kRankWaves * kWave)
-    cnt[i / E][i % E] = 0;
-  __syncthreads();
-  constexpr int R = kRankPerWave / kWave;
-  int ex[R], rk[R];
-  const int j0 = b * kPermChunk + w * kRankPerWave;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int j = j0 + r * kWave + lane;
-    const bool valid = j < TK;
-    const int e = valid ? idx[j] : 0;
-    uint64_t m = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool on = (e >> bit) & 1;
-      const uint64_t bal = __ballot(valid && on);
-      m &= on ? bal : ~bal;
-    }
-    ex[r] = e;
-    rk[r] = 0;
-    if (valid) {
-      const int base = cnt[w][e];  // every lane of the group reads first
-      rk[r] = base + __popcll(m & ((1ull << lane) - 1ull));
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (valid && (m >> lane) == 1ull) cnt[w][e] += __popcll(m);
-    __builtin_amdgcn_wave_barrier();
-  }
-  __syncthreads();
-  // per expert: chunk count, and each wave's first rank (in place)
-  for (int e = tid; e < E; e += kRankWaves * kWave) {
-    int run = 0;
-#pragma unroll
-    for (int q = 0; q < kRankWaves; ++q) {
-      const int c = cnt[q][e];
-      cnt[q][e] = run;
-      run += c;
-    }
-    block_hist[(long)b * E + e] = run;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int j = j0 + r * kWave + lane;
-    if (j < TK) rank[j] = cnt[w][ex[r]] + rk[r];
-  }
+  const long j0 = (long)blockIdx.x * kPermChunk;
+  const int n = (int)min((long)kPermChunk, TK - j0);
+  rank_chunk<kRankWaves, MOE_E_MAX>([&](int i) { return idx[j0 + i]; }, n, E,
+                                    nbits, j0, cnt,
+                                    block_hist + (long)blockIdx.x * E, rank);
 }
 
 // Exclusive scan over a block of NW waves (1024 threads by default) of N
@@ -583,10 +540,14 @@ hipError_t launch_transpose_pad(const void* src, int rows_max, int C,
   return hipGetLastError();
 }
 
-// tokens per scatter workgroup: ~64 KB of rows, at most kScatterThreads
-// copies
-int scatter_tokens_per_block(int K, long row_bytes) {
-  long tpb = 65536 / (row_bytes > 0 ? row_bytes : 1);
+// tokens per workgroup of the row scatter and of the combine: about
+// `bytes` of token rows, at most kScatterThreads copies. Measured on the
+// Mixtral-, DeepSeek-V3- and Qwen-MoE-like layers: 32 KB for the scatter
+// (permute stage 5.64 -> 5.72 TB/s, 4.95 -> 5.27, 3.76 -> 3.86), and for
+// the combine 64 KB at K <= 2 (32 KB: 5.44 -> 5.35 TB/s) but 32 KB at
+// larger K (5.45 -> 5.56, 4.88 -> 5.07)
+int scatter_tokens_per_block(int K, long row_bytes, long bytes = 32768) {
+  long tpb = bytes / (row_bytes > 0 ? row_bytes : 1);
   if (tpb < 1) tpb = 1;
   if (tpb > kScatterThreads / K) tpb = kScatterThreads / K;
   return (int)tpb;
@@ -600,10 +561,11 @@ hipError_t launch_hist_rank_scan(const int32_t* idx, int TK, int E,
                                  int32_t* block_hist, int32_t* rank,
                                  int32_t* counts, int32_t* offsets,
                                  int32_t* const* tile_off, hipStream_t s,
-                                 bool scan) {
+                                 bool scan, bool hist) {
   const int nblk = (TK + kPermChunk - 1) / kPermChunk;
-  hipLaunchKernelGGL(hist_rank_kernel, dim3(nblk), dim3(kRankWaves * kWave), 0,
-                     s, idx, TK, E, perm_nbits(E), block_hist, rank);
+  if (hist)
+    hipLaunchKernelGGL(hist_rank_kernel, dim3(nblk), dim3(kRankWaves * kWave), 0,
+                       s, idx, TK, E, perm_nbits(E), block_hist, rank);
   if (!scan) return hipGetLastError();
   TileOffPtrs tp;
   for (int i = 0; i < kNumTileBM; ++i) tp.p[i] = tile_off[i];
@@ -661,7 +623,8 @@ template <typename T>
 hipError_t launch_combine_t(const T* y, const int32_t* dest, const float* w,
                             const T* add, T* out, int Ttok, int K, int d,
                             hipStream_t s) {
-  const int tpb = scatter_tokens_per_block(K, (long)d * sizeof(T));
+  const int tpb = scatter_tokens_per_block(K, (long)d * sizeof(T),
+                                           K <= 2 ? 65536 : 32768);
   const dim3 grid((unsigned)((Ttok + tpb - 1) / tpb)), block(kScatterThreads);
   if (K == 2)
     hipLaunchKernelGGL((combine_k_kernel<T, 8, 2>), grid, block, 0, s, y, dest, w,

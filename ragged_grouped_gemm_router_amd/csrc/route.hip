@@ -9,6 +9,7 @@
 // order; the owning lane retires each winner. Lanes 0..K-1 then hold the
 // K winners and form the renormalised weights with two wave reductions.
 #include "launch.h"
+#include "rank.h"
 
 namespace moe {
 namespace {
@@ -98,7 +99,129 @@ __global__ __launch_bounds__(256) void topk_kernel(
   }
 }
 
+// Top-K with the permute's chunk ranking fused in, for E <= 32 with E a
+// multiple of 4, and K a divisor of kPermChunk: workgroup b takes the
+// kPermChunk / K tokens whose copies form permute chunk b, one thread per
+// token. A thread loads its token's row of logits in 16-byte pieces (EP/4
+// loads issued together; EP >= E, a multiple of 4), selects its K experts
+// by K passes over the E candidates (largest orderable key, lowest id
+// among equal keys: the same order as the wave kernel), then forms the
+// renormalised weights from the raw logits of the winners. The workgroup
+// then ranks the chunk's copies by expert (rank_chunk), so the permute
+// needs no histogram pass of its own.
+template <int NW, int EP>
+__global__ __launch_bounds__(NW * kWave) void topk_rank_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T,
+    int E, int K, int gate, int nbits, int32_t* __restrict__ idx,
+    float* __restrict__ wout, int32_t* __restrict__ block_hist,
+    int32_t* __restrict__ rank) {
+  constexpr int CT = NW * kWave;  // tokens of the chunk (= kPermChunk / K)
+  constexpr int KC = kPermChunk / CT;  // = K
+  constexpr int NQ = EP / 4;
+  __shared__ int32_t sidx[kPermChunk];
+  __shared__ int32_t cnt[NW][32];
+  const int tl = threadIdx.x;
+  const long t = (long)blockIdx.x * CT + tl;
+  if (t < T) {
+    const float* L = logits + t * E;
+    f32x4 v[NQ], bv[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {  // clamped addresses: no branch between
+      const int c = min(4 * q, E - 4);
+      v[q] = *(const f32x4*)(L + c);
+      bv[q] = bias ? *(const f32x4*)(bias + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    uint32_t key[EP];
+#pragma unroll
+    for (int e = 0; e < EP; ++e) {
+      const float x = v[e / 4][e % 4];
+      // the key is fp32(logit + bias) with a bias, the logit without one
+      key[e] = e < E ? orderable(bias ? x + bv[e / 4][e % 4] : x) : 0u;
+    }
+    int sel[KC];  // K winners, in (key desc, id asc) order
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      // every real key is above 0 (-inf maps to 0x007fffff), so 0 marks
+      // padding and retired candidates; the first largest key wins
+      uint32_t bk = 0;
+      int be = 0;
+#pragma unroll
+      for (int e = 0; e < EP; ++e) {
+        const bool better = key[e] > bk;
+        bk = better ? key[e] : bk;
+        be = better ? e : be;
+      }
+      sel[k] = be;
+#pragma unroll
+      for (int e = 0; e < EP; ++e) key[e] = e == be ? 0u : key[e];
+    }
+    float l[KC], z[KC];
+    float mx = -INFINITY, sum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      float x = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EP; ++e) x = e == sel[k] ? v[e / 4][e % 4] : x;
+      l[k] = x;
+      mx = fmaxf(mx, x);
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      z[k] = gate == MOE_GATE_SOFTMAX ? expf(l[k] - mx) : 1.0f / (1.0f + expf(-l[k]));
+      sum += z[k];
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      idx[t * KC + k] = sel[k];
+      wout[t * KC + k] = sum > 0.0f ? z[k] / sum : 1.0f / (float)KC;
+      sidx[tl * KC + k] = sel[k];
+    }
+  }
+  __syncthreads();
+  const long j0 = (long)blockIdx.x * kPermChunk;
+  const int n = (int)min((long)kPermChunk, (long)T * K - j0);
+  rank_chunk<NW, 32>([&](int i) { return sidx[i]; }, n, E, nbits, j0, cnt,
+                     block_hist + (long)blockIdx.x * E, rank);
+}
+
+template <int NW>
+hipError_t launch_topk_rank_nw(const float* logits, const float* bias, int T,
+                               int E, int K, int gate, int nbits, int32_t* idx,
+                               float* w, int32_t* block_hist, int32_t* rank,
+                               hipStream_t s) {
+  const dim3 grid((unsigned)((T + NW * kWave - 1) / (NW * kWave))), block(NW * kWave);
+  if (E <= 8)
+    hipLaunchKernelGGL((topk_rank_kernel<NW, 8>), grid, block, 0, s, logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank);
+  else if (E <= 16)
+    hipLaunchKernelGGL((topk_rank_kernel<NW, 16>), grid, block, 0, s, logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank);
+  else
+    hipLaunchKernelGGL((topk_rank_kernel<NW, 32>), grid, block, 0, s, logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// (up to 32 experts: with more, one thread's serial selection costs more
+// than the histogram pass it saves; measured on the 60-expert layer)
+bool topk_rank_supported(int E, int K) {
+  return E >= 4 && E <= 32 && E % 4 == 0 && K >= 1 && kPermChunk % K == 0 &&
+         kPermChunk / K >= kWave;
+}
+
+hipError_t launch_topk_rank(const float* logits, const float* bias, int T,
+                            int E, int K, int gate, int32_t* idx, float* w,
+                            int32_t* block_hist, int32_t* rank, hipStream_t s) {
+  if (!topk_rank_supported(E, K)) return hipErrorNotSupported;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  switch (kPermChunk / K / kWave) {  // waves per workgroup: 16 / K
+    case 16: return launch_topk_rank_nw<16>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, s);
+    case 8: return launch_topk_rank_nw<8>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, s);
+    case 4: return launch_topk_rank_nw<4>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, s);
+    case 2: return launch_topk_rank_nw<2>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, s);
+    default: return launch_topk_rank_nw<1>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, s);
+  }
+}
 
 hipError_t launch_topk(const float* logits, const float* bias, int T, int E,
                        int K, int gate, int32_t* idx, float* w,
