@@ -172,11 +172,13 @@ __device__ __forceinline__ bool lookup_tile(const GemmParams& p, Tile& t) {
 // scattered ones. The row pitch is padded by 8 floats so that the two
 // half-waves' stores (rows 4 apart) use disjoint banks. The caller has
 // finished reading LDS for operands; the LDS is free on return.
-template <int BM, int BN, int WM, int WN, int MB, int NB, int NT, int ROWS>
+template <int BM, int BN, int WM, int WN, int MB, int NB, int NT, int ROWS,
+          int PW = 8>
 struct StageOut {
   static constexpr int PITCH = BN + 8;
   static constexpr int BYTES = ROWS * PITCH * 4;
   static_assert(BM % ROWS == 0, "pass rows");
+  static_assert(PW % 8 == 0 && BN % PW == 0, "piece width");
 
   // rows: the tile's rows that are stored (a workgroup-uniform count);
   // passes wholly past them are skipped, since every store there would
@@ -207,13 +209,19 @@ struct StageOut {
         }
       }
       __syncthreads();
-      const int CH = min(ROWS, rows - r0) * (BN / 8);
+      const int CH = min(ROWS, rows - r0) * (BN / PW);
 #pragma unroll 2
       for (int c = tid; c < CH; c += NT) {
-        const int row = c / (BN / 8), col = (c % (BN / 8)) * 8;
-        const f32x4 lo = *(const f32x4*)(st + row * PITCH + col);
-        const f32x4 hi = *(const f32x4*)(st + row * PITCH + col + 4);
-        float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int row = c / (BN / PW), col = (c % (BN / PW)) * PW;
+        float v[PW];
+#pragma unroll
+        for (int q = 0; q < PW; q += 4) {
+          const f32x4 x = *(const f32x4*)(st + row * PITCH + col + q);
+          v[q] = x[0];
+          v[q + 1] = x[1];
+          v[q + 2] = x[2];
+          v[q + 3] = x[3];
+        }
         store(r0 + row, col, v);
       }
     }
@@ -387,41 +395,6 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm(GemmParams p) {
 // products land only in outputs the epilogue discards. K must be a
 // multiple of BK.
 // ---------------------------------------------------------------------------
-
-// MXFP8 epilogue of the up-projection: h = silu(a) * b quantised along N in
-// blocks of 32. In the 32x32 accumulator layout the 32 columns of one block
-// row sit in the 32 lanes of a half-wave (same register), so the block's
-// amax is a 5-step butterfly within the half.
-template <int WM, int WN, int MB, int NB>
-__device__ __forceinline__ void epilogue_swiglu_mx(const GemmParams& p,
-                                                   const Tile& t,
-                                                   f32x16 (&acc)[2][MB][NB],
-                                                   int wm, int wn, int lane) {
-  uint8_t* hq = (uint8_t*)p.C;
-  uint8_t* hs = (uint8_t*)p.C2;
-  const int ldq = p.ldc, lds_h = p.ldc / 32;
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int col = t.n0 + wn * WN + j * 32 + lane % 32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = t.m0 + wm * WM + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-        const float a = acc[0][i][j][r], b = acc[1][i][j][r];
-        const float h = a * fast_sigmoid(a) * b;
-        float m = fabsf(h);
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-        const int X = mx_block_exponent(m);
-        if (row < t.m_end && col < p.N) {
-          hq[(long)row * ldq + col] = (uint8_t)e4m3_encode(h * mx_inv_scale(X));
-          if (lane % 32 == 0) hs[(long)row * lds_h + col / 32] = (uint8_t)(X + 127);
-        }
-      }
-    }
-  }
-}
 
 // Fragment read order of a k-substep: the order in which its MFMAs, q =
 // (o * MB + i) * NB + j taking A block i and B block (o, j), first use
@@ -606,7 +579,6 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
       for (int q = 0; q < NSC; ++q) dst[q] = *(const uint32_t*)(sc_row[q] + kt * 4);
     }
   };
-
   f32x16 acc[NB_OPS][MB][NB];
 #pragma unroll
   for (int o = 0; o < NB_OPS; ++o)
@@ -705,63 +677,26 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
-  // DMA batches. Batch b = {A of k-tile b+S-1, B of k-tile b+S_B-1} fills
-  // the stages that the tile barrier ending k-tile b-1 frees: its first D1
-  // instructions are issued right after that barrier (in the last substep
-  // of tile b-1), the other N_LOAD - D1 spread over substeps 0 .. NSP-1 of
-  // tile b, so that the eight waves' DMA issue does not all fall into one
-  // substep. Every batch is issued whole between two consecutive tile
-  // barriers, in the same order, so the barriers' wait counts do not
-  // depend on the split. (MXFP8 products issue whole batches after the
-  // barrier: their scale loads share the wait count.)
-#ifndef MOE_DMA_AFTER_BAR
-#define MOE_DMA_AFTER_BAR 8  // eighths of a batch issued after the barrier
-#endif
-#ifndef MOE_DMA_SPREAD
-#define MOE_DMA_SPREAD 1     // substeps of the next tile taking the rest
-#endif
-  constexpr int D1 = MX ? N_LOAD : N_LOAD * MOE_DMA_AFTER_BAR / 8;
-  constexpr int NSP = D1 == N_LOAD ? 0 : (MOE_DMA_SPREAD < KS - 1 ? MOE_DMA_SPREAD : KS - 1);
-  static_assert(D1 == N_LOAD || NSP >= 1, "a split batch needs a substep for its rest");
-
   // Prologue: (scales of k-tile 0,) k-tiles 0 .. S-1 in flight, and the
   // B operands of k-tiles S .. S_B-1 (past the last tile, the last one
   // again, into stages nobody reads); wait for tile 0. With a deeper B
   // ring, MXFP8 scales run two tiles ahead: those of tile kt+1 are issued
   // before the B DMA of tile kt+2 (here: of tile 2), so that one is still
-  // the newest outstanding load at the tile barrier. With split batches
-  // the prologue issues k-tiles 0 .. S-2, the B of tiles S-1 .. S_B-2 and
-  // the first part of batch 0; batch 0's rest follows in tile 0.
+  // the newest outstanding load at the tile barrier.
   constexpr int NSC_RING = RING_B && MX ? NSC : 0;
   if (nk > 0) {  // (an empty group's tile writes zeros)
-  if constexpr (D1 == N_LOAD) {
-    load_scales(RING_B ? s_cur : s_nxt, 0);
+  load_scales(RING_B ? s_cur : s_nxt, 0);
 #pragma unroll
-    for (int i = 0; i < S; ++i)
+  for (int i = 0; i < S; ++i)
 #pragma unroll
-      for (int d = 0; d < N_LOAD; ++d)
-        issue_one(min(i, nk - 1), i, min(i, nk - 1), i, d);
-    if constexpr (RING_B) load_scales(s_nxt, min(1, nk - 1));
+    for (int d = 0; d < N_LOAD; ++d)
+      issue_one(min(i, nk - 1), i, min(i, nk - 1), i, d);
+  if constexpr (RING_B) load_scales(s_nxt, min(1, nk - 1));
 #pragma unroll
-    for (int i = S; i < S_B; ++i)
+  for (int i = S; i < S_B; ++i)
 #pragma unroll
-      for (int d = A_INS; d < N_LOAD; ++d) issue_one(0, 0, min(i, nk - 1), i, d);
-    barrier_after(std::integral_constant<int, (S - 1) * N_LOAD + NSC_RING + (S_B - S) * NBL>{});
-  } else {
-#pragma unroll
-    for (int i = 0; i + 1 < S; ++i)
-#pragma unroll
-      for (int d = 0; d < N_LOAD; ++d)
-        issue_one(min(i, nk - 1), i, min(i, nk - 1), i, d);
-#pragma unroll
-    for (int i = S - 1; i + 1 < S_B; ++i)
-#pragma unroll
-      for (int d = A_INS; d < N_LOAD; ++d) issue_one(0, 0, min(i, nk - 1), i, d);
-#pragma unroll
-    for (int d = 0; d < D1; ++d)
-      issue_one(min(S - 1, nk - 1), S - 1, min(S_B - 1, nk - 1), S_B - 1, d);
-    barrier_after(std::integral_constant<int, (S - 2) * N_LOAD + (S_B - S) * NBL + D1>{});
-  }
+    for (int d = A_INS; d < N_LOAD; ++d) issue_one(0, 0, min(i, nk - 1), i, d);
+  barrier_after(std::integral_constant<int, (S - 1) * N_LOAD + NSC_RING + (S_B - S) * NBL>{});
   if constexpr (MX && !RING_B) {
 #pragma unroll
     for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
@@ -772,22 +707,22 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 
   // One region per k-substep. The MFMAs run on fragments read a region
   // earlier; the memory instructions of the region (the next substep's
-  // fragment reads and the DMA instructions assigned to it) sit between
-  // them, at most a few per MFMA, so the in-order issue of a long memory
-  // burst never leaves the matrix pipe idle. The tile barrier waits until
-  // only the S-2 newest tiles' DMA (and, with a deeper B ring, the B DMA
-  // of the S_B-S newest B tiles) is outstanding, i.e. for tile kt+1. The
-  // first H MFMAs precede every new read: their wait for the current
-  // fragments then covers no read issued here. Every step is fenced with
-  // sched_barrier to keep this order. (MXFP8: the next tile's scales are
-  // fetched in the first region and swapped in after the tile barrier,
-  // once their wait is free.)
+  // fragment reads and, at the last substep of a k-tile, the DMA of k-tile
+  // kt+S into the stage tile kt used) sit between them, at most a few per
+  // MFMA, so the in-order issue of a long memory burst never leaves the
+  // matrix pipe idle. The tile barrier waits until only the S-2 newest
+  // tiles' DMA (and, with a deeper B ring, the B DMA of the S_B-S newest
+  // B tiles) is outstanding, i.e. for tile kt+1. The first H MFMAs
+  // precede every new read: their wait for the current fragments then
+  // covers no read issued here. Every step is fenced with sched_barrier to
+  // keep this order. (MXFP8: the next tile's scales are fetched in the
+  // first region and swapped in after the tile barrier, once their wait is
+  // free.)
   constexpr int H = N_MFMA >= 8 ? 2 : N_MFMA >= 2 ? 1 : 0;
 #define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
-  // stage of k-tile kt (kt mod S), of k-tile kt + 1 and of k-tile kt - 1,
-  // kept as counters
-  int st = 0, st_next = S > 1 ? 1 : 0, st_prev = S - 1;
-  int sbt = 0, sbt_next = 1, sbt_prev = S_B - 1;  // the same for the B ring
+  // stage of k-tile kt (kt mod S) and of k-tile kt + 1, kept as counters
+  int st = 0, st_next = S > 1 ? 1 : 0;
+  int sbt = 0, sbt_next = 1;  // the same for the B ring
   for (int kt = 0; kt < nk; ++kt) {
     const char* sa = lds + st * A_STRIDE;
     const char* sa_next = lds + st_next * A_STRIDE;
@@ -798,13 +733,9 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
       Frags& cur = (ks & 1) ? fb : fa;
       Frags& nxt = (ks & 1) ? fa : fb;
       const bool last = ks + 1 == KS;
-      // memory ops of this region: N_READ reads, plus D1 DMAs of batch
-      // kt+1 after the barrier (last substep) or DMAs [d_lo, d_hi) of
-      // batch kt (substeps below NSP)
+      // memory ops of this region: N_READ reads (+ N_LOAD DMAs if last)
       constexpr int NM_MAX = N_READ + N_LOAD;
-      const int d_lo = ks < NSP ? D1 + (N_LOAD - D1) * ks / (NSP > 0 ? NSP : 1) : 0;
-      const int d_hi = ks < NSP ? D1 + (N_LOAD - D1) * (ks + 1) / (NSP > 0 ? NSP : 1) : 0;
-      const int nm = N_READ + (last ? D1 : 0) + (d_hi - d_lo);
+      const int nm = last ? NM_MAX : N_READ;
       substep_scales(ks);
       MOE_FENCE();
 #pragma unroll
@@ -834,20 +765,17 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 #pragma unroll
         for (int mm = 0; mm < NM_MAX; ++mm) {
           if (mm < m || mm >= m_end) continue;
-          // reads spread evenly among the DMAs: op mm is a read iff the
-          // running read quota floor(x * N_READ / nm) steps at it
-          const int rb = mm * N_READ / nm;
-          if ((mm + 1) * N_READ / nm != rb) {
-            if (last)
+          if (!last) {
+            read_one(sa, sbb, ks + 1, nxt, mm);
+          } else {
+            // reads spread evenly among the DMAs: op mm is a read iff the
+            // running read quota floor(x * N_READ / NM_MAX) steps at it
+            const int rb = mm * N_READ / NM_MAX;
+            if ((mm + 1) * N_READ / NM_MAX != rb)
               read_one(sa_next, sbb_next, 0, nxt, rb);
             else
-              read_one(sa, sbb, ks + 1, nxt, rb);
-          } else if (last) {
-            issue_one(min(kt + S, nk - 1), st, min(kt + S_B, nk - 1), sbt,
-                      mm - rb);
-          } else {
-            issue_one(min(kt + S - 1, nk - 1), st_prev,
-                      min(kt + S_B - 1, nk - 1), sbt_prev, d_lo + mm - rb);
+              issue_one(min(kt + S, nk - 1), st, min(kt + S_B, nk - 1), sbt,
+                        mm - rb);
           }
           MOE_FENCE();
         }
@@ -856,10 +784,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
         MOE_FENCE();
       }
     }
-    st_prev = st;
     st = st_next;
     st_next = st_next + 1 == S ? 0 : st_next + 1;
-    sbt_prev = sbt;
     sbt = sbt_next;
     sbt_next = sbt_next + 1 == S_B ? 0 : sbt_next + 1;
   }
@@ -870,7 +796,40 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // accumulators, or the plain product), then any saved pre-activations
   using SO = StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>;
   if constexpr (EPI == kEpiSwigluMx) {
-    epilogue_swiglu_mx<WM, WN, MB, NB>(p, t, acc, wm, wn, lane);
+    // h through LDS in rows of the tile; each thread then quantises one
+    // whole 32-column block of a row: its amax in registers, 32 codes in
+    // two 16-byte stores and one scale byte (the accumulator layout spreads
+    // a block over a half-wave: a 5-step butterfly per element and one
+    // byte store per lane)
+    using SO32 = StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows, 32>;
+    uint8_t* hq = (uint8_t*)p.C;
+    uint8_t* hs = (uint8_t*)p.C2;
+    SO32::run(lds, wm, wn, lane,
+              [&](int i, int j, int r) {
+                const float a = acc[0][i][j][r], b = acc[NB_OPS - 1][i][j][r];
+                return a * fast_sigmoid(a) * b;
+              },
+              [&](int row, int col, const float* v) {
+                const int grow = t.m0 + row, gcol = t.n0 + col;
+                if (grow >= t.m_end || gcol >= p.N) return;
+                float m = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 32; ++q) m = fmaxf(m, fabsf(v[q]));
+                const int X = mx_block_exponent(m);
+                const float inv = mx_inv_scale(X);
+                uint32_t w[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                  w[q] = e4m3_encode(v[4 * q] * inv) |
+                         (e4m3_encode(v[4 * q + 1] * inv) << 8) |
+                         (e4m3_encode(v[4 * q + 2] * inv) << 16) |
+                         (e4m3_encode(v[4 * q + 3] * inv) << 24);
+                u32x4* dst = (u32x4*)(hq + (long)grow * p.ldc + gcol);
+                dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+                dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+                hs[(long)grow * (p.ldc / 32) + gcol / 32] = (uint8_t)(X + 127);
+              },
+              t.m_end - t.m0);
     auto put_bf16 = [&](void* dst) {
       return [=](int row, int col, const float* v) {
         const int grow = t.m0 + row, gcol = t.n0 + col;
