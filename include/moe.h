@@ -101,12 +101,26 @@ typedef struct moe_desc {
   int32_t flags;        /* MOE_FLAG_*                                      */
 } moe_desc;
 
+/* MX scale layout. Every MXFP8 operand here is E4M3 codes [rows, cols]
+ * (cols a multiple of 128) with one E8M0 code per 32 consecutive elements
+ * of a row, rows * cols / 32 bytes grouped by 128-column span: the code of
+ * block b (columns 32 b .. 32 b + 31) of row r is at byte
+ *     ((b / 4) * rows + r) * 4 + b % 4,
+ * i.e. [cols / 128][rows][4]. One span's four codes of a row form one
+ * aligned 4-byte word, and the words of consecutive rows are adjacent, so
+ * the scales that a 128-wide k-tile of a GEMM needs for 32 consecutive
+ * rows are one 128-byte line (a row-major [rows][cols / 32] array would
+ * spread them over 32 lines). A batch of operands ([B, rows, cols]) is laid
+ * out as the one operand of B * rows rows that stacks them. The block rule
+ * itself is moe_quantize_mxfp8's. */
+
 /* One set of SwiGLU expert weights [P3 §9]: y = W2 (silu(W1 x) * (W3 x)).
  * For the routed experts the leading dimension is E; for the shared
  * expert it is absent. With gemm_dtype == MOE_MXFP8 the w* pointers hold
  * E4M3 bytes (quantised by moe_quantize_mxfp8) and *_scales hold the
- * E8M0 codes, one per 32 elements along the row: w1/w3 scales are
- * [E, d_ff, d_model/32], w2 scales [E, d_model, d_ff/32]. */
+ * E8M0 codes, one per 32 elements along the row, in the MX scale layout
+ * of the stacked matrices: w1/w3 scales of E*d_ff rows and d_model
+ * columns, w2 scales of E*d_model rows and d_ff columns. */
 typedef struct moe_expert_weights {
   const void* w1;
   const void* w3;
@@ -143,10 +157,12 @@ typedef struct moe_fwd_args {
                                  T * d_model * 2 < 2^31, else
                                  MOE_EUNSUPPORTED. moe_backward still needs
                                  a materialised x_perm.                     */
-  uint8_t* x_perm_scales;     /* MXFP8 with x_perm: [T*K, d_model/32] E8M0   */
+  uint8_t* x_perm_scales;     /* MXFP8 with x_perm: E8M0, MX scale layout of
+                                 T*K rows, d_model columns                  */
   void* h;                    /* [T*K, d_ff] act. MXFP8: E4M3 codes [T*K,
-                                 d_ff] then E8M0 scales [T*K, d_ff/32]
-                                 (fits in a bf16-sized buffer)              */
+                                 d_ff] then their E8M0 scales (MX scale
+                                 layout, T*K * d_ff / 32 bytes; fits in a
+                                 bf16-sized buffer)                         */
   void* y_perm;               /* [T*K, d_model] act, unweighted expert out   */
   void* y_shared;             /* [T, d_model] act; required iff shared       */
   void* act_a;                /* [T*K, d_ff] act; required iff SAVE_ACTS     */
@@ -188,13 +204,13 @@ typedef struct moe_bwd_args {
      the weights quantised for the transposed products (moe_quantize_mxfp8_t):
      x_perm and h then hold the forward's E4M3 codes (h: codes then scales),
      routed the forward's MX weights (for the recomputed a, b). */
-  const uint8_t* x_perm_scales; /* [T*K, d_model/32] E8M0                    */
+  const uint8_t* x_perm_scales; /* E8M0, MX scale layout (as the forward's)  */
   const uint8_t* w2t;         /* [E, d_ff, d_model] E4M3: W2^T, blocks along
                                  d_model                                    */
-  const uint8_t* w2t_scales;  /* [E, d_ff, d_model/32]                       */
+  const uint8_t* w2t_scales;  /* E*d_ff rows, d_model columns (stacked)     */
   const uint8_t* w13t;        /* [E, d_model, 2*d_ff] E4M3: [W1^T | W3^T],
                                  blocks along d_ff                          */
-  const uint8_t* w13t_scales; /* [E, d_model, 2*d_ff/32]                     */
+  const uint8_t* w13t_scales; /* E*d_model rows, 2*d_ff columns (stacked)   */
   /* the same for the shared expert (MXFP8 with d_ff_shared > 0): shared
      holds its forward MX weights; ws2t [d_ff_shared, d_model],
      ws13t [d_model, 2*d_ff_shared], as w2t and w13t with E = 1 */
@@ -426,12 +442,12 @@ moe_status moe_balance_monitor(const moe_desc* desc, const float* load_hist,
  * data-gradient products [P3 §13.6: gradient times transposed weight]:
  * for each of `batch` bf16 [rows, cols] matrices src_b (contiguous),
  *   q_b[c, col_off + r] = E4M3 code of src_b[r, c] in 32-blocks along r,
- *   scales_b[c, (col_off + r) / 32] = the block's E8M0 code,
- * with q_b of row stride ldq (batch stride cols * ldq) and scales_b of
- * row stride ldq / 32 (batch stride cols * ldq / 32); same rule as
- * moe_quantize_mxfp8. W2 [E, d, f] -> w2t: (E, d, f, ldq = d, col_off 0);
- * W1, W3 [E, f, d] -> w13t: (E, f, d, ldq = 2 f, col_off 0 and f).
- * rows % 32 == 0, cols % 64 == 0, ldq % 32 == 0, col_off % 32 == 0 and
+ * with q_b of row stride ldq (batch stride cols * ldq), and the blocks'
+ * E8M0 codes in `scales`, the MX scale layout of the stacked
+ * [batch * cols, ldq] operand; same rule as moe_quantize_mxfp8.
+ * W2 [E, d, f] -> w2t: (E, d, f, ldq = d, col_off 0); W1, W3 [E, f, d] ->
+ * w13t: (E, f, d, ldq = 2 f, col_off 0 and f). rows % 32 == 0,
+ * cols % 64 == 0, ldq % 128 == 0, col_off % 128 == 0 and
  * col_off + rows <= ldq, else MOE_EUNSUPPORTED / MOE_EINVAL. */
 moe_status moe_quantize_mxfp8_t(const void* src_bf16, int64_t batch,
                                 int64_t rows, int64_t cols, uint8_t* q,
@@ -439,15 +455,15 @@ moe_status moe_quantize_mxfp8_t(const void* src_bf16, int64_t batch,
                                 void* stream);
 
 /* MX quantisation of a bf16 [rows, cols] matrix along its rows (cols a
- * multiple of 32) [P2 section on the TE mechanisms: MXFP8 grouped GEMM
+ * multiple of 128) [P2 section on the TE mechanisms: MXFP8 grouped GEMM
  * operands; P3 §13.6: fp8 with per-tile rather than per-tensor scales].
  * The pages fix no bit-level rule; this is the OCP MX v1.0 one: X = floor(log2(amax)) - 8
  * per 32-element block (clamped to [-127, 127]); scale code X + 127;
  * element = E4M3 round-to-nearest-even of v / 2^X, saturated to +-448.
- * Writes q [rows, cols] E4M3 bytes and scales [rows, cols/32] (device
- * pointers owned by the caller). NULL pointers, rows < 0 or cols <= 0 ->
- * MOE_EINVAL; cols % 32 != 0 -> MOE_EUNSUPPORTED; rows == 0 -> MOE_OK
- * with nothing enqueued. */
+ * Writes q [rows, cols] E4M3 bytes and the rows * cols / 32 scale codes
+ * in the MX scale layout (device pointers owned by the caller). NULL
+ * pointers, rows < 0 or cols <= 0 -> MOE_EINVAL; cols % 128 != 0 ->
+ * MOE_EUNSUPPORTED; rows == 0 -> MOE_OK with nothing enqueued. */
 moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows,
                               int64_t cols, uint8_t* q, uint8_t* scales,
                               void* stream);

@@ -354,7 +354,7 @@ hipError_t do_gemm2(const moe_desc* d, const void* h, const int32_t* off,
 }
 
 // MXFP8 expert GEMMs. h lives in the caller's h buffer as E4M3 codes
-// [T*K, d_ff] followed by E8M0 scales [T*K, d_ff/32].
+// [T*K, d_ff] followed by their E8M0 scales (span-grouped, T*K rows).
 // With a shared expert, x is quantised into the workspace and the shared
 // GEMMs run as one dense group, h_shared holding codes then scales.
 // gsrc != NULL: x_perm was not written; GEMM 1 gathers the rows of the
@@ -376,7 +376,7 @@ hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
   p.gsrc = gsrc; p.gdiv = d->K;
   p.B = rw->w1; p.B2 = rw->w3; p.ldb = dm; p.sB = (long)f * dm;
   p.Bs = rw->w1_scales; p.B2s = rw->w3_scales;
-  p.ld_s = dm / 32; p.sBs = (long)f * (dm / 32);
+  p.s_rows = gsrc ? d->T : TK;
   p.C = hq; p.C2 = hs; p.ldc = f;
   p.Sa = act_a; p.Sb = act_b;
   hipError_t e = gemm_mfma(kOpGemm1Mx, p, ws.tile_off, s);
@@ -386,7 +386,7 @@ hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
   p.M = TK; p.N = dm; p.K = f; p.G = d->E; p.off = offsets;
   p.A = hq; p.lda = f; p.As = hs;
   p.B = rw->w2; p.ldb = f; p.sB = (long)dm * f;
-  p.Bs = rw->w2_scales; p.ld_s = f / 32; p.sBs = (long)dm * (f / 32);
+  p.Bs = rw->w2_scales; p.s_rows = TK;
   p.C = y_perm; p.ldc = dm;
   p.slots = d->flags & MOE_FLAG_NO_TAIL_SPLIT ? 0 : -1;
   e = gemm_mfma(kOpGemm2Mx, p, ws.tile_off, s);
@@ -402,7 +402,7 @@ hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
   p.M = T; p.N = fs; p.K = dm;
   p.A = ws.xq; p.lda = dm; p.As = ws.xs;
   p.B = sw->w1; p.B2 = sw->w3; p.ldb = dm;
-  p.Bs = sw->w1_scales; p.B2s = sw->w3_scales; p.ld_s = dm / 32;
+  p.Bs = sw->w1_scales; p.B2s = sw->w3_scales; p.s_rows = T;
   p.C = sq; p.C2 = ss; p.ldc = fs;
   e = gemm_mfma(kOpGemm1Mx, p, ws.tile_off, s);
   if (e != hipSuccess) return e;
@@ -410,7 +410,7 @@ hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
   p.M = T; p.N = dm; p.K = fs;
   p.A = sq; p.lda = fs; p.As = ss;
   p.B = sw->w2; p.ldb = fs;
-  p.Bs = sw->w2_scales; p.ld_s = fs / 32;
+  p.Bs = sw->w2_scales; p.s_rows = T;
   p.C = y_shared; p.ldc = dm;
   return gemm_mfma(kOpGemm2Mx, p, ws.tile_off, s);
 }
@@ -485,7 +485,7 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.A = a->x_perm; p.lda = dm; p.As = a->x_perm_scales;
     p.B = a->routed.w1; p.B2 = a->routed.w3; p.ldb = dm; p.sB = (long)f * dm;
     p.Bs = a->routed.w1_scales; p.B2s = a->routed.w3_scales;
-    p.ld_s = dm / 32; p.sBs = (long)f * (dm / 32);
+    p.s_rows = TK;
     p.C = nullptr; p.C2 = w.da; p.C3 = w.db; p.ldc = f;
     MOE_TRY(gemm_mfma(kOpGemm1MxAct, p, w.tile_off, s));
   }
@@ -495,7 +495,7 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.M = T; p.N = fs; p.K = dm;
     p.A = w.sxq; p.lda = dm; p.As = w.sxs;
     p.B = a->shared.w1; p.B2 = a->shared.w3; p.ldb = dm;
-    p.Bs = a->shared.w1_scales; p.B2s = a->shared.w3_scales; p.ld_s = dm / 32;
+    p.Bs = a->shared.w1_scales; p.B2s = a->shared.w3_scales; p.s_rows = T;
     p.C = w.shq; p.C2 = w.shs; p.ldc = fs;
     p.Sa = w.sa; p.Sb = w.sb;
     MOE_TRY(gemm_mfma(kOpGemm1Mx, p, w.tile_off, s));
@@ -506,28 +506,29 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.M = TK; p.N = f; p.K = dm; p.G = E; p.off = a->offsets;
     p.A = w.dyq; p.lda = dm; p.As = w.dys;
     p.B = a->w2t; p.ldb = dm; p.sB = (long)f * dm;
-    p.Bs = a->w2t_scales; p.ld_s = dm / 32; p.sBs = (long)f * (dm / 32);
+    p.Bs = a->w2t_scales; p.s_rows = TK;
     p.C = w.da; p.C2 = w.db; p.ldc = f;
     p.aux_a = sa; p.aux_b = sb;
     MOE_TRY(gemm_mfma(kOpDgrad2Mx, p, w.tile_off, s));
     // [da | db] quantised along d_ff, side by side
+    // (db's scales start at column f: f / 128 spans of TK rows)
     MOE_TRY(launch_quantize_mxfp8_strided(w.da, TK, f, w.dgq, 2L * f, w.dgs,
-                                          2L * f / 32, s));
+                                          s));
     MOE_TRY(launch_quantize_mxfp8_strided(w.db, TK, f, w.dgq + f, 2L * f,
-                                          w.dgs + f / 32, 2L * f / 32, s));
+                                          w.dgs + (long)TK * f / 32, s));
   }
   if (shared) {  // dh_s = Q(dy) Ws2t, (da_s, db_s) in place, quantised
     GemmParams p = gp();
     p.M = T; p.N = fs; p.K = dm;
     p.A = w.sdyq; p.lda = dm; p.As = w.sdys;
-    p.B = a->ws2t; p.ldb = dm; p.Bs = a->ws2t_scales; p.ld_s = dm / 32;
+    p.B = a->ws2t; p.ldb = dm; p.Bs = a->ws2t_scales; p.s_rows = T;
     p.C = w.sa; p.C2 = w.sb; p.ldc = fs;
     p.aux_a = w.sa; p.aux_b = w.sb;
     MOE_TRY(gemm_mfma(kOpDgrad2Mx, p, w.tile_off, s));
     MOE_TRY(launch_quantize_mxfp8_strided(w.sa, T, fs, w.sdgq, 2L * fs, w.sdgs,
-                                          2L * fs / 32, s));
+                                          s));
     MOE_TRY(launch_quantize_mxfp8_strided(w.sb, T, fs, w.sdgq + fs, 2L * fs,
-                                          w.sdgs + fs / 32, 2L * fs / 32, s));
+                                          w.sdgs + (long)T * fs / 32, s));
   }
   record(a->events[3], s);
   {  // dx_perm = Q([da | db]) W13t_e
@@ -535,7 +536,7 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.M = TK; p.N = dm; p.K = 2 * f; p.G = E; p.off = a->offsets;
     p.A = w.dgq; p.lda = 2 * f; p.As = w.dgs;
     p.B = a->w13t; p.ldb = 2 * f; p.sB = (long)dm * 2 * f;
-    p.Bs = a->w13t_scales; p.ld_s = 2 * f / 32; p.sBs = (long)dm * (2 * f / 32);
+    p.Bs = a->w13t_scales; p.s_rows = TK;
     p.C = w.dx_perm; p.ldc = dm;
     p.slots = d->flags & MOE_FLAG_NO_TAIL_SPLIT ? 0 : -1;
     MOE_TRY(gemm_mfma(kOpGemm2Mx, p, w.tile_off, s));
@@ -544,7 +545,7 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     GemmParams p = gp();
     p.M = T; p.N = dm; p.K = 2 * fs;
     p.A = w.sdgq; p.lda = 2 * fs; p.As = w.sdgs;
-    p.B = a->ws13t; p.ldb = 2 * fs; p.Bs = a->ws13t_scales; p.ld_s = 2 * fs / 32;
+    p.B = a->ws13t; p.ldb = 2 * fs; p.Bs = a->ws13t_scales; p.s_rows = T;
     p.C = w.sdx; p.ldc = dm;
     MOE_TRY(gemm_mfma(kOpGemm2Mx, p, w.tile_off, s));
   }
@@ -760,12 +761,12 @@ moe_status moe_quantize_mxfp8_t(const void* src, int64_t batch, int64_t rows,
     return MOE_EINVAL;
   if (batch == 0 || rows == 0 || cols == 0) return MOE_OK;
   if (!src || !q || !scales || col_off + rows > ldq) return MOE_EINVAL;
-  if (rows % 32 || cols % 64 || ldq % 32 || col_off % 32 || rows > INT_MAX ||
+  if (rows % 32 || cols % 64 || ldq % 128 || col_off % 128 || rows > INT_MAX ||
       cols > INT_MAX || batch > 65535 || rows / 32 > 65535)
     return MOE_EUNSUPPORTED;
   return hip_status(launch_quantize_mxfp8_cols(src, batch, (int)rows,
                                                (int)cols, q + col_off, ldq,
-                                               scales + col_off / 32,
+                                               scales + col_off / 128 * batch * cols * 4,
                                                (hipStream_t)stream));
 }
 
@@ -1230,7 +1231,7 @@ moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows,
                               int64_t cols, uint8_t* q, uint8_t* scales,
                               void* stream) {
   if (!src_bf16 || !q || !scales || rows < 0 || cols <= 0) return MOE_EINVAL;
-  if (cols % 32) return MOE_EUNSUPPORTED;
+  if (cols % 128) return MOE_EUNSUPPORTED;
   if (rows == 0) return MOE_OK;
   return hip_status(launch_quantize_mxfp8(src_bf16, rows, cols, q, scales,
                                           (hipStream_t)stream));

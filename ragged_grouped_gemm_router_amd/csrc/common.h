@@ -106,10 +106,13 @@ struct GemmParams {
   const void* aux_a; const void* aux_b;  // kEpiSwigluBwd: saved a, b (ld = ldc)
   int tiles_m_max;                      // upper bound of row tiles (kSchedM)
   int group_n;                          // n-tiles per rasterization group
-  // MXFP8 operands: E8M0 scales per 32 elements along k, row stride ld_s
-  // bytes (= K/32); B scales have group stride sBs bytes.
+  // MXFP8 operands: E8M0 scales per 32 elements along k in the
+  // span-grouped layout ([K/128][rows][4], mx_scale_index): A's array has
+  // s_rows rows (all of A's rows, also when they are gathered); B's stacks
+  // the groups' N-row operands (G * N rows when grouped by rows, else N);
+  // the quantising epilogue writes C's scales for M rows.
   const uint8_t* As; const uint8_t* Bs; const uint8_t* B2s;
-  long ld_s; long sBs;
+  long s_rows;
   // gathered A rows (direct-to-LDS GEMM 1 only): row i of A (and of As)
   // is row gsrc[i] / gdiv of the A given, e.g. token t of copy j = t*K+k
   const int32_t* gsrc; int gdiv;

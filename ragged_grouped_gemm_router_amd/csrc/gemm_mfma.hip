@@ -18,6 +18,7 @@
 // logical tiles, and logical tiles are ordered n-group-major, then row
 // tile, then n within the group, so the ~32 tiles an XCD runs together
 // share B panels and A rows in that XCD's L2.
+#include <climits>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -552,31 +553,46 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     }
   };
 
-  // MXFP8: the 4 E8M0 codes of a row for one k-tile are one aligned dword;
-  // they are loaded a tile ahead (s_nxt) and swapped in at the tile barrier
+  // MXFP8: in the span-grouped scale arrays a row's 4 E8M0 codes for one
+  // k-tile are one aligned word and the words of consecutive rows are
+  // contiguous, so the 32 rows of a block read one 128-byte line. Each
+  // lane reads the words of its row of every block through buffer loads:
+  // one resource per operand, the row's byte offset per block in a VGPR
+  // (rows past the tile's end clamped, as for the data; B's rows counted
+  // in the stacked groups) and the k-tile's span as the scalar offset. They are loaded
+  // a tile ahead (s_nxt) and swapped in at the tile barrier.
   constexpr int NSC = MX ? MB + NB_OPS * NB : 1;
-  const uint8_t* sc_row[NSC];
+  int sa_off[MX ? MB : 1], sb_off[MX ? NB : 1];
+  Rsrc rsa = ra, rsb[NB_OPS];
+  const int rows_b = p.off ? p.G * p.N : p.N;  // rows of B's scale array
   uint32_t s_cur[NSC], s_nxt[NSC];
   if constexpr (MX) {
+    rsa = make_rsrc(p.As);
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int row = min(t.m0 + wm * WM + i * 32 + lane % 32, t.m_end - 1);
-      const long src = gather ? p.gsrc[row] / p.gdiv : row;
-      sc_row[i] = p.As + src * p.ld_s;
+      sa_off[i] = (gather ? p.gsrc[row] / p.gdiv : row) * 4;
     }
 #pragma unroll
     for (int o = 0; o < NB_OPS; ++o)
+      rsb[o] = make_rsrc(o ? p.B2s : p.Bs);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int row = min(t.n0 + wn * WN + j * 32 + lane % 32, p.N - 1);
-        sc_row[MB + o * NB + j] =
-            (o ? p.B2s : p.Bs) + (long)t.g * p.sBs + (long)row * p.ld_s;
-      }
+    for (int j = 0; j < NB; ++j)
+      sb_off[j] = (t.g * p.N + min(t.n0 + wn * WN + j * 32 + lane % 32, p.N - 1)) * 4;
   }
   auto load_scales = [&](uint32_t* dst, int kt) {
     if constexpr (MX) {
+      const int span = kt0 + kt;
 #pragma unroll
-      for (int q = 0; q < NSC; ++q) dst[q] = *(const uint32_t*)(sc_row[q] + kt * 4);
+      for (int i = 0; i < MB; ++i)
+        dst[i] = __builtin_amdgcn_raw_buffer_load_b32(
+            rsa, sa_off[i], span * (int)p.s_rows * 4, 0);
+#pragma unroll
+      for (int o = 0; o < NB_OPS; ++o)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          dst[MB + o * NB + j] = __builtin_amdgcn_raw_buffer_load_b32(
+              rsb[o], sb_off[j], span * rows_b * 4, 0);
     }
   };
   f32x16 acc[NB_OPS][MB][NB];
@@ -827,7 +843,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
                 u32x4* dst = (u32x4*)(hq + (long)grow * p.ldc + gcol);
                 dst[0] = u32x4{w[0], w[1], w[2], w[3]};
                 dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-                hs[(long)grow * (p.ldc / 32) + gcol / 32] = (uint8_t)(X + 127);
+                hs[mx_scale_index(grow, gcol / 32, p.M)] = (uint8_t)(X + 127);
               },
               t.m_end - t.m0);
     auto put_bf16 = [&](void* dst) {
@@ -1233,10 +1249,12 @@ hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
   // per SIMD, each holding 128 x 64 (128 x 32 x 2) in accumulators, or over
   // 4 waves, one per SIMD, each holding 128 x 128 (128 x 64 x 2). Eight
   // waves hide latency better and win for bf16; the single-B MXFP8 product
-  // takes four (its 8-wave form runs out of registers and spills).
+  // takes four (its 8-wave form runs out of registers and spills), the dual
+  // one always eight (its 4-wave form spills).
   if (big) {
     const int forced = big_tile_waves();
-    if (forced == 4 || (forced == 0 && MX && !DUAL)) {
+    constexpr bool can4 = !(MX && DUAL);
+    if (can4 && (forced == 4 || (forced == 0 && MX && !DUAL))) {
       // (the single-B MXFP8 product: its partial last round split as below)
       if constexpr (MX && !DUAL) {
         if (forced == 0 && p.slots != 0 && p.off) {
@@ -1248,7 +1266,8 @@ hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
           return launch_dl<128, 128, 2, 2, 2, false, EPI, TO, MX, kSchedM, 2>(q, s);
         }
       }
-      return launch_dl<256, DUAL ? 128 : 256, 2, 2, 2, DUAL, EPI, TO, MX>(p, s);
+      if constexpr (can4)
+        return launch_dl<256, DUAL ? 128 : 256, 2, 2, 2, DUAL, EPI, TO, MX>(p, s);
     }
     // bf16 row-grouped products: a partial last round of big tiles runs
     // as quarter tiles (128 x 128, or 128 x 64 x 2 dual) in a second launch
@@ -1321,9 +1340,13 @@ bool mfma_supported(GemmOp op, const GemmParams& p) {
   // contiguous) operands are loaded 8 rows at a time.
   if (p.K % 8) return false;
   // MXFP8 products run only on the direct-to-LDS kernel: whole 128-byte
-  // k-tiles (K % 128) and 32-column scale blocks in the output (N % 32)
+  // k-tiles (K % 128) and 32-column scale blocks in the output (N % 32);
+  // the scale arrays' byte offsets (rows x K / 32) fit the 32-bit buffer
+  // offsets
   if ((op == kOpGemm1Mx || op == kOpGemm2Mx || op == kOpGemm1MxAct ||
-       op == kOpDgrad2Mx) && (p.K % 128 || p.N % 32))
+       op == kOpDgrad2Mx) &&
+      (p.K % 128 || p.N % 32 || p.s_rows * (p.K / 32) > INT_MAX ||
+       (long)(p.off ? p.G : 1) * p.N * (p.K / 32) > INT_MAX))
     return false;
   if (op == kOpDgrad1 && p.K1 % 64) return false;
   if ((op == kOpDgrad2 || op == kOpDgrad1) && p.N % 8) return false;

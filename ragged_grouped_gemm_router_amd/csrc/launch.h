@@ -106,25 +106,30 @@ hipError_t launch_reduce_parts(int dtype, const float* part, long n, int G,
 hipError_t launch_add_inplace(int dtype, void* y, const void* x, long n,
                               hipStream_t s);
 
-// MXFP8 (E4M3 elements, E8M0 scale per 32 along rows).
-// Rows of a contiguous bf16 [rows, cols] into codes at q + r * ldq and
-// scales at scales + r * lds (q, scales offset to the first column).
+// MXFP8 (E4M3 elements, E8M0 scale per 32 along rows). Every scale array
+// is in the span-grouped layout of mx_scale_index: [cols/128][rows][4] for
+// an operand of `rows` rows; a pointer "offset to column c" (c a multiple
+// of 128) is the array's start plus c / 128 * rows * 4.
+// Rows of a contiguous bf16 [rows, cols] into codes at q + r * ldq and the
+// scales of the rows-row operand (q, scales offset to the first column).
 hipError_t launch_quantize_mxfp8_strided(const void* src, long rows,
                                          long cols, uint8_t* q, long ldq,
-                                         uint8_t* scales, long lds,
-                                         hipStream_t s);
-// Codes [rows, cols] + scales [rows, cols/32] -> bf16 [rows, cols].
+                                         uint8_t* scales, hipStream_t s);
+// Codes [rows, cols] + scales -> bf16 [rows, cols].
 hipError_t launch_dequantize_mxfp8(const uint8_t* q, const uint8_t* scales,
                                    long rows, long cols, void* out,
                                    hipStream_t s);
-// Per batch: bf16 [R, C] -> codes [C, ldq] (blocks along R), scales
-// [C, ldq/32]; q and scales offset to the first destination column, batch
-// strides C * ldq and C * ldq / 32. R % 32 == 0, C % 64 == 0.
+// Per batch: bf16 [R, C] -> codes [C, ldq] (blocks along R, batch stride
+// C * ldq) and the scales of the stacked [batch * C, ldq] operand; q and
+// scales offset to the first destination column. R % 32 == 0, C % 64 == 0.
 hipError_t launch_quantize_mxfp8_cols(const void* src, long batch, int R,
                                       int C, uint8_t* q, long ldq,
                                       uint8_t* scales, hipStream_t s);
+// Rows of a contiguous bf16 [rows, cols] (cols % 128 == 0) into codes
+// [rows, cols] and scales.
 hipError_t launch_quantize_mxfp8(const void* src, long rows, long cols,
                                  uint8_t* q, uint8_t* scales, hipStream_t s);
+// x [T, d] quantised into the T*K rows of x_perm at dest (codes, scales).
 hipError_t launch_scatter_rows_mxfp8(const void* x, int T, int K, int d,
                                      const int32_t* dest, uint8_t* xq,
                                      uint8_t* xs, hipStream_t s);

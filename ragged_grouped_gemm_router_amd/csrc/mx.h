@@ -12,6 +12,16 @@
 
 namespace moe {
 
+// Byte of the E8M0 code of 32-block `blk` (columns 32 blk .. 32 blk + 31)
+// of row r, in the scale array of an MX operand with R rows: the codes are
+// grouped by 128-column span, [cols/128][R][4], so that one span's four
+// codes of a row are one aligned word and consecutive rows' words are
+// contiguous (a GEMM k-tile of 128 columns reads the scales of 32
+// consecutive rows as one 128-byte line).
+__host__ __device__ inline long mx_scale_index(long r, long blk, long R) {
+  return ((blk >> 2) * R + r) * 4 + (blk & 3);
+}
+
 // E8M0 exponent X of a block from its largest magnitude (fp32).
 __device__ __forceinline__ int mx_block_exponent(float amax) {
   const int e = (int)((__float_as_uint(amax) >> 23) & 0xff);

@@ -47,12 +47,15 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return (c & 0x80u) ? -mag : mag;
 }
 
+// Scale arrays below are in the span-grouped MX layout (mx_scale_index).
+//
 // Strided form: block b of 32 is row b / bpr, block b % bpr of a
-// contiguous [rows, bpr * 32] source; codes go to q + row * ldq and
-// scales to scales + row * lds (both already offset to the first column).
+// contiguous [rows, bpr * 32] source; codes go to q + row * ldq, scales to
+// the scale array of a `rows`-row operand, both already offset to the
+// first column (a multiple of 128 columns).
 __global__ __launch_bounds__(256) void quantize_rows_strided_kernel(
     const bf16* __restrict__ src, long nblk, int bpr, uint8_t* __restrict__ q,
-    long ldq, uint8_t* __restrict__ scales, long lds) {
+    long ldq, uint8_t* __restrict__ scales) {
   const long b = blockIdx.x * 256L + threadIdx.x;
   if (b >= nblk) return;
   const long r = b / bpr;
@@ -62,18 +65,19 @@ __global__ __launch_bounds__(256) void quantize_rows_strided_kernel(
   u32x4* dst = (u32x4*)(q + r * ldq + blk * 32);
   dst[0] = u32x4{w[0], w[1], w[2], w[3]};
   dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-  scales[r * lds + blk] = (uint8_t)code;
+  scales[mx_scale_index(r, blk, nblk / bpr)] = (uint8_t)code;
 }
 
-// MX codes [rows, cols] with scales [rows, cols/32] back to bf16, one
-// thread per 32-block (exact: an E4M3 value times a power of two fits
-// bf16's 8-bit mantissa).
+// MX codes [rows, cols] with their scales (bpr = cols / 32 per row) back
+// to bf16, one thread per 32-block (exact: an E4M3 value times a power of
+// two fits bf16's 8-bit mantissa).
 __global__ __launch_bounds__(256) void dequantize_rows_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ scales,
-    long nblk, bf16* __restrict__ out) {
+    long nblk, int bpr, bf16* __restrict__ out) {
   const long b = blockIdx.x * 256L + threadIdx.x;
   if (b >= nblk) return;
-  const float sc = ldexpf(1.0f, (int)scales[b] - 127);
+  const float sc =
+      ldexpf(1.0f, (int)scales[mx_scale_index(b / bpr, b % bpr, nblk / bpr)] - 127);
   const u32x4* src = (const u32x4*)(q + b * 32);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -88,12 +92,14 @@ __global__ __launch_bounds__(256) void dequantize_rows_kernel(
 }
 
 // Transposing quantisation: batch b of a [R, C] bf16 source becomes
-// [C, ldq] codes with element (c, r) = Q(src[r][c]), in 32-blocks along r,
-// scales [C, ldq / 32]. A workgroup stages a 32 x 64 tile in LDS; thread
-// c < 64 then quantises column c's 32 values. (Used once per weight set.)
+// [C, ldq] codes with element (c, r) = Q(src[r][c]), in 32-blocks along r;
+// the scales are those of the stacked [batch * C, ldq] operand, from its
+// first column's 128-column span (q and scales already offset there). A workgroup stages a 32 x 64
+// tile in LDS; thread c < 64 then quantises column c's 32 values. (Used
+// once per weight set.)
 __global__ __launch_bounds__(256) void quantize_cols_kernel(
     const bf16* __restrict__ src, int R, int C, uint8_t* __restrict__ q,
-    long ldq, long q_bstride, uint8_t* __restrict__ scales, long s_bstride) {
+    long ldq, long q_bstride, uint8_t* __restrict__ scales) {
   __shared__ float tile[32][65];
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 32, b = blockIdx.z;
   const bf16* sb = src + (long)b * R * C;
@@ -114,12 +120,14 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(
   u32x4* dst = (u32x4*)(q + b * q_bstride + (long)(c0 + c) * ldq + r0);
   dst[0] = u32x4{w[0], w[1], w[2], w[3]};
   dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-  scales[b * s_bstride + (long)(c0 + c) * (ldq / 32) + r0 / 32] = (uint8_t)code;
+  scales[mx_scale_index((long)b * C + c0 + c, r0 / 32, (long)gridDim.z * C)] =
+      (uint8_t)code;
 }
 
 __global__ __launch_bounds__(256) void quantize_rows_kernel(
     const bf16* __restrict__ src, long nblk, int bpr, uint8_t* __restrict__ q,
     uint8_t* __restrict__ scales) {
+  // (codes stay in row order; one thread writes one block's scale byte)
   const long b = blockIdx.x * 256L + threadIdx.x;
   if (b >= nblk) return;
   uint32_t w[8];
@@ -127,12 +135,11 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
   u32x4* dst = (u32x4*)(q + b * 32);
   dst[0] = u32x4{w[0], w[1], w[2], w[3]};
   dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-  scales[b] = (uint8_t)code;
-  (void)bpr;
+  scales[mx_scale_index(b / bpr, b % bpr, nblk / bpr)] = (uint8_t)code;
 }
 
 // one thread per (token, 32-block): quantise once, write to the token's K
-// sorted slots
+// sorted slots (scales of the n / bpr * K-row x_perm)
 __global__ __launch_bounds__(256) void scatter_rows_mxfp8_kernel(
     const bf16* __restrict__ x, long n, int K, int bpr,
     const int32_t* __restrict__ dest, uint8_t* __restrict__ xq,
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(256) void scatter_rows_mxfp8_kernel(
     u32x4* dst = (u32x4*)(xq + (p * bpr + blk) * 32);
     dst[0] = u32x4{w[0], w[1], w[2], w[3]};
     dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-    xs[p * bpr + blk] = (uint8_t)code;
+    xs[mx_scale_index(p, blk, n / bpr * K)] = (uint8_t)code;
   }
 }
 
@@ -166,14 +173,12 @@ hipError_t launch_quantize_mxfp8(const void* src, long rows, long cols,
 
 hipError_t launch_quantize_mxfp8_strided(const void* src, long rows,
                                          long cols, uint8_t* q, long ldq,
-                                         uint8_t* scales, long lds,
-                                         hipStream_t s) {
+                                         uint8_t* scales, hipStream_t s) {
   const long nblk = rows * (cols / 32);
   if (nblk == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_rows_strided_kernel,
                      dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s,
-                     (const bf16*)src, nblk, (int)(cols / 32), q, ldq, scales,
-                     lds);
+                     (const bf16*)src, nblk, (int)(cols / 32), q, ldq, scales);
   return hipGetLastError();
 }
 
@@ -184,7 +189,7 @@ hipError_t launch_dequantize_mxfp8(const uint8_t* q, const uint8_t* scales,
   if (nblk == 0) return hipSuccess;
   hipLaunchKernelGGL(dequantize_rows_kernel,
                      dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s, q,
-                     scales, nblk, (bf16*)out);
+                     scales, nblk, (int)(cols / 32), (bf16*)out);
   return hipGetLastError();
 }
 
@@ -196,7 +201,7 @@ hipError_t launch_quantize_mxfp8_cols(const void* src, long batch, int R,
                      dim3((unsigned)(C / 64), (unsigned)(R / 32),
                           (unsigned)batch),
                      dim3(256), 0, s, (const bf16*)src, R, C, q, ldq,
-                     (long)C * ldq, scales, (long)C * (ldq / 32));
+                     (long)C * ldq, scales);
   return hipGetLastError();
 }
 

@@ -20,13 +20,28 @@ def is_mx(desc: B.MoeDesc) -> bool:
     return desc.gemm_dtype == B.MOE_MXFP8
 
 
+def mx_scale_shape(rows: int, cols: int):
+    """Shape of the E8M0 scales of an MX operand of `rows` (stacked) rows
+    and `cols` columns in the library's layout: [cols/128, rows, 4], the
+    four codes of one row's 128-column span side by side."""
+    return (cols // 128, rows, 4)
+
+
+def mx_scales_rows(sc: torch.Tensor, lead) -> torch.Tensor:
+    """The same codes row by row: [*lead, cols/32] (a layout change only;
+    lead = the operand's leading dimensions, e.g. (E, d_ff))."""
+    spans, rows, _ = sc.shape
+    return sc.permute(1, 0, 2).reshape(*lead, spans * 4)
+
+
 def quantize_mxfp8(t: torch.Tensor):
     """MX-quantise a bf16 tensor along its last dimension on the device:
-    (E4M3 codes as uint8 with t's shape, E8M0 scales [..., cols/32])."""
+    (E4M3 codes as uint8 with t's shape, E8M0 scales of the stacked
+    [numel / cols, cols] operand, shape mx_scale_shape)."""
     cols = t.shape[-1]
     rows = t.numel() // cols
     q = torch.empty(t.shape, dtype=torch.uint8, device=t.device)
-    sc = torch.empty(*t.shape[:-1], cols // 32, dtype=torch.uint8,
+    sc = torch.empty(mx_scale_shape(rows, cols), dtype=torch.uint8,
                      device=t.device)
     B.moe_quantize_mxfp8(t.contiguous(), rows, cols, q, sc)
     return q, sc
@@ -48,9 +63,9 @@ def _quantize_t(w1, w3, w2):
     E, f, d = w1.shape
     dev, u8 = w1.device, torch.uint8
     w2t = torch.empty(E, f, d, dtype=u8, device=dev)
-    w2t_s = torch.empty(E, f, d // 32, dtype=u8, device=dev)
+    w2t_s = torch.empty(mx_scale_shape(E * f, d), dtype=u8, device=dev)
     w13t = torch.empty(E, d, 2 * f, dtype=u8, device=dev)
-    w13t_s = torch.empty(E, d, 2 * f // 32, dtype=u8, device=dev)
+    w13t_s = torch.empty(mx_scale_shape(E * d, 2 * f), dtype=u8, device=dev)
     B.moe_quantize_mxfp8_t(w2.contiguous(), E, d, f, w2t, w2t_s, d)
     for col, w in ((0, w1), (f, w3)):
         B.moe_quantize_mxfp8_t(w.contiguous(), E, f, d, w13t, w13t_s, 2 * f,
@@ -72,8 +87,9 @@ def quantize_expert_weights_bwd(inp: dict) -> dict:
             w1, w3, w2 = w1[None], w3[None], w2[None]
         w2t, w2t_s, w13t, w13t_s = _quantize_t(w1, w3, w2)
         sq = (lambda t: t[0]) if tag else (lambda t: t)
-        out[f"w{tag}2t"], out[f"w{tag}2t_s"] = sq(w2t), sq(w2t_s)
-        out[f"w{tag}13t"], out[f"w{tag}13t_s"] = sq(w13t), sq(w13t_s)
+        # (the scales of E = 1 stacked operands are those of the one)
+        out[f"w{tag}2t"], out[f"w{tag}2t_s"] = sq(w2t), w2t_s
+        out[f"w{tag}13t"], out[f"w{tag}13t_s"] = sq(w13t), w13t_s
     return out
 
 
@@ -106,7 +122,8 @@ def alloc_forward(desc: B.MoeDesc, device="cuda", gather=False) -> dict:
     if is_mx(desc):
         u8 = torch.uint8
         bufs["x_perm"] = torch.empty(TK, d, dtype=u8, device=device)
-        bufs["x_perm_scales"] = torch.empty(TK, d // 32, dtype=u8, device=device)
+        bufs["x_perm_scales"] = torch.empty(mx_scale_shape(TK, d), dtype=u8,
+                                            device=device)
         bufs["h"] = torch.empty(TK * f + TK * (f // 32), dtype=u8, device=device)
     if gather:
         bufs["x_perm"] = bufs["x_perm_scales"] = None

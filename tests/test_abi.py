@@ -7,8 +7,10 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 from ragged_grouped_gemm_router_amd import binding as B
+from ragged_grouped_gemm_router_amd import layer as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
@@ -254,6 +256,38 @@ def test_quantize_t_validation():
     assert q(fake, 2, 64, 96, fake, fake, 64, 0, None) == B.MOE_EUNSUPPORTED
     assert q(fake, 0, 64, 128, None, None, 64, 0, None) == B.MOE_OK
     assert q(fake, -1, 64, 128, fake, fake, 64, 0, None) == B.MOE_EINVAL
+    # the destination's 128-column scale spans: ldq and col_off multiples
+    # of 128
+    assert q(fake, 2, 64, 128, fake, fake, 192, 64, None) == B.MOE_EUNSUPPORTED
+    assert q(fake, 2, 64, 128, fake, fake, 96, 0, None) == B.MOE_EUNSUPPORTED
+
+
+def test_quantize_validation():
+    lib = B.load()
+    fake = 0x1000
+    q = lib.moe_quantize_mxfp8
+    assert q(None, 4, 128, fake, fake, None) == B.MOE_EINVAL
+    assert q(fake, 4, 0, fake, fake, None) == B.MOE_EINVAL
+    assert q(fake, 4, 96, fake, fake, None) == B.MOE_EUNSUPPORTED
+    assert q(fake, 0, 128, fake, fake, None) == B.MOE_OK
+
+
+def test_mx_scale_layout_views():
+    """The scale arrays' layout: the code of block b of row r of an
+    R-row operand at byte ((b // 4) * R + r) * 4 + b % 4; the Python
+    views take it to rows of cols / 32 codes and back."""
+    R, cols = 5, 384
+    flat = torch.arange(R * cols // 32, dtype=torch.int64)
+    sc = flat.reshape(L.mx_scale_shape(R, cols))
+    rows = L.mx_scales_rows(sc, (R,))
+    for r in range(R):
+        for b in range(cols // 32):
+            assert rows[r, b] == ((b // 4) * R + r) * 4 + b % 4
+    # stacked batches: row r of operand e is row e * R + r
+    E = 3
+    sc = torch.arange(E * R * cols // 32).reshape(L.mx_scale_shape(E * R, cols))
+    per = L.mx_scales_rows(sc, (E, R))
+    assert per[2, 1, 5] == ((5 // 4) * E * R + 2 * R + 1) * 4 + 5 % 4
 
 
 def test_transposed_wgrad_workspace():

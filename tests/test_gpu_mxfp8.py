@@ -57,6 +57,7 @@ def test_quantizer_bit_exact():
     q, s = L.quantize_mxfp8(x.to(DEV))
     torch.cuda.synchronize()
     ref_q, ref_c = oracle.mx_quantize(x.double())
+    s = L.mx_scales_rows(s, x.shape[:-1])
     assert torch.equal(s.cpu(), ref_c)
     got = decode(q, s)
     want = oracle.mx_dequantize(ref_q, ref_c)
@@ -91,12 +92,14 @@ def test_mxfp8_forward_parity(cfg):
     idx, w, counts, offsets, src, dest = check_routing_exact(cfg, cinp, bufs)
     # quantised permute: codes and scales of each x_perm row exact
     rq, rc = oracle.mx_quantize(cinp["x"][src // cfg.K].double())
-    assert torch.equal(bufs["x_perm_scales"].cpu(), rc)
-    assert torch.equal(decode(bufs["x_perm"], bufs["x_perm_scales"]),
-                       oracle.mx_dequantize(rq, rc))
-    # weights quantised on the device agree with the oracle's rule
-    q1, c1 = oracle.mx_quantize(cinp["w1"][0].double())
-    assert torch.equal(mx["w1_s"][0].cpu(), c1)
+    xs = L.mx_scales_rows(bufs["x_perm_scales"], (cfg.T * cfg.K,))
+    assert torch.equal(xs.cpu(), rc)
+    assert torch.equal(decode(bufs["x_perm"], xs), oracle.mx_dequantize(rq, rc))
+    # weights quantised on the device agree with the oracle's rule (the
+    # last expert: its rows come last in the stacked scale array)
+    q1, c1 = oracle.mx_quantize(cinp["w1"][-1].double())
+    w1s = L.mx_scales_rows(mx["w1_s"], (cfg.E, cfg.f))
+    assert torch.equal(w1s[-1].cpu(), c1)
     sh = (cinp["ws1"], cinp["ws3"], cinp["ws2"])
     ref = oracle.forward_mxfp8(cinp["x"], cinp["w1"], cinp["w3"], cinp["w2"],
                                idx, w, *sh)

@@ -35,20 +35,24 @@ CASES = [
 
 def test_transposing_quantiser_exact():
     g = torch.Generator().manual_seed(40)
+    # R = 96 rows land at column 128 of a 256-wide destination: a partial
+    # last span, and spans before and after that stay untouched
     E, R, C = 3, 96, 192
     src = (torch.randn(E, R, C, generator=g) * 2.0).to(torch.bfloat16)
-    ldq, col = 2 * R, R
+    ldq, col = 256, 128
     q = torch.zeros(E, C, ldq, dtype=torch.uint8, device=DEV)
-    sc = torch.zeros(E, C, ldq // 32, dtype=torch.uint8, device=DEV)
+    sc = torch.zeros(L.mx_scale_shape(E * C, ldq), dtype=torch.uint8, device=DEV)
     B.moe_quantize_mxfp8_t(src.to(DEV), E, R, C, q, sc, ldq, col)
     torch.cuda.synchronize()
+    rows = L.mx_scales_rows(sc, (E, C)).cpu()
     for e in range(E):
         rq, rc = oracle.mx_quantize(src[e].double().T)
-        got_c = sc[e, :, col // 32:].cpu()
-        assert torch.equal(got_c, rc)
-        codes = q[e, :, col:].cpu().view(torch.float8_e4m3fn).double()
+        assert torch.equal(rows[e, :, col // 32:(col + R) // 32], rc)
+        codes = q[e, :, col:col + R].cpu().view(torch.float8_e4m3fn).double()
         assert torch.equal(codes, rq)
-        assert (q[e, :, :col] == 0).all() and (sc[e, :, :col // 32] == 0).all()
+        assert (q[e, :, :col] == 0).all() and (q[e, :, col + R:] == 0).all()
+        assert (rows[e, :, :col // 32] == 0).all()
+        assert (rows[e, :, (col + R) // 32:] == 0).all()
 
 
 def _mx_train(cfg, ginp, save_acts=False):
