@@ -112,7 +112,9 @@ typedef struct moe_desc {
  * rows are one 128-byte line (a row-major [rows][cols / 32] array would
  * spread them over 32 lines). A batch of operands ([B, rows, cols]) is laid
  * out as the one operand of B * rows rows that stacks them. The block rule
- * itself is moe_quantize_mxfp8's. */
+ * itself is moe_quantize_mxfp8's.
+ * Scale arrays (and an MXFP8 h buffer, which ends in one) start on a
+ * 4-byte boundary; calls given another return MOE_EINVAL. */
 
 /* One set of SwiGLU expert weights [P3 §9]: y = W2 (silu(W1 x) * (W3 x)).
  * For the routed experts the leading dimension is E; for the shared

@@ -415,9 +415,14 @@ hipError_t do_experts_mx(const moe_desc* d, const void* x_perm,
   return gemm_mfma(kOpGemm2Mx, p, ws.tile_off, s);
 }
 
+// MX scale arrays are read and written a 4-code word at a time.
+bool scale_ptr_ok(const void* p) {
+  return p && ((uintptr_t)p & 3) == 0;
+}
+
 bool mx_weights_ok(const moe_expert_weights* w) {
-  return w && w->w1 && w->w3 && w->w2 && w->w1_scales && w->w3_scales &&
-         w->w2_scales;
+  return w && w->w1 && w->w3 && w->w2 && scale_ptr_ok(w->w1_scales) &&
+         scale_ptr_ok(w->w3_scales) && scale_ptr_ok(w->w2_scales);
 }
 
 // gsrc != NULL: x_perm is x itself and GEMM 1 gathers its rows through
@@ -760,7 +765,8 @@ moe_status moe_quantize_mxfp8_t(const void* src, int64_t batch, int64_t rows,
   if (batch < 0 || rows < 0 || cols < 0 || ldq < 0 || col_off < 0)
     return MOE_EINVAL;
   if (batch == 0 || rows == 0 || cols == 0) return MOE_OK;
-  if (!src || !q || !scales || col_off + rows > ldq) return MOE_EINVAL;
+  if (!src || !q || !scale_ptr_ok(scales) || col_off + rows > ldq)
+    return MOE_EINVAL;
   if (rows % 32 || cols % 64 || ldq % 128 || col_off % 128 || rows > INT_MAX ||
       cols > INT_MAX || batch > 65535 || rows / 32 > 65535)
     return MOE_EUNSUPPORTED;
@@ -857,7 +863,8 @@ moe_status moe_permute(const moe_desc* d, const void* x,
   if (!x || !topk_idx || !counts || !offsets || !sorted_src || !dest ||
       !x_perm || !ws)
     return MOE_EINVAL;
-  if (d->gemm_dtype == MOE_MXFP8 && !x_perm_scales) return MOE_EINVAL;
+  if (d->gemm_dtype == MOE_MXFP8 && !scale_ptr_ok(x_perm_scales))
+    return MOE_EINVAL;
   if (ws_bytes < fwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
   FwdWs w;
   fwd_ws_layout(d, (char*)ws, &w);
@@ -881,7 +888,9 @@ moe_status moe_grouped_gemm_swiglu(const moe_desc* d, const void* x_perm,
   if (!x_perm || !offsets || !weights_ok(routed) || !h || !y_perm || !ws)
     return MOE_EINVAL;
   const bool mx = d->gemm_dtype == MOE_MXFP8;
-  if (mx && (!x_perm_scales || !mx_weights_ok(routed))) return MOE_EINVAL;
+  if (mx && (!scale_ptr_ok(x_perm_scales) || !scale_ptr_ok(h) ||
+             !mx_weights_ok(routed)))
+    return MOE_EINVAL;
   const bool use_shared = x_shared && d->d_ff_shared > 0;
   if (use_shared && (!weights_ok(shared) || !y_shared)) return MOE_EINVAL;
   if ((d->flags & MOE_FLAG_SAVE_ACTS) && (!act_a || !act_b)) return MOE_EINVAL;
@@ -939,7 +948,8 @@ moe_status check_fwd_args(const moe_desc* d, const moe_fwd_args* a) {
   const bool save = d->flags & MOE_FLAG_SAVE_ACTS;
   if (save && (!a->act_a || !a->act_b)) return MOE_EINVAL;
   const bool mx = d->gemm_dtype == MOE_MXFP8;
-  if (mx && ((!gather && !a->x_perm_scales) || !mx_weights_ok(&a->routed)))
+  if (mx && ((!gather && !scale_ptr_ok(a->x_perm_scales)) ||
+             !scale_ptr_ok(a->h) || !mx_weights_ok(&a->routed)))
     return MOE_EINVAL;
   if (mx && shared && !mx_weights_ok(&a->shared)) return MOE_EINVAL;
   return MOE_OK;
@@ -1059,12 +1069,14 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     return MOE_EINVAL;
   if ((a->act_a == nullptr) != (a->act_b == nullptr)) return MOE_EINVAL;
   if (d->gemm_dtype == MOE_MXFP8) {
-    if (!a->x_perm_scales || !a->w2t || !a->w2t_scales || !a->w13t ||
-        !a->w13t_scales || !a->routed.w1_scales || !a->routed.w3_scales)
+    if (!scale_ptr_ok(a->x_perm_scales) || !scale_ptr_ok(a->h) || !a->w2t ||
+        !scale_ptr_ok(a->w2t_scales) || !a->w13t ||
+        !scale_ptr_ok(a->w13t_scales) || !mx_weights_ok(&a->routed))
       return MOE_EINVAL;
     if (d->d_ff_shared > 0 &&
         (!mx_weights_ok(&a->shared) || !a->dws1 || !a->dws3 || !a->dws2 ||
-         !a->ws2t || !a->ws2t_scales || !a->ws13t || !a->ws13t_scales))
+         !a->ws2t || !scale_ptr_ok(a->ws2t_scales) || !a->ws13t ||
+         !scale_ptr_ok(a->ws13t_scales)))
       return MOE_EINVAL;
     if (ws_bytes < bwd_ws_layout(d, nullptr, nullptr)) return MOE_EWORKSPACE;
     return hip_status(do_backward_mx(d, a, ws, (hipStream_t)stream));
@@ -1230,7 +1242,8 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
 moe_status moe_quantize_mxfp8(const void* src_bf16, int64_t rows,
                               int64_t cols, uint8_t* q, uint8_t* scales,
                               void* stream) {
-  if (!src_bf16 || !q || !scales || rows < 0 || cols <= 0) return MOE_EINVAL;
+  if (!src_bf16 || !q || !scale_ptr_ok(scales) || rows < 0 || cols <= 0)
+    return MOE_EINVAL;
   if (cols % 128) return MOE_EUNSUPPORTED;
   if (rows == 0) return MOE_OK;
   return hip_status(launch_quantize_mxfp8(src_bf16, rows, cols, q, scales,

@@ -49,6 +49,16 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 
 // Scale arrays below are in the span-grouped MX layout (mx_scale_index).
 //
+// The four scale codes of a 128-column span as one word, in the lane
+// holding the span's first block (bpr % 4 == 0, so the four blocks of a
+// span sit in four consecutive threads, all of them active or none: a
+// launch's thread count is a multiple of 4). Lanes of other blocks get 0.
+__device__ __forceinline__ uint32_t span_word(uint32_t code) {
+  const uint32_t c1 = __shfl_down(code, 1), c2 = __shfl_down(code, 2),
+                 c3 = __shfl_down(code, 3);
+  return code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+}
+
 // Strided form: block b of 32 is row b / bpr, block b % bpr of a
 // contiguous [rows, bpr * 32] source; codes go to q + row * ldq, scales to
 // the scale array of a `rows`-row operand, both already offset to the
@@ -61,11 +71,12 @@ __global__ __launch_bounds__(256) void quantize_rows_strided_kernel(
   const long r = b / bpr;
   const int blk = (int)(b % bpr);
   uint32_t w[8];
-  const uint32_t code = quant32(src + b * 32, w);
+  const uint32_t code = span_word(quant32(src + b * 32, w));
   u32x4* dst = (u32x4*)(q + r * ldq + blk * 32);
   dst[0] = u32x4{w[0], w[1], w[2], w[3]};
   dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-  scales[mx_scale_index(r, blk, nblk / bpr)] = (uint8_t)code;
+  if ((blk & 3) == 0)
+    *(uint32_t*)(scales + mx_scale_index(r, blk, nblk / bpr)) = code;
 }
 
 // MX codes [rows, cols] with their scales (bpr = cols / 32 per row) back
@@ -131,11 +142,12 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
   const long b = blockIdx.x * 256L + threadIdx.x;
   if (b >= nblk) return;
   uint32_t w[8];
-  const uint32_t code = quant32(src + b * 32, w);
+  const uint32_t code = span_word(quant32(src + b * 32, w));
   u32x4* dst = (u32x4*)(q + b * 32);
   dst[0] = u32x4{w[0], w[1], w[2], w[3]};
   dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-  scales[mx_scale_index(b / bpr, b % bpr, nblk / bpr)] = (uint8_t)code;
+  if ((b & 3) == 0)
+    *(uint32_t*)(scales + mx_scale_index(b / bpr, b % bpr, nblk / bpr)) = code;
 }
 
 // one thread per (token, 32-block): quantise once, write to the token's K
@@ -149,13 +161,14 @@ __global__ __launch_bounds__(256) void scatter_rows_mxfp8_kernel(
   const long t = i / bpr;
   const int blk = (int)(i % bpr);
   uint32_t w[8];
-  const uint32_t code = quant32(x + t * bpr * 32 + blk * 32, w);
+  const uint32_t code = span_word(quant32(x + t * bpr * 32 + blk * 32, w));
   for (int k = 0; k < K; ++k) {
     const long p = dest[t * K + k];
     u32x4* dst = (u32x4*)(xq + (p * bpr + blk) * 32);
     dst[0] = u32x4{w[0], w[1], w[2], w[3]};
     dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-    xs[mx_scale_index(p, blk, n / bpr * K)] = (uint8_t)code;
+    if ((blk & 3) == 0)
+      *(uint32_t*)(xs + mx_scale_index(p, blk, n / bpr * K)) = code;
   }
 }
 

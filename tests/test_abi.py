@@ -270,6 +270,10 @@ def test_quantize_validation():
     assert q(fake, 4, 0, fake, fake, None) == B.MOE_EINVAL
     assert q(fake, 4, 96, fake, fake, None) == B.MOE_EUNSUPPORTED
     assert q(fake, 0, 128, fake, fake, None) == B.MOE_OK
+    # scale arrays are written a 4-code word at a time
+    assert q(fake, 4, 128, fake, fake + 2, None) == B.MOE_EINVAL
+    qt = lib.moe_quantize_mxfp8_t
+    assert qt(fake, 2, 64, 128, fake, fake + 1, 128, 0, None) == B.MOE_EINVAL
 
 
 def test_mx_scale_layout_views():
