@@ -46,8 +46,10 @@ moe_status check_desc(const moe_desc* d) {
   return MOE_OK;
 }
 
-// Forward scratch: permute histogram, tile prefixes, shared-expert hidden.
+// Forward scratch: permute histogram, tile prefixes, shared-expert hidden,
+// the split router GEMM's partial products.
 struct FwdWs {
+  float* router_part;  // [router_split.G, T, E] fp32 when G > 1
   int32_t* block_hist;
   int32_t* rank;
   uint8_t* xq;  // MXFP8: x quantised once (shared expert, gathered GEMM 1):
@@ -101,10 +103,50 @@ struct BwdWs {
   void* sx_bf;
 };
 
+bool force_simt();
+
+// The router GEMM inside the whole forward, bf16 on the direct-to-LDS
+// kernel: its contraction over d_model is split into G ranges of kmul
+// columns (whole k-tiles of 64) whose partial products the top-K kernel
+// sums in order. G brings the launch to about kRouterWgs workgroups (one
+// per CU for the 64 x 256 tile, two for the smaller ones; a fixed count,
+// so that G, the workspace and the logits' rounding depend on the
+// descriptor alone), at most kRouterMaxSplit splits and kRouterPartBytes of
+// partials.
+// G = 1: one range of all d_model columns.
+constexpr long kRouterWgs = 256;
+constexpr size_t kRouterPartBytes = (size_t)32 << 20;
+struct RouterSplit {
+  int G, kmul;
+};
+RouterSplit router_split(const moe_desc* d) {
+  RouterSplit r{1, d->d_model};
+  if (d->act_dtype != MOE_BF16 || d->d_model % 64 || d->T <= 0 ||
+      force_simt() || !gemm_direct_ok())
+    return r;
+  const int bm = d->E <= 32 ? 32 : 64;
+  const int bn = d->E <= 32 ? 32 : d->E <= 64 ? 64 : 256;
+  const long tiles = cdiv(d->T, bm) * cdiv(d->E, bn);
+  const long target = bn == 256 ? kRouterWgs : 2 * kRouterWgs;
+  const int kt = d->d_model / 64;
+  long G = (target + tiles / 2) / tiles;
+  const long part = (long)d->T * d->E * (long)sizeof(float);
+  G = std::min<long>({G, (long)kRouterMaxSplit, (long)kt,
+                      (long)(kRouterPartBytes / part)});
+  if (G <= 1) return r;
+  const int per = (int)cdiv(kt, G);  // k-tiles per split
+  r.G = (int)cdiv(kt, per);
+  r.kmul = per * 64;
+  return r;
+}
+
 size_t fwd_ws_layout(const moe_desc* d, char* base, FwdWs* w) {
   const long TK = (long)d->T * d->K;
   const long nblk = cdiv(TK, kPermChunk);
   size_t o = 0;
+  const RouterSplit rs = router_split(d);
+  if (w) w->router_part = rs.G > 1 ? (float*)(base + o) : nullptr;
+  if (rs.G > 1) o = align_up(o + sizeof(float) * (size_t)rs.G * d->T * d->E);
   if (w) w->block_hist = (int32_t*)(base + o);
   o = align_up(o + sizeof(int32_t) * (size_t)(d->E * (nblk > 0 ? nblk : 1)));
   if (w) w->rank = (int32_t*)(base + o);
@@ -124,8 +166,6 @@ size_t fwd_ws_layout(const moe_desc* d, char* base, FwdWs* w) {
   }
   return o;
 }
-
-bool force_simt();
 
 // The weight gradients (bf16, in the MXFP8 backward too) run on the
 // direct-to-LDS kernel from transposed operands when the widths allow and
@@ -275,23 +315,37 @@ hipError_t do_route(const moe_desc* d, const void* x, const void* wr,
                     float* logits_out, int32_t* idx, float* w, hipStream_t s,
                     const FwdWs* ws = nullptr, bool* ranked = nullptr) {
   const float* L = logits_in;
+  int G = 1;  // partial products of the split router GEMM in L
   if (!L) {
+    // (a forward's workspace holds the partials of a split; on its own
+    // the router GEMM runs as one contraction)
+    const RouterSplit rs = ws ? router_split(d) : RouterSplit{1, d->d_model};
     GemmParams p = gp();
     p.M = d->T; p.N = d->E; p.K = d->d_model;
     p.A = x; p.lda = d->d_model;
     p.B = wr; p.ldb = d->d_model;
     p.C = logits_out; p.ldc = d->E;
+    p.G = rs.G; p.kmul = rs.kmul;
+    if (rs.G > 1) {
+      G = rs.G;
+      p.C = ws->router_part;
+      p.sC = (long)d->T * d->E;
+    }
     hipError_t e = run_gemm(kOpRouter, d->act_dtype, p, nullptr, s);
     if (e != hipSuccess) return e;
-    L = logits_out;
+    L = G > 1 ? ws->router_part : logits_out;
   }
   if (ranked) *ranked = false;
-  if (ws && ranked && topk_rank_supported(d->E, d->K)) {
+  // (the fused kernel moves logits rows in 16-byte pieces)
+  const bool al16 = ((uintptr_t)L & 15) == 0 &&
+                    (G == 1 || ((uintptr_t)logits_out & 15) == 0);
+  if (ws && ranked && al16 && topk_rank_supported(d->E, d->K)) {
     *ranked = true;
     return launch_topk_rank(L, bias, d->T, d->E, d->K, d->gate, idx, w,
-                            ws->block_hist, ws->rank, s);
+                            ws->block_hist, ws->rank, s, G, logits_out);
   }
-  return launch_topk(L, bias, d->T, d->E, d->K, d->gate, idx, w, s);
+  return launch_topk(L, bias, d->T, d->E, d->K, d->gate, idx, w, s, G,
+                     logits_out);
 }
 
 // x_perm == NULL: only the indices (the expert GEMM gathers its rows from

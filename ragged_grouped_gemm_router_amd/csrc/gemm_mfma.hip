@@ -1420,10 +1420,25 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   if (p.K % 64 == 0 && !force_staged()) {
     switch (op) {
       case kOpRouter:
-        // one wave per 32 x 32 tile, eight k-tiles in flight, so the
-        // skinny product spreads over every CU and hides latency (E = 256
-        // on the DeepSeek-V3 shape: 1024 tiles; route stage 0.093 ->
-        // 0.084 ms against 64 tiles of 128 x 128 in 3 stages)
+        // Up to 32 experts, one contraction: one wave per 32 x 32 tile,
+        // eight k-tiles in flight, so the skinny product spreads over
+        // every CU and hides latency. Otherwise a contraction-grouped
+        // launch with arithmetic ranges: p.G splits of p.kmul columns of
+        // d_model (the partial products at C + g * sC, summed by the
+        // top-K kernel), on tiles as wide as the experts allow (64 x 256
+        // above 64 experts), so x leaves HBM once and every column tile
+        // streams only its split of W_r.
+        if (p.G > 1 || p.N > 32) {
+          if (p.off || p.kmul % 64 || p.kmul <= 0) return hipErrorInvalidValue;
+          if (p.N <= 32)
+            return launch_dl<32, 32, 8, 1, 1, false, kEpiStore, float, false,
+                             kSchedK>(p, s);
+          if (p.N <= 64)
+            return launch_dl<64, 64, 4, 2, 2, false, kEpiStore, float, false,
+                             kSchedK>(p, s);
+          return launch_dl<64, 256, 4, 2, 2, false, kEpiStore, float, false,
+                           kSchedK>(p, s);
+        }
         return launch_dl<32, 32, 8, 1, 1, false, kEpiStore, float, false>(p, s);
       case kOpGemm1:
         if (skip)

@@ -7,10 +7,15 @@ namespace moe {
 
 // Copies handled by one histogram / ranking workgroup.
 constexpr int kPermChunk = 1024;
+// Most partial products a split router GEMM hands to the top-K kernels.
+constexpr int kRouterMaxSplit = 8;
 
+// Top-K gate over fp32 logits [T, E]. G > 1: `logits` holds G partial
+// products [G, T, E] of a split router GEMM; they are summed in the order
+// g = 0 .. G-1 into lout [T, E] and the gate runs on that sum.
 hipError_t launch_topk(const float* logits, const float* bias, int T, int E,
                        int K, int gate, int32_t* idx, float* w,
-                       hipStream_t s);
+                       hipStream_t s, int G = 1, float* lout = nullptr);
 
 // Top-K fused with the permute's chunk ranking (E <= 32, K a divisor of
 // kPermChunk with at least 64 tokens per chunk): idx, w as launch_topk,
@@ -19,7 +24,8 @@ hipError_t launch_topk(const float* logits, const float* bias, int T, int E,
 bool topk_rank_supported(int E, int K);
 hipError_t launch_topk_rank(const float* logits, const float* bias, int T,
                             int E, int K, int gate, int32_t* idx, float* w,
-                            int32_t* block_hist, int32_t* rank, hipStream_t s);
+                            int32_t* block_hist, int32_t* rank, hipStream_t s,
+                            int G = 1, float* lout = nullptr);
 
 // Counting sort of the T*K copies by expert (stable in the copy index).
 // block_hist: [nblk, E] int32 scratch, nblk = ceil(TK / kPermChunk), left

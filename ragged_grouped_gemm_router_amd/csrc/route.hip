@@ -1,13 +1,20 @@
 // Top-K gate: one wavefront per token.
 //
-// Each lane holds ceil(E/64) candidates as 64-bit keys: the high word is
-// the selection key mapped to an unsigned integer whose order is the
-// float order (-0.0 folded onto +0.0, NaN onto -inf), the low word is
-// ~expert_id, so the unsigned maximum is the largest key and, among equal
-// keys, the lowest expert id. K rounds of a lane-local max plus a 6-step
-// butterfly max over the wave pick the winners in (key desc, id asc)
-// order; the owning lane retires each winner. Lanes 0..K-1 then hold the
-// K winners and form the renormalised weights with two wave reductions.
+// Each lane holds ceil(E/64) candidates (expert e = lane + 64 c) with a
+// 32-bit selection key: the selection value mapped to an unsigned integer
+// whose order is the float order (-0.0 folded onto +0.0, NaN onto -inf).
+// The K-th largest key is found by a 32-step binary search on its bits,
+// each step counting the candidates at or above a trial value with one
+// ballot per candidate slot. The winners are the keys above it and, among
+// the keys equal to it, the lowest expert ids. They are compacted in id
+// order into LDS; lanes 0..K-1 then take one winner each, rank it (key
+// descending, id ascending: the output order) and form the renormalised
+// weight from the winners' raw logits.
+//
+// Split router GEMM (G > 1): `logits` holds G partial products of the
+// logits, pstride floats apart; both kernels sum a token's partials in the
+// order g = 0, 1, .., G - 1 (fp32), write that sum to lout and select
+// from it.
 #include "launch.h"
 #include "rank.h"
 
@@ -19,17 +26,6 @@ __device__ __forceinline__ uint32_t orderable(float v) {
   if (v == 0.0f) b = 0u;                // -0.0 ties +0.0
   if (v != v) b = 0xff800000u;          // NaN counts as -inf
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -44,59 +40,100 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// number of lanes below this one whose bit is set in m
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 template <int CPL>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T,
     int E, int K, int gate, int32_t* __restrict__ idx,
-    float* __restrict__ wout) {
-  const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
-  if (t >= T) return;
+    float* __restrict__ wout, int G, long pstride, float* __restrict__ lout) {
+  __shared__ uint32_t s_key[4][MOE_K_MAX];
+  __shared__ int32_t s_id[4][MOE_K_MAX];
+  __shared__ float s_l[4][MOE_K_MAX];
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+  const int t = blockIdx.x * (256 / kWave) + wv;
+  if (t >= T) return;  // (the whole wave)
   const float* L = logits + (long)t * E;
 
-  uint64_t key[CPL];
+  float lg[CPL];
+  uint32_t key[CPL];  // 0 marks padding: every real key is above it
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int e = lane + kWave * c;
+    lg[c] = 0.0f;
+    key[c] = 0u;
     if (e < E) {
+      // every partial's load issued at once (clamped to the last one),
+      // added in order while g < G
       float v = L[e];
-      if (bias) v = v + bias[e];
-      key[c] = ((uint64_t)orderable(v) << 32) | (uint32_t)(~(uint32_t)e);
-    } else {
-      key[c] = 0;  // below every real key (-inf maps to 0x007fffff)
+      if (G > 1) {
+        float pv[kRouterMaxSplit];
+#pragma unroll
+        for (int g = 1; g < kRouterMaxSplit; ++g) pv[g] = L[min(g, G - 1) * pstride + e];
+#pragma unroll
+        for (int g = 1; g < kRouterMaxSplit; ++g) v = g < G ? v + pv[g] : v;
+        lout[(long)t * E + e] = v;
+      }
+      lg[c] = v;
+      key[c] = orderable(bias ? v + bias[e] : v);
     }
   }
-
-  int mine = -1;
-  for (int k = 0; k < K; ++k) {
-    uint64_t best = 0;
+  // the K-th largest key: the largest value with at least K keys at or
+  // above it (E >= K real keys, all >= 0x007fffff, so it is one of them)
+  uint32_t thr = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t trial = thr | (1u << bit);
+    int n = 0;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) best = key[c] > best ? key[c] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(~(uint32_t)best);
-    if ((e & (kWave - 1)) == lane) {
+    for (int c = 0; c < CPL; ++c) n += __popcll(__ballot(key[c] >= trial));
+    if (n >= K) thr = trial;
+  }
+  // winners: every key above thr, then the lowest ids among keys equal to
+  // it (ids ascend with c, then with the lane)
+  int need = K;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c)
-        if (c == (e >> 6)) key[c] = 0;
+  for (int c = 0; c < CPL; ++c) need -= __popcll(__ballot(key[c] > thr));
+  int base = 0;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const uint64_t eq = __ballot(key[c] == thr);
+    const bool win = key[c] > thr || (key[c] == thr && lanes_below(eq) < need);
+    need -= __popcll(eq);
+    const uint64_t wm = __ballot(win);
+    if (win) {
+      const int p = base + lanes_below(wm);
+      s_key[wv][p] = key[c];
+      s_id[wv][p] = lane + kWave * c;
+      s_l[wv][p] = lg[c];
     }
-    if (lane == k) mine = e;
+    base += __popcll(wm);
   }
-
-  // weights from the raw logits of the winners (lanes 0..K-1)
-  const bool act = lane < K;
-  const float l = act ? L[mine] : 0.0f;
-  float z;
-  if (gate == MOE_GATE_SOFTMAX) {
-    const float mx = wave_max(act ? l : -INFINITY);
-    z = act ? expf(l - mx) : 0.0f;
-  } else {
-    z = act ? 1.0f / (1.0f + expf(-l)) : 0.0f;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane >= K) return;
+  // rank of this lane's winner, and the weights over the K raw logits
+  const uint32_t mk = s_key[wv][lane];
+  const float l = s_l[wv][lane];
+  int rank = 0;
+  float mx = -INFINITY;
+  for (int j = 0; j < K; ++j) {
+    const uint32_t kj = s_key[wv][j];
+    rank += kj > mk || (kj == mk && j < lane);
+    mx = fmaxf(mx, s_l[wv][j]);
   }
-  const float s = wave_sum(z);
-  if (act) {
-    idx[(long)t * K + lane] = mine;
-    wout[(long)t * K + lane] = s > 0.0f ? z / s : 1.0f / (float)K;
+  float sum = 0.0f;
+  for (int j = 0; j < K; ++j) {
+    const float lj = s_l[wv][j];
+    sum += gate == MOE_GATE_SOFTMAX ? expf(lj - mx) : 1.0f / (1.0f + expf(-lj));
   }
+  const float z = gate == MOE_GATE_SOFTMAX ? expf(l - mx) : 1.0f / (1.0f + expf(-l));
+  idx[(long)t * K + rank] = s_id[wv][lane];
+  wout[(long)t * K + rank] = sum > 0.0f ? z / sum : 1.0f / (float)K;
 }
 
 // Top-K with the permute's chunk ranking fused in, for E <= 32 with E a
@@ -114,7 +151,7 @@ __global__ __launch_bounds__(NW * kWave) void topk_rank_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T,
     int E, int K, int gate, int nbits, int32_t* __restrict__ idx,
     float* __restrict__ wout, int32_t* __restrict__ block_hist,
-    int32_t* __restrict__ rank) {
+    int32_t* __restrict__ rank, int G, long pstride, float* __restrict__ lout) {
   constexpr int CT = NW * kWave;  // tokens of the chunk (= kPermChunk / K)
   constexpr int KC = kPermChunk / CT;  // = K
   constexpr int NQ = EP / 4;
@@ -130,6 +167,25 @@ __global__ __launch_bounds__(NW * kWave) void topk_rank_kernel(
       const int c = min(4 * q, E - 4);
       v[q] = *(const f32x4*)(L + c);
       bv[q] = bias ? *(const f32x4*)(bias + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (G > 1) {  // (as the wave kernel: all loads first, then in order)
+      f32x4 pv[kRouterMaxSplit - 1][NQ];
+#pragma unroll
+      for (int g = 1; g < kRouterMaxSplit; ++g)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          pv[g - 1][q] = *(const f32x4*)(L + min(g, G - 1) * pstride + min(4 * q, E - 4));
+#pragma unroll
+      for (int g = 1; g < kRouterMaxSplit; ++g)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[q][i] = g < G ? v[q][i] + pv[g - 1][q][i] : v[q][i];
+    }
+    if (G > 1) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if (4 * q < E) *(f32x4*)(lout + t * E + 4 * q) = v[q];
     }
     uint32_t key[EP];
 #pragma unroll
@@ -188,14 +244,15 @@ template <int NW>
 hipError_t launch_topk_rank_nw(const float* logits, const float* bias, int T,
                                int E, int K, int gate, int nbits, int32_t* idx,
                                float* w, int32_t* block_hist, int32_t* rank,
-                               hipStream_t s) {
+                               int G, float* lout, hipStream_t s) {
   const dim3 grid((unsigned)((T + NW * kWave - 1) / (NW * kWave))), block(NW * kWave);
+  const long ps = (long)T * E;
   if (E <= 8)
-    hipLaunchKernelGGL((topk_rank_kernel<NW, 8>), grid, block, 0, s, logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank);
+    hipLaunchKernelGGL((topk_rank_kernel<NW, 8>), grid, block, 0, s, logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, G, ps, lout);
   else if (E <= 16)
-    hipLaunchKernelGGL((topk_rank_kernel<NW, 16>), grid, block, 0, s, logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank);
+    hipLaunchKernelGGL((topk_rank_kernel<NW, 16>), grid, block, 0, s, logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, G, ps, lout);
   else
-    hipLaunchKernelGGL((topk_rank_kernel<NW, 32>), grid, block, 0, s, logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank);
+    hipLaunchKernelGGL((topk_rank_kernel<NW, 32>), grid, block, 0, s, logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, G, ps, lout);
   return hipGetLastError();
 }
 
@@ -210,34 +267,38 @@ bool topk_rank_supported(int E, int K) {
 
 hipError_t launch_topk_rank(const float* logits, const float* bias, int T,
                             int E, int K, int gate, int32_t* idx, float* w,
-                            int32_t* block_hist, int32_t* rank, hipStream_t s) {
+                            int32_t* block_hist, int32_t* rank, hipStream_t s,
+                            int G, float* lout) {
+  if (G < 1 || G > kRouterMaxSplit || (G > 1 && !lout)) return hipErrorInvalidValue;
   if (!topk_rank_supported(E, K)) return hipErrorNotSupported;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   switch (kPermChunk / K / kWave) {  // waves per workgroup: 16 / K
-    case 16: return launch_topk_rank_nw<16>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, s);
-    case 8: return launch_topk_rank_nw<8>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, s);
-    case 4: return launch_topk_rank_nw<4>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, s);
-    case 2: return launch_topk_rank_nw<2>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, s);
-    default: return launch_topk_rank_nw<1>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, s);
+    case 16: return launch_topk_rank_nw<16>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, G, lout, s);
+    case 8: return launch_topk_rank_nw<8>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, G, lout, s);
+    case 4: return launch_topk_rank_nw<4>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, G, lout, s);
+    case 2: return launch_topk_rank_nw<2>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, G, lout, s);
+    default: return launch_topk_rank_nw<1>(logits, bias, T, E, K, gate, nbits, idx, w, block_hist, rank, G, lout, s);
   }
 }
 
 hipError_t launch_topk(const float* logits, const float* bias, int T, int E,
-                       int K, int gate, int32_t* idx, float* w,
-                       hipStream_t s) {
+                       int K, int gate, int32_t* idx, float* w, hipStream_t s,
+                       int G, float* lout) {
+  if (G < 1 || G > kRouterMaxSplit || (G > 1 && !lout)) return hipErrorInvalidValue;
   const dim3 grid((T + 3) / 4), block(256);
   const int cpl = (E + kWave - 1) / kWave;
+  const long ps = (long)T * E;
   if (cpl <= 1)
-    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, bias, T, E, K, gate, idx, w);
+    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, bias, T, E, K, gate, idx, w, G, ps, lout);
   else if (cpl <= 2)
-    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, bias, T, E, K, gate, idx, w);
+    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, bias, T, E, K, gate, idx, w, G, ps, lout);
   else if (cpl <= 4)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, bias, T, E, K, gate, idx, w);
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, bias, T, E, K, gate, idx, w, G, ps, lout);
   else if (cpl <= 8)
-    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, bias, T, E, K, gate, idx, w);
+    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, bias, T, E, K, gate, idx, w, G, ps, lout);
   else
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, bias, T, E, K, gate, idx, w);
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, bias, T, E, K, gate, idx, w, G, ps, lout);
   return hipGetLastError();
 }
 

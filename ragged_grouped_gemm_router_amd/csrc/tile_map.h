@@ -33,7 +33,9 @@ struct Tile {
 //
 // Contraction-grouped products (kSchedK): every (group, row tile, column
 // tile) of G fixed-size [M, N] outputs; group g contracts over
-// [off[g] * kmul, off[g + 1] * kmul).
+// [off[g] * kmul, off[g + 1] * kmul), or, with no offsets (a split of one
+// contraction into G partial products), over [g * kmul, min(K, (g + 1) *
+// kmul)), empty past K.
 template <int BM, int BN, int SCHED, int TAIL = 0>
 __host__ __device__ inline bool decode_tile(const GemmParams& p, int block,
                                             int grid, Tile& t) {
@@ -91,8 +93,13 @@ __host__ __device__ inline bool decode_tile(const GemmParams& p, int block,
   t.n0 = (rem % tiles_n) * BN;
   t.m_end = p.M;
   const int km = p.kmul > 0 ? p.kmul : 1;
-  t.k_beg = p.off[t.g] * km;
-  t.k_end = p.off[t.g + 1] * km;
+  if (p.off) {
+    t.k_beg = p.off[t.g] * km;
+    t.k_end = p.off[t.g + 1] * km;
+  } else {
+    t.k_beg = t.g * km < p.K ? t.g * km : p.K;
+    t.k_end = t.k_beg + km < p.K ? t.k_beg + km : p.K;
+  }
   return true;
 }
 

@@ -129,6 +129,37 @@ void check_k_grouped(int M, int N, const std::vector<int32_t>& off, int kmul) {
   expect_once(seen, "k-grouped coverage", p.G);
 }
 
+// A split contraction (no offsets): G partial products of one [M, N]
+// output, split g over [g * kmul, min(K, (g + 1) * kmul)); together the
+// splits cover [0, K) once, and every (split, row tile, column tile) is
+// decoded once.
+template <int BM, int BN>
+void check_k_split(int M, int N, int K, int G, int kmul) {
+  GemmParams p{};
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.G = G;
+  p.kmul = kmul;
+  const long grid = launch_grid<BM, BN, kSchedK>(p);
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  std::vector<int> seen((long)G * tm * tn, 0);
+  std::vector<int> kcover(K, 0);
+  for (long b = 0; b < grid; ++b) {
+    Tile t;
+    if (!decode_tile<BM, BN, kSchedK>(p, (int)b, (int)grid, t)) continue;
+    if (t.g < 0 || t.g >= G || t.m0 % BM || t.n0 % BN || t.m0 >= M || t.n0 >= N)
+      fail("split tile", t.g, t.m0, t.n0);
+    if (t.k_beg < 0 || t.k_end > K || t.k_beg > t.k_end)
+      fail("split range", t.g, t.k_beg, t.k_end);
+    if (++seen[((long)t.g * tm + t.m0 / BM) * tn + t.n0 / BN] == 1 &&
+        t.m0 == 0 && t.n0 == 0)
+      for (int k = t.k_beg; k < t.k_end; ++k) ++kcover[k];
+  }
+  expect_once(seen, "split coverage", G);
+  expect_once(kcover, "split contraction coverage", G);
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -199,6 +230,13 @@ int main(int argc, char** argv) {
     const int Mk = 64 * uni(1, 8) + (uni(0, 1) ? 0 : 32);
     check_k_grouped<256, 256>(Mk, pr.N, pr.off, 1);
     check_k_grouped<128, 128>(Mk, pr.N, tile_prefix(pr.counts, 64), 64);
+    // the router GEMM split over its contraction, in the library's tiles
+    // (k-tiles of 64 shared out evenly; some splits may be empty)
+    const int Mr = uni(1, 3000), Nr = uni(1, 300), Kr = 64 * uni(1, 120);
+    const int G = uni(1, 8), kmul = 64 * ((Kr / 64 + G - 1) / G);
+    check_k_split<32, 32>(Mr, Nr, Kr, G, kmul);
+    check_k_split<64, 64>(Mr, Nr, Kr, G, kmul);
+    check_k_split<64, 256>(Mr, Nr, Kr, G, kmul);
   }
   std::printf("OK %d cases, %ld cells checked\n", n_cases, g_checked);
   return 0;
