@@ -20,6 +20,8 @@ pytestmark = pytest.mark.gpu
 # and has ragged tails. Shapes mirror the full workloads' structure.
 SMALL = [
     mi.TINY_FP32,
+    # ~512 rows per expert: big tiles whose ragged last tile skips its
+    # empty 32-row blocks (groups below 1024 rows)
     mi.MoEConfig("mixtral_like_T2048_d256_f512_E8_K2", 2048, 256, 512, 8, 2),
     mi.MoEConfig("mixtral_like_f32_T512_d128_f192_E8_K2", 512, 128, 192, 8, 2,
                  dtype="f32"),
