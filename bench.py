@@ -37,11 +37,11 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (the fp32 path runs on VALU)
 # the kernel built from sources with this digest and nothing else.
 GEMM1_TRAFFIC = {
     "workload": "mixtral8x7b_T8192_d4096_f14336_E8_K2",
-    "src_digest": "585266f5d97b8fd2",
-    "fetch_bytes": 7_964_329_088,
+    "src_digest": "16a40acd2ccf7e5c",
+    "fetch_bytes": 8_034_385_920,
     "write_bytes": 469_762_048,
 }
-GEMM_SOURCES = ("gemm_mfma.hip", "common.h", "gemm.h")
+GEMM_SOURCES = ("gemm_mfma.hip", "common.h", "gemm.h", "tile_map.h")
 
 
 def gemm_src_digest():
