@@ -37,8 +37,8 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (the fp32 path runs on VALU)
 # the kernel built from sources with this digest and nothing else.
 GEMM1_TRAFFIC = {
     "workload": "mixtral8x7b_T8192_d4096_f14336_E8_K2",
-    "src_digest": "16a40acd2ccf7e5c",
-    "fetch_bytes": 8_034_385_920,
+    "src_digest": "1933e98e684d8fd0",
+    "fetch_bytes": 7_923_828_736,
     "write_bytes": 469_762_048,
 }
 GEMM_SOURCES = ("gemm_mfma.hip", "common.h", "gemm.h", "tile_map.h")
@@ -416,6 +416,24 @@ def main():
                                   "p90": round(float(q[2]), 4),
                                   "n": len(step_ms)}
     line["graph_replay"] = graph
+    if args.mxfp8:
+        # the MXFP8 layer against the bf16 one on the same batch (both from
+        # this library, outside the timed region; the bf16 layer is held
+        # to the exact fp64 oracle within 1e-2 by the parity tests)
+        dbf = B.make_desc(cfg.T, cfg.d, cfg.f, cfg.E, cfg.K, cfg.f_shared,
+                          cfg.gate, cfg.dtype)
+        bb = {k: v for k, v in batches[0].items() if k not in ("mx", "mx_bwd")}
+        fb = L.alloc_forward(dbf, dev, gather=args.gather)
+        L.forward(dbf, bb, fb)
+        torch.cuda.synchronize()
+        ref = fb["out"].double()
+        err = ((bufs[0]["out"].double() - ref).abs().max() /
+               ref.abs().max()).item()
+        line["mxfp8_error"] = {
+            "max_rel_err_vs_bf16_layer": round(err, 5),
+            "what": "max|out_mxfp8 - out_bf16| / max|out_bf16| over the "
+                    "whole output of batch 0"}
+        del fb
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(cfg, base, bufs[0]["logits"],

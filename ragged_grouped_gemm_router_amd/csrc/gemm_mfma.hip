@@ -1249,11 +1249,12 @@ hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
   // per SIMD, each holding 128 x 64 (128 x 32 x 2) in accumulators, or over
   // 4 waves, one per SIMD, each holding 128 x 128 (128 x 64 x 2). Eight
   // waves hide latency better and win for bf16; the single-B MXFP8 product
-  // takes four (its 8-wave form runs out of registers and spills), the dual
-  // one always eight (its 4-wave form spills).
+  // takes four (its 8-wave form runs out of registers and spills); the dual
+  // products always take eight (their 4-wave forms spill, so they are not
+  // built).
   if (big) {
     const int forced = big_tile_waves();
-    constexpr bool can4 = !(MX && DUAL);
+    constexpr bool can4 = !DUAL;
     if (can4 && (forced == 4 || (forced == 0 && MX && !DUAL))) {
       // (the single-B MXFP8 product: its partial last round split as below)
       if constexpr (MX && !DUAL) {
