@@ -180,9 +180,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral",
                     choices=["mixtral", "deepseek", "skewed", "qwen", "tiny"])
-    ap.add_argument("--cpu-tokens", type=int, default=6144,
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens of the workload the fp64 oracle runs for the "
-                         "CPU baseline (about 10 s on 16 host cores)")
+                         "CPU baseline, at most all of them (the whole "
+                         "Mixtral-shaped workload: about 7 s on 16 host cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph-replays", type=int, default=20,
                     help="after the timed steps, replay the step captured in "
@@ -437,7 +438,7 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(cfg, base, bufs[0]["logits"],
-                                            args.cpu_tokens)
+                                            min(args.cpu_tokens, cfg.T))
     print(json.dumps(line), flush=True)
 
 
