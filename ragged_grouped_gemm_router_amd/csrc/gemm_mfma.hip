@@ -1248,39 +1248,31 @@ hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
   // big: 256 x 256 outputs (256 x 128 x 2 dual), either over 8 waves, two
   // per SIMD, each holding 128 x 64 (128 x 32 x 2) in accumulators, or over
   // 4 waves, one per SIMD, each holding 128 x 128 (128 x 64 x 2). Eight
-  // waves hide latency better and win for bf16; the single-B MXFP8 product
-  // takes four (its 8-wave form runs out of registers and spills); the dual
-  // products always take eight (their 4-wave forms spill, so they are not
-  // built).
+  // waves hide latency better and win (the single-B MXFP8 product too,
+  // since its scale words take one 32-bit offset per block: MXFP8 GEMM 2
+  // 0.915 -> 0.88 ms and the MX dgrad2 1.86 -> 1.57 ms on the Mixtral
+  // shape); the 4-wave single-B forms remain for comparison
+  // (MOE_BIG_TILE_WAVES=4), and the dual products' 4-wave forms, which
+  // spill, are not built.
   if (big) {
     const int forced = big_tile_waves();
     constexpr bool can4 = !DUAL;
-    if (can4 && (forced == 4 || (forced == 0 && MX && !DUAL))) {
-      // (the single-B MXFP8 product: its partial last round split as below)
-      if constexpr (MX && !DUAL) {
-        if (forced == 0 && p.slots != 0 && p.off) {
-          GemmParams q = p;
-          if (q.slots < 0) q.slots = num_cus();
-          hipError_t e = launch_dl<256, 256, 2, 2, 2, false, EPI, TO, MX,
-                                   kSchedM, 1, false, false, 3>(q, s);
-          if (e != hipSuccess) return e;
-          return launch_dl<128, 128, 2, 2, 2, false, EPI, TO, MX, kSchedM, 2>(q, s);
-        }
-      }
+    if (can4 && forced == 4) {
       if constexpr (can4)
         return launch_dl<256, DUAL ? 128 : 256, 2, 2, 2, DUAL, EPI, TO, MX>(p, s);
     }
-    // bf16 row-grouped products: a partial last round of big tiles runs
-    // as quarter tiles (128 x 128, or 128 x 64 x 2 dual) in a second launch
+    // Row-grouped products (all but the dual MXFP8 one): a partial last
+    // round of big tiles runs as quarter tiles (128 x 128, or 128 x 64 x 2
+    // dual) in a second launch.
     // B runs in a 3-stage ring of its own (A in 2, all 160 KB of LDS), so
     // two k-tiles of weights are in flight. Groups of about half a tile
     // (SKIP) stream their weights with too little MFMA work per k-tile to
     // cover one k-tile of HBM latency (measured on the DeepSeek-V3 shape:
     // GEMM 1 3.37 -> 3.12 ms); the full tiles gain less (Mixtral-shaped
     // GEMM 2 1.75 -> 1.69 ms, GEMM 1 3.38 -> 3.36 ms; MXFP8 GEMM 2
-    // 1.24 -> 1.18 ms, with the single-B 4-wave tile above)
+    // 1.24 -> 1.18 ms, measured on its 4-wave tile)
     constexpr int SB = 3;
-    if constexpr (!MX) {
+    if constexpr (!MX || !DUAL) {  // (the dual MXFP8 product gained nothing)
       if (p.slots != 0 && p.off) {
         GemmParams q = p;
         if (q.slots < 0) q.slots = num_cus();
