@@ -22,6 +22,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
+#include <utility>
 
 #include "gemm.h"
 #include "mx.h"
@@ -66,6 +67,34 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const char* a) {
 // 16 bytes per lane from r + voff + soff into LDS at dst + 16 * lane. (A
 // plain function: called straight from a kernel template, the builtin
 // keeps clang's host pass from emitting that kernel's launch stub.)
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1 in order: a loop
+// whose index is a constant expression in the body
+template <typename Fn, int... I>
+__device__ __forceinline__ void static_for_seq(Fn&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// Tile barrier of the direct-to-LDS kernels: this wave's LDS reads are
+// complete and at most N of its loads are outstanding (vmcnt N, lgkmcnt 0),
+// then all waves meet. Loads complete in issue order, so N = the loads
+// issued after the newest ones the next stage needs. Before the barrier
+// only a compiler barrier keeps LDS accesses in place: a release fence
+// would also wait for every DMA write to LDS (vmcnt 0), including the
+// newest ones left in flight on purpose, into a stage no wave reads before
+// a later barrier. The acquire fence keeps later LDS reads below it.
+template <int N>
+__device__ __forceinline__ void tile_barrier() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void dma16(Rsrc r, char* dst, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
@@ -682,15 +711,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     }
   };
 
-  // Tile barrier: this wave's LDS reads and DMA writes are complete (vmcnt
-  // and lgkmcnt at the given counts), then all waves meet. The fences order
-  // LDS accesses around the barrier without waiting for other memory.
   auto barrier_after = [&](auto vm_left) {
-    constexpr int n = decltype(vm_left)::value;
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    tile_barrier<decltype(vm_left)::value>();
   };
 
   // Prologue: (scales of k-tile 0,) k-tiles 0 .. S-1 in flight, and the
@@ -700,6 +722,15 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // before the B DMA of tile kt+2 (here: of tile 2), so that one is still
   // the newest outstanding load at the tile barrier.
   constexpr int NSC_RING = RING_B && MX ? NSC : 0;
+  // SPREAD (B ring one stage deeper than A's): the B DMA of k-tile
+  // kt + S_B - 1 goes into the B stage that tile kt - 1 used, free since the
+  // barrier that ended tile kt - 1, and is spread over the regions of
+  // substeps 0 .. KS-2 of tile kt; the region after a tile barrier then
+  // issues only A's DMA, half the burst (a whole k-tile's DMA at once
+  // outruns the CU's load path, and both waves of a SIMD stall behind it).
+  // The barrier's wait is unchanged: the newest NBL loads at the end of
+  // tile kt are still B's, of k-tile kt + S_B - 1.
+  constexpr bool SPREAD = RING_B;
   if (nk > 0) {  // (an empty group's tile writes zeros)
   load_scales(RING_B ? s_cur : s_nxt, 0);
 #pragma unroll
@@ -708,11 +739,14 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     for (int d = 0; d < N_LOAD; ++d)
       issue_one(min(i, nk - 1), i, min(i, nk - 1), i, d);
   if constexpr (RING_B) load_scales(s_nxt, min(1, nk - 1));
+  if constexpr (!SPREAD) {
 #pragma unroll
-  for (int i = S; i < S_B; ++i)
+    for (int i = S; i < S_B; ++i)
 #pragma unroll
-    for (int d = A_INS; d < N_LOAD; ++d) issue_one(0, 0, min(i, nk - 1), i, d);
-  barrier_after(std::integral_constant<int, (S - 1) * N_LOAD + NSC_RING + (S_B - S) * NBL>{});
+      for (int d = A_INS; d < N_LOAD; ++d) issue_one(0, 0, min(i, nk - 1), i, d);
+  }
+  barrier_after(std::integral_constant<int, (S - 1) * N_LOAD + NSC_RING +
+                                                (SPREAD ? 0 : (S_B - S) * NBL)>{});
   if constexpr (MX && !RING_B) {
 #pragma unroll
     for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
@@ -739,29 +773,36 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // stage of k-tile kt (kt mod S) and of k-tile kt + 1, kept as counters
   int st = 0, st_next = S > 1 ? 1 : 0;
   int sbt = 0, sbt_next = 1;  // the same for the B ring
+  int sbt_prev = S_B - 1;     // B stage of k-tile kt - 1
   for (int kt = 0; kt < nk; ++kt) {
     const char* sa = lds + st * A_STRIDE;
     const char* sa_next = lds + st_next * A_STRIDE;
     const char* sbb = lds + B_BASE + sbt * B_STRIDE;
     const char* sbb_next = lds + B_BASE + sbt_next * B_STRIDE;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    static_for<KS>([&](auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
       Frags& cur = (ks & 1) ? fb : fa;
       Frags& nxt = (ks & 1) ? fa : fb;
-      const bool last = ks + 1 == KS;
-      // memory ops of this region: N_READ reads (+ N_LOAD DMAs if last)
+      constexpr bool last = ks + 1 == KS;
+      // memory ops of this region: N_READ reads and the DMA instructions
+      // [d_lo, d_hi) of a k-tile (all N_LOAD at the last substep, or with
+      // SPREAD A's there and a share of B's at each earlier substep)
       constexpr int NM_MAX = N_READ + N_LOAD;
-      const int nm = last ? NM_MAX : N_READ;
+      constexpr int d_lo = !SPREAD || last ? 0 : A_INS + ks * NBL / (KS - 1);
+      constexpr int d_hi = !SPREAD ? (last ? N_LOAD : 0)
+                           : last  ? A_INS
+                                   : A_INS + (ks + 1) * NBL / (KS - 1);
+      constexpr int nm = N_READ + d_hi - d_lo;
       substep_scales(ks);
       MOE_FENCE();
 #pragma unroll
       for (int q = 0; q < H; ++q) mfma_one(cur, q);
       MOE_FENCE();
-      if (ks == 0 && !RING_B) {
+      if constexpr (ks == 0 && !RING_B) {
         load_scales(s_nxt, min(kt + 1, nk - 1));
         MOE_FENCE();
       }
-      if (last) {
+      if constexpr (last) {
         // Branch-free so the wait counters stay exact: past the last tile
         // the reads return unused data and the DMA fetches the last k-tile
         // again into a stage that is no longer read.
@@ -781,17 +822,19 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 #pragma unroll
         for (int mm = 0; mm < NM_MAX; ++mm) {
           if (mm < m || mm >= m_end) continue;
-          if (!last) {
-            read_one(sa, sbb, ks + 1, nxt, mm);
-          } else {
-            // reads spread evenly among the DMAs: op mm is a read iff the
-            // running read quota floor(x * N_READ / NM_MAX) steps at it
-            const int rb = mm * N_READ / NM_MAX;
-            if ((mm + 1) * N_READ / NM_MAX != rb)
+          // reads spread evenly among the DMAs: op mm is a read iff the
+          // running read quota floor(x * N_READ / nm) steps at it
+          const int rb = mm * N_READ / nm;
+          if ((mm + 1) * N_READ / nm != rb) {
+            if constexpr (last)
               read_one(sa_next, sbb_next, 0, nxt, rb);
             else
-              issue_one(min(kt + S, nk - 1), st, min(kt + S_B, nk - 1), sbt,
-                        mm - rb);
+              read_one(sa, sbb, ks + 1, nxt, rb);
+          } else if constexpr (last) {
+            issue_one(min(kt + S, nk - 1), st, min(kt + S_B, nk - 1), sbt,
+                      d_lo + mm - rb);
+          } else {
+            issue_one(0, 0, min(kt + S_B - 1, nk - 1), sbt_prev, d_lo + mm - rb);
           }
           MOE_FENCE();
         }
@@ -799,9 +842,10 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
         mfma_one(cur, q);
         MOE_FENCE();
       }
-    }
+    });
     st = st_next;
     st_next = st_next + 1 == S ? 0 : st_next + 1;
+    sbt_prev = sbt;
     sbt = sbt_next;
     sbt_next = sbt_next + 1 == S_B ? 0 : sbt_next + 1;
   }
@@ -1077,11 +1121,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
                                                            acc[0][i][j], 0, 0, 0);
   };
   auto barrier_after = [&](auto vm_left) {
-    constexpr int n = decltype(vm_left)::value;
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    tile_barrier<decltype(vm_left)::value>();
   };
 
   if (nk > 0) {
