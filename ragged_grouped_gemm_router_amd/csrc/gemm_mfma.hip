@@ -465,7 +465,7 @@ template <> struct Fmt<true> {
 
 template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
           typename TO, bool MX, int SCHED = kSchedM, int TAIL = 0,
-          bool SKIP = false, bool KCAT = false, int SB = 0>
+          int SKIP = 0, bool KCAT = false, int SB = 0>
 __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) {
   using F = Fmt<MX>;
   typedef typename F::Frag Frag;
@@ -690,17 +690,20 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // SKIP: 32-row blocks of this wave that hold rows of the group: a
   // ragged row tile skips the MFMAs of blocks wholly past the group's end
   // (their rows would be clamped copies, never stored); loads and barriers
-  // run unchanged, so every wait count stays exact. For groups of about
-  // half a tile, where it halves the MFMA work; its branches cost the
-  // full tiles of large groups about 1.5%, and a 4-wave tile (256
-  // accumulator registers) would spill.
-  constexpr bool kSkipTail = SKIP && SCHED == kSchedM && N_MFMA * 16 <= 128;
+  // run unchanged, so every wait count stays exact. SKIP 1: one copy of
+  // the k-loop, with a branch per MFMA (groups of about half a tile, where
+  // every tile is ragged). SKIP 2 (large groups, most tiles full): the
+  // k-loop is compiled twice and a wave whose blocks all hold rows runs the
+  // copy without the branches; the dual MXFP8 tile keeps one copy (two
+  // spill). A 4-wave tile, 256 accumulator registers, would spill with the
+  // branches.
+  constexpr bool kSkipTail = SKIP != 0 && SCHED == kSchedM && N_MFMA * 16 <= 128;
   const int act_mb = __builtin_amdgcn_readfirstlane(
       min(MB, max(0, (t.m_end - t.m0 - wm * WM + 31) / 32)));
-  // MFMA q of a substep, q = (o * MB + i) * NB + j
-  auto mfma_one = [&](const Frags& f, int q) {
+  // MFMA q of a substep, q = (o * MB + i) * NB + j; sk: the skipping copy
+  auto mfma_one = [&](const Frags& f, int q, auto sk) {
     const int o = q / (MB * NB), i = (q / NB) % MB, j = q % NB;
-    if (kSkipTail && i >= act_mb) return;
+    if (decltype(sk)::value && i >= act_mb) return;
     if constexpr (MX) {
       acc[o][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           f.a[i], f.b[o][j], acc[o][i][j], 0, 0, 0, (int)sc[i], 0,
@@ -770,6 +773,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // free.)
   constexpr int H = N_MFMA >= 8 ? 2 : N_MFMA >= 2 ? 1 : 0;
 #define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
+  auto kloop = [&](auto sk) {
   // stage of k-tile kt (kt mod S) and of k-tile kt + 1, kept as counters
   int st = 0, st_next = S > 1 ? 1 : 0;
   int sbt = 0, sbt_next = 1;  // the same for the B ring
@@ -796,7 +800,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
       substep_scales(ks);
       MOE_FENCE();
 #pragma unroll
-      for (int q = 0; q < H; ++q) mfma_one(cur, q);
+      for (int q = 0; q < H; ++q) mfma_one(cur, q, sk);
       MOE_FENCE();
       if constexpr (ks == 0 && !RING_B) {
         load_scales(s_nxt, min(kt + 1, nk - 1));
@@ -839,7 +843,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
           MOE_FENCE();
         }
         m = m_end;
-        mfma_one(cur, q);
+        mfma_one(cur, q, sk);
         MOE_FENCE();
       }
     });
@@ -849,6 +853,12 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     sbt = sbt_next;
     sbt_next = sbt_next + 1 == S_B ? 0 : sbt_next + 1;
   }
+  };
+  constexpr bool kTwoCopies = kSkipTail && SKIP == 2 && !(MX && DUAL);
+  if (kSkipTail && (!kTwoCopies || act_mb < MB))
+    kloop(std::integral_constant<bool, kSkipTail>{});
+  else
+    kloop(std::false_type{});
 #undef MOE_FENCE
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load may still target LDS at exit
@@ -1245,7 +1255,7 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 
 template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
           typename TO, bool MX, int SCHED = kSchedM, int TAIL = 0,
-          bool SKIP = false, bool KCAT = false, int SB = 0>
+          int SKIP = 0, bool KCAT = false, int SB = 0>
 hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
   const long tiles = launch_grid<BM, BN, SCHED, TAIL>(p);
   if (tiles <= 0) return hipSuccess;
@@ -1283,7 +1293,7 @@ int num_cus() {
   return cached[dev];
 }
 
-template <bool DUAL, int EPI, typename TO, bool MX = false, bool SKIP = false>
+template <bool DUAL, int EPI, typename TO, bool MX = false, int SKIP = 0>
 hipError_t launch_dl_sized(bool big, const GemmParams& p, hipStream_t s) {
   // big: 256 x 256 outputs (256 x 128 x 2 dual), either over 8 waves, two
   // per SIMD, each holding 128 x 64 (128 x 32 x 2) in accumulators, or over
@@ -1426,13 +1436,16 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
         (op == kOpGemm1 || op == kOpGemm2 || op == kOpDgrad2 || op == kOpDgrad1 ||
          op == kOpGemm1Mx || op == kOpGemm1MxAct))
       big = skip = true;
-    // forward products whose groups average under 4 big tiles: a ragged
-    // last tile is a large share of each group's work, so its empty
-    // blocks' MFMAs are skipped too (Qwen-MoE-like layer, ~546 rows per
-    // expert: GEMM 1 0.52 -> 0.49 ms, GEMM 2 0.57 -> 0.545 ms; from 4096
-    // rows down the branches cost the Mixtral shape 2%)
-    if (big && !skip && p.off && rows_per_group < 1024 &&
-        (op == kOpGemm1 || op == kOpGemm2 || op == kOpGemm1Mx))
+    // bf16 forward products with big groups: each group's ragged last
+    // tile skips its empty blocks' MFMAs too, while the waves of full
+    // tiles run the copy of the k-loop without the skip branches (Mixtral
+    // shape: GEMM 1 3.09 -> 3.02 ms; skewed forward 754 -> 777 TFLOP/s;
+    // Qwen-MoE-like layer, ~546 rows per expert: GEMM 1 0.47 -> 0.44 ms).
+    // The dual MXFP8 tile has one copy, whose per-MFMA branches cost full
+    // tiles about 2%, so there only groups under 4 big tiles take it.
+    if (big && !skip && p.off &&
+        (op == kOpGemm1 || op == kOpGemm2 ||
+         (op == kOpGemm1Mx && rows_per_group < 1024)))
       tskip = true;
     const int bm = op == kOpRouter ? 32 : big ? 256 : 128;
     if (p.off) {
@@ -1484,12 +1497,12 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
         }
         return launch_dl<32, 32, 8, 1, 1, false, kEpiStore, float, false>(p, s);
       case kOpGemm1:
-        if (skip || tskip)
-          return launch_dl_sized<true, kEpiSwiglu, bf16, false, true>(big, p, s);
+        if (skip) return launch_dl_sized<true, kEpiSwiglu, bf16, false, 1>(big, p, s);
+        if (tskip) return launch_dl_sized<true, kEpiSwiglu, bf16, false, 2>(big, p, s);
         return launch_dl_sized<true, kEpiSwiglu, bf16>(big, p, s);
       case kOpGemm2:
-        if (skip || tskip)
-          return launch_dl_sized<false, kEpiStore, bf16, false, true>(big, p, s);
+        if (skip) return launch_dl_sized<false, kEpiStore, bf16, false, 1>(big, p, s);
+        if (tskip) return launch_dl_sized<false, kEpiStore, bf16, false, 2>(big, p, s);
         return launch_dl_sized<false, kEpiStore, bf16>(big, p, s);
       case kOpDgrad2T:
         return launch_dl_sized<false, kEpiSwigluBwd, bf16>(big, p, s);
@@ -1549,10 +1562,10 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
                : launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false, kSchedK>(p, s);
   if (op == kOpGemm1Mx)
     return skip || tskip
-               ? launch_dl_sized<true, kEpiSwigluMx, bf16, true, true>(big, p, s)
+               ? launch_dl_sized<true, kEpiSwigluMx, bf16, true, 1>(big, p, s)
                : launch_dl_sized<true, kEpiSwigluMx, bf16, true>(big, p, s);
   if (op == kOpGemm1MxAct)
-    return skip ? launch_dl_sized<true, kEpiSwiglu, bf16, true, true>(big, p, s)
+    return skip ? launch_dl_sized<true, kEpiSwiglu, bf16, true, 1>(big, p, s)
                 : launch_dl_sized<true, kEpiSwiglu, bf16, true>(big, p, s);
   if (op == kOpDgrad2Mx)
     return launch_dl_sized<false, kEpiSwigluBwd, bf16, true>(big, p, s);
