@@ -1504,7 +1504,11 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
         if (skip) return launch_dl_sized<false, kEpiStore, bf16, false, 1>(big, p, s);
         if (tskip) return launch_dl_sized<false, kEpiStore, bf16, false, 2>(big, p, s);
         return launch_dl_sized<false, kEpiStore, bf16>(big, p, s);
+      // the data gradients skip the ragged last tiles' empty blocks as the
+      // forward products do (the branch-free copy for full tiles)
       case kOpDgrad2T:
+        if (big && p.off)
+          return launch_dl_sized<false, kEpiSwigluBwd, bf16, false, 2>(big, p, s);
         return launch_dl_sized<false, kEpiSwigluBwd, bf16>(big, p, s);
       case kOpDgrad1T:
         if (p.K1 % 64 || p.K != 2 * p.K1) return hipErrorNotSupported;
@@ -1512,11 +1516,14 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
           GemmParams q = p;
           if (q.slots < 0) q.slots = num_cus();
           hipError_t e = launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
-                                   kSchedM, 1, false, true, 3>(q, s);
+                                   kSchedM, 1, 2, true, 3>(q, s);
           if (e != hipSuccess) return e;
           return launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false,
-                           kSchedM, 2, false, true>(q, s);
+                           kSchedM, 2, 2, true>(q, s);
         }
+        if (big && p.off)
+          return launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
+                           kSchedM, 0, 2, true, 3>(p, s);
         return big ? launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
                                kSchedM, 0, false, true, 3>(p, s)
                    : launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false,
