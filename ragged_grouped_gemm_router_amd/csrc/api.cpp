@@ -79,11 +79,6 @@ struct BwdWs {
   void* daT;
   void* dbT;
   long ldT;
-  // weights transposed for the data-gradient products: W2^T [E, d_ff,
-  // d_model], then (reusing its space) W1^T and W3^T [E, d_model, d_ff]
-  void* w2t;
-  void* w1t;
-  void* w3t;
   // MXFP8: dy_perm and [da | db] quantised, h dequantised for dW2
   uint8_t* dyq;
   uint8_t* dys;
@@ -185,13 +180,6 @@ bool wgrad_t_ok(const moe_desc* d) {
          gemm_direct_ok();
 }
 
-// bf16 backward with experts of 512+ rows: the data-gradient products read
-// the weights transposed once per step (the MXFP8 backward takes them
-// transposed and quantised from the caller)
-bool dgrad_t_ok(const moe_desc* d) {
-  return wgrad_t_ok(d) && d->gemm_dtype == MOE_BF16;
-}
-
 size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
   const size_t TK = (size_t)d->T * d->K, b = act_bytes(d->act_dtype);
   size_t o = 0;
@@ -231,12 +219,6 @@ size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
     for (int i = 0; i < 5; ++i) {
       if (t[i]) *t[i] = base + o;
       o = align_up(o + b * rows[i] * ldT);
-    }
-    if (dgrad_t_ok(d)) {
-      if (w) w->w2t = w->w1t = base + o;
-      o = align_up(o + b * (size_t)d->E * f * dm);
-      if (w) w->w3t = base + o;
-      o = align_up(o + b * (size_t)d->E * f * dm);
     }
   }
   if (d->gemm_dtype == MOE_MXFP8) {
@@ -1179,14 +1161,7 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.B = a->routed.w2; p.ldb = f; p.sB = (long)dm * f;
     p.C = w.da; p.C2 = w.db; p.ldc = f;
     p.aux_a = sa; p.aux_b = sb;
-    if (dgrad_t_ok(d)) {  // experts of 512+ rows: W2 transposed once per
-                          // step, so the product reads it k-contiguous
-      MOE_TRY(launch_transpose_batched(a->routed.w2, E, dm, f, w.w2t, s));
-      p.B = w.w2t; p.ldb = dm; p.sB = (long)f * dm;
-      MOE_TRY(gemm_mfma(kOpDgrad2T, p, w.tile_off, s));
-    } else {
-      MOE_TRY(run_gemm(kOpDgrad2, dt, p, w.tile_off, s));
-    }
+    MOE_TRY(run_gemm(kOpDgrad2, dt, p, w.tile_off, s));
   }
   if (shared) {  // ungated: dh_s = dy Ws2, (da_s, db_s) in place of (a_s, b_s)
     GemmParams p = gp();
@@ -1204,15 +1179,8 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     p.A = w.da; p.A2 = w.db; p.lda = f;
     p.B = a->routed.w1; p.B2 = a->routed.w3; p.ldb = dm; p.sB = (long)f * dm;
     p.C = w.dx_perm; p.ldc = dm;
-    if (dgrad_t_ok(d)) {  // W1, W3 transposed (into the space of W2^T)
-      MOE_TRY(launch_transpose_batched(a->routed.w1, E, f, dm, w.w1t, s));
-      MOE_TRY(launch_transpose_batched(a->routed.w3, E, f, dm, w.w3t, s));
-      p.B = w.w1t; p.B2 = w.w3t; p.ldb = f; p.sB = (long)dm * f;
-      p.slots = d->flags & MOE_FLAG_NO_TAIL_SPLIT ? 0 : -1;
-      MOE_TRY(gemm_mfma(kOpDgrad1T, p, w.tile_off, s));
-    } else {
-      MOE_TRY(run_gemm(kOpDgrad1, dt, p, w.tile_off, s));
-    }
+    p.slots = d->flags & MOE_FLAG_NO_TAIL_SPLIT ? 0 : -1;
+    MOE_TRY(run_gemm(kOpDgrad1, dt, p, w.tile_off, s));
   }
   if (shared) {  // dx_s = da_s Ws1 + db_s Ws3
     GemmParams p = gp();

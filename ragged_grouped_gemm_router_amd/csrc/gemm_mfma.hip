@@ -59,8 +59,14 @@ __device__ __forceinline__ Rsrc make_rsrc_n(const void* base, long bytes) {
                                            kBufWord3);
 }
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-// ds_read_b64_tr_b16 (see the backward kernel for the lane layout).
-__device__ __forceinline__ s16x4 lds_read_tr16(const char* a) {
+// ds_read_b64_tr_b16 (lane layout: see the k-major B of the direct-to-LDS
+// kernel). The restrict qualifier gives the inlined read alias-scope
+// metadata, as a plain LDS load carries type-based alias metadata; without
+// it the compiler's wait insertion makes every such read wait for all LDS
+// DMA in flight (vmcnt(0)), which drains the prefetch of the next k-tiles.
+// The kernels order their DMA and fragment reads with explicit waits (the
+// tile barrier).
+__device__ __forceinline__ s16x4 lds_read_tr16(const char* __restrict__ a) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)a);
 }
@@ -465,7 +471,7 @@ template <> struct Fmt<true> {
 
 template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
           typename TO, bool MX, int SCHED = kSchedM, int TAIL = 0,
-          int SKIP = 0, bool KCAT = false, int SB = 0>
+          int SKIP = 0, bool KCAT = false, int SB = 0, bool BKM = false>
 __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) {
   using F = Fmt<MX>;
   typedef typename F::Frag Frag;
@@ -501,6 +507,19 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // kt + 1 in issue order, so that count covers no A load only when the B
   // ring is exactly one stage deeper than A's.
   static_assert(!RING_B || SB == S + 1, "B ring depth must be S + 1");
+  // BKM: B stored k-major, element (n, k) of a group at B[k * ldb + n] (the
+  // weights of the data-gradient products, read as the forward stores
+  // them). A k-tile is DMA'd as it lies: BK k-rows of BN elements, the
+  // 16-byte chunk c of k-row k at position c ^ (4 * (k & 3)), CPK chunks
+  // per k-row and KPI k-rows per 1 KB wave instruction, the same
+  // instruction count as the row-major form. A fragment (32 columns x 16 k)
+  // is two ds_read_b64_tr_b16: within each 16-lane group, lane j points at
+  // k-row kb + j / 4, columns c0 + 4 (j % 4) .. +3, and the read hands lane
+  // i the four k values kb .. kb + 3 of column c0 + i. Rows kb .. kb + 3
+  // then sit in distinct quarters of the 64 banks: conflict-free.
+  static_assert(!BKM || (!MX && !DUAL && SCHED == kSchedM && BN % 128 == 0 &&
+                         BN <= 512), "k-major B");
+  constexpr int CPK = BN / 8, KPI = BKM ? 64 / CPK : 1;
 
   // the epilogue stages 128 rows at a time (the quantising one only for
   // the optional pre-activation copies)
@@ -539,18 +558,25 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     const int src = gather ? p.gsrc[grow] / p.gdiv : grow - t.m0;
     a_off[j] = src * (int)p.lda * F::ES + swz<CPR>(row, phys) * 16;
   }
+  // (k-major B: based at the tile's first column; a lane's chunk past
+  // column N is clamped to the last in-range one, its data reaching only
+  // output columns past N)
+  const long b_base = (long)t.g * p.sB + (BKM ? (long)t.n0 : (long)t.n0 * p.ldb);
   Rsrc rb[NB_OPS];
-  rb[0] = make_rsrc((const char*)p.B +
-                    ((long)t.g * p.sB + (long)t.n0 * p.ldb) * F::ES);
-  if (DUAL)
-    rb[NB_OPS - 1] = make_rsrc((const char*)p.B2 +
-                               ((long)t.g * p.sB + (long)t.n0 * p.ldb) * F::ES);
+  rb[0] = make_rsrc((const char*)p.B + b_base * F::ES);
+  if (DUAL) rb[NB_OPS - 1] = make_rsrc((const char*)p.B2 + b_base * F::ES);
   int b_off[B_INS];
 #pragma unroll
   for (int j = 0; j < B_INS; ++j) {
-    const int row = (j * NW + wave) * RPI + r_in;
-    const int grow = min(t.n0 + row, p.N - 1);
-    b_off[j] = (grow - t.n0) * p.ldb * F::ES + swz<CPR>(row, phys) * 16;
+    if constexpr (BKM) {
+      const int kr = (j * NW + wave) * KPI + lane / CPK;
+      const int c = (lane % CPK) ^ (4 * (kr & 3));
+      b_off[j] = kr * p.ldb * 2 + min(c * 8, p.N - t.n0 - 8) * 2;
+    } else {
+      const int row = (j * NW + wave) * RPI + r_in;
+      const int grow = min(t.n0 + row, p.N - 1);
+      b_off[j] = (grow - t.n0) * p.ldb * F::ES + swz<CPR>(row, phys) * 16;
+    }
   }
   // KCAT: the contraction runs over [A | A2] . [B ; B2], the first K1
   // indices from A, B (k-tiles below nk1) and the rest from A2, B2, all
@@ -560,8 +586,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   Rsrc ra2 = ra, rb2 = rb[0];
   if (KCAT) {
     ra2 = make_rsrc((const char*)p.A2 + (long)t.m0 * p.lda * F::ES);
-    rb2 = make_rsrc((const char*)p.B2 +
-                    ((long)t.g * p.sB + (long)t.n0 * p.ldb) * F::ES);
+    rb2 = make_rsrc((const char*)p.B2 + b_base * F::ES);
   }
 
   // DMA instruction d of a k-tile (d < A_INS: operand A of k-tile kt
@@ -574,7 +599,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
             a_off[d], k0);
     } else {
       const bool second = KCAT && ktb >= nk1;
-      const int k0 = (kt0 + ktb - (second ? nk1 : 0)) * RB;
+      // byte offset of the k-tile: along the row, or BK k-rows down
+      const int k0 = (kt0 + ktb - (second ? nk1 : 0)) * (BKM ? BK * p.ldb * 2 : RB);
       const int o = (d - A_INS) / B_INS, j = (d - A_INS) % B_INS;
       dma16(second ? rb2 : rb[o],
             lds + B_BASE + sbs * B_STRIDE + o * B_BYTES + (j * NW + wave) * 1024,
@@ -645,6 +671,29 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   const int lrow = lane % 32, half = lane / 32, sw = swz<CPR>(lrow, 0);
   const int a_row0 = (wm * WM + lrow) * RB;
   const int b_row0 = (wn * WN + lrow) * RB;
+  // k-major B: the lane's byte offset in the stage for block j at substep
+  // 0 (the substep and the second read add k-row multiples, immediates)
+  int bkm_off[BKM ? NB : 1];
+  if constexpr (BKM) {
+    const int grp = lane / 16, gj = lane % 16;
+    const int kl = 8 * (grp >> 1) + (gj >> 2);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int c = wn * WN + j * 32 + 16 * (grp & 1) + 4 * (gj & 3);
+      bkm_off[j] = kl * (BN * 2) + (((c >> 3) ^ (4 * (kl & 3))) * 16) + (c & 7) * 2;
+    }
+  }
+  auto read_bkm = [&](const char* sbo, int j, int ks) {
+    Frag f{};
+    if constexpr (BKM) {
+      const char* q = sbo + bkm_off[j] + ks * 16 * (BN * 2);
+      const s16x4 v0 = lds_read_tr16(q), v1 = lds_read_tr16(q + 4 * (BN * 2));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 w = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      f = __builtin_bit_cast(Frag, w);
+    }
+    return f;
+  };
   auto read_frag = [&](const char* rowp, int ks) {
     if constexpr (MX) {
       // The scaled MFMA takes bytes 0-15 of a lane from the substep's first
@@ -675,7 +724,10 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
       f.a[r] = read_frag(sa + a_row0 + r * 32 * RB, ks);
     } else {
       const int o = (r - MB) / NB, j = (r - MB) % NB;
-      f.b[o][j] = read_frag(sbb + b_row0 + o * B_BYTES + j * 32 * RB, ks);
+      if constexpr (BKM)
+        f.b[o][j] = read_bkm(sbb + o * B_BYTES, j, ks);
+      else
+        f.b[o][j] = read_frag(sbb + b_row0 + o * B_BYTES + j * 32 * RB, ks);
     }
   };
   // per-lane E8M0 scale operands of one substep: block ks*2 + lane/32
@@ -1255,12 +1307,12 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 
 template <int BM, int BN, int S, int WGM, int WGN, bool DUAL, int EPI,
           typename TO, bool MX, int SCHED = kSchedM, int TAIL = 0,
-          int SKIP = 0, bool KCAT = false, int SB = 0>
+          int SKIP = 0, bool KCAT = false, int SB = 0, bool BKM = false>
 hipError_t launch_dl(const GemmParams& p, hipStream_t s) {
   const long tiles = launch_grid<BM, BN, SCHED, TAIL>(p);
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, S, WGM, WGN, DUAL, EPI, TO, MX, SCHED, TAIL, SKIP, KCAT, SB>),
+  hipLaunchKernelGGL((mfma_gemm_dl<BM, BN, S, WGM, WGN, DUAL, EPI, TO, MX, SCHED, TAIL, SKIP, KCAT, SB, BKM>),
                      dim3((unsigned)tiles), dim3(WGM * WGN * kWave), 0, s, p);
   return hipGetLastError();
 }
@@ -1504,49 +1556,51 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
         if (skip) return launch_dl_sized<false, kEpiStore, bf16, false, 1>(big, p, s);
         if (tskip) return launch_dl_sized<false, kEpiStore, bf16, false, 2>(big, p, s);
         return launch_dl_sized<false, kEpiStore, bf16>(big, p, s);
-      // the data gradients skip the ragged last tiles' empty blocks as the
-      // forward products do (the branch-free copy for full tiles)
-      case kOpDgrad2T:
-        if (big && p.off)
-          return launch_dl_sized<false, kEpiSwigluBwd, bf16, false, 2>(big, p, s);
-        return launch_dl_sized<false, kEpiSwigluBwd, bf16>(big, p, s);
-      case kOpDgrad1T:
-        if (p.K1 % 64 || p.K != 2 * p.K1) return hipErrorNotSupported;
-        if (big && p.slots != 0 && p.off) {  // split last round, as GEMM 2
-          GemmParams q = p;
-          if (q.slots < 0) q.slots = num_cus();
-          hipError_t e = launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
-                                   kSchedM, 1, 2, true, 3>(q, s);
-          if (e != hipSuccess) return e;
-          return launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false,
-                           kSchedM, 2, 2, true>(q, s);
-        }
-        if (big && p.off)
-          return launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
-                           kSchedM, 0, 2, true, 3>(p, s);
-        return big ? launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
-                               kSchedM, 0, false, true, 3>(p, s)
-                   : launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false,
-                               kSchedM, 0, false, true>(p, s);
       default:
         break;
+    }
+  }
+  // Data gradients from the weights as stored (k-major B) on the forward's
+  // direct-to-LDS kernel: B ring, spread DMA, empty-block skip and split
+  // last round as there, the B fragments read with transposing LDS reads
+  // (DeepSeek-V3 shape: dgrad2 2.80 -> 1.68 ms, dgrad1 4.78 -> 3.31 ms
+  // against the transposing-read backward kernel; Mixtral shape: the same
+  // speed as from weights transposed once per step, whose transposes, 1 ms
+  // per step, it saves). The k-tile offset rides in a 32-bit scalar, so
+  // one part's k rows of one group's weights span under 2 GiB.
+  if (!force_staged() && (op == kOpDgrad2 || op == kOpDgrad1) && p.ldb % 8 == 0 &&
+      (long)(op == kOpDgrad1 ? p.K1 : p.K) * p.ldb * 2 <= INT_MAX) {
+    if (op == kOpDgrad2 && p.K % 64 == 0) {
+      if (skip)
+        return launch_dl<256, 256, 2, 2, 4, false, kEpiSwigluBwd, bf16, false,
+                         kSchedM, 0, 1, false, 3, true>(p, s);
+      return big ? launch_dl<256, 256, 2, 2, 4, false, kEpiSwigluBwd, bf16, false,
+                             kSchedM, 0, 2, false, 3, true>(p, s)
+                 : launch_dl<128, 128, 2, 2, 2, false, kEpiSwigluBwd, bf16, false,
+                             kSchedM, 0, 0, false, 0, true>(p, s);
+    }
+    if (op == kOpDgrad1 && p.K1 % 64 == 0 && p.K == 2 * p.K1) {
+      if (skip)
+        return launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
+                         kSchedM, 0, 1, true, 3, true>(p, s);
+      if (big && p.slots != 0 && p.off) {  // split last round, as GEMM 2
+        GemmParams q = p;
+        if (q.slots < 0) q.slots = num_cus();
+        hipError_t e = launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
+                                 kSchedM, 1, 2, true, 3, true>(q, s);
+        if (e != hipSuccess) return e;
+        return launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false,
+                         kSchedM, 2, 2, true, 0, true>(q, s);
+      }
+      return big ? launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false,
+                             kSchedM, 0, 2, true, 3, true>(p, s)
+                 : launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false,
+                             kSchedM, 0, 0, true, 0, true>(p, s);
     }
   }
   // backward products on the direct-to-LDS kernel with k-major operands
   if (!force_staged()) {
     const bool w4 = big_tile_waves() == 4;
-    if (skip && op == kOpDgrad2 && p.K % 64 == 0)
-      return launch_t<256, 256, 2, 4, false, true, false, kEpiSwigluBwd, kSchedM, true>(p, s);
-    if (skip && op == kOpDgrad1 && p.K1 % 64 == 0 && p.K == 2 * p.K1)
-      return launch_t<256, 256, 2, 4, false, true, true, kEpiStore, kSchedM, true>(p, s);
-    if (op == kOpDgrad2 && p.K % 64 == 0)
-      return !big ? launch_t<128, 128, 2, 2, false, true, false, kEpiSwigluBwd, kSchedM>(p, s)
-             : w4 ? launch_t<256, 256, 2, 2, false, true, false, kEpiSwigluBwd, kSchedM>(p, s)
-                  : launch_t<256, 256, 2, 4, false, true, false, kEpiSwigluBwd, kSchedM>(p, s);
-    if (op == kOpDgrad1 && p.K1 % 64 == 0 && p.K == 2 * p.K1)
-      return !big ? launch_t<128, 128, 2, 2, false, true, true, kEpiStore, kSchedM>(p, s)
-             : w4 ? launch_t<256, 256, 2, 2, false, true, true, kEpiStore, kSchedM>(p, s)
-                  : launch_t<256, 256, 2, 4, false, true, true, kEpiStore, kSchedM>(p, s);
     if (op == kOpWgrad)
       return !big ? launch_t<128, 128, 2, 2, true, true, false, kEpiStore, kSchedK>(p, s)
              : w4 ? launch_t<256, 256, 2, 2, true, true, false, kEpiStore, kSchedK>(p, s)

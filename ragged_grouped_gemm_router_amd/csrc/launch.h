@@ -71,10 +71,6 @@ hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y,
                               void* dy_perm, float* d_w, int T, int K, int d,
                               hipStream_t s);
 
-// dst[b, c, r] = src[b, r, c] for B matrices [R, C] of bf16 (R and C
-// multiples of 64).
-hipError_t launch_transpose_batched(const void* src, int B, int R, int C,
-                                    void* dst, hipStream_t s);
 // Per-expert transpose with zero padding to 64 rows: src [rows, C] bf16 ->
 // dst [C, ldd], expert e's rows at columns 64 * t64[e] ... (C % 64 == 0,
 // ldd >= 64 * (rows_max / 64 + E + 1)).

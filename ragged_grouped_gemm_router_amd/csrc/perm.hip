@@ -460,33 +460,6 @@ int perm_nbits(int E) {
   return nbits;
 }
 
-// dst[b, c, r] = src[b, r, c] (R, C multiples of 64). Each wave moves a
-// 64 x 64 block of matrix blockIdx.z (rows 64 * blockIdx.y, columns
-// 64 * (4 * blockIdx.x + wave)): lane l loads the 8 x 8 piece at rows
-// 8 (l % 8), columns 8 (l / 8) as eight 16-byte row pieces, transposes it
-// in registers and stores eight 16-byte pieces, so every load and store
-// instruction of the wave covers 128-byte contiguous segments.
-__global__ __launch_bounds__(256) void transpose_batched_kernel(
-    const bf16* __restrict__ src, int R, int C, bf16* __restrict__ dst) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int cblk = blockIdx.x * 4 + wave;
-  if (cblk * 64 >= C) return;
-  const long base = (long)blockIdx.z * R * C;
-  const int r = blockIdx.y * 64 + (lane % 8) * 8;
-  const int c = cblk * 64 + (lane / 8) * 8;
-  bf16x8 v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    v[i] = *(const bf16x8*)(src + base + (long)(r + i) * C + c);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    bf16x8 o;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = v[i][j];
-    *(bf16x8*)(dst + base + (long)(c + j) * R + r) = o;
-  }
-}
-
 // Transpose with per-group padding: for each expert e with rows
 // [off[e], off[e+1]) of src [rows, C] (bf16), dst[c, 64 * t64[e] + i] =
 // src[off[e] + i, c] for i < count_e, and zero up to the next multiple of
@@ -520,15 +493,6 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(
 }
 
 }  // namespace
-
-hipError_t launch_transpose_batched(const void* src, int B, int R, int C,
-                                    void* dst, hipStream_t s) {
-  if (B <= 0 || R <= 0 || C <= 0) return hipSuccess;
-  if (R % 64 || C % 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(transpose_batched_kernel, dim3((C / 64 + 3) / 4, R / 64, B), dim3(256),
-                     0, s, (const bf16*)src, R, C, (bf16*)dst);
-  return hipGetLastError();
-}
 
 hipError_t launch_transpose_pad(const void* src, int rows_max, int C,
                                 const int32_t* off, const int32_t* t64, int E,
