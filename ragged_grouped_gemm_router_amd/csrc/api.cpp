@@ -70,15 +70,6 @@ struct BwdWs {
   void* sh;
   void* sdx;
   int32_t* srange;
-  // bf16 weight gradients from transposed operands, each expert's rows
-  // padded to 64 (ld = ldT): x_perm^T, dy_perm^T [d, ldT], h^T, da^T, db^T
-  // [f, ldT]
-  void* xT;
-  void* dyT;
-  void* hT;
-  void* daT;
-  void* dbT;
-  long ldT;
   // MXFP8: dy_perm and [da | db] quantised, h dequantised for dW2
   uint8_t* dyq;
   uint8_t* dys;
@@ -162,24 +153,6 @@ size_t fwd_ws_layout(const moe_desc* d, char* base, FwdWs* w) {
   return o;
 }
 
-// The weight gradients (bf16, in the MXFP8 backward too) run on the
-// direct-to-LDS kernel from transposed operands when the widths allow and
-// the experts average at least 512
-// rows (eight k-tiles; with fewer, the transposes and the pipeline fill
-// cost more than the faster loop saves). MOE_WGRAD_T=0 keeps the
-// transposing-read kernel, for comparison.
-bool wgrad_t_ok(const moe_desc* d) {
-  static const bool env_off = [] {
-    const char* e = tuning_env("MOE_WGRAD_T");
-    return e && strcmp(e, "0") == 0;
-  }();
-  return d->act_dtype == MOE_BF16 &&
-         (d->gemm_dtype == MOE_BF16 || d->gemm_dtype == MOE_MXFP8) &&
-         d->d_model % 64 == 0 && d->d_ff % 64 == 0 &&
-         (long)d->T * d->K >= 512L * d->E && !env_off && !force_simt() &&
-         gemm_direct_ok();
-}
-
 size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
   const size_t TK = (size_t)d->T * d->K, b = act_bytes(d->act_dtype);
   size_t o = 0;
@@ -207,19 +180,6 @@ size_t bwd_ws_layout(const moe_desc* d, char* base, BwdWs* w) {
     o = align_up(o + b * T * d->d_model);
     if (w) w->srange = (int32_t*)(base + o);
     o = align_up(o + 2 * sizeof(int32_t));
-  }
-  if (wgrad_t_ok(d)) {
-    const size_t ldT = 64 * (TK / 64 + d->E + 1);
-    const size_t dm = d->d_model, f = d->d_ff;
-    if (w) w->ldT = (long)ldT;
-    void** t[5] = {w ? &w->xT : nullptr, w ? &w->dyT : nullptr,
-                   w ? &w->hT : nullptr, w ? &w->daT : nullptr,
-                   w ? &w->dbT : nullptr};
-    const size_t rows[5] = {dm, dm, f, f, f};
-    for (int i = 0; i < 5; ++i) {
-      if (t[i]) *t[i] = base + o;
-      o = align_up(o + b * rows[i] * ldT);
-    }
   }
   if (d->gemm_dtype == MOE_MXFP8) {
     const size_t dm = d->d_model, f = d->d_ff;
@@ -594,31 +554,16 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
   MOE_TRY(launch_combine(MOE_BF16, w.dx_perm, a->dest, nullptr,
                          shared ? w.sdx : nullptr, a->dx, d->T, d->K, dm, s));
   record(a->events[5], s);
-  // weight gradients in bf16; with experts of 512+ rows from transposed,
-  // group-padded operands as in the bf16 backward
-  const bool wt = wgrad_t_ok(d);
-  const int32_t* t64 = w.tile_off[tile_bm_slot(64)];
+  // weight gradients in bf16, as in the bf16 backward
   {  // dW2_e = dy_perm^T h, h dequantised from the forward's codes
     const uint8_t* hq = (const uint8_t*)a->h;
     MOE_TRY(launch_dequantize_mxfp8(hq, hq + (size_t)TK * f, TK, f, w.h_bf, s));
     GemmParams p = gp();
-    p.M = dm; p.N = f; p.G = E;
+    p.M = dm; p.N = f; p.G = E; p.off = a->offsets;
+    p.A = w.dy_perm; p.lda = dm;
+    p.B = w.h_bf; p.ldb = f;
     p.C = a->dw2; p.ldc = f; p.sC = (long)dm * f;
-    if (wt) {
-      MOE_TRY(launch_transpose_pad(w.dy_perm, TK, dm, a->offsets, t64, E,
-                                   w.dyT, w.ldT, s));
-      MOE_TRY(launch_transpose_pad(w.h_bf, TK, f, a->offsets, t64, E, w.hT,
-                                   w.ldT, s));
-      p.off = t64; p.kmul = 64;
-      p.A = w.dyT; p.lda = w.ldT;
-      p.B = w.hT; p.ldb = w.ldT;
-      MOE_TRY(gemm_mfma(kOpWgradT, p, w.tile_off, s));
-    } else {
-      p.off = a->offsets;
-      p.A = w.dy_perm; p.lda = dm;
-      p.B = w.h_bf; p.ldb = f;
-      MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
-    }
+    MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
   }
   if (shared) {  // dWs2 = dy^T h_s, h_s dequantised; x dequantised too
     MOE_TRY(launch_dequantize_mxfp8(w.shq, w.shs, T, fs, w.sh, s));
@@ -635,29 +580,13 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
   // dx_perm buffer, free after the gather-sum)
   MOE_TRY(launch_dequantize_mxfp8((const uint8_t*)a->x_perm, a->x_perm_scales,
                                   TK, dm, w.dx_perm, s));
-  if (wt) {
-    MOE_TRY(launch_transpose_pad(w.dx_perm, TK, dm, a->offsets, t64, E, w.xT,
-                                 w.ldT, s));
-    MOE_TRY(launch_transpose_pad(w.da, TK, f, a->offsets, t64, E, w.daT,
-                                 w.ldT, s));
-    MOE_TRY(launch_transpose_pad(w.db, TK, f, a->offsets, t64, E, w.dbT,
-                                 w.ldT, s));
-  }
   for (int which = 0; which < 2; ++which) {
     GemmParams p = gp();
-    p.M = f; p.N = dm; p.G = E;
+    p.M = f; p.N = dm; p.G = E; p.off = a->offsets;
+    p.A = which ? w.db : w.da; p.lda = f;
+    p.B = w.dx_perm; p.ldb = dm;
     p.C = which ? a->dw3 : a->dw1; p.ldc = dm; p.sC = (long)f * dm;
-    if (wt) {
-      p.off = t64; p.kmul = 64;
-      p.A = which ? w.dbT : w.daT; p.lda = w.ldT;
-      p.B = w.xT; p.ldb = w.ldT;
-      MOE_TRY(gemm_mfma(kOpWgradT, p, w.tile_off, s));
-    } else {
-      p.off = a->offsets;
-      p.A = which ? w.db : w.da; p.lda = f;
-      p.B = w.dx_perm; p.ldb = dm;
-      MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
-    }
+    MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
     if (shared) {  // dWs1 = da_s^T x, dWs3 = db_s^T x (x as quantised)
       GemmParams q = gp();
       q.M = fs; q.N = dm; q.G = 1; q.off = w.srange;
@@ -1194,20 +1123,7 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
   MOE_TRY(launch_combine(dt, w.dx_perm, a->dest, nullptr,
                          shared ? w.sdx : nullptr, a->dx, d->T, d->K, dm, s));
   record(a->events[5], s);
-  const bool wt = wgrad_t_ok(d);
-  const int32_t* t64 = w.tile_off[tile_bm_slot(64)];
-  if (wt) {  // dW2_e = (dy_perm^T)_e (h^T)_e^T from padded transposes
-    MOE_TRY(launch_transpose_pad(w.dy_perm, TK, dm, a->offsets, t64, E, w.dyT,
-                                 w.ldT, s));
-    MOE_TRY(launch_transpose_pad(a->h, TK, f, a->offsets, t64, E, w.hT,
-                                 w.ldT, s));
-    GemmParams p = gp();
-    p.M = dm; p.N = f; p.G = E; p.off = t64; p.kmul = 64;
-    p.A = w.dyT; p.lda = w.ldT;
-    p.B = w.hT; p.ldb = w.ldT;
-    p.C = a->dw2; p.ldc = f; p.sC = (long)dm * f;
-    MOE_TRY(gemm_mfma(kOpWgradT, p, w.tile_off, s));
-  } else {  // dW2_e = dy_perm_e^T h_e
+  {  // dW2_e = dy_perm_e^T h_e
     GemmParams p = gp();
     p.M = dm; p.N = f; p.G = E; p.off = a->offsets;
     p.A = w.dy_perm; p.lda = dm;
@@ -1224,29 +1140,13 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
     MOE_TRY(run_gemm(kOpWgrad, dt, p, w.tile_off, s));
   }
   record(a->events[6], s);
-  if (wt) {
-    MOE_TRY(launch_transpose_pad(a->x_perm, TK, dm, a->offsets, t64, E, w.xT,
-                                 w.ldT, s));
-    MOE_TRY(launch_transpose_pad(w.da, TK, f, a->offsets, t64, E, w.daT,
-                                 w.ldT, s));
-    MOE_TRY(launch_transpose_pad(w.db, TK, f, a->offsets, t64, E, w.dbT,
-                                 w.ldT, s));
-  }
   for (int which = 0; which < 2; ++which) {  // dW1_e = da^T x_perm, dW3_e
     GemmParams p = gp();
-    p.M = f; p.N = dm; p.G = E;
+    p.M = f; p.N = dm; p.G = E; p.off = a->offsets;
+    p.A = which ? w.db : w.da; p.lda = f;
+    p.B = a->x_perm; p.ldb = dm;
     p.C = which ? a->dw3 : a->dw1; p.ldc = dm; p.sC = (long)f * dm;
-    if (wt) {
-      p.off = t64; p.kmul = 64;
-      p.A = which ? w.dbT : w.daT; p.lda = w.ldT;
-      p.B = w.xT; p.ldb = w.ldT;
-      MOE_TRY(gemm_mfma(kOpWgradT, p, w.tile_off, s));
-    } else {
-      p.off = a->offsets;
-      p.A = which ? w.db : w.da; p.lda = f;
-      p.B = a->x_perm; p.ldb = dm;
-      MOE_TRY(run_gemm(kOpWgrad, dt, p, w.tile_off, s));
-    }
+    MOE_TRY(run_gemm(kOpWgrad, dt, p, w.tile_off, s));
     if (shared) {  // dWs1 = da_s^T x, dWs3 = db_s^T x
       GemmParams q = gp();
       q.M = fs; q.N = dm; q.G = 1; q.off = w.srange;

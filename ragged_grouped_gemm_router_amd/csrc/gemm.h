@@ -19,8 +19,6 @@ enum GemmOp : int {
   kOpRouterDw = 9,  // part_g[E,d] = d_logits_g^T x_g over token range g (fp32)
   kOpGemm1MxAct = 10,  // GEMM 1 on MXFP8 operands; bf16 h (optional), a, b
   kOpDgrad2Mx = 11,    // dh = dy_perm W2_e on MXFP8 operands -> (da, db) bf16
-  kOpWgradT = 12,      // dW_e = L_e R_e^T with L, R transposed and each
-                       // group's columns padded to 64 (zeros): k contiguous
 };
 
 // Row-tile heights for which the permute step publishes tile prefixes.

@@ -1282,6 +1282,259 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
                                                               value, store, t.m_end - t.m0);
 }
 
+// Weight gradients C_g = A_g^T B_g over each group's row range (the
+// contraction-grouped products, both operands k-major: element (r, k) at
+// X[k * ld + r]) as a persistent kernel. Workgroup b takes the tiles
+// first + j * gridDim.x (first: b's slot, each XCD a contiguous share of
+// every round of tiles) and runs them as one stream of k-tiles: during the
+// k-tile of step s it issues the DMA of step s + 2, also when that step
+// belongs to its next tile, so a tile's first operands arrive while the
+// tile before it still computes. An empty row range is one k-tile of zeros
+// (the tile stores zeros). The MFMAs take their operands swapped and
+// accumulate C^T: element r of lane l is C row l % 32, column
+// 8 (r / 4) + 4 (l / 32) + r % 4 of the 32 x 32 block, so a register quad
+// holds four consecutive columns of one row. A swap of lane halves
+// (v_permlane32_swap) gathers eight, and the epilogue stores 16-byte row
+// pieces straight from registers, with no LDS staging and no barrier,
+// while the next tile's DMA is in flight.
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
+  typedef bf16x8 Frag;
+  constexpr int NW = WGM * WGN;
+  constexpr int RB = 128, BK = 64, KS = BK / 16;  // bytes / elements / substeps
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  // DMA instructions per wave and k-tile (1 KB each)
+  constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;
+  constexpr int N_LOAD = A_INS + B_INS;
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile shape");
+  static_assert(BM >= 128 && BN >= 128 && BM <= 512 && BN <= 512, "tile shape");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int tiles_mn = (p.M + BM - 1) / BM * tiles_n;
+  const int n_tiles = p.G * tiles_mn;
+  const int grid = (int)gridDim.x;
+  const int first = xcd_remap_n((int)blockIdx.x, grid);
+  const int km = p.kmul > 0 ? p.kmul : 1;
+  // the group offsets through the constant address space: scalar loads,
+  // whose wait (lgkmcnt) leaves the DMA and stores in flight (a vector
+  // load here would wait for all of them)
+  typedef const __attribute__((address_space(4))) int32_t* OffPtr;
+  const OffPtr off = (OffPtr)p.off;
+
+  // a position in the k-tile stream: tile j of this workgroup, its k-tile kt
+  struct Cur {
+    int j, kt, nk, g, m0, n0, k_beg, k_end;
+  };
+  auto start_tile = [&](Cur& c) {  // first k-tile of tile c.j; false past the end
+    const int L = first + c.j * grid;
+    if (L >= n_tiles) return false;
+    c.g = L / tiles_mn;
+    const int rem = L - c.g * tiles_mn;
+    c.m0 = rem / tiles_n * BM;
+    c.n0 = rem % tiles_n * BN;
+    c.k_beg = off[c.g] * km;
+    c.k_end = off[c.g + 1] * km;
+    c.nk = max(1, (c.k_end - c.k_beg + BK - 1) / BK);
+    c.kt = 0;
+    return true;
+  };
+  auto next_step = [&](Cur& c) {
+    if (++c.kt < c.nk) return true;
+    ++c.j;
+    return start_tile(c);
+  };
+
+  // DMA instruction d of the k-tile at c into stage st (d < A_INS: A's
+  // rows [m0, m0 + BM), else B's [n0, n0 + BN)), as it lies: 1024 / (2R)
+  // k-rows of R elements, 16-byte chunk ch of k-row k at position
+  // ch ^ (4 (k & 3)). The resource ends with the group's rows, so k-rows
+  // past them read zeros; live = false (past the last step) reads zeros
+  // only.
+  auto issue_one = [&](const Cur& c, bool live, int st, int d) {
+    const bool is_a = d < A_INS;
+    const int jd = is_a ? d : d - A_INS;
+    const int cpk = (is_a ? BM : BN) / 8;  // chunks per k-row
+    const int kr = (jd * NW + wave) * (64 / cpk) + lane / cpk;
+    const int ch = (lane % cpk) ^ (4 * (kr & 3));
+    const int kbase = c.k_beg + c.kt * BK;
+    const int rows_left = live ? c.k_end - kbase : 0;
+    const long ld = is_a ? p.lda : p.ldb;
+    const int r0 = is_a ? c.m0 : c.n0;
+    const char* base = (const char*)(is_a ? p.A : p.B) + ((long)kbase * ld + r0) * 2;
+    char* dst = lds + st * STAGE + (is_a ? 0 : A_BYTES) + (jd * NW + wave) * 1024;
+    dma16(make_rsrc_n(base, ((long)rows_left * ld - r0) * 2), dst,
+          kr * (int)ld * 2 + ch * 16, 0);
+  };
+
+  // fragment (32 rows x 16 k) by two transposing reads of 4 k each: within
+  // each 16-lane group lane j points at k-row kb + j / 4, elements
+  // r0 + 4 (j % 4) .. +3, and lane i receives the four k of element r0 + i
+  const int grp = lane / 16, gj = lane % 16;
+  auto read_km = [&](const char* op, int R, int row0, int ks) {
+    const int r = row0 + 16 * (grp & 1) + 4 * (gj & 3);
+    s16x4 v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = ks * 16 + 8 * (grp >> 1) + 4 * h + (gj >> 2);
+      const int c = (r >> 3) ^ (4 * (k & 3));
+      v[h] = lds_read_tr16(op + k * (R * 2) + c * 16 + (r & 7) * 2);
+    }
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 w = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(Frag, w);
+  };
+  struct Frags {
+    Frag a[MB], b[NB];
+  };
+  constexpr int N_READ = MB + NB;
+  constexpr int N_MFMA = MB * NB;
+  constexpr ReadOrder<MB, NB, 1, (N_MFMA >= 8)> kOrder{};
+  auto read_one = [&](const char* sb, int ks, Frags& f, int m) {
+    const int r = kOrder.r[m];
+    if (r < MB)
+      f.a[r] = read_km(sb, BM, wm * WM + r * 32, ks);
+    else
+      f.b[r - MB] = read_km(sb + A_BYTES, BN, wn * WN + (r - MB) * 32, ks);
+  };
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+  auto mfma_one = [&](const Frags& f, int q) {  // C^T block (i, j)
+    const int i = q / NB, j = q % NB;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  };
+
+  // the finished tile at c from registers: block (i, j), quads 2 pr and
+  // 2 pr + 1 packed to bf16 (columns 16 pr + 4 half .. and 16 pr + 8 +
+  // 4 half ..), lane halves swapped so that lane l < 32 holds columns
+  // 16 pr + 8 .. +15 and lane l + 32 columns 16 pr .. +7 of row l
+  auto store_tile = [&](const Cur& c) {
+    bf16* C = (bf16*)p.C + (long)c.g * p.sC;
+    const int half = lane / 32;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int row = c.m0 + wm * WM + i * 32 + lane % 32;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        uint32_t w[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const bf16 lo = (bf16)acc[i][j][4 * q + 2 * h];
+            const bf16 hi = (bf16)acc[i][j][4 * q + 2 * h + 1];
+            w[q][h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          }
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(w[2 * pr + 1][h], w[2 * pr][h],
+                                                             false, false);
+            w[2 * pr + 1][h] = sw[0];
+            w[2 * pr][h] = sw[1];
+          }
+          const int col = c.n0 + wn * WN + j * 32 + 16 * pr + (half ? 0 : 8);
+          if (row < p.M && col < p.N)
+            *(u32x4*)(C + (long)row * p.ldc + col) =
+                u32x4{w[2 * pr + 1][0], w[2 * pr + 1][1], w[2 * pr][0], w[2 * pr][1]};
+        }
+        acc[i][j] = f32x16{};
+      }
+    }
+  };
+
+  Cur cc;
+  cc.j = 0;
+  if (!start_tile(cc)) return;
+  // prologue: steps 0 and 1 into stages 0 and 1, the load cursor at step 2
+  Cur cl = cc;
+#pragma unroll
+  for (int d = 0; d < N_LOAD; ++d) issue_one(cl, true, 0, d);
+  bool live = next_step(cl);
+#pragma unroll
+  for (int d = 0; d < N_LOAD; ++d) issue_one(cl, live, 1, d);
+  live = live && next_step(cl);
+  tile_barrier<N_LOAD>();
+  Frags fa, fb;
+#pragma unroll
+  for (int r = 0; r < N_READ; ++r) read_one(lds, 0, fa, r);
+
+  // One region per k-substep, as the backward kernel's: the substep's
+  // MFMAs with the next substep's fragment reads (and, at the last, the
+  // DMA of step s + 2 into this step's stage, after the barrier that ends
+  // every wave's reads of it) spread among them. The barrier waits for
+  // everything outstanding: step s + 1's DMA and any stores of the tile
+  // before (loads and stores retire out of order with each other).
+  constexpr int H = N_MFMA >= 8 ? 2 : 1;
+#define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
+  int st = 0;
+  for (;;) {
+    const char* sb = lds + st * STAGE;
+    const char* sb_next = lds + (st ^ 1) * STAGE;
+    static_for<KS>([&](auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
+      Frags& cur = (ks & 1) ? fb : fa;
+      Frags& nxt = (ks & 1) ? fa : fb;
+      constexpr bool last = ks + 1 == KS;
+      constexpr int NM_MAX = N_READ + N_LOAD;
+      constexpr int nm = last ? NM_MAX : N_READ;
+      MOE_FENCE();
+#pragma unroll
+      for (int q = 0; q < H; ++q) mfma_one(cur, q);
+      MOE_FENCE();
+      if constexpr (last) {
+        tile_barrier<0>();
+        MOE_FENCE();
+      }
+      int m = 0;
+#pragma unroll
+      for (int q = H; q < N_MFMA; ++q) {
+        const int m_end = (q - H + 1) * nm / (N_MFMA - H);
+#pragma unroll
+        for (int mm = 0; mm < NM_MAX; ++mm) {
+          if (mm < m || mm >= m_end) continue;
+          if constexpr (!last) {
+            read_one(sb, ks + 1, nxt, mm);
+          } else {
+            const int rb = mm * N_READ / NM_MAX;
+            if ((mm + 1) * N_READ / NM_MAX != rb)
+              read_one(sb_next, 0, nxt, rb);
+            else
+              issue_one(cl, live, st, mm - rb);
+          }
+          MOE_FENCE();
+        }
+        m = m_end;
+        mfma_one(cur, q);
+        MOE_FENCE();
+      }
+    });
+    if (cc.kt + 1 == cc.nk) {
+      store_tile(cc);
+      ++cc.j;
+      if (!start_tile(cc)) break;
+    } else {
+      ++cc.kt;
+    }
+    if (live) live = next_step(cl);
+    st ^= 1;
+  }
+#undef MOE_FENCE
+  __builtin_amdgcn_s_waitcnt(0);  // no load may still target LDS at exit
+}
+
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, bool KCAT,
           int EPI, int SCHED, bool SKIP = false>
 hipError_t launch_t(const GemmParams& p, hipStream_t s) {
@@ -1343,6 +1596,19 @@ int num_cus() {
     cached[dev] = n;
   }
   return cached[dev];
+}
+
+// the persistent weight-gradient kernel: one workgroup per CU (fewer when
+// there are fewer tiles)
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_wgrad(const GemmParams& p, hipStream_t s) {
+  const long tiles = (long)p.G * ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
+  const long grid = tiles < num_cus() ? tiles : num_cus();
+  hipLaunchKernelGGL((mfma_wgrad<BM, BN, WGM, WGN>), dim3((unsigned)grid),
+                     dim3(WGM * WGN * kWave), 0, s, p);
+  return hipGetLastError();
 }
 
 template <bool DUAL, int EPI, typename TO, bool MX = false, int SKIP = 0>
@@ -1446,12 +1712,21 @@ bool mfma_supported(GemmOp op, const GemmParams& p) {
   if (op == kOpDgrad1 && p.K1 % 64) return false;
   if ((op == kOpDgrad2 || op == kOpDgrad1) && p.N % 8) return false;
   if (op == kOpWgrad && (p.M % 8 || p.N % 8)) return false;
-  if (op == kOpWgradT && (p.lda % 64 || p.ldb % 64 || p.N % 8)) return false;
   // router backward: d_logits rows padded to whole k-tiles (row-major A
   // of the dx product), 16-byte aligned k-rows and output pieces
   if (op == kOpRouterDx && (p.lda % 64 || p.ldb % 8 || p.N % 8)) return false;
   if (op == kOpRouterDw && (p.lda % 8 || p.ldb % 8 || p.N % 8)) return false;
   return true;
+}
+
+// MOE_WGRAD_PERSIST=0 keeps the weight gradients on the tile-per-workgroup
+// backward kernel, for comparison
+bool wgrad_persist() {
+  static const bool v = [] {
+    const char* e = tuning_env("MOE_WGRAD_PERSIST");
+    return !(e && strcmp(e, "0") == 0);
+  }();
+  return v;
 }
 
 bool gemm1_gather_supported(int K) { return K % 64 == 0 && !force_staged(); }
@@ -1469,7 +1744,7 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   // skip: one 256-row tile per group with the empty 32-row blocks' MFMAs
   // skipped; tskip: the same skip in big tiles of groups below 1024 rows
   bool big, skip = false, tskip = false;
-  if (op == kOpWgrad || op == kOpRouterDw || op == kOpWgradT) {
+  if (op == kOpWgrad || op == kOpRouterDw) {
     big = p.M >= 256 && p.N >= 256;
   } else if (op == kOpRouterDx) {
     big = false;
@@ -1600,10 +1875,10 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   }
   // backward products on the direct-to-LDS kernel with k-major operands
   if (!force_staged()) {
-    const bool w4 = big_tile_waves() == 4;
-    if (op == kOpWgrad)
+    if (op == kOpWgrad && big && wgrad_persist())
+      return launch_wgrad<256, 256, 2, 4>(p, s);
+    if (op == kOpWgrad)  // (the big form only for comparison)
       return !big ? launch_t<128, 128, 2, 2, true, true, false, kEpiStore, kSchedK>(p, s)
-             : w4 ? launch_t<256, 256, 2, 2, true, true, false, kEpiStore, kSchedK>(p, s)
                   : launch_t<256, 256, 2, 4, true, true, false, kEpiStore, kSchedK>(p, s);
     // router backward: dx += d_logits Wr (Wr read k-major as stored), and
     // fp32 partial sums of d_logits^T x over token ranges
@@ -1613,14 +1888,6 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
       return !big ? launch_t<128, 128, 2, 2, true, true, false, kEpiStoreF32, kSchedK>(p, s)
                   : launch_t<256, 256, 2, 4, true, true, false, kEpiStoreF32, kSchedK>(p, s);
   }
-  // weight gradients from transposed, group-padded operands: both k
-  // contiguous, so the forward's direct-to-LDS kernel takes them
-  // (B in its own 3-stage ring, as the forward's big tiles: Mixtral-shaped
-  // dW2 2.37 -> 2.23 ms, dW1/dW3 unchanged)
-  if (op == kOpWgradT)
-    return big ? launch_dl<256, 256, 2, 2, 4, false, kEpiStore, bf16, false, kSchedK,
-                           0, false, false, 3>(p, s)
-               : launch_dl<128, 128, 2, 2, 2, false, kEpiStore, bf16, false, kSchedK>(p, s);
   if (op == kOpGemm1Mx)
     return skip || tskip
                ? launch_dl_sized<true, kEpiSwigluMx, bf16, true, 1>(big, p, s)

@@ -71,12 +71,6 @@ hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y,
                               void* dy_perm, float* d_w, int T, int K, int d,
                               hipStream_t s);
 
-// Per-expert transpose with zero padding to 64 rows: src [rows, C] bf16 ->
-// dst [C, ldd], expert e's rows at columns 64 * t64[e] ... (C % 64 == 0,
-// ldd >= 64 * (rows_max / 64 + E + 1)).
-hipError_t launch_transpose_pad(const void* src, int rows_max, int C,
-                                const int32_t* off, const int32_t* t64, int E,
-                                void* dst, long ldd, hipStream_t s);
 
 // Router backward. d_logits [T,E] fp32 and the same in the activation
 // dtype (d_logits_a, rows of ld_a elements, zero past E); split [G+1]

@@ -460,49 +460,7 @@ int perm_nbits(int E) {
   return nbits;
 }
 
-// Transpose with per-group padding: for each expert e with rows
-// [off[e], off[e+1]) of src [rows, C] (bf16), dst[c, 64 * t64[e] + i] =
-// src[off[e] + i, c] for i < count_e, and zero up to the next multiple of
-// 64. Workgroup (rt, ct) moves the 64 x 64 block of padded row tile rt
-// (t64 = row-tile prefix at height 64) and columns [64 ct, 64 ct + 64)
-// through LDS.
-__global__ __launch_bounds__(256) void transpose_pad_kernel(
-    const bf16* __restrict__ src, int C, const int32_t* __restrict__ off,
-    const int32_t* __restrict__ t64, int E, bf16* __restrict__ dst, long ldd) {
-  __shared__ bf16 tile[64][72];
-  const int rt = blockIdx.x;
-  if (rt >= t64[E]) return;
-  const int e = upper_group(t64, E, rt);
-  const int r0 = off[e] + (rt - t64[e]) * 64, r_end = off[e + 1];
-  const int c0 = blockIdx.y * 64;
-  for (int q = threadIdx.x; q < 64 * 8; q += 256) {
-    const int r = q / 8, cc = (q % 8) * 8;
-    bf16x8 v = {};
-    if (r0 + r < r_end) v = *(const bf16x8*)(src + (long)(r0 + r) * C + c0 + cc);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tile[r][cc + i] = v[i];
-  }
-  __syncthreads();
-  for (int q = threadIdx.x; q < 64 * 8; q += 256) {
-    const int c = q / 8, rr = (q % 8) * 8;
-    bf16x8 o;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = tile[rr + i][c];
-    *(bf16x8*)(dst + (long)(c0 + c) * ldd + (long)rt * 64 + rr) = o;
-  }
-}
-
 }  // namespace
-
-hipError_t launch_transpose_pad(const void* src, int rows_max, int C,
-                                const int32_t* off, const int32_t* t64, int E,
-                                void* dst, long ldd, hipStream_t s) {
-  const long rt_max = (rows_max + 63) / 64 + E;  // upper bound of row tiles
-  hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)rt_max, C / 64),
-                     dim3(256), 0, s, (const bf16*)src, C, off, t64, E,
-                     (bf16*)dst, ldd);
-  return hipGetLastError();
-}
 
 // tokens per workgroup of the row scatter and of the combine: about
 // `bytes` of token rows, at most kScatterThreads copies. Measured on the

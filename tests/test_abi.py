@@ -294,11 +294,16 @@ def test_mx_scale_layout_views():
     assert per[2, 1, 5] == ((5 // 4) * E * R + 2 * R + 1) * 4 + 5 % 4
 
 
-def test_transposed_wgrad_workspace():
-    """bf16 backward with widths that are multiples of 64 and experts of at
-    least 512 rows on average reserves the transposed, group-padded
-    operands of the weight gradients: (2 d + 3 f) x 64 (T K / 64 + E + 1)
-    bf16 elements."""
-    d = B.make_desc(2048, 128, 192, 8, 2)  # 512 rows per expert on average
-    ldT = 64 * (4096 // 64 + 8 + 1)
-    assert _ws(d, True) >= 2 * (2 * 128 + 3 * 192) * ldT
+def test_bf16_backward_workspace_exact():
+    """The bf16 backward (no shared expert) keeps only the tile prefixes of
+    the four row-tile heights and dy_perm, da, db and dx_perm, each block
+    aligned to 256 bytes: the data and weight gradients read the weights
+    and activations as stored, with no transposed copies."""
+    def al(n):
+        return (n + 255) // 256 * 256
+    for T, dm, f, E, K in ((2048, 128, 192, 8, 2), (4096, 7168, 2048, 256, 8)):
+        d = B.make_desc(T, dm, f, E, K)
+        TK = T * K
+        want = (4 * al(4 * (E + 1)) + 2 * al(2 * TK * dm) +
+                2 * al(2 * TK * f))
+        assert _ws(d, True) == want, (T, dm, f, E, K)

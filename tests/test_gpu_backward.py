@@ -20,11 +20,10 @@ CASES = [
                  dtype="f32"),
     mi.MoEConfig("skewed_like_T1024_d128_f192_E16_K4", 1024, 128, 192, 16, 4,
                  synth_logits=True, n_zero=3, zipf_s=1.2),
-    # >= 512 rows per expert on average: weight gradients from the
-    # transposed, group-padded operands (ragged N with f = 192; empty
-    # experts in the skewed case)
-    mi.MoEConfig("wgrad_t_T2048_d256_f192_E4_K2", 2048, 256, 192, 4, 2),
-    mi.MoEConfig("wgrad_t_skewed_T4096_d128_f256_E16_K4", 4096, 128, 256, 16,
+    # >= 512 rows per expert on average: weight-gradient tiles of many
+    # k-tiles (ragged N with f = 192; empty experts in the skewed case)
+    mi.MoEConfig("long_k_T2048_d256_f192_E4_K2", 2048, 256, 192, 4, 2),
+    mi.MoEConfig("long_k_skewed_T4096_d128_f256_E16_K4", 4096, 128, 256, 16,
                  4, synth_logits=True, n_zero=3, zipf_s=1.2),
     mi.MoEConfig("many_experts_T256_d256_f128_E64_K8_sigmoid", 256, 256, 128,
                  64, 8, gate="sigmoid", bias=True),
@@ -39,6 +38,12 @@ CASES = [
                  16),
     # E = 6: the router's output rows are not 16-byte aligned
     mi.MoEConfig("six_experts_T1024_d128_f192_E6_K2", 1024, 128, 192, 6, 2),
+    # the persistent weight-gradient kernel (256 x 256 tiles) with partial
+    # row and column tiles (d = 320, f = 264), empty experts (zero
+    # gradients from a k-tile of zeros), experts of one to several k-tiles
+    # (Zipf loads) and 320 tiles per product, more than one per workgroup
+    mi.MoEConfig("wgrad_persist_T1024_d320_f264_E80_K2", 1024, 320, 264, 80,
+                 2, synth_logits=True, n_zero=3, zipf_s=1.2),
 ]
 
 

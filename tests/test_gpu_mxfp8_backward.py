@@ -21,10 +21,10 @@ CASES = [
     mi.MoEConfig("mxb_sigmoid_T512_d256_f256_E16_K4", 512, 256, 256, 16, 4,
                  gate="sigmoid", bias=True),
     mi.MoEConfig("mxb_tail_T333_d384_f256_E16_K3", 333, 384, 256, 16, 3),
-    # >= 512 rows per expert on average: weight gradients from transposed,
-    # group-padded operands (empty experts in the skewed case)
-    mi.MoEConfig("mxb_wgrad_t_T2048_d256_f256_E4_K2", 2048, 256, 256, 4, 2),
-    mi.MoEConfig("mxb_wgrad_t_skewed_T4096_d128_f256_E16_K4", 4096, 128, 256,
+    # >= 512 rows per expert on average: weight-gradient tiles of many
+    # k-tiles, on the persistent kernel (empty experts in the skewed case)
+    mi.MoEConfig("mxb_long_k_T2048_d256_f256_E4_K2", 2048, 256, 256, 4, 2),
+    mi.MoEConfig("mxb_long_k_skewed_T4096_d128_f256_E16_K4", 4096, 128, 256,
                  16, 4, synth_logits=True, n_zero=3, zipf_s=1.2),
     mi.MoEConfig("mxb_skewed_T1024_d256_f256_E16_K4", 1024, 256, 256, 16, 4,
                  synth_logits=True, n_zero=3, zipf_s=1.2),
