@@ -772,11 +772,18 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 
   // Prologue: (scales of k-tile 0,) k-tiles 0 .. S-1 in flight, and the
   // B operands of k-tiles S .. S_B-1 (past the last tile, the last one
-  // again, into stages nobody reads); wait for tile 0. With a deeper B
-  // ring, MXFP8 scales run two tiles ahead: those of tile kt+1 are issued
-  // before the B DMA of tile kt+2 (here: of tile 2), so that one is still
-  // the newest outstanding load at the tile barrier.
-  constexpr int NSC_RING = RING_B && MX ? NSC : 0;
+  // again, into stages nobody reads); wait for tile 0. MXFP8 scales of the
+  // dual products run one tile ahead: those of tile kt+1 are issued at the
+  // start of tile kt, ahead of that tile's DMA, so the tile barrier's own
+  // wait covers them and their copy into s_cur after it waits for nothing.
+  // The single-B products with a deeper B ring (SC2) issue them two tiles
+  // ahead, right after the barrier, so that the B DMA of tile kt+2 is
+  // still the newest load at the next barrier: the compiler then rotates
+  // them through a third register set and waits for loads a few MFMAs old
+  // at its copy, which costs the dual tile 1-5% of GEMM 1 and the
+  // single-B one nothing.
+  constexpr bool SC2 = MX && RING_B && !DUAL;
+  constexpr int NSC_RING = SC2 ? NSC : 0;
   // SPREAD (B ring one stage deeper than A's): the B DMA of k-tile
   // kt + S_B - 1 goes into the B stage that tile kt - 1 used, free since the
   // barrier that ended tile kt - 1, and is spread over the regions of
@@ -787,13 +794,13 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   // tile kt are still B's, of k-tile kt + S_B - 1.
   constexpr bool SPREAD = RING_B;
   if (nk > 0) {  // (an empty group's tile writes zeros)
-  load_scales(RING_B ? s_cur : s_nxt, 0);
+  load_scales(SC2 ? s_cur : s_nxt, 0);
 #pragma unroll
   for (int i = 0; i < S; ++i)
 #pragma unroll
     for (int d = 0; d < N_LOAD; ++d)
       issue_one(min(i, nk - 1), i, min(i, nk - 1), i, d);
-  if constexpr (RING_B) load_scales(s_nxt, min(1, nk - 1));
+  if constexpr (SC2) load_scales(s_nxt, min(1, nk - 1));
   if constexpr (!SPREAD) {
 #pragma unroll
     for (int i = S; i < S_B; ++i)
@@ -802,7 +809,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   }
   barrier_after(std::integral_constant<int, (S - 1) * N_LOAD + NSC_RING +
                                                 (SPREAD ? 0 : (S_B - S) * NBL)>{});
-  if constexpr (MX && !RING_B) {
+  if constexpr (MX && !SC2) {
 #pragma unroll
     for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
   }
@@ -854,7 +861,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 #pragma unroll
       for (int q = 0; q < H; ++q) mfma_one(cur, q, sk);
       MOE_FENCE();
-      if constexpr (ks == 0 && !RING_B) {
+      if constexpr (ks == 0 && MX && !SC2) {
         load_scales(s_nxt, min(kt + 1, nk - 1));
         MOE_FENCE();
       }
@@ -866,7 +873,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
         if constexpr (MX) {
 #pragma unroll
           for (int q = 0; q < NSC; ++q) s_cur[q] = s_nxt[q];
-          if constexpr (RING_B) load_scales(s_nxt, min(kt + 2, nk - 1));
+          if constexpr (SC2) load_scales(s_nxt, min(kt + 2, nk - 1));
         }
         MOE_FENCE();
       }
