@@ -44,6 +44,11 @@ CASES = [
     # (Zipf loads) and 320 tiles per product, more than one per workgroup
     mi.MoEConfig("wgrad_persist_T1024_d320_f264_E80_K2", 1024, 320, 264, 80,
                  2, synth_logits=True, n_zero=3, zipf_s=1.2),
+    # ~256 rows per expert: the data gradients on 256 x 256 tiles reading
+    # the weights k-major, each with a partial last column tile (dgrad2:
+    # N = f = 448, dgrad1: N = d = 320) whose DMA chunks past N are clamped
+    mi.MoEConfig("kmajor_ragged_n_T1024_d320_f448_E8_K2", 1024, 320, 448, 8,
+                 2),
 ]
 
 
