@@ -1055,11 +1055,12 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 //
 // SCHED = kSchedK contracts over each group's ragged row range (weight
 // gradients: C_g = A_g^T B_g); k-tiles past the range read zeros, since
-// every k-tile's buffer resource ends at the range end. KCAT contracts over
-// the concatenation [A | A2] . [B ; B2] with K1 rows in the first part.
-template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, bool KCAT,
-          int EPI, int SCHED, bool SKIP = false>
+// every k-tile's buffer resource ends at the range end. (It serves the
+// router backward and the weight gradients with outputs below 256 in a
+// dimension.)
+template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int EPI, int SCHED>
 __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
+  static_assert(EPI == kEpiStore || EPI == kEpiStoreF32 || EPI == kEpiAccum, "epilogue");
   typedef bf16x8 Frag;
   constexpr int NW = WGM * WGN, S = 2;
   constexpr int RB = 128, BK = 64, KS = BK / 16;  // bytes / elements / substeps
@@ -1083,11 +1084,9 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WGN, wn = wave % WGN;
 
-  // k-tiles: rows [k_beg, k_end) of the contraction (SCHED K), else
-  // [0, K) or its two halves (KCAT)
-  const int kspan = SCHED == kSchedK ? t.k_end - t.k_beg : (KCAT ? p.K1 : p.K);
-  const int nk1 = (kspan + BK - 1) / BK;
-  const int nk = KCAT ? 2 * nk1 : nk1;
+  // k-tiles: rows [k_beg, k_end) of the contraction (SCHED K), else [0, K)
+  const int kspan = SCHED == kSchedK ? t.k_end - t.k_beg : p.K;
+  const int nk = (kspan + BK - 1) / BK;
 
   // Source of DMA instruction d of operand X (rows [r0, r0 + R) of the
   // tile) for k-tile kt. Row-major: 8 rows of 128 bytes, as the forward.
@@ -1095,8 +1094,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
   // k-tile's first row and ends with the valid rows (zeros past them).
   auto dma = [&](const void* X, int ld, int r0, int r_end, int R, bool km,
                  int kt, char* dst, int d) {
-    const int kt_part = KCAT && kt >= nk1 ? kt - nk1 : kt;
-    const int kbase = (SCHED == kSchedK ? t.k_beg : 0) + kt_part * BK;
+    const int kbase = (SCHED == kSchedK ? t.k_beg : 0) + kt * BK;
     if (!km) {
       const int row = (d * NW + wave) * 8 + lane / 8, phys = lane % 8;
       const int grow = min(r0 + row, r_end - 1);
@@ -1106,26 +1104,20 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
       const int cpk = R / 8;  // chunks per k-row
       const int kr = (d * NW + wave) * (64 / cpk) + lane / cpk;
       const int c = (lane % cpk) ^ (4 * (kr & 3));
-      const int rows_left =
-          SCHED == kSchedK ? t.k_end - kbase : kspan - kt_part * BK;
+      const int rows_left = SCHED == kSchedK ? t.k_end - kbase : kspan - kt * BK;
       const char* base = (const char*)X + ((long)kbase * ld + r0) * 2;
       dma16(make_rsrc_n(base, ((long)rows_left * ld - r0) * 2), dst,
             kr * ld * 2 + c * 16, 0);
     }
   };
-  const void* Aop[2] = {p.A, KCAT ? p.A2 : p.A};
-  const void* Bop[2] = {(const char*)p.B + (SCHED == kSchedM ? (long)t.g * p.sB * 2 : 0),
-                        (const char*)(KCAT ? p.B2 : p.B) +
-                            (SCHED == kSchedM ? (long)t.g * p.sB * 2 : 0)};
+  const void* Bop = (const char*)p.B + (SCHED == kSchedM ? (long)t.g * p.sB * 2 : 0);
   auto issue_one = [&](int kt, int stage, int d) {
     char* base = lds + stage * STAGE;
-    const int part = KCAT && kt >= nk1 ? 1 : 0;
     if (d < A_INS) {
-      dma(Aop[part], p.lda, t.m0, t.m_end, BM, A_KM, kt, base + (d * NW + wave) * 1024, d);
+      dma(p.A, p.lda, t.m0, t.m_end, BM, A_KM, kt, base + (d * NW + wave) * 1024, d);
     } else {
       const int j = d - A_INS;
-      dma(Bop[part], p.ldb, t.n0, p.N, BN, B_KM, kt,
-          base + A_BYTES + (j * NW + wave) * 1024, j);
+      dma(Bop, p.ldb, t.n0, p.N, BN, B_KM, kt, base + A_BYTES + (j * NW + wave) * 1024, j);
     }
   };
   auto issue = [&](int kt, int stage) {
@@ -1178,14 +1170,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[0][i][j] = f32x16{};
-  // SKIP: as in the forward kernel, the MFMAs of 32-row blocks wholly
-  // past the group's end are skipped (groups of about half a tile)
-  constexpr bool kSkipTail = SKIP && SCHED == kSchedM && N_MFMA * 16 <= 128;
-  const int act_mb = __builtin_amdgcn_readfirstlane(
-      min(MB, max(0, (t.m_end - t.m0 - wm * WM + 31) / 32)));
   auto mfma_one = [&](const Frags& f, int q) {
     const int i = q / NB, j = q % NB;
-    if (kSkipTail && i >= act_mb) return;
     acc[0][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j],
                                                            acc[0][i][j], 0, 0, 0);
   };
@@ -1264,25 +1250,12 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
       float* Cf = (float*)p.C + c_off + o;
       *(f32x4*)Cf = f32x4{v[0], v[1], v[2], v[3]};
       *(f32x4*)(Cf + 4) = f32x4{v[4], v[5], v[6], v[7]};
-    } else if constexpr (EPI == kEpiAccum) {
+    } else {  // kEpiAccum
       const bf16x8 c8 = *(const bf16x8*)(C + o);
       float s[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) s[q] = (float)c8[q] + v[q];
       *(bf16x8*)(C + o) = pack8(s);
-    } else {  // SwiGLU backward from dh = v and the saved a, b
-      const bf16x8 a8 = *(const bf16x8*)((const bf16*)p.aux_a + o);
-      const bf16x8 b8 = *(const bf16x8*)((const bf16*)p.aux_b + o);
-      float da[8], db[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float a = (float)a8[q], b = (float)b8[q];
-        const float sg = fast_sigmoid(a);
-        da[q] = v[q] * b * sg * (1.0f + a * (1.0f - sg));
-        db[q] = v[q] * a * sg;
-      }
-      *(bf16x8*)(C + o) = pack8(da);
-      *(bf16x8*)((bf16*)p.C2 + o) = pack8(db);
     }
   };
   StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>::run(lds, wm, wn, lane,
@@ -1304,7 +1277,14 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
 // (v_permlane32_swap) gathers eight, and the epilogue stores 16-byte row
 // pieces straight from registers, with no LDS staging and no barrier,
 // while the next tile's DMA is in flight.
-template <int BM, int BN, int WGM, int WGN>
+//
+// RING: as in the forward kernel, B runs in a ring of three stages and A
+// in two (all 160 KB of LDS): the B DMA of step s + 2 goes into the B stage
+// of step s - 1 and is spread over substeps 0 .. KS-2 of step s, and only
+// A's DMA follows the tile barrier, whose wait then leaves those B loads
+// in flight. After a tile's stores the barrier waits for everything
+// (loads and stores retire out of order with each other).
+template <int BM, int BN, int WGM, int WGN, bool RING = true>
 __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
   typedef bf16x8 Frag;
   constexpr int NW = WGM * WGN;
@@ -1312,13 +1292,15 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
-  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int SB = RING ? 3 : 2;  // B stages (A: 2)
+  constexpr int B_BASE = 2 * A_BYTES;
   // DMA instructions per wave and k-tile (1 KB each)
   constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW;
-  constexpr int N_LOAD = A_INS + B_INS;
+  constexpr int N_LOAD = A_INS + B_INS, NBL = B_INS;
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile shape");
   static_assert(BM >= 128 && BN >= 128 && BM <= 512 && BN <= 512, "tile shape");
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  static_assert(2 * A_BYTES + SB * B_BYTES <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * A_BYTES + SB * B_BYTES];
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -1364,7 +1346,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
   // ch ^ (4 (k & 3)). The resource ends with the group's rows, so k-rows
   // past them read zeros; live = false (past the last step) reads zeros
   // only.
-  auto issue_one = [&](const Cur& c, bool live, int st, int d) {
+  auto issue_one = [&](const Cur& c, bool live, int sa, int sb, int d) {
     const bool is_a = d < A_INS;
     const int jd = is_a ? d : d - A_INS;
     const int cpk = (is_a ? BM : BN) / 8;  // chunks per k-row
@@ -1375,7 +1357,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
     const long ld = is_a ? p.lda : p.ldb;
     const int r0 = is_a ? c.m0 : c.n0;
     const char* base = (const char*)(is_a ? p.A : p.B) + ((long)kbase * ld + r0) * 2;
-    char* dst = lds + st * STAGE + (is_a ? 0 : A_BYTES) + (jd * NW + wave) * 1024;
+    char* dst = (is_a ? lds + sa * A_BYTES : lds + B_BASE + sb * B_BYTES) +
+                (jd * NW + wave) * 1024;
     dma16(make_rsrc_n(base, ((long)rows_left * ld - r0) * 2), dst,
           kr * (int)ld * 2 + ch * 16, 0);
   };
@@ -1403,12 +1386,12 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
   constexpr int N_READ = MB + NB;
   constexpr int N_MFMA = MB * NB;
   constexpr ReadOrder<MB, NB, 1, (N_MFMA >= 8)> kOrder{};
-  auto read_one = [&](const char* sb, int ks, Frags& f, int m) {
+  auto read_one = [&](const char* pa, const char* pb, int ks, Frags& f, int m) {
     const int r = kOrder.r[m];
     if (r < MB)
-      f.a[r] = read_km(sb, BM, wm * WM + r * 32, ks);
+      f.a[r] = read_km(pa, BM, wm * WM + r * 32, ks);
     else
-      f.b[r - MB] = read_km(sb + A_BYTES, BN, wn * WN + (r - MB) * 32, ks);
+      f.b[r - MB] = read_km(pb, BN, wn * WN + (r - MB) * 32, ks);
   };
 
   f32x16 acc[MB][NB];
@@ -1468,15 +1451,15 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
   // prologue: steps 0 and 1 into stages 0 and 1, the load cursor at step 2
   Cur cl = cc;
 #pragma unroll
-  for (int d = 0; d < N_LOAD; ++d) issue_one(cl, true, 0, d);
+  for (int d = 0; d < N_LOAD; ++d) issue_one(cl, true, 0, 0, d);
   bool live = next_step(cl);
 #pragma unroll
-  for (int d = 0; d < N_LOAD; ++d) issue_one(cl, live, 1, d);
+  for (int d = 0; d < N_LOAD; ++d) issue_one(cl, live, 1, 1, d);
   live = live && next_step(cl);
   tile_barrier<N_LOAD>();
   Frags fa, fb;
 #pragma unroll
-  for (int r = 0; r < N_READ; ++r) read_one(lds, 0, fa, r);
+  for (int r = 0; r < N_READ; ++r) read_one(lds, lds + B_BASE, 0, fa, r);
 
   // One region per k-substep, as the backward kernel's: the substep's
   // MFMAs with the next substep's fragment reads (and, at the last, the
@@ -1486,23 +1469,39 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
   // before (loads and stores retire out of order with each other).
   constexpr int H = N_MFMA >= 8 ? 2 : 1;
 #define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
-  int st = 0;
+  int sa = 0;                                   // A stage of step s
+  int sbt = 0, sbt_next = 1, sbt_prev = SB - 1;  // B stages of steps s, s+1, s-1
+  bool stores_out = false;  // a tile's stores issued since the last full wait
   for (;;) {
-    const char* sb = lds + st * STAGE;
-    const char* sb_next = lds + (st ^ 1) * STAGE;
+    const char* pa = lds + sa * A_BYTES;
+    const char* pa_next = lds + (sa ^ 1) * A_BYTES;
+    const char* pb = lds + B_BASE + sbt * B_BYTES;
+    const char* pb_next = lds + B_BASE + sbt_next * B_BYTES;
     static_for<KS>([&](auto ks_c) {
       constexpr int ks = decltype(ks_c)::value;
       Frags& cur = (ks & 1) ? fb : fa;
       Frags& nxt = (ks & 1) ? fa : fb;
       constexpr bool last = ks + 1 == KS;
+      // memory ops of this region: N_READ reads and the DMA instructions
+      // [d_lo, d_hi) of step s + 2 (with the ring: A's after the barrier,
+      // a share of B's at each earlier substep; else all after it)
       constexpr int NM_MAX = N_READ + N_LOAD;
-      constexpr int nm = last ? NM_MAX : N_READ;
+      constexpr int d_lo = !RING || last ? 0 : A_INS + ks * NBL / (KS - 1);
+      constexpr int d_hi = !RING ? (last ? N_LOAD : 0)
+                           : last ? A_INS
+                                  : A_INS + (ks + 1) * NBL / (KS - 1);
+      constexpr int nm = N_READ + d_hi - d_lo;
       MOE_FENCE();
 #pragma unroll
       for (int q = 0; q < H; ++q) mfma_one(cur, q);
       MOE_FENCE();
       if constexpr (last) {
-        tile_barrier<0>();
+        if (!RING || stores_out) {
+          tile_barrier<0>();
+          stores_out = false;
+        } else {
+          tile_barrier<NBL>();
+        }
         MOE_FENCE();
       }
       int m = 0;
@@ -1512,14 +1511,14 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
 #pragma unroll
         for (int mm = 0; mm < NM_MAX; ++mm) {
           if (mm < m || mm >= m_end) continue;
-          if constexpr (!last) {
-            read_one(sb, ks + 1, nxt, mm);
-          } else {
-            const int rb = mm * N_READ / NM_MAX;
-            if ((mm + 1) * N_READ / NM_MAX != rb)
-              read_one(sb_next, 0, nxt, rb);
+          const int rb = mm * N_READ / nm;
+          if ((mm + 1) * N_READ / nm != rb) {
+            if constexpr (last)
+              read_one(pa_next, pb_next, 0, nxt, rb);
             else
-              issue_one(cl, live, st, mm - rb);
+              read_one(pa, pb, ks + 1, nxt, rb);
+          } else {
+            issue_one(cl, live, sa, RING ? sbt_prev : sbt, d_lo + mm - rb);
           }
           MOE_FENCE();
         }
@@ -1530,25 +1529,28 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
     });
     if (cc.kt + 1 == cc.nk) {
       store_tile(cc);
+      stores_out = true;
       ++cc.j;
       if (!start_tile(cc)) break;
     } else {
       ++cc.kt;
     }
     if (live) live = next_step(cl);
-    st ^= 1;
+    sa ^= 1;
+    sbt_prev = sbt;
+    sbt = sbt_next;
+    sbt_next = sbt_next + 1 == SB ? 0 : sbt_next + 1;
   }
 #undef MOE_FENCE
   __builtin_amdgcn_s_waitcnt(0);  // no load may still target LDS at exit
 }
 
-template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, bool KCAT,
-          int EPI, int SCHED, bool SKIP = false>
+template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int EPI, int SCHED>
 hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   const long tiles = launch_grid<BM, BN, SCHED>(p);
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mfma_gemm_t<BM, BN, WGM, WGN, A_KM, B_KM, KCAT, EPI, SCHED, SKIP>),
+  hipLaunchKernelGGL((mfma_gemm_t<BM, BN, WGM, WGN, A_KM, B_KM, EPI, SCHED>),
                      dim3((unsigned)tiles), dim3(WGM * WGN * kWave), 0, s, p);
   return hipGetLastError();
 }
@@ -1607,13 +1609,13 @@ int num_cus() {
 
 // the persistent weight-gradient kernel: one workgroup per CU (fewer when
 // there are fewer tiles)
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, bool RING = true>
 hipError_t launch_wgrad(const GemmParams& p, hipStream_t s) {
   const long tiles = (long)p.G * ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
   const long grid = tiles < num_cus() ? tiles : num_cus();
-  hipLaunchKernelGGL((mfma_wgrad<BM, BN, WGM, WGN>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((mfma_wgrad<BM, BN, WGM, WGN, RING>), dim3((unsigned)grid),
                      dim3(WGM * WGN * kWave), 0, s, p);
   return hipGetLastError();
 }
@@ -1727,11 +1729,12 @@ bool mfma_supported(GemmOp op, const GemmParams& p) {
 }
 
 // MOE_WGRAD_PERSIST=0 keeps the weight gradients on the tile-per-workgroup
-// backward kernel, for comparison
-bool wgrad_persist() {
-  static const bool v = [] {
+// backward kernel, 2 runs the persistent one without its B ring, for
+// comparison
+int wgrad_persist() {
+  static const int v = [] {
     const char* e = tuning_env("MOE_WGRAD_PERSIST");
-    return !(e && strcmp(e, "0") == 0);
+    return e ? atoi(e) : 1;
   }();
   return v;
 }
@@ -1883,17 +1886,18 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   // backward products on the direct-to-LDS kernel with k-major operands
   if (!force_staged()) {
     if (op == kOpWgrad && big && wgrad_persist())
-      return launch_wgrad<256, 256, 2, 4>(p, s);
+      return wgrad_persist() == 2 ? launch_wgrad<256, 256, 2, 4, false>(p, s)
+                                  : launch_wgrad<256, 256, 2, 4>(p, s);
     if (op == kOpWgrad)  // (the big form only for comparison)
-      return !big ? launch_t<128, 128, 2, 2, true, true, false, kEpiStore, kSchedK>(p, s)
-                  : launch_t<256, 256, 2, 4, true, true, false, kEpiStore, kSchedK>(p, s);
+      return !big ? launch_t<128, 128, 2, 2, true, true, kEpiStore, kSchedK>(p, s)
+                  : launch_t<256, 256, 2, 4, true, true, kEpiStore, kSchedK>(p, s);
     // router backward: dx += d_logits Wr (Wr read k-major as stored), and
     // fp32 partial sums of d_logits^T x over token ranges
     if (op == kOpRouterDx)
-      return launch_t<128, 128, 2, 2, false, true, false, kEpiAccum, kSchedM>(p, s);
+      return launch_t<128, 128, 2, 2, false, true, kEpiAccum, kSchedM>(p, s);
     if (op == kOpRouterDw)
-      return !big ? launch_t<128, 128, 2, 2, true, true, false, kEpiStoreF32, kSchedK>(p, s)
-                  : launch_t<256, 256, 2, 4, true, true, false, kEpiStoreF32, kSchedK>(p, s);
+      return !big ? launch_t<128, 128, 2, 2, true, true, kEpiStoreF32, kSchedK>(p, s)
+                  : launch_t<256, 256, 2, 4, true, true, kEpiStoreF32, kSchedK>(p, s);
   }
   if (op == kOpGemm1Mx)
     return skip || tskip
