@@ -526,7 +526,19 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
   constexpr int kEpiRows = BM > 128 ? 128 : BM;
   constexpr int EPI_BYTES =
       StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>::BYTES;
-  __shared__ __attribute__((aligned(1024))) char lds[RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES];
+  // TACC: the bf16-output products other than the quantising one take the
+  // MFMA operands swapped and accumulate C^T (element r of lane l: row
+  // l % 32, column 8 (r / 4) + 4 (l / 32) + r % 4 of the 32 x 32 block), so
+  // the epilogue hands 8-column row pieces straight from registers to the
+  // stores after one swap of lane halves per pair of register quads, with
+  // no LDS staging and no barrier. Not the 4-wave big tile (it would
+  // spill), and not the SwiGLU backward, whose loads of the saved a and b
+  // would come in 32-byte row pieces instead of whole rows (dgrad2 13%
+  // slower on the Mixtral shape)
+  constexpr bool TACC = !MX && sizeof(TO) == 2 && EPI != kEpiSwigluMx &&
+                        EPI != kEpiSwigluBwd && !(NW == 4 && BM == 256);
+  __shared__ __attribute__((aligned(1024))) char
+      lds[TACC || RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES];
 
   // the tile; grouped contraction (SCHED K): k-tiles [kt0, kt0 + nk) of
   // the group's range, which the host pads to whole k-tiles
@@ -760,6 +772,9 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
       acc[o][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           f.a[i], f.b[o][j], acc[o][i][j], 0, 0, 0, (int)sc[i], 0,
           (int)sc[MB + o * NB + j]);
+    } else if constexpr (TACC) {
+      acc[o][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          f.b[o][j], f.a[i], acc[o][i][j], 0, 0, 0);
     } else {
       acc[o][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           f.a[i], f.b[o][j], acc[o][i][j], 0, 0, 0);
@@ -921,9 +936,46 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
 #undef MOE_FENCE
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load may still target LDS at exit
-  // through LDS in 16-byte row pieces: the output (SwiGLU of the two
-  // accumulators, or the plain product), then any saved pre-activations
+  // 16-byte row pieces, through LDS or (TACC) straight from registers: the
+  // output (SwiGLU of the two accumulators, or the plain product), then
+  // any saved pre-activations. value(i, j, r) is element r of block (i, j);
+  // store(row, col, v) takes 8 consecutive columns of one tile row.
   using SO = StageOut<BM, BN, WM, WN, MB, NB, NW * kWave, kEpiRows>;
+  auto out = [&](auto value, auto store, int rows) {
+    if constexpr (TACC) {
+      // quads 2 pr and 2 pr + 1 hold columns 16 pr + 4 half .. +3 and
+      // 16 pr + 8 + 4 half .. +3 of row l % 32; after the swap lane l < 32
+      // holds 16 pr + 8 .. +15 and lane l + 32 holds 16 pr .. +7
+      const int half = lane / 32;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        if (wm * WM + i * 32 >= rows) continue;  // (wave-uniform)
+        const int row = wm * WM + i * 32 + lane % 32;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          float x[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[r] = value(i, j, r);
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const auto sw = __builtin_amdgcn_permlane32_swap(
+                  __builtin_bit_cast(uint32_t, x[4 * (2 * pr + 1) + e]),
+                  __builtin_bit_cast(uint32_t, x[4 * (2 * pr) + e]), false, false);
+              x[4 * (2 * pr + 1) + e] = __builtin_bit_cast(float, (uint32_t)sw[0]);
+              x[4 * (2 * pr) + e] = __builtin_bit_cast(float, (uint32_t)sw[1]);
+            }
+            const float v[8] = {x[8 * pr + 4], x[8 * pr + 5], x[8 * pr + 6], x[8 * pr + 7],
+                                x[8 * pr], x[8 * pr + 1], x[8 * pr + 2], x[8 * pr + 3]};
+            store(row, wn * WN + j * 32 + 16 * pr + (half ? 0 : 8), v);
+          }
+        }
+      }
+    } else {
+      SO::run(lds, wm, wn, lane, value, store, rows);
+    }
+  };
   if constexpr (EPI == kEpiSwigluMx) {
     // h through LDS in rows of the tile; each thread then quantises one
     // whole 32-column block of a row: its amax in registers, 32 codes in
@@ -998,25 +1050,21 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
     };
     if constexpr (EPI == kEpiSwiglu) {
       if (p.C)
-        SO::run(lds, wm, wn, lane,
-                [&](int i, int j, int r) {
-                  const float a = acc[0][i][j][r], b = acc[NB_OPS - 1][i][j][r];
-                  return a * fast_sigmoid(a) * b;
-                },
-                put((TO*)p.C), t.m_end - t.m0);
+        out([&](int i, int j, int r) {
+              const float a = acc[0][i][j][r], b = acc[NB_OPS - 1][i][j][r];
+              return a * fast_sigmoid(a) * b;
+            },
+            put((TO*)p.C), t.m_end - t.m0);
       if (p.C2)
-        SO::run(lds, wm, wn, lane,
-                [&](int i, int j, int r) { return acc[0][i][j][r]; },
-                put((TO*)p.C2), t.m_end - t.m0);
+        out([&](int i, int j, int r) { return acc[0][i][j][r]; }, put((TO*)p.C2),
+            t.m_end - t.m0);
       if (p.C3)
-        SO::run(lds, wm, wn, lane,
-                [&](int i, int j, int r) { return acc[NB_OPS - 1][i][j][r]; },
-                put((TO*)p.C3), t.m_end - t.m0);
+        out([&](int i, int j, int r) { return acc[NB_OPS - 1][i][j][r]; },
+            put((TO*)p.C3), t.m_end - t.m0);
     } else if constexpr (EPI == kEpiSwigluBwd) {
       // dh = acc; (da, db) from the pre-activations a, b (bf16, ld = ldc),
       // which may share their buffers with da, db
-      SO::run(lds, wm, wn, lane,
-              [&](int i, int j, int r) { return acc[0][i][j][r]; },
+      out([&](int i, int j, int r) { return acc[0][i][j][r]; },
               [&](int row, int col, const float* v) {
                 const int grow = t.m0 + row, gcol = t.n0 + col;
                 if (grow >= t.m_end || gcol >= p.N) return;
@@ -1035,9 +1083,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_dl(GemmParams p) 
                 *(bf16x8*)((bf16*)p.C2 + o) = pack8(db);
               }, t.m_end - t.m0);
     } else {
-      SO::run(lds, wm, wn, lane,
-              [&](int i, int j, int r) { return acc[0][i][j][r]; },
-              put((TO*)p.C + (SCHED == kSchedK ? (long)t.g * p.sC : 0)), t.m_end - t.m0);
+      out([&](int i, int j, int r) { return acc[0][i][j][r]; },
+          put((TO*)p.C + (SCHED == kSchedK ? (long)t.g * p.sC : 0)), t.m_end - t.m0);
     }
   }
 }
