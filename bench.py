@@ -37,9 +37,9 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (the fp32 path runs on VALU)
 # the kernel built from sources with this digest and nothing else.
 GEMM1_TRAFFIC = {
     "workload": "mixtral8x7b_T8192_d4096_f14336_E8_K2",
-    "src_digest": "2b40473a4bde1fd9",
-    "fetch_bytes": 13_238_364_160,
-    "write_bytes": 469_762_048,
+    "src_digest": "521ad5d213860814",
+    "fetch_bytes": 12_902_324_224,
+    "write_bytes": 470_102_016,
 }
 GEMM_SOURCES = ("gemm_mfma.hip", "common.h", "gemm.h", "tile_map.h")
 
