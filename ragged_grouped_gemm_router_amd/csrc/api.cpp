@@ -559,7 +559,7 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     const uint8_t* hq = (const uint8_t*)a->h;
     MOE_TRY(launch_dequantize_mxfp8(hq, hq + (size_t)TK * f, TK, f, w.h_bf, s));
     GemmParams p = gp();
-    p.M = dm; p.N = f; p.G = E; p.off = a->offsets;
+    p.M = dm; p.N = f; p.G = E; p.off = a->offsets; p.k_total = TK;
     p.A = w.dy_perm; p.lda = dm;
     p.B = w.h_bf; p.ldb = f;
     p.C = a->dw2; p.ldc = f; p.sC = (long)dm * f;
@@ -569,7 +569,7 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
     MOE_TRY(launch_dequantize_mxfp8(w.shq, w.shs, T, fs, w.sh, s));
     MOE_TRY(launch_dequantize_mxfp8(w.sxq, w.sxs, T, dm, w.sx_bf, s));
     GemmParams p = gp();
-    p.M = dm; p.N = fs; p.G = 1; p.off = w.srange;
+    p.M = dm; p.N = fs; p.G = 1; p.off = w.srange; p.k_total = d->T;
     p.A = a->dy; p.lda = dm;
     p.B = w.sh; p.ldb = fs;
     p.C = a->dws2; p.ldc = fs;
@@ -582,14 +582,14 @@ hipError_t do_backward_mx(const moe_desc* d, const moe_bwd_args* a, void* ws,
                                   TK, dm, w.dx_perm, s));
   for (int which = 0; which < 2; ++which) {
     GemmParams p = gp();
-    p.M = f; p.N = dm; p.G = E; p.off = a->offsets;
+    p.M = f; p.N = dm; p.G = E; p.off = a->offsets; p.k_total = TK;
     p.A = which ? w.db : w.da; p.lda = f;
     p.B = w.dx_perm; p.ldb = dm;
     p.C = which ? a->dw3 : a->dw1; p.ldc = dm; p.sC = (long)f * dm;
     MOE_TRY(run_gemm(kOpWgrad, MOE_BF16, p, w.tile_off, s));
     if (shared) {  // dWs1 = da_s^T x, dWs3 = db_s^T x (x as quantised)
       GemmParams q = gp();
-      q.M = fs; q.N = dm; q.G = 1; q.off = w.srange;
+      q.M = fs; q.N = dm; q.G = 1; q.off = w.srange; q.k_total = d->T;
       q.A = which ? w.sb : w.sa; q.lda = fs;
       q.B = w.sx_bf; q.ldb = dm;
       q.C = which ? a->dws3 : a->dws1; q.ldc = dm;
@@ -1125,7 +1125,7 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
   record(a->events[5], s);
   {  // dW2_e = dy_perm_e^T h_e
     GemmParams p = gp();
-    p.M = dm; p.N = f; p.G = E; p.off = a->offsets;
+    p.M = dm; p.N = f; p.G = E; p.off = a->offsets; p.k_total = TK;
     p.A = w.dy_perm; p.lda = dm;
     p.B = a->h; p.ldb = f;
     p.C = a->dw2; p.ldc = f; p.sC = (long)dm * f;
@@ -1133,7 +1133,7 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
   }
   if (shared) {  // dWs2 = dy^T h_s
     GemmParams p = gp();
-    p.M = dm; p.N = fs; p.G = 1; p.off = w.srange;
+    p.M = dm; p.N = fs; p.G = 1; p.off = w.srange; p.k_total = d->T;
     p.A = a->dy; p.lda = dm;
     p.B = w.sh; p.ldb = fs;
     p.C = a->dws2; p.ldc = fs;
@@ -1142,14 +1142,14 @@ moe_status moe_backward(const moe_desc* d, const moe_bwd_args* a, void* ws,
   record(a->events[6], s);
   for (int which = 0; which < 2; ++which) {  // dW1_e = da^T x_perm, dW3_e
     GemmParams p = gp();
-    p.M = f; p.N = dm; p.G = E; p.off = a->offsets;
+    p.M = f; p.N = dm; p.G = E; p.off = a->offsets; p.k_total = TK;
     p.A = which ? w.db : w.da; p.lda = f;
     p.B = a->x_perm; p.ldb = dm;
     p.C = which ? a->dw3 : a->dw1; p.ldc = dm; p.sC = (long)f * dm;
     MOE_TRY(run_gemm(kOpWgrad, dt, p, w.tile_off, s));
     if (shared) {  // dWs1 = da_s^T x, dWs3 = db_s^T x
       GemmParams q = gp();
-      q.M = fs; q.N = dm; q.G = 1; q.off = w.srange;
+      q.M = fs; q.N = dm; q.G = 1; q.off = w.srange; q.k_total = d->T;
       q.A = which ? w.sb : w.sa; q.lda = fs;
       q.B = a->x; q.ldb = dm;
       q.C = which ? a->dws3 : a->dws1; q.ldc = dm;

@@ -124,6 +124,9 @@ struct GemmParams {
   // for the split of a partial last round into quarter tiles; 0 = no
   // split, -1 = the device's CU count (resolved by the launcher)
   int slots;
+  // kSchedK: the rows contracted over all groups (the sum of the group
+  // ranges), a hint for the kernel choice known on the host; 0 = unknown
+  long k_total;
 };
 
 }  // namespace moe

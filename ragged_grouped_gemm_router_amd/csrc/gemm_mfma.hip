@@ -1331,7 +1331,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_gemm_t(GemmParams p) {
 // A's DMA follows the tile barrier, whose wait then leaves those B loads
 // in flight. After a tile's stores the barrier waits for everything
 // (loads and stores retire out of order with each other).
-template <int BM, int BN, int WGM, int WGN, bool RING = true>
+template <int BM, int BN, int WGM, int WGN, bool RING = true, int DW = WGM * WGN>
 __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
   typedef bf16x8 Frag;
   constexpr int NW = WGM * WGN;
@@ -1393,11 +1393,10 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
   // ch ^ (4 (k & 3)). The resource ends with the group's rows, so k-rows
   // past them read zeros; live = false (past the last step) reads zeros
   // only.
-  auto issue_one = [&](const Cur& c, bool live, int sa, int sb, int d) {
-    const bool is_a = d < A_INS;
-    const int jd = is_a ? d : d - A_INS;
+  static_assert(NW % DW == 0 && DW >= 1, "DMA waves");
+  auto issue_one = [&](const Cur& c, bool live, int sa, int sb, bool is_a, int jd) {
     const int cpk = (is_a ? BM : BN) / 8;  // chunks per k-row
-    const int kr = (jd * NW + wave) * (64 / cpk) + lane / cpk;
+    const int kr = (jd * DW + wave) * (64 / cpk) + lane / cpk;
     const int ch = (lane % cpk) ^ (4 * (kr & 3));
     const int kbase = c.k_beg + c.kt * BK;
     const int rows_left = live ? c.k_end - kbase : 0;
@@ -1405,7 +1404,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
     const int r0 = is_a ? c.m0 : c.n0;
     const char* base = (const char*)(is_a ? p.A : p.B) + ((long)kbase * ld + r0) * 2;
     char* dst = (is_a ? lds + sa * A_BYTES : lds + B_BASE + sb * B_BYTES) +
-                (jd * NW + wave) * 1024;
+                (jd * DW + wave) * 1024;
     dma16(make_rsrc_n(base, ((long)rows_left * ld - r0) * 2), dst,
           kr * (int)ld * 2 + ch * 16, 0);
   };
@@ -1495,100 +1494,121 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
   Cur cc;
   cc.j = 0;
   if (!start_tile(cc)) return;
-  // prologue: steps 0 and 1 into stages 0 and 1, the load cursor at step 2
-  Cur cl = cc;
-#pragma unroll
-  for (int d = 0; d < N_LOAD; ++d) issue_one(cl, true, 0, 0, d);
-  bool live = next_step(cl);
-#pragma unroll
-  for (int d = 0; d < N_LOAD; ++d) issue_one(cl, live, 1, 1, d);
-  live = live && next_step(cl);
-  tile_barrier<N_LOAD>();
-  Frags fa, fb;
-#pragma unroll
-  for (int r = 0; r < N_READ; ++r) read_one(lds, lds + B_BASE, 0, fa, r);
 
-  // One region per k-substep, as the backward kernel's: the substep's
-  // MFMAs with the next substep's fragment reads (and, at the last, the
-  // DMA of step s + 2 into this step's stage, after the barrier that ends
-  // every wave's reads of it) spread among them. The barrier waits for
-  // everything outstanding: step s + 1's DMA and any stores of the tile
-  // before (loads and stores retire out of order with each other).
-  constexpr int H = N_MFMA >= 8 ? 2 : 1;
+  // DW < NW: only waves 0 .. DW-1 issue the DMA (NW / DW times their share
+  // each). The others never wait for the vector-memory counter, so their
+  // tile barrier waits for no stores of theirs; the barrier still releases
+  // only once the DMA waves have their loads (and their own stores) done.
+  auto run = [&](auto role) {
+    constexpr bool DMAW = decltype(role)::value;
+    constexpr int AI = DMAW ? A_INS * NW / DW : 0;  // A / B DMA per wave and step
+    constexpr int BI = DMAW ? B_INS * NW / DW : 0;
+    constexpr int NL = AI + BI;
+    auto issue = [&](const Cur& c, bool live, int sa_, int sb_, int d) {
+      if constexpr (DMAW) issue_one(c, live, sa_, sb_, d < AI, d < AI ? d : d - AI);
+    };
+    auto barrier_n = [&](auto n) {  // wait for this wave's DMA, leaving n
+      if constexpr (DMAW) tile_barrier<decltype(n)::value>();
+      else tile_barrier<63>();  // (LDS reads only)
+    };
+    // prologue: steps 0 and 1 into stages 0 and 1, the load cursor at step 2
+    Cur cl = cc;
+#pragma unroll
+    for (int d = 0; d < NL; ++d) issue(cl, true, 0, 0, d);
+    bool live = next_step(cl);
+#pragma unroll
+    for (int d = 0; d < NL; ++d) issue(cl, live, 1, 1, d);
+    live = live && next_step(cl);
+    barrier_n(std::integral_constant<int, NL>{});
+    Frags fa, fb;
+#pragma unroll
+    for (int r = 0; r < N_READ; ++r) read_one(lds, lds + B_BASE, 0, fa, r);
+
+    // One region per k-substep, as the backward kernel's: the substep's
+    // MFMAs with the next substep's fragment reads (and the DMA of step
+    // s + 2) spread among them.
+    constexpr int H = N_MFMA >= 8 ? 2 : 1;
 #define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
-  int sa = 0;                                   // A stage of step s
-  int sbt = 0, sbt_next = 1, sbt_prev = SB - 1;  // B stages of steps s, s+1, s-1
-  bool stores_out = false;  // a tile's stores issued since the last full wait
-  for (;;) {
-    const char* pa = lds + sa * A_BYTES;
-    const char* pa_next = lds + (sa ^ 1) * A_BYTES;
-    const char* pb = lds + B_BASE + sbt * B_BYTES;
-    const char* pb_next = lds + B_BASE + sbt_next * B_BYTES;
-    static_for<KS>([&](auto ks_c) {
-      constexpr int ks = decltype(ks_c)::value;
-      Frags& cur = (ks & 1) ? fb : fa;
-      Frags& nxt = (ks & 1) ? fa : fb;
-      constexpr bool last = ks + 1 == KS;
-      // memory ops of this region: N_READ reads and the DMA instructions
-      // [d_lo, d_hi) of step s + 2 (with the ring: A's after the barrier,
-      // a share of B's at each earlier substep; else all after it)
-      constexpr int NM_MAX = N_READ + N_LOAD;
-      constexpr int d_lo = !RING || last ? 0 : A_INS + ks * NBL / (KS - 1);
-      constexpr int d_hi = !RING ? (last ? N_LOAD : 0)
-                           : last ? A_INS
-                                  : A_INS + (ks + 1) * NBL / (KS - 1);
-      constexpr int nm = N_READ + d_hi - d_lo;
-      MOE_FENCE();
-#pragma unroll
-      for (int q = 0; q < H; ++q) mfma_one(cur, q);
-      MOE_FENCE();
-      if constexpr (last) {
-        if (!RING || stores_out) {
-          tile_barrier<0>();
-          stores_out = false;
-        } else {
-          tile_barrier<NBL>();
-        }
+    int sa = 0;                                   // A stage of step s
+    int sbt = 0, sbt_next = 1, sbt_prev = SB - 1;  // B stages of steps s, s+1, s-1
+    bool stores_out = false;  // a tile's stores issued since the last full wait
+    for (;;) {
+      const char* pa = lds + sa * A_BYTES;
+      const char* pa_next = lds + (sa ^ 1) * A_BYTES;
+      const char* pb = lds + B_BASE + sbt * B_BYTES;
+      const char* pb_next = lds + B_BASE + sbt_next * B_BYTES;
+      static_for<KS>([&](auto ks_c) {
+        constexpr int ks = decltype(ks_c)::value;
+        Frags& cur = (ks & 1) ? fb : fa;
+        Frags& nxt = (ks & 1) ? fa : fb;
+        constexpr bool last = ks + 1 == KS;
+        // memory ops of this region: N_READ reads and the DMA instructions
+        // [d_lo, d_hi) of step s + 2 (with the ring: A's after the
+        // barrier, a share of B's at each earlier substep; else all after)
+        constexpr int NM_MAX = N_READ + NL;
+        constexpr int d_lo = !RING || last ? 0 : AI + ks * BI / (KS - 1);
+        constexpr int d_hi = !RING ? (last ? NL : 0)
+                             : last ? AI
+                                    : AI + (ks + 1) * BI / (KS - 1);
+        constexpr int nm = N_READ + d_hi - d_lo;
         MOE_FENCE();
-      }
-      int m = 0;
 #pragma unroll
-      for (int q = H; q < N_MFMA; ++q) {
-        const int m_end = (q - H + 1) * nm / (N_MFMA - H);
-#pragma unroll
-        for (int mm = 0; mm < NM_MAX; ++mm) {
-          if (mm < m || mm >= m_end) continue;
-          const int rb = mm * N_READ / nm;
-          if ((mm + 1) * N_READ / nm != rb) {
-            if constexpr (last)
-              read_one(pa_next, pb_next, 0, nxt, rb);
-            else
-              read_one(pa, pb, ks + 1, nxt, rb);
+        for (int q = 0; q < H; ++q) mfma_one(cur, q);
+        MOE_FENCE();
+        if constexpr (last) {
+          // the DMA of step s + 1 (with the ring, B's of step s + 2 may stay
+          // in flight); after a tile's stores everything
+          if (!RING || stores_out) {
+            barrier_n(std::integral_constant<int, 0>{});
+            stores_out = false;
           } else {
-            issue_one(cl, live, sa, RING ? sbt_prev : sbt, d_lo + mm - rb);
+            barrier_n(std::integral_constant<int, BI>{});
           }
           MOE_FENCE();
         }
-        m = m_end;
-        mfma_one(cur, q);
-        MOE_FENCE();
+        int m = 0;
+#pragma unroll
+        for (int q = H; q < N_MFMA; ++q) {
+          const int m_end = (q - H + 1) * nm / (N_MFMA - H);
+#pragma unroll
+          for (int mm = 0; mm < NM_MAX; ++mm) {
+            if (mm < m || mm >= m_end) continue;
+            const int rb = mm * N_READ / nm;
+            if ((mm + 1) * N_READ / nm != rb) {
+              if constexpr (last)
+                read_one(pa_next, pb_next, 0, nxt, rb);
+              else
+                read_one(pa, pb, ks + 1, nxt, rb);
+            } else {
+              issue(cl, live, sa, RING ? sbt_prev : sbt, d_lo + mm - rb);
+            }
+            MOE_FENCE();
+          }
+          m = m_end;
+          mfma_one(cur, q);
+          MOE_FENCE();
+        }
+      });
+      if (cc.kt + 1 == cc.nk) {
+        store_tile(cc);
+        stores_out = true;
+        ++cc.j;
+        if (!start_tile(cc)) break;
+      } else {
+        ++cc.kt;
       }
-    });
-    if (cc.kt + 1 == cc.nk) {
-      store_tile(cc);
-      stores_out = true;
-      ++cc.j;
-      if (!start_tile(cc)) break;
-    } else {
-      ++cc.kt;
+      if (live) live = next_step(cl);
+      sa ^= 1;
+      sbt_prev = sbt;
+      sbt = sbt_next;
+      sbt_next = sbt_next + 1 == SB ? 0 : sbt_next + 1;
     }
-    if (live) live = next_step(cl);
-    sa ^= 1;
-    sbt_prev = sbt;
-    sbt = sbt_next;
-    sbt_next = sbt_next + 1 == SB ? 0 : sbt_next + 1;
-  }
 #undef MOE_FENCE
+  };
+  if (DW == NW || wave < DW)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
   __builtin_amdgcn_s_waitcnt(0);  // no load may still target LDS at exit
 }
 
@@ -1656,13 +1676,13 @@ int num_cus() {
 
 // the persistent weight-gradient kernel: one workgroup per CU (fewer when
 // there are fewer tiles)
-template <int BM, int BN, int WGM, int WGN, bool RING = true>
+template <int BM, int BN, int WGM, int WGN, bool RING = true, int DW = WGM * WGN>
 hipError_t launch_wgrad(const GemmParams& p, hipStream_t s) {
   const long tiles = (long)p.G * ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
   const long grid = tiles < num_cus() ? tiles : num_cus();
-  hipLaunchKernelGGL((mfma_wgrad<BM, BN, WGM, WGN, RING>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((mfma_wgrad<BM, BN, WGM, WGN, RING, DW>), dim3((unsigned)grid),
                      dim3(WGM * WGN * kWave), 0, s, p);
   return hipGetLastError();
 }
@@ -1776,8 +1796,9 @@ bool mfma_supported(GemmOp op, const GemmParams& p) {
 }
 
 // MOE_WGRAD_PERSIST=0 keeps the weight gradients on the tile-per-workgroup
-// backward kernel, 2 runs the persistent one without its B ring, for
-// comparison
+// backward kernel, 2 runs the persistent one without its B ring, 3 and 4
+// with the DMA from half of the waves or from all of them whatever the
+// group sizes, for comparison
 int wgrad_persist() {
   static const int v = [] {
     const char* e = tuning_env("MOE_WGRAD_PERSIST");
@@ -1933,8 +1954,19 @@ hipError_t gemm_mfma(GemmOp op, GemmParams p,
   // backward products on the direct-to-LDS kernel with k-major operands
   if (!force_staged()) {
     if (op == kOpWgrad && big && wgrad_persist())
-      return wgrad_persist() == 2 ? launch_wgrad<256, 256, 2, 4, false>(p, s)
-                                  : launch_wgrad<256, 256, 2, 4>(p, s);
+    {
+      // DMA from half the waves when the groups average 256 rows or more
+      // (four k-steps and up per tile): the other half then passes each
+      // barrier without waiting for its stores (weight gradients of
+      // groups of ~550 to 2048 rows 5-8% faster). Groups of ~128 rows (two
+      // k-steps per tile) measured 3-5% slower that way, the doubled DMA
+      // issue of the loading waves no longer hidden between tiles.
+      const int v = wgrad_persist();
+      const bool half = v == 3 || (v == 1 && p.k_total >= 256L * (p.G > 0 ? p.G : 1));
+      return v == 2 ? launch_wgrad<256, 256, 2, 4, false>(p, s)
+             : half ? launch_wgrad<256, 256, 2, 4, true, 4>(p, s)
+                    : launch_wgrad<256, 256, 2, 4>(p, s);
+    }
     if (op == kOpWgrad)  // (the big form only for comparison)
       return !big ? launch_t<128, 128, 2, 2, true, true, kEpiStore, kSchedK>(p, s)
                   : launch_t<256, 256, 2, 4, true, true, kEpiStore, kSchedK>(p, s);
