@@ -49,6 +49,12 @@ CASES = [
     # N = f = 448, dgrad1: N = d = 320) whose DMA chunks past N are clamped
     mi.MoEConfig("kmajor_ragged_n_T1024_d320_f448_E8_K2", 1024, 320, 448, 8,
                  2),
+    # groups averaging 256 rows: the persistent weight-gradient kernel with
+    # its DMA from half of the waves, 288 tiles per product (more than one
+    # per workgroup on 256 CUs), partial row and column tiles (d = 576,
+    # f = 520), Zipf loads and empty experts
+    mi.MoEConfig("wgrad_half_dma_T4096_d576_f520_E32_K2", 4096, 576, 520, 32,
+                 2, synth_logits=True, n_zero=3, zipf_s=1.2),
 ]
 
 
