@@ -1454,12 +1454,12 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
   // 2 pr + 1 packed to bf16 (columns 16 pr + 4 half .. and 16 pr + 8 +
   // 4 half ..), lane halves swapped so that lane l < 32 holds columns
   // 16 pr + 8 .. +15 and lane l + 32 columns 16 pr .. +7 of row l
-  auto store_tile = [&](const Cur& c) {
+  // (inlined: a call would keep acc in scratch memory)
+  auto store_tile = [&](const Cur& c) __attribute__((always_inline)) {
     bf16* C = (bf16*)p.C + (long)c.g * p.sC;
     const int half = lane / 32;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const int row = c.m0 + wm * WM + i * 32 + lane % 32;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         uint32_t w[4][2];
@@ -1472,6 +1472,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
             w[q][h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                       ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
           }
+        u32x4 v[2];
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
 #pragma unroll
@@ -1481,10 +1482,25 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
             w[2 * pr + 1][h] = sw[0];
             w[2 * pr][h] = sw[1];
           }
-          const int col = c.n0 + wn * WN + j * 32 + 16 * pr + (half ? 0 : 8);
-          if (row < p.M && col < p.N)
-            *(u32x4*)(C + (long)row * p.ldc + col) =
-                u32x4{w[2 * pr + 1][0], w[2 * pr + 1][1], w[2 * pr][0], w[2 * pr][1]};
+          // columns 16 pr + 8 .. +15 of row lane % 32 (lanes 0-31), 16 pr ..
+          // +7 (lanes 32-63)
+          v[pr] = u32x4{w[2 * pr + 1][0], w[2 * pr + 1][1], w[2 * pr][0], w[2 * pr][1]};
+        }
+        // Swap the odd 16-lane rows of v[0] with the even ones of v[1]: v[0]
+        // then holds rows 0-15 of the block, v[1] rows 16-31, with lanes o,
+        // 16 + o, 32 + o, 48 + o holding columns 8, 24, 0, 16 (+0 .. 7) of
+        // row o. Each store then writes 16 rows x 64 bytes, not 32 x 32.
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const auto sw = __builtin_amdgcn_permlane16_swap(v[0][e], v[1][e], false, false);
+          v[0][e] = sw[0];
+          v[1][e] = sw[1];
+        }
+        const int col = c.n0 + wn * WN + j * 32 + 16 * ((lane >> 4) & 1) + (half ? 0 : 8);
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const int row = c.m0 + wm * WM + i * 32 + 16 * pr + lane % 16;
+          if (row < p.M && col < p.N) *(u32x4*)(C + (long)row * p.ldc + col) = v[pr];
         }
         acc[i][j] = f32x16{};
       }
