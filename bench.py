@@ -37,9 +37,9 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (the fp32 path runs on VALU)
 # the kernel built from sources with this digest and nothing else.
 GEMM1_TRAFFIC = {
     "workload": "mixtral8x7b_T8192_d4096_f14336_E8_K2",
-    "src_digest": "bb8110fcb7377867",
-    "fetch_bytes": 13_191_172_096,
-    "write_bytes": 470_080_512,
+    "src_digest": "3648892f22876e68",
+    "fetch_bytes": 13_497_974_784,
+    "write_bytes": 470_019_072,
 }
 GEMM_SOURCES = ("gemm_mfma.hip", "common.h", "gemm.h", "tile_map.h")
 
