@@ -1456,10 +1456,12 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
   // 16 pr + 8 .. +15 and lane l + 32 columns 16 pr .. +7 of row l
   // (inlined: a call would keep acc in scratch memory)
   auto store_tile = [&](const Cur& c) __attribute__((always_inline)) {
+    constexpr bool BFLY = NB == 2 && DW == NW;
     bf16* C = (bf16*)p.C + (long)c.g * p.sC;
     const int half = lane / 32;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
+      u32x4 vj[2][2];
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         uint32_t w[4][2];
@@ -1496,13 +1498,47 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void mfma_wgrad(GemmParams p) {
           v[0][e] = sw[0];
           v[1][e] = sw[1];
         }
-        const int col = c.n0 + wn * WN + j * 32 + 16 * ((lane >> 4) & 1) + (half ? 0 : 8);
+        if constexpr (!BFLY) {
+          const int col = c.n0 + wn * WN + j * 32 + 16 * ((lane >> 4) & 1) + (half ? 0 : 8);
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const int row = c.m0 + wm * WM + i * 32 + 16 * pr + lane % 16;
-          if (row < p.M && col < p.N) *(u32x4*)(C + (long)row * p.ldc + col) = v[pr];
+          for (int pr = 0; pr < 2; ++pr) {
+            const int row = c.m0 + wm * WM + i * 32 + 16 * pr + lane % 16;
+            if (row < p.M && col < p.N) *(u32x4*)(C + (long)row * p.ldc + col) = v[pr];
+          }
+        } else {
+          vj[j][0] = v[0];
+          vj[j][1] = v[1];
         }
         acc[i][j] = f32x16{};
+      }
+      if constexpr (BFLY) {
+        // exchange the column half (j) with lane bit 3 (rows o and o ^ 8 of
+        // a 16-lane row): register k then holds rows 16 pr + 8 k + lane % 8,
+        // all 64 columns (lane bit 3 the half), 8 rows x 128 bytes a store.
+        // Only where every wave waits for its stores at the next barrier
+        // (all waves issue DMA): there whole lines drain faster (DeepSeek-V3
+        // dW1 + dW3 5.12 -> 4.86 ms); with half of the waves loading, the
+        // extra exchange costs more than it saves (Mixtral, skewed and
+        // Qwen-MoE-like weight gradients 2-4% slower).
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const bool up = (lane & 8) != 0;
+          u32x4 n0, n1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t x1 = (uint32_t)__builtin_amdgcn_update_dpp(
+                0, (int)vj[1][pr][e], 0x128, 0xf, 0xf, false);  // row_ror:8
+            const uint32_t x0 = (uint32_t)__builtin_amdgcn_update_dpp(
+                0, (int)vj[0][pr][e], 0x128, 0xf, 0xf, false);
+            n0[e] = up ? x1 : vj[0][pr][e];
+            n1[e] = up ? vj[1][pr][e] : x0;
+          }
+          const int col = c.n0 + wn * WN + 32 * ((lane >> 3) & 1) + 16 * ((lane >> 4) & 1) +
+                          (half ? 0 : 8);
+          const int row0 = c.m0 + wm * WM + i * 32 + 16 * pr + (lane & 7);
+          if (row0 < p.M && col < p.N) *(u32x4*)(C + (long)row0 * p.ldc + col) = n0;
+          if (row0 + 8 < p.M && col < p.N) *(u32x4*)(C + (long)(row0 + 8) * p.ldc + col) = n1;
+        }
       }
     }
   };
