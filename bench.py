@@ -37,9 +37,9 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (the fp32 path runs on VALU)
 # the kernel built from sources with this digest and nothing else.
 GEMM1_TRAFFIC = {
     "workload": "mixtral8x7b_T8192_d4096_f14336_E8_K2",
-    "src_digest": "3648892f22876e68",
-    "fetch_bytes": 13_497_974_784,
-    "write_bytes": 470_019_072,
+    "src_digest": "03584a3f922ad71f",
+    "fetch_bytes": 13_179_877_376,
+    "write_bytes": 469_981_184,
 }
 GEMM_SOURCES = ("gemm_mfma.hip", "common.h", "gemm.h", "tile_map.h")
 
